@@ -1,0 +1,157 @@
+/*
+ * libw4a16 -- W4A16 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ *   y[M, N] = x[M, K] . dequant(Wq)^T (+ bias[N])
+ *
+ * The operation is the one the page "[ROCm][Kernel] Add
+ * HybridW4A16LinearKernel: Triton prefill + HIP skinny decode" describes in
+ * its description: fp16/bf16 activations, 4-bit weights packed eight per
+ * int32 in an [N, K/8] tensor shared by the decode and prefill paths,
+ * symmetric uint4b8 (w = (q - 8) * s) or asymmetric uint4 (w = (q - zp) * s)
+ * with one scale (and zero point) per row and group of 32, 64 or 128
+ * consecutive k; small M goes to a skinny decode kernel, larger M to a
+ * dequantising GEMM.  Zero points are packed int32 [N/8, G], eight rows per
+ * word, as the page "Upstream sync 67/N: merge 382bbd5144
+ * HybridW4A16LinearKernel (conflict)" states in the section "Upstream's Python
+ * side is kept -- and it does NOT work here".
+ *
+ * Layout contract (all tensors contiguous, row-major):
+ *   wq     int32  [N, K/8]  word j of row n holds k = 8j .. 8j+7; nibble t
+ *                           (bits 4t..4t+3) holds k-offset (0,2,4,6,1,3,5,7)[t].
+ *                           Bits are unsigned (int32 or uint32 storage).
+ *   zp     int32  [N/8, G]  nibble i of word (r, j) is the zero point of row 8r+i
+ *                           and group j.  NULL selects symmetric uint4b8 (z = 8).
+ *   scales act    [N, G]    G = K / group_size.
+ *   x      act    [M, K]    y act [M, N]; bias act [N] or NULL.
+ *   act is fp16 (W4A16_F16) or bf16 (W4A16_BF16), one dtype for x, scales,
+ *   bias and y.
+ *
+ * Numerics: the library computes with the exact dequantised weights
+ * (q - z) * s, accumulates in fp32, adds the bias in fp32 and rounds each
+ * output once, to nearest-even, to the activation dtype.  w4a16_dequant
+ * returns (q - z) * s rounded once, to nearest-even, to the activation dtype.
+ *
+ * Conventions shared by every entry point:
+ *   - The caller owns every buffer.  The library keeps no pointer after a
+ *     call returns and allocates no device memory in any call.
+ *   - Device entry points are asynchronous on `stream` (a hipStream_t; NULL is
+ *     the default stream).  They never synchronise and make no HIP call that
+ *     is illegal during stream capture once a device has been initialised
+ *     (the first call on a device queries its properties).
+ *   - Errors are reported by the returned status and a thread-local message
+ *     (w4a16_last_error); the library never aborts and never prints.
+ *   - Only gfx950 is supported; other devices get W4A16_ERR_UNSUPPORTED.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_ABI_VERSION 1
+
+typedef enum w4a16_status {
+  W4A16_OK = 0,
+  W4A16_ERR_INVALID_ARG = 1,  /* bad shape, group size, NULL pointer, aliasing */
+  W4A16_ERR_UNSUPPORTED = 2,  /* device is not gfx950, or the case is outside the accept set */
+  W4A16_ERR_ALIGNMENT = 3,    /* a pointer is not aligned as required */
+  W4A16_ERR_DEVICE = 4,       /* a HIP runtime query failed */
+  W4A16_ERR_LAUNCH = 5,       /* a kernel launch failed */
+  W4A16_ERR_WORKSPACE = 6     /* workspace missing or smaller than w4a16_workspace_size */
+} w4a16_status;
+
+typedef enum w4a16_dtype { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype;
+
+typedef enum w4a16_path {
+  W4A16_PATH_AUTO = 0,  /* pick by M, N, K, group and dtype */
+  W4A16_PATH_GEMV = 1,  /* skinny split-K decode kernel (M <= W4A16_GEMV_MAX_M) */
+  W4A16_PATH_GEMM = 2   /* dequantise-into-LDS MFMA GEMM */
+} w4a16_path;
+
+/* Largest M the skinny decode kernel accepts. */
+#define W4A16_GEMV_MAX_M 64
+
+/* ABI version of the loaded library (W4A16_ABI_VERSION it was built with). */
+int w4a16_abi_version(void);
+
+/* Message describing the last failing call on this thread ("" after success).
+ * Valid until the next library call on the same thread. */
+const char* w4a16_last_error(void);
+
+/* ---------------------------------------------------------------- host ---
+ * Host-side packing, run once per weight.  Buffers are host memory owned by
+ * the caller.  q and zp values must lie in 0..15.
+ *
+ * w4a16_pack_weights:   q uint8 [N, K] -> wq int32 [N, K/8]; K % 8 == 0.
+ * w4a16_unpack_weights: the inverse (every 32-bit word is valid input).
+ * w4a16_pack_zeros:     z uint8 [N, G] -> zpk int32 [N/8, G]; N % 8 == 0.
+ * w4a16_unpack_zeros:   the inverse.
+ * Errors: W4A16_ERR_INVALID_ARG on NULL pointers, negative sizes, sizes not
+ * divisible as stated, or a code above 15 (nothing is written then).
+ */
+w4a16_status w4a16_pack_weights(const uint8_t* q, int64_t N, int64_t K, int32_t* wq);
+w4a16_status w4a16_unpack_weights(const int32_t* wq, int64_t N, int64_t K, uint8_t* q);
+w4a16_status w4a16_pack_zeros(const uint8_t* z, int64_t N, int64_t G, int32_t* zpk);
+w4a16_status w4a16_unpack_zeros(const int32_t* zpk, int64_t N, int64_t G, uint8_t* z);
+
+/* Validates the arguments of w4a16_linear without touching any device.
+ * Rules: group_size in {32, 64, 128} (the pages' accept set); K >= group_size
+ * and K % group_size == 0; N >= 1; N % 8 == 0 when zp != NULL; M >= 0;
+ * dtype is W4A16_F16 or W4A16_BF16; x, wq, scales, y non-NULL when M > 0;
+ * x and wq 16-byte aligned, scales/bias/y 2-byte aligned, zp 4-byte aligned;
+ * y must not overlap x, wq, scales, zp or bias. */
+w4a16_status w4a16_check_args(const void* x, const int32_t* wq, const void* scales,
+                              const int32_t* zp, const void* bias, const void* y,
+                              int64_t M, int64_t N, int64_t K, int32_t group_size,
+                              int32_t dtype);
+
+/* The path W4A16_PATH_AUTO resolves to for this problem (host only). */
+w4a16_path w4a16_select_path(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                             int32_t dtype, int32_t has_zp);
+
+/* Workspace bytes w4a16_linear needs for this problem and path (AUTO allowed).
+ * 0 means none.  The workspace must be zero-filled before its first use; every
+ * completed call leaves it zero-filled again, so it can be reused by later
+ * calls on the same stream.  Calls that overlap in time must not share one. */
+size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                            int32_t dtype, int32_t has_zp, int32_t path);
+
+/* -------------------------------------------------------------- device ---
+ * y = x . dequant(wq, scales, zp)^T (+ bias), on the current HIP device,
+ * asynchronously on `stream`.  All pointers are device pointers.  M == 0 is a
+ * no-op.  `workspace` may be NULL when w4a16_workspace_size(...) is 0.
+ * Errors: any w4a16_check_args error; W4A16_ERR_UNSUPPORTED on a device that
+ * is not gfx950; W4A16_ERR_WORKSPACE; W4A16_ERR_DEVICE; W4A16_ERR_LAUNCH. */
+w4a16_status w4a16_linear(const void* x, const int32_t* wq, const void* scales,
+                          const int32_t* zp, const void* bias, void* y,
+                          int64_t M, int64_t N, int64_t K, int32_t group_size,
+                          int32_t dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* w4a16_linear with the path forced (tests and the dispatch sweep).
+ * W4A16_PATH_GEMV with M > W4A16_GEMV_MAX_M is W4A16_ERR_UNSUPPORTED. */
+w4a16_status w4a16_linear_path(const void* x, const int32_t* wq, const void* scales,
+                               const int32_t* zp, const void* bias, void* y,
+                               int64_t M, int64_t N, int64_t K, int32_t group_size,
+                               int32_t dtype, void* workspace, size_t workspace_bytes,
+                               void* stream, int32_t path);
+
+/* Dequantised weights w[N, K] (activation dtype): (q - z) * s rounded once to
+ * nearest-even.  Device pointers; same layout rules as w4a16_linear. */
+w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t* zp,
+                           void* w, int64_t N, int64_t K, int32_t group_size,
+                           int32_t dtype, void* stream);
+
+/* The 4-bit codes q[N, K] (uint8, 0..15) unpacked on the device from wq. */
+w4a16_status w4a16_unpack_device(const int32_t* wq, uint8_t* q, int64_t N, int64_t K,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,176 @@
+// Device-side building blocks shared by the W4A16 kernels (gfx950 only).
+//
+// Weight words follow the layout of include/w4a16.h: nibble t of a word holds
+// k-offset (0,2,4,6,1,3,5,7)[t], so (w >> 4i) & 0x000F000F places the
+// consecutive pair (k = 2i, 2i+1) in the low and high 16-bit halves.
+//
+// Dequantisation uses the exponent-OR ("magic number") trick named in the
+// description of "[ROCm][Kernel] Add HybridW4A16LinearKernel: Triton prefill
+// + HIP skinny decode": OR-ing a nibble into the mantissa of a power of two
+// whose unit in the last place is 1 yields magic + q exactly, with no integer
+// to float conversion.  fp16 uses 1024 (0x6400), bf16 uses 128 (0x4300).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+template <int DT>
+struct Magic;
+template <>
+struct Magic<DT_F16> {
+  static constexpr uint32_t pair = 0x64006400u;  // two fp16 1024.0
+  static constexpr uint32_t neg = 0xE400u;       // fp16 -1024.0; OR a nibble z for -(1024+z)
+  static constexpr float value = 1024.0f;
+};
+template <>
+struct Magic<DT_BF16> {
+  static constexpr uint32_t pair = 0x43004300u;  // two bf16 128.0
+  static constexpr uint32_t neg = 0xC300u;       // bf16 -128.0; OR a nibble z for -(128+z)
+  static constexpr float value = 128.0f;
+};
+
+// magic + q for the weight pair (k = 2i, 2i+1) of a word, as two act values
+template <int DT>
+__device__ __forceinline__ uint32_t magic_pair(uint32_t w, int i) {
+  return ((w >> (4 * i)) & 0x000F000Fu) | Magic<DT>::pair;
+}
+
+// -(magic + z) in both halves of a word
+template <int DT>
+__device__ __forceinline__ uint32_t neg_magic_pair(uint32_t z) {
+  const uint32_t h = Magic<DT>::neg | z;
+  return h | (h << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float act_to_f32(uint16_t b) {
+  if constexpr (DT == DT_F16) {
+    return (float)__builtin_bit_cast(_Float16, b);
+  } else {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+  }
+}
+
+// float32 -> activation dtype, round to nearest even (v_cvt_f16_f32 /
+// v_cvt_pk_bf16_f32 under the default rounding mode)
+template <int DT>
+__device__ __forceinline__ uint16_t f32_to_act(float f) {
+  if constexpr (DT == DT_F16) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+  } else {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t f32x2_to_act_pair(float lo, float hi) {
+  if constexpr (DT == DT_F16) {
+    half2_t h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+  } else {
+    bf16x2_t h = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+}
+
+// 16x16x32 MFMA, fp32 accumulate.  Operand layout (per lane l of the wave):
+//   A[i][k]: i = l % 16, k = 8 * (l / 16) + e, e = 0..7 (the 8 packed values)
+//   B[k][j]: j = l % 16, same k
+//   D[i][j]: j = l % 16, i = 4 * (l / 16) + r, r = 0..3
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == DT_F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+// 4x4 transpose of dwords across the four 16-lane rows of a wave:
+// on entry lane row j holds v[t] = element (j, t); on exit it holds (t, j).
+// Two rounds of row swaps: rows {0,1} <-> {2,3}, then odd <-> even rows.
+__device__ __forceinline__ void transpose_rows4(u32x4& v) {
+  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  v[0] = c[0];
+  v[1] = c[1];
+  v[2] = d[0];
+  v[3] = d[1];
+}
+
+// Exact dequantisation of one word (8 weights) to activation-dtype pairs:
+// out[i] holds k = 2i (low half) and 2i+1 (high half), each (q - z) * s
+// rounded once to nearest even.
+//   fp16: (magic + q) - (magic + z) is exact in fp16 (|q - z| <= 15), the
+//         product with s is one correctly rounded fp16 multiply.
+//   bf16: fma(128 + q, s, -(128 + z) * s) in fp32 is exact (both products fit
+//         in 16 significant bits and the result is a multiple of ulp(s)), then
+//         one nearest-even conversion to bf16.
+// s_pair: the scale in both halves (fp16 path); s_f32 / c_f32 = s and
+// -(128 + z) * s (bf16 path); nmz_pair = -(magic + z) in both halves.
+template <int DT>
+__device__ __forceinline__ void dequant_word_exact(uint32_t w, uint32_t s_pair, uint32_t nmz_pair,
+                                                   float s_f32, float c_f32, uint32_t out[4]) {
+  if constexpr (DT == DT_F16) {
+    const half2_t s2 = __builtin_bit_cast(half2_t, s_pair);
+    const half2_t nmz = __builtin_bit_cast(half2_t, nmz_pair);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2_t v = __builtin_bit_cast(half2_t, magic_pair<DT_F16>(w, i));
+      v = v + nmz;
+      v = v * s2;
+      out[i] = __builtin_bit_cast(uint32_t, v);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t t = w >> (4 * i);
+      const float lo = __builtin_bit_cast(float, ((t << 16) & 0x000F0000u) | 0x43000000u);
+      const float hi = __builtin_bit_cast(float, (t & 0x000F0000u) | 0x43000000u);
+      out[i] = f32x2_to_act_pair<DT_BF16>(__builtin_fmaf(lo, s_f32, c_f32),
+                                          __builtin_fmaf(hi, s_f32, c_f32));
+    }
+  }
+}
+
+// per (row, group) constants for dequant_word_exact
+template <int DT>
+struct GroupConst {
+  uint32_t s_pair;
+  uint32_t nmz_pair;
+  float s_f32;
+  float c_f32;
+};
+
+template <int DT>
+__device__ __forceinline__ GroupConst<DT> group_const(uint16_t s_bits, uint32_t z) {
+  GroupConst<DT> g;
+  g.s_pair = (uint32_t)s_bits | ((uint32_t)s_bits << 16);
+  g.nmz_pair = neg_magic_pair<DT>(z);
+  g.s_f32 = act_to_f32<DT>(s_bits);
+  // -(128 + z) * s is exact in fp32 (8 + 8 significant bits); used by bf16 only
+  g.c_f32 = -(128.0f + (float)z) * g.s_f32;
+  return g;
+}
+
+__device__ __forceinline__ uint32_t zero_point(const uint32_t* zp, int n, int G, int grp) {
+  return (zp[(size_t)(n >> 3) * G + grp] >> (4 * (n & 7))) & 0xFu;
+}
+
+}  // namespace w4a16

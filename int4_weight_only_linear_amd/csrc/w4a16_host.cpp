@@ -1,0 +1,350 @@
+// Host side of libw4a16: the C ABI declared in include/w4a16.h -- argument
+// validation, packing, a per-device property cache, path selection, and the
+// launch of the kernels on the caller's stream.
+//
+// Validation follows the accept set the pages describe for the kernel's
+// `can_implement` (quantisation type, activation dtype, group size and K
+// divisibility; "Upstream sync 67/N: merge 382bbd5144 HybridW4A16LinearKernel
+// (conflict)", reviewer's item 2), and the zero-point contract of the same
+// page's section "Upstream's Python side is kept -- and it does NOT work here".
+#include "w4a16.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "w4a16_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w4a16_status fail(w4a16_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+w4a16_status ok() {
+  g_last_error.clear();
+  return W4A16_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+// ---- per-device properties, filled once per device ------------------------
+struct DeviceInfo {
+  bool ready = false;
+  hipError_t err = hipSuccess;
+  bool gfx950 = false;
+  int cu_count = 0;
+  char arch[64] = {0};
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_device_mutex;
+
+w4a16_status device_info(const DeviceInfo** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W4A16_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(W4A16_ERR_DEVICE, "device ordinal %d out of range", dev);
+  DeviceInfo& d = g_devices[dev];
+  {
+    std::lock_guard<std::mutex> lock(g_device_mutex);
+    if (!d.ready) {
+      hipDeviceProp_t prop;
+      d.err = hipGetDeviceProperties(&prop, dev);
+      if (d.err == hipSuccess) {
+        std::snprintf(d.arch, sizeof(d.arch), "%s", prop.gcnArchName);
+        d.cu_count = prop.multiProcessorCount;
+        d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                   (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+      }
+      d.ready = true;
+    }
+  }
+  if (d.err != hipSuccess)
+    return fail(W4A16_ERR_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(d.err));
+  if (!d.gfx950)
+    return fail(W4A16_ERR_UNSUPPORTED, "libw4a16 supports gfx950 only; this device is %s", d.arch);
+  *out = &d;
+  return W4A16_OK;
+}
+
+size_t act_bytes(int64_t n) { return (size_t)n * 2; }
+
+bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
+
+// Decode-kernel threshold.  The pages route M <= 5 to their skinny kernel
+// (on RDNA); on MI355X the skinny kernel stays on the HBM roofline further,
+// so the crossover is a measured table rather than the pages' constant.
+int64_t gemv_threshold(int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t has_zp) {
+  (void)N; (void)K; (void)group; (void)dtype; (void)has_zp;
+  if (const char* env = std::getenv("W4A16_M_THRESHOLD")) {
+    const long v = std::strtol(env, nullptr, 10);
+    if (v >= 0 && v <= W4A16_GEMV_MAX_M) return v;
+  }
+  return 32;
+}
+
+w4a16_path resolve_path(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,
+                        int32_t has_zp, int32_t path) {
+  if (path == W4A16_PATH_GEMV || path == W4A16_PATH_GEMM) return (w4a16_path)path;
+  if (const char* env = std::getenv("W4A16_FORCE_PATH")) {
+    if (std::strcmp(env, "gemv") == 0) return W4A16_PATH_GEMV;
+    if (std::strcmp(env, "gemm") == 0) return W4A16_PATH_GEMM;
+  }
+  return M <= gemv_threshold(N, K, group, dtype, has_zp) ? W4A16_PATH_GEMV : W4A16_PATH_GEMM;
+}
+
+constexpr int kPlanningCUs = 256;  // MI355X; the launch plan uses the device's own count
+
+size_t workspace_for(int64_t M, int64_t N, int64_t K, w4a16_path path, int cu_count) {
+  if (M <= 0) return 0;
+  if (path == W4A16_PATH_GEMV) {
+    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, cu_count);
+    return w4a16::gemv_workspace_bytes(plan, M, N);
+  }
+  return w4a16::gemm_workspace_bytes(M, N, K, cu_count);
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("W4A16_LOG");
+    return e && *e && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, const int32_t* zp,
+                         const void* bias, void* y, int64_t M, int64_t N, int64_t K,
+                         int32_t group_size, int32_t dtype, void* workspace,
+                         size_t workspace_bytes, void* stream, int32_t path) {
+  w4a16_status st = w4a16_check_args(x, wq, scales, zp, bias, y, M, N, K, group_size, dtype);
+  if (st != W4A16_OK) return st;
+  if (path < W4A16_PATH_AUTO || path > W4A16_PATH_GEMM)
+    return fail(W4A16_ERR_INVALID_ARG, "unknown path %d", (int)path);
+  if (M == 0) return ok();
+  const DeviceInfo* dev = nullptr;
+  st = device_info(&dev);
+  if (st != W4A16_OK) return st;
+  const w4a16_path p = resolve_path(M, N, K, group_size, dtype, zp != nullptr, path);
+  if (p == W4A16_PATH_GEMV && M > W4A16_GEMV_MAX_M)
+    return fail(W4A16_ERR_UNSUPPORTED, "the decode kernel takes M <= %d, got M=%lld",
+                W4A16_GEMV_MAX_M, (long long)M);
+  const size_t need = workspace_for(M, N, K, p, dev->cu_count);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(W4A16_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+
+  w4a16::LinearArgs a{x, wq, scales, zp, bias, y, M, N, K, group_size, dtype};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p == W4A16_PATH_GEMV) {
+    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, dev->cu_count);
+    if (log_enabled())
+      std::fprintf(stderr,
+                   "[w4a16] gemv M=%lld N=%lld K=%lld g=%d %s %s tiles=%d splits=%d waves=%d\n",
+                   (long long)M, (long long)N, (long long)K, group_size,
+                   dtype == W4A16_F16 ? "f16" : "bf16", zp ? "asym" : "sym", plan.tiles,
+                   plan.splits, plan.waves);
+    e = w4a16::launch_gemv(a, plan, workspace, s);
+  } else {
+    if (log_enabled())
+      std::fprintf(stderr, "[w4a16] gemm M=%lld N=%lld K=%lld g=%d %s %s\n", (long long)M,
+                   (long long)N, (long long)K, group_size, dtype == W4A16_F16 ? "f16" : "bf16",
+                   zp ? "asym" : "sym");
+    e = w4a16::launch_gemm(a, workspace, dev->cu_count, s);
+  }
+  if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char* w4a16_last_error(void) { return g_last_error.c_str(); }
+
+// nibble t of a word holds k-offset (0,2,4,6,1,3,5,7)[t]; the inverse map:
+static const int kSlotOfKoff[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+
+w4a16_status w4a16_pack_weights(const uint8_t* q, int64_t N, int64_t K, int32_t* wq) {
+  if (!q || !wq) return fail(W4A16_ERR_INVALID_ARG, "pack_weights: NULL pointer");
+  if (N < 0 || K < 0 || K % 8) return fail(W4A16_ERR_INVALID_ARG, "pack_weights: need N >= 0, K >= 0, K %% 8 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
+  for (int64_t i = 0; i < N * K; ++i)
+    if (q[i] > 15) return fail(W4A16_ERR_INVALID_ARG, "pack_weights: code %u at %lld exceeds 15", (unsigned)q[i], (long long)i);
+  const int64_t J = K / 8;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t j = 0; j < J; ++j) {
+      const uint8_t* src = q + n * K + j * 8;
+      uint32_t w = 0;
+      for (int i = 0; i < 8; ++i) w |= (uint32_t)src[i] << (4 * kSlotOfKoff[i]);
+      wq[n * J + j] = (int32_t)w;
+    }
+  return ok();
+}
+
+w4a16_status w4a16_unpack_weights(const int32_t* wq, int64_t N, int64_t K, uint8_t* q) {
+  if (!q || !wq) return fail(W4A16_ERR_INVALID_ARG, "unpack_weights: NULL pointer");
+  if (N < 0 || K < 0 || K % 8) return fail(W4A16_ERR_INVALID_ARG, "unpack_weights: need N >= 0, K >= 0, K %% 8 == 0");
+  const int64_t J = K / 8;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t j = 0; j < J; ++j) {
+      const uint32_t w = (uint32_t)wq[n * J + j];
+      uint8_t* dst = q + n * K + j * 8;
+      for (int i = 0; i < 8; ++i) dst[i] = (uint8_t)((w >> (4 * kSlotOfKoff[i])) & 0xFu);
+    }
+  return ok();
+}
+
+w4a16_status w4a16_pack_zeros(const uint8_t* z, int64_t N, int64_t G, int32_t* zpk) {
+  if (!z || !zpk) return fail(W4A16_ERR_INVALID_ARG, "pack_zeros: NULL pointer");
+  if (N < 0 || G < 0 || N % 8) return fail(W4A16_ERR_INVALID_ARG, "pack_zeros: need N >= 0, G >= 0, N %% 8 == 0 (N=%lld)", (long long)N);
+  for (int64_t i = 0; i < N * G; ++i)
+    if (z[i] > 15) return fail(W4A16_ERR_INVALID_ARG, "pack_zeros: zero point %u at %lld exceeds 15", (unsigned)z[i], (long long)i);
+  for (int64_t r = 0; r < N / 8; ++r)
+    for (int64_t g = 0; g < G; ++g) {
+      uint32_t w = 0;
+      for (int i = 0; i < 8; ++i) w |= (uint32_t)z[(r * 8 + i) * G + g] << (4 * i);
+      zpk[r * G + g] = (int32_t)w;
+    }
+  return ok();
+}
+
+w4a16_status w4a16_unpack_zeros(const int32_t* zpk, int64_t N, int64_t G, uint8_t* z) {
+  if (!z || !zpk) return fail(W4A16_ERR_INVALID_ARG, "unpack_zeros: NULL pointer");
+  if (N < 0 || G < 0 || N % 8) return fail(W4A16_ERR_INVALID_ARG, "unpack_zeros: need N >= 0, G >= 0, N %% 8 == 0");
+  for (int64_t r = 0; r < N / 8; ++r)
+    for (int64_t g = 0; g < G; ++g) {
+      const uint32_t w = (uint32_t)zpk[r * G + g];
+      for (int i = 0; i < 8; ++i) z[(r * 8 + i) * G + g] = (uint8_t)((w >> (4 * i)) & 0xFu);
+    }
+  return ok();
+}
+
+w4a16_status w4a16_check_args(const void* x, const int32_t* wq, const void* scales,
+                              const int32_t* zp, const void* bias, const void* y, int64_t M,
+                              int64_t N, int64_t K, int32_t group_size, int32_t dtype) {
+  if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+    return fail(W4A16_ERR_INVALID_ARG, "activation dtype must be fp16 (0) or bf16 (1), got %d", (int)dtype);
+  if (!valid_group(group_size))
+    return fail(W4A16_ERR_UNSUPPORTED, "group size must be 32, 64 or 128, got %d", (int)group_size);
+  if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M must be >= 0, got %lld", (long long)M);
+  if (N < 1) return fail(W4A16_ERR_INVALID_ARG, "N must be >= 1, got %lld", (long long)N);
+  if (K < group_size || K % group_size)
+    return fail(W4A16_ERR_INVALID_ARG, "K must be a positive multiple of the group size %d, got K=%lld",
+                (int)group_size, (long long)K);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || M * K > INT64_MAX / 2 || N * K > INT64_MAX / 2)
+    return fail(W4A16_ERR_INVALID_ARG, "problem too large");
+  if (zp && N % 8)
+    return fail(W4A16_ERR_INVALID_ARG, "packed zero points need N %% 8 == 0, got N=%lld", (long long)N);
+  if (M == 0) return ok();
+  if (!x || !wq || !scales || !y) return fail(W4A16_ERR_INVALID_ARG, "x, wq, scales and y must not be NULL");
+  if (!aligned(x, 16)) return fail(W4A16_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  if (!aligned(wq, 16)) return fail(W4A16_ERR_ALIGNMENT, "wq must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(y, 2) || (bias && !aligned(bias, 2)))
+    return fail(W4A16_ERR_ALIGNMENT, "scales, bias and y must be 2-byte aligned");
+  if (zp && !aligned(zp, 4)) return fail(W4A16_ERR_ALIGNMENT, "zp must be 4-byte aligned");
+  const int64_t G = K / group_size;
+  const size_t ybytes = act_bytes(M * N);
+  if (overlap(y, ybytes, x, act_bytes(M * K)) || overlap(y, ybytes, wq, (size_t)N * (K / 8) * 4) ||
+      overlap(y, ybytes, scales, act_bytes(N * G)) ||
+      (zp && overlap(y, ybytes, zp, (size_t)(N / 8) * G * 4)) ||
+      (bias && overlap(y, ybytes, bias, act_bytes(N))))
+    return fail(W4A16_ERR_INVALID_ARG, "y must not overlap any input");
+  return ok();
+}
+
+w4a16_path w4a16_select_path(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t dtype,
+                             int32_t has_zp) {
+  return resolve_path(M, N, K, group_size, dtype, has_zp, W4A16_PATH_AUTO);
+}
+
+size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t dtype,
+                            int32_t has_zp, int32_t path) {
+  if (M <= 0 || N <= 0 || K <= 0 || !valid_group(group_size)) return 0;
+  const w4a16_path p = resolve_path(M, N, K, group_size, dtype, has_zp, path);
+  int cus = kPlanningCUs;
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    const DeviceInfo* d = nullptr;
+    if (device_info(&d) == W4A16_OK) cus = d->cu_count;
+    g_last_error.clear();
+  }
+  return workspace_for(M, N, K, p, cus);
+}
+
+w4a16_status w4a16_linear(const void* x, const int32_t* wq, const void* scales, const int32_t* zp,
+                          const void* bias, void* y, int64_t M, int64_t N, int64_t K,
+                          int32_t group_size, int32_t dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return linear_impl(x, wq, scales, zp, bias, y, M, N, K, group_size, dtype, workspace,
+                     workspace_bytes, stream, W4A16_PATH_AUTO);
+}
+
+w4a16_status w4a16_linear_path(const void* x, const int32_t* wq, const void* scales,
+                               const int32_t* zp, const void* bias, void* y, int64_t M, int64_t N,
+                               int64_t K, int32_t group_size, int32_t dtype, void* workspace,
+                               size_t workspace_bytes, void* stream, int32_t path) {
+  return linear_impl(x, wq, scales, zp, bias, y, M, N, K, group_size, dtype, workspace,
+                     workspace_bytes, stream, path);
+}
+
+w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t* zp, void* w,
+                           int64_t N, int64_t K, int32_t group_size, int32_t dtype, void* stream) {
+  if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+    return fail(W4A16_ERR_INVALID_ARG, "activation dtype must be fp16 (0) or bf16 (1), got %d", (int)dtype);
+  if (!valid_group(group_size))
+    return fail(W4A16_ERR_UNSUPPORTED, "group size must be 32, 64 or 128, got %d", (int)group_size);
+  if (N < 1 || K < group_size || K % group_size)
+    return fail(W4A16_ERR_INVALID_ARG, "need N >= 1 and K a positive multiple of the group size");
+  if (zp && N % 8) return fail(W4A16_ERR_INVALID_ARG, "packed zero points need N %% 8 == 0");
+  if (!wq || !scales || !w) return fail(W4A16_ERR_INVALID_ARG, "wq, scales and w must not be NULL");
+  if (!aligned(wq, 4) || !aligned(w, 16) || !aligned(scales, 2) || (zp && !aligned(zp, 4)))
+    return fail(W4A16_ERR_ALIGNMENT, "w must be 16-byte aligned, wq and zp 4-byte, scales 2-byte");
+  const DeviceInfo* dev = nullptr;
+  w4a16_status st = device_info(&dev);
+  if (st != W4A16_OK) return st;
+  hipError_t e = w4a16::launch_dequant(wq, scales, zp, w, N, K, group_size, dtype,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+w4a16_status w4a16_unpack_device(const int32_t* wq, uint8_t* q, int64_t N, int64_t K, void* stream) {
+  if (N < 0 || K < 0 || K % 8) return fail(W4A16_ERR_INVALID_ARG, "need N >= 0, K >= 0, K %% 8 == 0");
+  if (N == 0 || K == 0) return ok();
+  if (!wq || !q) return fail(W4A16_ERR_INVALID_ARG, "wq and q must not be NULL");
+  if (!aligned(wq, 4) || !aligned(q, 8)) return fail(W4A16_ERR_ALIGNMENT, "wq must be 4-byte and q 8-byte aligned");
+  const DeviceInfo* dev = nullptr;
+  w4a16_status st = device_info(&dev);
+  if (st != W4A16_OK) return st;
+  hipError_t e = w4a16::launch_unpack(wq, q, N, K, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

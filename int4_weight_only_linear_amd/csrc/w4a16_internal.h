@@ -1,0 +1,61 @@
+// Internal interface between the host library (argument checks, device cache,
+// dispatch) and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+struct LinearArgs {
+  const void* x;
+  const int32_t* wq;
+  const void* scales;
+  const int32_t* zp;  // NULL: symmetric
+  const void* bias;   // may be NULL
+  void* y;
+  int64_t M, N, K;
+  int group;
+  int dtype;
+};
+
+// ---- skinny decode kernel ------------------------------------------------
+// One workgroup owns 16 output rows (one MFMA column tile) and one K range
+// ("split"); its waves take the 128-wide k-steps of that range in turn and
+// are reduced through LDS.  With more than one split, each workgroup stores
+// fp32 partial sums and the last one to finish a row tile adds them up in
+// split order (counter in the workspace), so results are deterministic.  That
+// workgroup also zeroes the partial sums it consumed and its counter, so a
+// completed call leaves the whole workspace zero for the next one, whatever
+// its shape.
+constexpr int kGemvRowsPerTile = 16;
+constexpr int kGemvKStep = 128;       // k per wave step: 4 chunks of 32
+constexpr int kGemvMaxWaves = 16;     // 1024 threads
+constexpr int kGemvMaxMTiles = 4;     // M <= 64
+
+struct GemvPlan {
+  int tiles;             // ceil(N / 16)
+  int ksteps;            // ceil(K / 128)
+  int splits;            // K ranges per row tile
+  int ksteps_per_split;
+  int waves;             // waves per workgroup
+  int mtiles;            // 16-row M tiles (1, 2 or 4)
+};
+
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int cu_count);
+size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N);
+hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& p, void* workspace,
+                       hipStream_t stream);
+
+// ---- prefill GEMM ----------------------------------------------------------
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cu_count);
+hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipStream_t stream);
+
+// ---- elementwise -----------------------------------------------------------
+hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* zp, void* w,
+                          int64_t N, int64_t K, int group, int dtype, hipStream_t stream);
+hipError_t launch_unpack(const int32_t* wq, uint8_t* q, int64_t N, int64_t K,
+                         hipStream_t stream);
+
+}  // namespace w4a16

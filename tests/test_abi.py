@@ -1,0 +1,186 @@
+"""The C-ABI boundary on the host: the library loads, exports what the header
+declares, packs exactly as the oracle does, and validates arguments without a
+device.  No compute call reaches a GPU here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import int4_weight_only_linear_amd as L
+from int4_weight_only_linear_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_functions():
+    assert _declared_functions() == sorted(B.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version():
+    assert L.w4a16_abi_version() == 1
+    m = re.search(r"#define W4A16_ABI_VERSION (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == L.w4a16_abi_version()
+    m = re.search(r"#define W4A16_GEMV_MAX_M (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == L.GEMV_MAX_M
+
+
+# ---- packing: the library's C++ against the oracle --------------------------
+
+@pytest.mark.parametrize("N,K", [(1, 8), (8, 32), (37, 96), (256, 256), (64, 4096)])
+def test_pack_weights_matches_oracle(N, K):
+    q = np.random.default_rng(N * 7 + K).integers(0, 16, (N, K), dtype=np.uint8)
+    wq = L.w4a16_pack_weights(q)
+    assert np.array_equal(wq, O.pack_weights(q))
+    assert np.array_equal(L.w4a16_unpack_weights(wq), q)
+    assert np.array_equal(O.unpack_weights(wq), q)
+
+
+def test_unpack_weights_all_words_matches_oracle():
+    words = np.random.default_rng(3).integers(0, 2**32, (16, 64), dtype=np.uint64)
+    words = words.astype(np.uint32).view(np.int32)
+    assert np.array_equal(L.w4a16_unpack_weights(words), O.unpack_weights(words))
+    assert np.array_equal(L.w4a16_pack_weights(L.w4a16_unpack_weights(words)), words)
+
+
+@pytest.mark.parametrize("N,G", [(8, 1), (16, 3), (4096, 32)])
+def test_pack_zeros_matches_oracle(N, G):
+    z = np.random.default_rng(N + G).integers(0, 16, (N, G), dtype=np.uint8)
+    zpk = L.w4a16_pack_zeros(z)
+    assert np.array_equal(zpk, O.pack_zeros(z))
+    assert np.array_equal(L.w4a16_unpack_zeros(zpk), z)
+
+
+def test_pack_worked_words():
+    assert L.w4a16_pack_weights(np.arange(8, dtype=np.uint8)[None]).view(np.uint32)[0, 0] == 0x75316420
+    assert L.w4a16_pack_zeros(np.arange(8, dtype=np.uint8)[:, None]).view(np.uint32)[0, 0] == 0x76543210
+
+
+def test_pack_errors():
+    with pytest.raises(L.W4A16Error, match="exceeds 15"):
+        L.w4a16_pack_weights(np.full((1, 8), 16, dtype=np.uint8))
+    with pytest.raises(L.W4A16Error, match="K % 8"):
+        B._check(B.lib.w4a16_pack_weights(np.zeros(12, np.uint8).ctypes.data, 1, 12,
+                                          np.zeros(2, np.int32).ctypes.data))
+    with pytest.raises(L.W4A16Error, match="N % 8"):
+        B._check(B.lib.w4a16_pack_zeros(np.zeros(12, np.uint8).ctypes.data, 12, 1,
+                                        np.zeros(2, np.int32).ctypes.data))
+    with pytest.raises(L.W4A16Error, match="NULL"):
+        B._check(B.lib.w4a16_pack_weights(None, 1, 8, None))
+
+
+# ---- argument validation (host only: fake, never dereferenced pointers) -----
+
+P = 1 << 20  # a 256-byte aligned fake address; check_args never dereferences
+
+
+def _args(**kw):
+    a = dict(x=P, wq=2 * P, s=3 * P, zp=None, bias=None, y=4 * P, M=1, N=64, K=256, g=128, dt=1)
+    a.update(kw)
+    return a
+
+
+def _check(**kw):
+    a = _args(**kw)
+    return B.lib.w4a16_check_args(a["x"], a["wq"], a["s"], a["zp"], a["bias"], a["y"], a["M"],
+                                  a["N"], a["K"], a["g"], a["dt"])
+
+
+def test_check_args_accepts_valid():
+    assert _check() == 0
+    assert _check(zp=5 * P, bias=6 * P, dt=0, g=32, K=96, M=5) == 0
+    assert L.w4a16_last_error() == ""
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(g=16), 2, "group size"),
+    (dict(g=256), 2, "group size"),
+    (dict(K=200), 1, "multiple of the group"),
+    (dict(K=64, g=128), 1, "multiple of the group"),
+    (dict(N=0), 1, "N must be"),
+    (dict(M=-1), 1, "M must be"),
+    (dict(dt=2), 1, "dtype"),
+    (dict(zp=5 * P, N=60), 1, "N % 8"),
+    (dict(x=None), 1, "NULL"),
+    (dict(y=None), 1, "NULL"),
+    (dict(x=P + 8), 3, "x must be 16-byte"),
+    (dict(wq=2 * P + 4), 3, "wq must be 16-byte"),
+    (dict(s=3 * P + 1), 3, "2-byte"),
+    (dict(zp=5 * P + 2), 3, "zp must be 4-byte"),
+    (dict(y=P + 64), 1, "overlap"),            # y inside x
+    (dict(y=2 * P, x=P), 1, "overlap"),        # y on top of wq
+])
+def test_check_args_rejects(kw, status, msg):
+    assert _check(**kw) == status
+    assert msg in L.w4a16_last_error()
+
+
+def test_m_zero_is_accepted_without_pointers():
+    assert _check(M=0, x=None, wq=None, s=None, y=None) == 0
+
+
+def test_linear_rejects_before_touching_a_device():
+    # invalid arguments are reported by validation, before any HIP call
+    st = B.lib.w4a16_linear(P, 2 * P, 3 * P, None, None, 4 * P, 1, 64, 256, 48, 1, None, 0, None)
+    assert st == 2 and "group size" in L.w4a16_last_error()
+    st = B.lib.w4a16_linear_path(P, 2 * P, 3 * P, None, None, 4 * P, 1, 64, 256, 128, 1, None, 0,
+                                 None, 7)
+    assert st == 1 and "unknown path" in L.w4a16_last_error()
+
+
+def test_zero_point_dtype_message_is_the_pages():
+    torch = pytest.importorskip("torch")
+    golden = [l for l in open(os.path.join(GOLDEN, "zp_dtype_error.txt")) if not l.startswith("#")]
+    want = golden[0].strip()
+    x = torch.zeros(1, 256, dtype=torch.float16)
+    wq = torch.zeros(64, 32, dtype=torch.int32)
+    s = torch.zeros(64, 2, dtype=torch.float16)
+    zp = torch.zeros(64, 2, dtype=torch.float16)     # the unpacked contract the pages reject
+    with pytest.raises(RuntimeError) as e:
+        L.w4a16_linear(x, wq, s, zp, group_size=128)
+    assert str(e.value).startswith(want)
+    assert "torch.float16" in str(e.value)
+
+
+# ---- path selection and workspace sizing (host logic) -----------------------
+
+def test_select_path_by_m():
+    for M in (1, 2, 5, 8, 16, 32):
+        assert L.w4a16_select_path(M, 4096, 4096, 128, 1, 1) == L.PATH_GEMV
+    for M in (65, 128, 1920):
+        assert L.w4a16_select_path(M, 4096, 4096, 128, 1, 1) == L.PATH_GEMM
+
+
+def test_select_path_env_override(monkeypatch):
+    monkeypatch.setenv("W4A16_FORCE_PATH", "gemm")
+    assert L.w4a16_select_path(1, 4096, 4096, 128, 1, 1) == L.PATH_GEMM
+    monkeypatch.setenv("W4A16_FORCE_PATH", "gemv")
+    assert L.w4a16_select_path(128, 4096, 4096, 128, 1, 1) == L.PATH_GEMV
+
+
+def test_workspace_size():
+    # enough row tiles for every CU: no split, no workspace
+    assert L.w4a16_workspace_size(1, 28672, 4096, 128, 1, 1) == 0
+    # fewer row tiles than CUs: K is split and the workspace holds counters + partials
+    ws = L.w4a16_workspace_size(4, 2560, 9728, 128, 0, 0)
+    assert ws > 0
+    tiles = 2560 // 16
+    assert ws >= 256 * ((tiles * 4 + 255) // 256) + 2 * 4 * 2560 * 4
+    assert L.w4a16_workspace_size(0, 2560, 9728, 128, 0, 0) == 0
+    assert L.w4a16_workspace_size(128, 4096, 4096, 128, 1, 1, L.PATH_GEMM) == 0

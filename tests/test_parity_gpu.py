@@ -1,0 +1,260 @@
+"""GPU parity: libw4a16 (through its C ABI) against the CPU oracle.
+
+Integer work (device unpacking) and the dequantised weights are compared bit
+for bit; linear outputs within the stated tolerance (max|y - y_ref| <=
+5e-3 * max|y_ref| for bf16, 2e-3 for fp16), plus bit-exact properties
+(one-hot activations, all-eight weights, symmetric == asymmetric with zero
+point 8, power-of-two scaling, run-to-run determinism).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import make_case, CONFIGS
+from gpu_util import DeviceCase, assert_close, device_to_bits, note, oracle_rows, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import int4_weight_only_linear_amd as L  # noqa: E402  (fails loudly if the library is missing)
+
+GEMV, GEMM, AUTO = L.PATH_GEMV, L.PATH_GEMM, L.PATH_AUTO
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    note(f"[gpu] {request.node.nodeid}")
+
+
+def paths_for(M):
+    return (GEMV, GEMM) if M <= L.GEMV_MAX_M else (GEMM,)
+
+
+# ---- integer and dequantisation work: bit exact -----------------------------
+
+@pytest.mark.parametrize("N,K", [(8, 32), (37, 96), (256, 256), (4096, 14336)])
+def test_unpack_device_bit_exact(N, K):
+    q = np.random.default_rng(N + K).integers(0, 16, (N, K), dtype=np.uint8)
+    wq = torch.from_numpy(L.w4a16_pack_weights(q)).cuda()
+    got = L.w4a16_unpack_device(wq).cpu().numpy()
+    assert np.array_equal(got, O.unpack_weights(O.pack_weights(q)))
+    assert np.array_equal(got, q)
+
+
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("N,K", [(8, 128), (40, 384), (264, 1152)])
+def test_dequant_bit_exact(dt, sym, g, N, K):
+    c = make_case(1, N, K, g, dt, sym, False, seed=("dq", N, K, g, dt, sym))
+    d = DeviceCase(c)
+    w = device_to_bits(L.w4a16_dequant(d.wq, d.s, d.zp, group_size=g))
+    zpk = None if sym else O.pack_zeros(c.zp)
+    ref = O.dequant_act(O.pack_weights(c.q), c.s_bits, zpk, N, K, g, dt)
+    assert np.array_equal(w, ref)
+
+
+@pytest.mark.parametrize("name,dt,sym", [("llama", O.BF16, False), ("qwen", O.F16, True)])
+def test_dequant_bit_exact_full_layer(name, dt, sym):
+    K, N = (4096, 4096) if name == "llama" else (2560, 6144)
+    c = make_case(1, N, K, 128, dt, sym, False, seed=("dqfull", name))
+    d = DeviceCase(c)
+    w = device_to_bits(L.w4a16_dequant(d.wq, d.s, d.zp, group_size=128))
+    zpk = None if sym else O.pack_zeros(c.zp)
+    assert np.array_equal(w, O.dequant_act(O.pack_weights(c.q), c.s_bits, zpk, N, K, 128, dt))
+
+
+def test_dequant_scale_extremes_bit_exact():
+    # scales spanning the formats' range, including fp16 subnormal products
+    for dt in (O.F16, O.BF16):
+        c = make_case(1, 16, 128, 32, dt, False, False, seed=("dqx", dt))
+        rng = np.random.default_rng(11)
+        s = (2.0 ** rng.uniform(-14 if dt == O.F16 else -60, 10, c.s_bits.shape)).astype(np.float32)
+        c.s_bits = O.f32_to_act_bits(s, dt)
+        d = DeviceCase(c)
+        w = device_to_bits(L.w4a16_dequant(d.wq, d.s, d.zp, group_size=32))
+        assert np.array_equal(w, O.dequant_act(O.pack_weights(c.q), c.s_bits, O.pack_zeros(c.zp),
+                                               16, 128, 32, dt))
+
+
+# ---- linear: tolerance parity on grids that span tiles and ragged tails ------
+
+@pytest.mark.parametrize("path", [GEMV, GEMM, AUTO])
+def test_tiny_config(path):
+    # M=1, K=N=256, group 32, symmetric, fp16, no bias
+    c = make_case(1, 256, 256, 32, O.F16, True, False, seed=("tiny",))
+    assert_close(DeviceCase(c).run(path), oracle_rows(c), O.F16, "tiny")
+
+
+GRID = [
+    # (M, N, K, g)
+    (1, 8, 128, 32), (1, 40, 384, 128), (3, 264, 1152, 64), (5, 128, 4096, 128),
+    (16, 520, 640, 32), (17, 96, 512, 128), (40, 264, 1152, 64), (64, 136, 256, 32),
+    (70, 264, 1152, 128), (130, 200, 640, 64), (257, 136, 384, 32),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g", GRID)
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("sym,bias", [(True, False), (False, True)])
+def test_linear_grid(M, N, K, g, dt, sym, bias):
+    c = make_case(M, N, K, g, dt, sym, bias, seed=("grid", M, N, K, g, dt, sym, bias))
+    d = DeviceCase(c)
+    ref = oracle_rows(c)
+    for path in paths_for(M):
+        assert_close(d.run(path), ref, dt, f"path {path}")
+
+
+def test_ragged_n_not_multiple_of_eight_symmetric():
+    # symmetric weights allow any N; N = 13 leaves a partial row tile
+    for dt in (O.F16, O.BF16):
+        c = make_case(3, 13, 256, 64, dt, True, True, seed=("rag13", dt))
+        d = DeviceCase(c)
+        for path in (GEMV, GEMM):
+            assert_close(d.run(path), oracle_rows(c), dt, f"path {path}")
+
+
+def test_k_single_group_and_odd_chunks():
+    # K = 96 (three 32-k chunks: a partial 128-k step) and K = g
+    for K, g in ((96, 32), (32, 32), (64, 64), (128, 128), (160, 32)):
+        c = make_case(2, 24, K, g, O.BF16, False, False, seed=("kodd", K, g))
+        d = DeviceCase(c)
+        for path in (GEMV, GEMM):
+            assert_close(d.run(path), oracle_rows(c), O.BF16, f"K={K} path {path}")
+
+
+def test_m_zero_is_a_no_op():
+    c = make_case(1, 64, 256, 128, O.F16, True, False, seed=("m0",))
+    d = DeviceCase(c)
+    x0 = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    y = L.w4a16_linear(x0, d.wq, d.s, None, group_size=128)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 64)
+
+
+# ---- bit-exact properties ------------------------------------------------------
+
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("g", [32, 128])
+def test_one_hot_x_reproduces_dequantised_weight(dt, g):
+    N, K = 48, 512
+    c = make_case(1, N, K, g, dt, False, False, seed=("onehot", dt, g))
+    d = DeviceCase(c)
+    W = O.dequant_act(O.pack_weights(c.q), c.s_bits, O.pack_zeros(c.zp), N, K, g, dt)
+    one = 0x3C00 if dt == O.F16 else 0x3F80
+    for k in (0, 1, 6, 7, 8, 31, 32, 100, 255, 256, 511):
+        x = np.zeros((1, K), dtype=np.uint16)
+        x[0, k] = one
+        d.set_x(x)
+        for path in (GEMV, GEMM):
+            y = d.run(path)
+            assert np.array_equal(y[0], W[:, k]), f"k={k} path={path}"
+
+
+@pytest.mark.parametrize("path", [GEMV, GEMM])
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+def test_all_eights_symmetric_gives_bias(path, dt):
+    # every weight is (8 - 8) * s = +0.  The GEMM multiplies those zeros, and
+    # the fp16 decode kernel multiplies q - z = 0: both give the bias (or +0)
+    # bit for bit.  The bf16 decode kernel forms sum x*(128+q) - (128+z)*sum x
+    # in fp32, so it leaves a residue of the order of fp32 round-off.
+    for bias in (False, True):
+        c = make_case(4, 64, 512, 64, dt, True, bias, seed=("eights", bias, dt))
+        c.q[:] = 8
+        y = DeviceCase(c).run(path)
+        want = np.broadcast_to(c.bias_bits, y.shape) if bias else np.zeros_like(y)
+        if path == GEMV and dt == O.BF16:
+            err = np.abs(O.bf16_bits_to_f64(y) - O.bf16_bits_to_f64(want)).max()
+            assert err <= 1e-4
+        else:
+            assert np.array_equal(y, want)     # +0.0 exactly, no negative zeros
+
+
+@pytest.mark.parametrize("path", [GEMV, GEMM])
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+def test_symmetric_equals_asymmetric_with_eight(path, dt):
+    c = make_case(5, 128, 1024, 128, dt, True, True, seed=("se", dt))
+    y_sym = DeviceCase(c).run(path)
+    c.zp = np.full((128, 8), 8, dtype=np.uint8)
+    y_asym = DeviceCase(c).run(path)
+    assert np.array_equal(y_sym, y_asym)
+
+
+@pytest.mark.parametrize("path", [GEMV, GEMM])
+def test_power_of_two_scaling_is_exact(path):
+    c = make_case(3, 64, 1024, 128, O.F16, False, False, seed=("p2",))
+    y1 = O.f16_bits_to_f64(DeviceCase(c).run(path))
+    c.s_bits = O.f32_to_f16_bits(O.f16_bits_to_f64(c.s_bits).astype(np.float32) * 4)
+    y4 = O.f16_bits_to_f64(DeviceCase(c).run(path))
+    assert np.array_equal(y4, 4 * y1)
+
+
+def test_determinism_with_split_k():
+    # N = 2560 gives fewer row tiles than CUs, so K is split across workgroups
+    c = make_case(4, 2560, 9728, 128, O.BF16, False, False, seed=("det",))
+    d = DeviceCase(c)
+    a = d.run(GEMV)
+    for _ in range(3):
+        assert np.array_equal(d.run(GEMV), a)
+    assert_close(a, oracle_rows(c), O.BF16, "split-K")
+
+
+def test_workspace_reuse_across_shapes():
+    # one workspace shared by split-K calls of different shapes, in an order
+    # where a later call's counters sit where an earlier call's partial sums were
+    shapes = [(5, 264, 4096, 128), (4, 2560, 9728, 128), (2, 40, 1024, 64), (3, 1024, 4096, 32)]
+    cases = [make_case(M, N, K, g, O.BF16, False, False, seed=("reuse", M, N, K, g))
+             for (M, N, K, g) in shapes]
+    devs = [DeviceCase(c) for c in cases]
+    refs = [oracle_rows(c) for c in cases]
+    for _ in range(2):
+        for d, ref in zip(devs, refs):
+            assert_close(d.run(GEMV), ref, O.BF16, "reuse")
+
+
+def test_workspace_errors():
+    c = make_case(1, 2560, 9728, 128, O.BF16, False, False, seed=("ws",))
+    d = DeviceCase(c)
+    need = L.w4a16_workspace_size(1, 2560, 9728, 128, O.BF16, True, GEMV)
+    assert need > 0
+    y = torch.empty((1, 2560), dtype=torch.bfloat16, device="cuda")
+    from int4_weight_only_linear_amd import _binding as B
+    st = B.lib.w4a16_linear_path(d.x.data_ptr(), d.wq.data_ptr(), d.s.data_ptr(), d.zp.data_ptr(),
+                                 None, y.data_ptr(), 1, 2560, 9728, 128, O.BF16, None, 0,
+                                 torch.cuda.current_stream().cuda_stream, GEMV)
+    assert st == 6 and "workspace" in L.w4a16_last_error()
+
+
+# ---- the workloads at full size, on sampled output rows -----------------------
+
+def _config_points(name):
+    c = CONFIGS[name]
+    for li, layer in enumerate(c.layers):
+        for g in c.groups:
+            for sym in c.symmetric:
+                for dt in c.dtypes:
+                    for bias in c.bias:
+                        yield pytest.param(name, li, layer.K, layer.N, g, sym, dt, bias,
+                                           id=f"{name}-K{layer.K}-N{layer.N}-g{g}-{'sym' if sym else 'asym'}-{'f16' if dt == 0 else 'bf16'}{'-bias' if bias else ''}")
+
+
+ALL_POINTS = [p for n in ("llama8b_decode", "qwen3_4b_decode", "llama8b_prefill", "sweep")
+              for p in _config_points(n)]
+
+
+@pytest.mark.parametrize("name,li,K,N,g,sym,dt,bias", ALL_POINTS)
+def test_config_full_size(name, li, K, N, g, sym, dt, bias):
+    Ms = CONFIGS[name].Ms
+    c = make_case(max(Ms), N, K, g, dt, sym, bias, seed=(name, li, g, sym, dt, bias))
+    d = DeviceCase(c)
+    rows = sample_rows(N, seed=li)
+    full_x = c.x_bits
+    for M in Ms:
+        x = full_x[:M].copy()
+        d.set_x(x)
+        ref = oracle_rows(c, rows)
+        for path in (AUTO,) + paths_for(M):
+            y = d.run(path)
+            assert_close(y[:, rows], ref, dt, f"M={M} path={path}")
