@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 linear path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step = one decode token through the four W4A16 linear layers of a
+Llama-3.1-8B-shaped block (fused QKV 4096x6144, O 4096x4096, gate+up
+4096x28672, down 14336x4096; asymmetric uint4 with packed zero points,
+group 128, bf16 activations, M = 1).  Inputs are seeded synthetic tensors of
+those shapes (no checkpoint), resident in HBM before timing starts.  Each
+step reads a different copy of the weights from a pool larger than the
+256 MB Infinity Cache, so the weights stream from HBM as they do when
+consecutive layers differ.  The step's four launches are captured once per
+copy in a HIP graph and replayed, so the host's launch overhead is not
+measured.
+
+Printed: one JSON line with decode GB/s (algorithmic bytes / time), the
+roofline of the decode kernel (per-launch HIP-event durations over the timed
+steps), the prefill TFLOP/s at M = 1920 on the Llama-3.1-8B prefill layers,
+and the CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "decode HBM GB/s (% of peak) at M=1; prefill TFLOP/s (% MFMA peak) at M=1920"
+
+DECODE_LAYERS = ((4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096))  # (K, N)
+PREFILL_LAYERS = ((4096, 6144), (4096, 28672), (14336, 4096))
+GROUP = 128
+
+
+def decode_bytes(M, N, K, g, asym=True, bias=False):
+    """Algorithmic bytes of one call: weights, scales, packed zero points, x, y (+bias)."""
+    b = N * K // 2 + 2 * N * (K // g) + 2 * M * K + 2 * M * N
+    if asym:
+        b += (N // 8) * (K // g) * 4
+    if bias:
+        b += 2 * N
+    return b
+
+
+def build_layer(K, N, M, seed, device):
+    import torch
+    from synth import make_case
+    import int4_weight_only_linear_amd as L
+    c = make_case(M, N, K, GROUP, 1, False, False, seed=seed)
+    wq = torch.from_numpy(L.w4a16_pack_weights(c.q)).to(device)
+    zp = torch.from_numpy(L.w4a16_pack_zeros(c.zp)).to(device)
+    s = torch.from_numpy(c.s_bits.view(np.int16)).to(device).view(torch.bfloat16)
+    x = torch.from_numpy(c.x_bits.view(np.int16)).to(device).view(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    return dict(K=K, N=N, M=M, wq=wq, zp=zp, s=s, x=x, y=y, case=c)
+
+
+class Launcher:
+    """Pre-marshalled C calls (pointers resolved once) for capture and timing."""
+
+    def __init__(self, layer, wq, zp, s):
+        import torch
+        import int4_weight_only_linear_amd as L
+        from int4_weight_only_linear_amd import _binding as B
+        self.B = B
+        self.args = (layer["x"].data_ptr(), wq.data_ptr(), s.data_ptr(), zp.data_ptr(), None,
+                     layer["y"].data_ptr(), layer["M"], layer["N"], layer["K"], GROUP, L.W4A16_BF16)
+        need = L.w4a16_workspace_size(layer["M"], layer["N"], layer["K"], GROUP, L.W4A16_BF16, True)
+        self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=layer["x"].device) if need else None
+
+    def __call__(self, stream_ptr):
+        ws = None if self.ws is None else self.ws.data_ptr()
+        nbytes = 0 if self.ws is None else self.ws.numel()
+        self.B._check(self.B.lib.w4a16_linear(*self.args, ws, nbytes, stream_ptr))
+
+
+def time_graphs(graphs, steps, warmup):
+    import torch
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def capture(launch_lists, stream):
+    import torch
+    graphs = []
+    for launches in launch_lists:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            sp = torch.cuda.current_stream().cuda_stream
+            for fn in launches:
+                fn(sp)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def per_launch_durations(launch_lists, steps):
+    """Each launch bracketed by HIP events on its own stream: ms per layer."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    nl = len(launch_lists[0])
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nl)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        launches = launch_lists[i % len(launch_lists)]
+        for j, fn in enumerate(launches):
+            ev[i][j][0].record(stream)
+            fn(sp)
+            ev[i][j][1].record(stream)
+    torch.cuda.synchronize()
+    return [float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
+            for j in range(nl)]
+
+
+def cpu_baseline(layers_host, budget_s=30.0):
+    """The oracle (untuned) on this host: one decode step over the layers, 1 thread."""
+    import contextlib
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        ctx = contextlib.nullcontext()
+    total_bytes = 0
+    t_total = 0.0
+    done = []
+    with ctx:
+        for (K, N, c) in layers_host:
+            zpk = O.pack_zeros(c.zp)
+            wq = O.pack_weights(c.q)
+            t0 = time.perf_counter()
+            O.linear_ref(c.x_bits, wq, c.s_bits, zpk, None, c.M, N, K, GROUP, 1)
+            t_total += time.perf_counter() - t0
+            total_bytes += decode_bytes(c.M, N, K, GROUP)
+            done.append(f"{K}x{N}")
+            del wq, zpk
+            if t_total > budget_s:
+                break
+    return dict(value=total_bytes / t_total / 1e9, unit="GB/s", cores=1, kind="oracle",
+                seconds=round(t_total, 3),
+                sample=("oracle linear_ref (unpack + exact fp32 dequant + fp64 GEMV) over one M=1 "
+                        f"decode step, layers {', '.join(done)} (K x N), single thread; packing not timed"))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=0, help="weight copies in the rotation pool (0: >= 1 GiB)")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: libw4a16 has no multi-GPU path in this build "
+              "(the row- and column-parallel sharding of the layer is described, not built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    import int4_weight_only_linear_amd as L  # noqa: F401  (loads libw4a16; raises if missing)
+
+    # ---- decode: four layers at M = 1, weight copies rotated through HBM ----
+    layers = [build_layer(K, N, 1, ("bench-decode", K, N), dev) for (K, N) in DECODE_LAYERS]
+    set_bytes = sum(l["wq"].numel() * 4 + l["s"].numel() * 2 + l["zp"].numel() * 4 for l in layers)
+    copies = args.copies or max(2, math.ceil((1 << 30) / set_bytes))
+    pool = [[(l["wq"], l["zp"], l["s"]) for l in layers]]
+    for _ in range(copies - 1):
+        pool.append([(wq.clone(), zp.clone(), s.clone()) for (wq, zp, s) in pool[0]])
+    launch_lists = [[Launcher(l, *pool[c][i]) for i, l in enumerate(layers)] for c in range(copies)]
+    side = torch.cuda.Stream()
+    for fns in launch_lists[:1]:            # first calls: device query, outside capture
+        for fn in fns:
+            fn(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    graphs = capture(launch_lists, side)
+    ms_step = time_graphs(graphs, args.steps, args.warmup)
+    step_bytes = sum(decode_bytes(1, l["N"], l["K"], GROUP) for l in layers)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # per-launch kernel durations (same launches, eager, HIP events on the launch stream)
+    durs = per_launch_durations(launch_lists, args.steps)
+    per_layer = []
+    for l, d in zip(layers, durs):
+        b = decode_bytes(1, l["N"], l["K"], GROUP)
+        per_layer.append(dict(K=l["K"], N=l["N"], bytes=b, us=round(d * 1e3, 3),
+                              GBs=round(b / (d * 1e-3) / 1e9, 1),
+                              frac=round(b / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)))
+    mean_bytes = step_bytes / len(layers)
+    mean_ms = float(np.mean(durs))
+    achieved = mean_bytes / (mean_ms * 1e-3) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="gemv_kernel<bf16, M-tiles 1, group 128, asym>",
+                    mean_launch_us=round(mean_ms * 1e3, 3), bytes_per_launch=int(mean_bytes),
+                    per_layer=per_layer)
+
+    # ---- prefill: M = 1920 on the three prefill layers ----
+    prefill = None
+    if not args.no_prefill:
+        players = [build_layer(K, N, 1920, ("bench-prefill", K, N), dev) for (K, N) in PREFILL_LAYERS]
+        plaunch = [[Launcher(l, l["wq"], l["zp"], l["s"]) for l in players]]
+        for fn in plaunch[0]:
+            fn(torch.cuda.current_stream().cuda_stream)
+        pgraphs = capture(plaunch, side)
+        pms = time_graphs(pgraphs, args.prefill_steps, max(2, args.prefill_steps // 5))
+        pdurs = per_launch_durations(plaunch, args.prefill_steps)
+        flops = sum(2 * 1920 * N * K for (K, N) in PREFILL_LAYERS)
+        tflops = flops / (pms * 1e-3) / 1e12
+        prefill = dict(workload="Llama-3.1-8B-shaped prefill, M=1920, layers (K,N) "
+                                + ", ".join(f"({K},{N})" for K, N in PREFILL_LAYERS)
+                                + ", asym uint4 g128, bf16",
+                       ms_per_pass=round(pms, 4), tflops=round(tflops, 1),
+                       frac_of_peak=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                       peak_tflops=MFMA_BF16_PEAK_TFLOPS,
+                       per_layer=[dict(K=K, N=N, us=round(d * 1e3, 2),
+                                       tflops=round(2 * 1920 * N * K / (d * 1e-3) / 1e12, 1))
+                                  for (K, N), d in zip(PREFILL_LAYERS, pdurs)])
+        del players, plaunch, pgraphs
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        host_layers = [(l["K"], l["N"], l["case"]) for l in layers]
+        cpu = cpu_baseline(host_layers)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3.1-8B-shaped decode step, M=1: W4A16 layers (K,N) "
+                        + ", ".join(f"({K},{N})" for K, N in DECODE_LAYERS)
+                        + "; asymmetric uint4, packed int32 zero points, group 128, bf16",
+            "global_batch": 1,
+            "weight_copies": copies,
+            "weight_pool_bytes": int(set_bytes * copies),
+            "bytes_per_step": int(step_bytes),
+            "graph_replay": True,
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "prefill": prefill,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,6 +47,40 @@ __device__ __forceinline__ uint32_t magic_pair(uint32_t w, int i) {
   return ((w >> (4 * i)) & 0x000F000Fu) | Magic<DT>::pair;
 }
 
+// A 32-bit constant the compiler must keep in a VGPR.  gfx9 VOP3 encodings
+// take no literal constants and read at most one SGPR, so (w & mask) | magic
+// becomes a single v_and_or_b32 only when one of the two constants already
+// sits in a VGPR; otherwise the compiler splits it into v_and_b32 + v_or_b32.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+// The four magic pairs of one word: out[i] = magic + (k = 2i, 2i+1), three
+// shifts and four AND-ORs.  mask_v = vgpr_const(0x000F000F).
+template <int DT>
+__device__ __forceinline__ u32x4 magic_word(uint32_t w, uint32_t mask_v) {
+  return u32x4{(w & mask_v) | Magic<DT>::pair, ((w >> 4) & mask_v) | Magic<DT>::pair,
+               ((w >> 8) & mask_v) | Magic<DT>::pair, ((w >> 12) & mask_v) | Magic<DT>::pair};
+}
+
+// fp16 pair add on scalar words.  (Applying __builtin_bit_cast to an element
+// of an ext_vector in an unrolled loop was miscompiled by this compiler: the
+// later elements read the already-updated first one.  Keep such arithmetic
+// on scalars and build vectors from the results.)
+__device__ __forceinline__ uint32_t add_f16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) + __builtin_bit_cast(half2_t, b));
+}
+
+// fp16: the four pairs q - z of one word, exact: (1024 + q) + (-(1024 + z))
+__device__ __forceinline__ u32x4 qz_word_f16(uint32_t w, uint32_t mask_v, uint32_t nmz) {
+  constexpr uint32_t P = Magic<DT_F16>::pair;
+  const uint32_t p0 = (w & mask_v) | P, p1 = ((w >> 4) & mask_v) | P;
+  const uint32_t p2 = ((w >> 8) & mask_v) | P, p3 = ((w >> 12) & mask_v) | P;
+  return u32x4{add_f16x2(p0, nmz), add_f16x2(p1, nmz), add_f16x2(p2, nmz), add_f16x2(p3, nmz)};
+}
+
 // -(magic + z) in both halves of a word
 template <int DT>
 __device__ __forceinline__ uint32_t neg_magic_pair(uint32_t z) {

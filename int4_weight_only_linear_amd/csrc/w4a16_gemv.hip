@@ -1,33 +1,43 @@
-// Skinny split-K W4A16 decode kernel for gfx950 (M <= 64).
+// Skinny split-K W4A16 decode kernels for gfx950 (M <= 64).
 //
 // The pages' decode path ("[ROCm][Kernel] Add HybridW4A16LinearKernel: Triton
 // prefill + HIP skinny decode", description) is a split-K skinny GEMM for
-// small M that dequantises with the exponent-OR trick.  This kernel keeps the
-// split-K idea and the trick, and re-plans the rest for CDNA4:
+// small M that dequantises with the exponent-OR trick.  These kernels keep the
+// split-K idea and the trick, and re-plan the rest for CDNA4:
 //
-// * Work unit: 16 output rows (the MFMA column tile) x one 128-wide k-step.
-//   Each lane of a wave issues one 16-byte non-temporal load per k-step: lane
-//   (j = lane % 16, r = lane / 16) reads chunk r (32 k) of row n0 + j.  A
-//   4x4 dword transpose across the four 16-lane rows (permlane swaps) then
-//   leaves, in register t, word r of chunk t -- exactly the B operand layout
-//   of v_mfma_f32_16x16x32 for chunk t.
+// * Work unit: 16 output rows (one MFMA column tile) x one 128-wide k-step.
+//   Lane (j = lane % 16, r = lane / 16) issues one 16-byte non-temporal load
+//   per k-step, chunk r (32 k) of row n0 + j.  A 4x4 dword transpose across
+//   the four 16-lane rows (permlane swaps) then leaves, in register t, word r
+//   of chunk t -- exactly the B operand layout of v_mfma_f32_16x16x32 for
+//   chunk t, so every MFMA covers 32 k of one quantisation group.
 // * The scale is factored out of the dot product: per group the wave forms
-//   sum_k x[m,k] * (q[n,k] - z[n,g]) in fp32 and then adds s[n,g] times that
-//   sum into the accumulator.  For fp16, B = (1024 + q) - (1024 + z) is exact
-//   with one packed add per weight pair; bf16 has no packed add on gfx950, so
-//   it multiplies B = 128 + q (the AND-OR alone, exact) and removes the
-//   offset with a second MFMA against the constant B = -(128 + z).  Nothing
-//   is rounded to the activation dtype before the output, and no per-weight
-//   multiply by the scale is needed.
-// * x rows (M <= 16 per MFMA row tile, zero-padded) are read straight from
-//   global memory (L2-resident), so there is no LDS staging and no limit on
-//   K * M (the pages' converged kernel streams the overflow from global for
-//   the same reason, "[ROCm] Converge the two W4A16 linear kernels onto the
-//   upstream shell", "What this does").
-// * The waves of a workgroup take the k-steps of its K range in turn and are
-//   reduced through LDS in wave order; with several K ranges per row tile the
-//   partial sums go through the workspace and the last workgroup to arrive
-//   adds them in range order.  Results do not depend on scheduling.
+//   sum_k x[m,k] * (q[n,k] - z[n,g]) in fp32 and adds s[n,g] times it to the
+//   accumulator; nothing is rounded to the activation dtype before the output.
+//   B is built by the AND-OR alone (magic + q, exact).  fp16 removes the
+//   offset with one packed add per weight pair, (1024 + q) - (1024 + z), exact.
+//   bf16 has no packed add on gfx950, so it keeps B = 128 + q and subtracts
+//   (128 + z) * sum_k x[m,k] per group in fp32, the group sums of x being
+//   formed once per workgroup while x is staged.
+// * A workgroup owns one row tile and one K range.  Its waves take
+//   contiguous runs of k-steps and issue every load up front, x and the
+//   per-group scales and zero points first (staged in LDS, coalesced), then
+//   the weights; each k-step waits only for its own weights, so the dot
+//   products of early k-steps overlap the arrival of later ones.
+// * The host splits K across workgroups when there are fewer row tiles than
+//   CUs, or when a K range would not fit the LDS budget; so there is no limit
+//   on K * M (the pages' converged kernel likewise streams the overflow from
+//   global, "[ROCm] Converge the two W4A16 linear kernels onto the upstream
+//   shell", "What this does").
+// * Waves are reduced through LDS in wave order; with several K ranges per
+//   row tile the partial sums go through the workspace and the last workgroup
+//   to arrive adds them in range order.  Results do not depend on scheduling.
+//
+// gemv_small_kernel serves M <= 16 (one MFMA row tile).  gemv_wide_kernel
+// serves 16 < M <= 64 with up to four row tiles, reading the A operands from
+// global memory (L2-resident) instead of staging x.
+#include <type_traits>
+
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
 
@@ -47,106 +57,24 @@ struct GemvParams {
   int ksteps;   // ceil(nchunks / 4)
   int ksteps_per_split;
   int splits;
+  int kpw;      // k-steps per wave (contiguous runs)
 };
 
-template <int DT, int MT, int GS, bool ASYM>
-__global__ __launch_bounds__(1024) void gemv_kernel(const GemvParams p) {
-  constexpr int CPG = GS / 32;  // 32-k chunks per quantisation group (1, 2 or 4)
-  constexpr int NEL = MT * 256;  // accumulator elements per wave
-  __shared__ float red[kGemvMaxWaves * NEL];
-  __shared__ int last_flag;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  const int col = lane & 15;  // MFMA column = output row within the tile
-  const int row4 = lane >> 4;  // 16-lane row of the wave
-  const int tile = blockIdx.x;
-  const int split = blockIdx.y;
-  const int n = tile * kGemvRowsPerTile + col;
-  const bool nvalid = n < p.N;
-  const uint32_t* wrow = p.wq + (size_t)(nvalid ? n : 0) * (p.K >> 3);
-  const uint16_t* srow = p.scales + (size_t)(nvalid ? n : 0) * p.G;
-
-  const int ks_begin = split * p.ksteps_per_split;
-  const int ks_end = min(p.ksteps, ks_begin + p.ksteps_per_split);
-
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int ks = ks_begin + wave; ks < ks_end; ks += nwaves) {
-    const int c0 = ks * 4;
-    u32x4 wv = {0u, 0u, 0u, 0u};
-    if (nvalid && c0 + row4 < p.nchunks)
-      wv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (size_t)(c0 + row4) * 4));
-    transpose_rows4(wv);
-
-    f32x4 tmp[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) tmp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint32_t bc = neg_magic_pair<DT>(8u);
-
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = c0 + t;
-      if (c >= p.nchunks) break;
-      const int grp = c / CPG;
-      if (ASYM && (t % CPG == 0)) {
-        const uint32_t z = nvalid ? zero_point(p.zp, n, p.G, grp) : 8u;
-        bc = neg_magic_pair<DT>(z);
-      }
-      u32x4 bq;
-      if constexpr (DT == DT_F16) {
-        // fp16: (1024 + q) - (1024 + z) is exact, so B = q - z directly
-        const half2_t nmz = __builtin_bit_cast(half2_t, bc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          bq[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, magic_pair<DT>(wv[t], i)) + nmz);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bq[i] = magic_pair<DT>(wv[t], i);
-      }
-      const u32x4 bcv = {bc, bc, bc, bc};
-      const int k = c * 32 + row4 * 8;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + col;
-        u32x4 a = {0u, 0u, 0u, 0u};
-        if (m < p.M) a = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + k);
-        tmp[mt] = mfma16x16x32<DT>(a, bq, tmp[mt]);
-        // bf16 has no packed add on gfx950: B = 128 + q, and a second MFMA
-        // against the constant -(128 + z) removes the offset in fp32
-        if constexpr (DT == DT_BF16) tmp[mt] = mfma16x16x32<DT>(a, bcv, tmp[mt]);
-      }
-      if ((t % CPG == CPG - 1) || c + 1 == p.nchunks) {
-        const float s = nvalid ? act_to_f32<DT>(srow[grp]) : 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt] += s * tmp[mt];
-          tmp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-    }
-  }
-
-  // ---- cross-wave reduction in wave order ----
-  float* mine = red + wave * NEL;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mine[(mt * 4 + r) * 64 + lane] = acc[mt][r];
-  __syncthreads();
-
-  for (int e = threadIdx.x; e < NEL; e += blockDim.x) {
-    float v = 0.f;
-    for (int w = 0; w < nwaves; ++w) v += red[w * NEL + e];
+// Store or hand over the reduced sums of one row tile: with one K range the
+// output (+ bias, one rounding); otherwise the fp32 partial, and the last
+// workgroup to finish the tile adds the partials in range order.
+template <int DT>
+__device__ __forceinline__ void finish_tile(const GemvParams& p, const float* red, int nwaves,
+                                            int nel, int tile, int split, int* last_flag) {
+  for (int e = threadIdx.x; e < nel; e += blockDim.x) {
     const int mt = e >> 8;
     const int r = (e >> 6) & 3;
     const int l = e & 63;
     const int m = mt * 16 + 4 * (l >> 4) + r;
     const int nn = tile * kGemvRowsPerTile + (l & 15);
     if (m < p.M && nn < p.N) {
+      float v = 0.f;
+      for (int w = 0; w < nwaves; ++w) v += red[w * nel + e];
       if (p.splits == 1) {
         if (p.bias) v += act_to_f32<DT>(p.bias[nn]);
         p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v);
@@ -155,19 +83,17 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvParams p) {
       }
     }
   }
-
   if (p.splits == 1) return;
 
-  // ---- split fix-up: the last workgroup of this row tile adds the ranges ----
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_ACQ_REL,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = (prev == (uint32_t)(p.splits - 1));
+    *last_flag = (prev == (uint32_t)(p.splits - 1));
   }
   __syncthreads();
-  if (!last_flag) return;
+  if (!*last_flag) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   for (int e = threadIdx.x; e < 16 * p.M; e += blockDim.x) {
     const int m = e >> 4;
@@ -189,23 +115,327 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// M <= 16
+// ---------------------------------------------------------------------------
+template <int DT, int GS, bool ASYM, int KPW, int XPT>
+__global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
+  constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
+  constexpr int SEG_PER_GRP = GS / 8;   // 16-byte x segments per group (4, 8, 16)
+  constexpr int SPT = (32 * KPW) / GS;  // scale loads per thread (see plan_gemv)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int last_flag;
 
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int cu_count) {
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  // wave index as a wave-uniform (scalar) value, so the per-wave k-step
+  // bookkeeping below stays in SGPRs and its branches are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = nthr >> 6;
+  const int col = lane & 15;   // MFMA column: output row within the tile
+  const int row4 = lane >> 4;  // 16-lane row of the wave
+  const int tile = blockIdx.x;
+  const int split = blockIdx.y;
+  const int n0 = tile * kGemvRowsPerTile;
+  const int n = n0 + col;
+  const int nc = min(n, p.N - 1);  // rows past N load row N-1; their outputs are dropped
+
+  const int ks_begin = split * p.ksteps_per_split;
+  const int ks_end = min(p.ksteps, ks_begin + p.ksteps_per_split);
+  const int k0 = ks_begin * kGemvKStep;
+  const int kr = min(p.K, ks_end * kGemvKStep) - k0;  // a multiple of GS
+  const int grp0 = k0 / GS;
+  const int ngr = kr / GS;
+  const int segs = kr >> 3;
+  const int xstride = kr + 8;  // padded LDS row of x, in halves
+  const int my_first = ks_begin + wave * p.kpw;
+  const int my_steps = max(0, min(p.kpw, ks_end - my_first));
+
+  // LDS layout (gemv_small_lds_bytes sizes it the same way)
+  float* red = reinterpret_cast<float*>(smem);                         // [nwaves][256]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(red + nwaves * 256);      // [M][xstride]
+  float* xsum = reinterpret_cast<float*>(xs + p.M * xstride);          // [ngr][16]
+  uint16_t* sl = reinterpret_cast<uint16_t*>(xsum + ngr * 16);         // [16][ngr]
+  uint32_t* zl = reinterpret_cast<uint32_t*>(sl + 16 * ngr);             // [2][ngr]
+
+  // ---- 1. loads: x, scales and zero points (to be staged), then weights ----
+  // Branch-free: addresses are clamped and results masked where used, so the
+  // loads go out back to back and every wait has an exact count.
+  const int xsegs = p.M * segs;
+  u32x4 xr[XPT];
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int e = min(tid + j * nthr, xsegs - 1);
+    const int m = e / segs;
+    xr[j] = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + k0 + (e - m * segs) * 8);
+  }
+  uint32_t sr[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int e = min(tid + j * nthr, 16 * ngr - 1);
+    const int r = e / ngr;
+    sr[j] = p.scales[(size_t)min(n0 + r, p.N - 1) * p.G + grp0 + (e - r * ngr)];
+  }
+  uint32_t zr = 0u;
+  if constexpr (ASYM) {
+    const int e = min(tid, 2 * ngr - 1);
+    const int rr = e / ngr;
+    zr = p.zp[(size_t)min((n0 >> 3) + rr, (p.N >> 3) - 1) * p.G + grp0 + (e - rr * ngr)];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t* wrow = p.wq + (size_t)nc * (p.K >> 3);
+  u32x4 wv[KPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int ks = min(my_first + i, ks_end - 1);
+    const int c = min(ks * 4 + row4, p.nchunks - 1);
+    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (size_t)c * 4));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. stage x, its group sums (bf16), scales and zero points in LDS ----
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int e = tid + j * nthr;
+    const int m = e / segs;
+    const int seg = e - m * segs;
+    if (e < xsegs) *reinterpret_cast<u32x4*>(xs + m * xstride + seg * 8) = xr[j];
+    if constexpr (DT == DT_BF16) {
+      // sum of this segment's 8 values, then over the SEG_PER_GRP consecutive
+      // lanes that hold one group (groups never straddle rows or the end)
+      float v = 0.f;
+      const uint32_t u[4] = {xr[j][0], xr[j][1], xr[j][2], xr[j][3]};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v += __builtin_bit_cast(float, u[q] << 16);
+        v += __builtin_bit_cast(float, u[q] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int off = 1; off < SEG_PER_GRP; off <<= 1) v += __shfl_xor(v, off);
+      if (e < xsegs && (seg % SEG_PER_GRP) == 0) xsum[(seg / SEG_PER_GRP) * 16 + m] = v;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int e = tid + j * nthr;
+    if (e < 16 * ngr) sl[e] = (uint16_t)sr[j];
+  }
+  if constexpr (ASYM) {
+    if (tid < 2 * ngr) zl[tid] = zr;
+  }
+  __syncthreads();
+
+  // ---- 3. dot products, one k-step at a time as its weights arrive ----
+  const uint32_t mask_v = vgpr_const(0x000F000Fu);
+  const uint16_t* xrow = xs + min(col, p.M - 1) * xstride + row4 * 8;  // rows >= M: any valid row
+  const uint16_t* srow_l = sl + col * ngr;
+  const uint32_t* zrow_l = zl + (col >> 3) * ngr;
+  const int zshift = 4 * (col & 7);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+  // one k-step (four 32-k chunks); FULL: all four chunks lie inside K, so no
+  // per-chunk checks (the common case; only a K that is not a multiple of 128
+  // has a partial last step, and groups never straddle it)
+  auto kstep = [&](const u32x4 wraw, const int c0, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    u32x4 wt = wraw;
+    transpose_rows4(wt);
+    f32x4 ch[2];
+    uint32_t nmz = neg_magic_pair<DT>(8u);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = c0 + t;
+      if (!FULL && c >= p.nchunks) break;
+      const int gl = c / CPG - grp0;  // group within this K range
+      if constexpr (DT == DT_F16 && ASYM) {
+        if (t % CPG == 0) nmz = neg_magic_pair<DT>((zrow_l[gl] >> zshift) & 0xFu);
+      }
+      // fp16: B = q - z exactly; bf16: B = 128 + q
+      const u32x4 bq = (DT == DT_F16) ? qz_word_f16(wt[t], mask_v, nmz) : magic_word<DT>(wt[t], mask_v);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(xrow + (c * 32 - k0));
+      // two independent accumulation chains inside a group
+      if (t % CPG < 2)
+        ch[t & 1] = mfma16x16x32<DT>(a, bq, f32x4{0.f, 0.f, 0.f, 0.f});
+      else
+        ch[t & 1] = mfma16x16x32<DT>(a, bq, ch[t & 1]);
+      if (t % CPG == CPG - 1) {
+        const f32x4 g = (CPG == 1) ? ch[t & 1] : ch[0] + ch[1];
+        const float s = act_to_f32<DT>(srow_l[gl]);
+        if constexpr (DT == DT_F16) {
+          acc += s * g;
+        } else {
+          // subtract (128 + z) * sum_k x[m, k] for this lane's four rows m
+          const uint32_t z = ASYM ? (zrow_l[gl] >> zshift) & 0xFu : 8u;
+          const f32x4 xg = *reinterpret_cast<const f32x4*>(xsum + gl * 16 + 4 * row4);
+          const float sc = -s * (128.0f + (float)z);
+          acc += s * g;
+          acc += sc * xg;
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    if (i >= my_steps) break;
+    const int c0 = (my_first + i) * 4;
+    if (c0 + 4 <= p.nchunks)
+      kstep(wv[i], c0, std::true_type{});
+    else
+      kstep(wv[i], c0, std::false_type{});
+  }
+
+  // ---- 4. reduce the waves in order, then the K ranges ----
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave * 256 + r * 64 + lane] = acc[r];
+  __syncthreads();
+  finish_tile<DT>(p, red, nwaves, 256, tile, split, &last_flag);
+}
+
+// ---------------------------------------------------------------------------
+// 16 < M <= 64: MT row tiles, A operands from global memory
+// ---------------------------------------------------------------------------
+template <int DT, int MT, int GS, bool ASYM, int KPW>
+__global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
+  constexpr int CPG = GS / 32;
+  constexpr int GPS = 4 / CPG;
+  constexpr int NEL = MT * 256;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int last_flag;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int col = lane & 15;
+  const int row4 = lane >> 4;
+  const int tile = blockIdx.x;
+  const int split = blockIdx.y;
+  const int n = tile * kGemvRowsPerTile + col;
+  const int nc = min(n, p.N - 1);
+  const uint32_t* wrow = p.wq + (size_t)nc * (p.K >> 3);
+  const uint16_t* srow = p.scales + (size_t)nc * p.G;
+
+  const int ks_begin = split * p.ksteps_per_split;
+  const int ks_end = min(p.ksteps, ks_begin + p.ksteps_per_split);
+  const int my_first = ks_begin + wave * p.kpw;
+  const int my_steps = max(0, min(p.kpw, ks_end - my_first));
+  float* red = reinterpret_cast<float*>(smem);
+
+  u32x4 wv[KPW];
+  uint32_t sv[KPW][GPS];
+  uint32_t zw[KPW][GPS];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int ks = min(my_first + i, ks_end - 1);
+    const int c = min(ks * 4 + row4, p.nchunks - 1);
+    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (size_t)c * 4));
+#pragma unroll
+    for (int h = 0; h < GPS; ++h) {
+      const int grp = min((ks * 4 + h * CPG) / CPG, p.G - 1);
+      sv[i][h] = srow[grp];
+      zw[i][h] = ASYM ? p.zp[(size_t)(nc >> 3) * p.G + grp] : 0u;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t mask_v = vgpr_const(0x000F000Fu);
+
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    if (i >= my_steps) break;
+    const int c0 = (my_first + i) * 4;
+    u32x4 wt = wv[i];
+    transpose_rows4(wt);
+    f32x4 tq[MT], tc[MT];
+    uint32_t bc = neg_magic_pair<DT>(8u);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = c0 + t;
+      if (c >= p.nchunks) break;
+      if (ASYM && (t % CPG == 0)) bc = neg_magic_pair<DT>((zw[i][t / CPG] >> (4 * (n & 7))) & 0xFu);
+      const u32x4 bq = (DT == DT_F16) ? qz_word_f16(wt[t], mask_v, bc) : magic_word<DT>(wt[t], mask_v);
+      const u32x4 bcv = {bc, bc, bc, bc};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = min(mt * 16 + col, p.M - 1);  // rows >= M: any valid row
+        const u32x4 a = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + c * 32 + row4 * 8);
+        const bool fresh = (t % CPG) == 0;
+        tq[mt] = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : tq[mt]);
+        // bf16: a second MFMA against the constant -(128 + z) removes the offset
+        if constexpr (DT == DT_BF16)
+          tc[mt] = mfma16x16x32<DT>(a, bcv, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : tc[mt]);
+      }
+      if (t % CPG == CPG - 1) {
+        const float s = act_to_f32<DT>((uint16_t)sv[i][t / CPG]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt] += s * tq[mt];
+          if constexpr (DT == DT_BF16) acc[mt] += s * tc[mt];
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave * NEL + (mt * 4 + r) * 64 + lane] = acc[mt][r];
+  __syncthreads();
+  finish_tile<DT>(p, red, nwaves, NEL, tile, split, &last_flag);
+}
+
+// ---------------------------------------------------------------------------
+// planning and launch
+// ---------------------------------------------------------------------------
+
+size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int ksteps_per_split, int group) {
+  const size_t red = (size_t)waves * mtiles * 256 * sizeof(float);
+  if (mtiles > 1) return red;
+  const size_t kr = (size_t)ksteps_per_split * kGemvKStep;
+  const size_t ngr = kr / (size_t)group;
+  return red + (size_t)M * (kr + 8) * sizeof(uint16_t)  // x
+         + ngr * 16 * sizeof(float)                     // group sums of x
+         + 16 * ngr * sizeof(uint16_t)                  // scales
+         + 2 * ngr * sizeof(uint32_t);                  // zero-point words
+}
+
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   GemvPlan p;
   p.tiles = (int)((N + kGemvRowsPerTile - 1) / kGemvRowsPerTile);
   p.ksteps = (int)((K + kGemvKStep - 1) / kGemvKStep);
   p.mtiles = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.xlds = p.mtiles == 1;
+  // k-steps per wave: at most kGemvStepsPerWave; with x staged, also few
+  // enough that a thread stages at most kGemvXSegsPerThread x segments
+  // (M * 16 segments per k-step, 64 threads per wave).  The scale and
+  // zero-point staging then needs at most 32 * kpw / group and 4 * kpw /
+  // group loads per thread, which the kernel's fixed counts cover.
+  int kpw = kGemvStepsPerWave;
+  if (p.xlds) {
+    const int cap = (int)((4 * kGemvXSegsPerThread) / M);
+    if (cap < kpw) kpw = cap < 1 ? 1 : cap;
+  }
+  p.kpw = kpw;
+  // split K until every row tile has enough workgroups to cover the CUs, a
+  // workgroup has at most kGemvMaxWaves waves, and its LDS fits the budget
   int splits = 1;
-  if (p.tiles < cu_count) {
-    splits = (cu_count + p.tiles - 1) / p.tiles;
+  if (p.tiles < cu_count) splits = (cu_count + p.tiles - 1) / p.tiles;
+  for (;;) {
     if (splits > p.ksteps) splits = p.ksteps;
+    int kps = (p.ksteps + splits - 1) / splits;
+    const int waves = (kps + kpw - 1) / kpw;
+    if (splits == p.ksteps ||
+        (waves <= kGemvMaxWaves && gemv_lds_bytes(waves, p.mtiles, M, kps, group) <= kGemvLdsBudget))
+      break;
+    ++splits;
   }
   p.ksteps_per_split = (p.ksteps + splits - 1) / splits;
   p.splits = (p.ksteps + p.ksteps_per_split - 1) / p.ksteps_per_split;
-  int waves = (p.ksteps_per_split + 1) / 2;
-  if (waves < 1) waves = 1;
-  if (waves > kGemvMaxWaves) waves = kGemvMaxWaves;
-  p.waves = waves;
+  p.waves = (p.ksteps_per_split + kpw - 1) / kpw;
+  p.lds_bytes = gemv_lds_bytes(p.waves, p.mtiles, M, p.ksteps_per_split, group);
   return p;
 }
 
@@ -221,7 +451,12 @@ template <int DT, int MT, int GS, bool ASYM>
 static hipError_t launch_t(const GemvParams& prm, const GemvPlan& plan, hipStream_t s) {
   dim3 grid(plan.tiles, plan.splits);
   dim3 block(plan.waves * 64);
-  hipLaunchKernelGGL((gemv_kernel<DT, MT, GS, ASYM>), grid, block, 0, s, prm);
+  constexpr int KPW = kGemvStepsPerWave;
+  if constexpr (MT == 1)
+    hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, KPW, kGemvXSegsPerThread>), grid, block,
+                       plan.lds_bytes, s, prm);
+  else
+    hipLaunchKernelGGL((gemv_wide_kernel<DT, MT, GS, ASYM, KPW>), grid, block, plan.lds_bytes, s, prm);
   return hipGetLastError();
 }
 
@@ -252,6 +487,9 @@ static hipError_t launch_m(const GemvParams& prm, int group, const GemvPlan& pla
 
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspace,
                        hipStream_t stream) {
+  if (plan.waves < 1 || plan.waves > kGemvMaxWaves || plan.lds_bytes > kGemvLdsBudget ||
+      plan.kpw < 1 || plan.kpw > kGemvStepsPerWave)
+    return hipErrorInvalidConfiguration;
   GemvParams prm;
   prm.x = static_cast<const uint16_t*>(a.x);
   prm.wq = reinterpret_cast<const uint32_t*>(a.wq);
@@ -274,6 +512,7 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
   prm.ksteps = plan.ksteps;
   prm.ksteps_per_split = plan.ksteps_per_split;
   prm.splits = plan.splits;
+  prm.kpw = plan.kpw;
   return a.dtype == DT_F16 ? launch_m<DT_F16>(prm, a.group, plan, stream)
                            : launch_m<DT_BF16>(prm, a.group, plan, stream);
 }

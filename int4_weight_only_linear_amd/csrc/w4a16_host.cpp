@@ -117,10 +117,10 @@ w4a16_path resolve_path(int64_t M, int64_t N, int64_t K, int32_t group, int32_t 
 
 constexpr int kPlanningCUs = 256;  // MI355X; the launch plan uses the device's own count
 
-size_t workspace_for(int64_t M, int64_t N, int64_t K, w4a16_path path, int cu_count) {
+size_t workspace_for(int64_t M, int64_t N, int64_t K, int32_t group, w4a16_path path, int cu_count) {
   if (M <= 0) return 0;
   if (path == W4A16_PATH_GEMV) {
-    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, cu_count);
+    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, group, cu_count);
     return w4a16::gemv_workspace_bytes(plan, M, N);
   }
   return w4a16::gemm_workspace_bytes(M, N, K, cu_count);
@@ -150,7 +150,7 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
   if (p == W4A16_PATH_GEMV && M > W4A16_GEMV_MAX_M)
     return fail(W4A16_ERR_UNSUPPORTED, "the decode kernel takes M <= %d, got M=%lld",
                 W4A16_GEMV_MAX_M, (long long)M);
-  const size_t need = workspace_for(M, N, K, p, dev->cu_count);
+  const size_t need = workspace_for(M, N, K, group_size, p, dev->cu_count);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
                 workspace_bytes, workspace ? "" : " (NULL)");
@@ -161,7 +161,7 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p == W4A16_PATH_GEMV) {
-    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, dev->cu_count);
+    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, group_size, dev->cu_count);
     if (log_enabled())
       std::fprintf(stderr,
                    "[w4a16] gemv M=%lld N=%lld K=%lld g=%d %s %s tiles=%d splits=%d waves=%d\n",
@@ -294,7 +294,7 @@ size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size,
     if (device_info(&d) == W4A16_OK) cus = d->cu_count;
     g_last_error.clear();
   }
-  return workspace_for(M, N, K, p, cus);
+  return workspace_for(M, N, K, group_size, p, cus);
 }
 
 w4a16_status w4a16_linear(const void* x, const int32_t* wq, const void* scales, const int32_t* zp,

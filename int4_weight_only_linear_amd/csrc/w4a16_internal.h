@@ -33,6 +33,12 @@ constexpr int kGemvRowsPerTile = 16;
 constexpr int kGemvKStep = 128;       // k per wave step: 4 chunks of 32
 constexpr int kGemvMaxWaves = 16;     // 1024 threads
 constexpr int kGemvMaxMTiles = 4;     // M <= 64
+constexpr int kGemvStepsPerWave = 8;  // k-steps whose loads a wave keeps in flight
+constexpr int kGemvXSegsPerThread = 4;  // 16-byte x loads per thread when x is staged
+// Dynamic LDS per decode workgroup (cross-wave reduction + staged x).  The
+// kernel's LDS layout and the host's plan both size it with gemv_lds_bytes,
+// and the plan splits K until it fits this budget.
+constexpr size_t kGemvLdsBudget = 64 * 1024;
 
 struct GemvPlan {
   int tiles;             // ceil(N / 16)
@@ -41,9 +47,13 @@ struct GemvPlan {
   int ksteps_per_split;
   int waves;             // waves per workgroup
   int mtiles;            // 16-row M tiles (1, 2 or 4)
+  int kpw;               // k-steps per wave (upper bound)
+  bool xlds;             // x staged in LDS (M <= 16)
+  size_t lds_bytes;      // dynamic LDS of one workgroup
 };
 
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int cu_count);
+size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int ksteps_per_split, int group);
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N);
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& p, void* workspace,
                        hipStream_t stream);
