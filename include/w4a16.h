@@ -16,8 +16,13 @@
  * side is kept -- and it does NOT work here".
  *
  * Layout contract (all tensors contiguous, row-major):
- *   wq     int32  [N, K/8]  word j of row n holds k = 8j .. 8j+7; nibble t
- *                           (bits 4t..4t+3) holds k-offset (0,2,4,6,1,3,5,7)[t].
+ *   wq     int32  [N, K/8]  each word holds one 8-k slice of its row: the weight
+ *                           at k = 8L + (0,2,4,6,1,3,5,7)[t] of slice L sits in
+ *                           nibble t (bits 4t..4t+3).  Words are stored in slice
+ *                           order except inside each complete run of 16 words
+ *                           (128 k) of a row, which is stored as the 4x4
+ *                           transpose: stored word 4r+t holds slice 4t+r of the
+ *                           run.  A last, incomplete run stays in slice order.
  *                           Bits are unsigned (int32 or uint32 storage).
  *   zp     int32  [N/8, G]  nibble i of word (r, j) is the zero point of row 8r+i
  *                           and group j.  NULL selects symmetric uint4b8 (z = 8).

@@ -1,8 +1,11 @@
 // Device-side building blocks shared by the W4A16 kernels (gfx950 only).
 //
 // Weight words follow the layout of include/w4a16.h: nibble t of a word holds
-// k-offset (0,2,4,6,1,3,5,7)[t], so (w >> 4i) & 0x000F000F places the
-// consecutive pair (k = 2i, 2i+1) in the low and high 16-bit halves.
+// k-offset (0,2,4,6,1,3,5,7)[t] of its 8-k slice, so (w >> 4i) & 0x000F000F
+// places the consecutive pair (k = 2i, 2i+1) in the low and high 16-bit
+// halves; complete 128-k runs of a row store their 16 words as a 4x4
+// transpose (word 4r+t holds slice 4t+r), so a 16-byte load of words
+// 4r..4r+3 yields slice r of each of the run's four 32-k chunks.
 //
 // Dequantisation uses the exponent-OR ("magic number") trick named in the
 // description of "[ROCm][Kernel] Add HybridW4A16LinearKernel: Triton prefill
@@ -79,6 +82,13 @@ __device__ __forceinline__ u32x4 qz_word_f16(uint32_t w, uint32_t mask_v, uint32
   const uint32_t p0 = (w & mask_v) | P, p1 = ((w >> 4) & mask_v) | P;
   const uint32_t p2 = ((w >> 8) & mask_v) | P, p3 = ((w >> 12) & mask_v) | P;
   return u32x4{add_f16x2(p0, nmz), add_f16x2(p1, nmz), add_f16x2(p2, nmz), add_f16x2(p3, nmz)};
+}
+
+// The 8-k slice held by stored word j of a row of J words (see above).
+__device__ __forceinline__ int slice_of_stored_word(int j, int J) {
+  const int run = j >> 4, p = j & 15;
+  if ((run + 1) * 16 > J) return j;
+  return (run << 4) + 4 * (p & 3) + (p >> 2);
 }
 
 // -(magic + z) in both halves of a word

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t n = idx / words_per_row;
-    const int64_t j = idx - n * words_per_row;
+    const int64_t j = slice_of_stored_word((int)(idx - n * words_per_row), (int)words_per_row);
     const int64_t grp = (j * 8) / group;
     const uint16_t sbits = scales[n * G + grp];
     const uint32_t z = ASYM ? zero_point(zp, (int)n, (int)G, (int)grp) : 8u;
@@ -34,12 +34,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   }
 }
 
-// nibble t holds k-offset (0,2,4,6,1,3,5,7)[t]; output bytes in k order
+// nibble t holds k-offset (0,2,4,6,1,3,5,7)[t] of the word's slice; output
+// bytes in k order
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ wq,
-                                                     uint8_t* __restrict__ q, int64_t words) {
+                                                     uint8_t* __restrict__ q, int64_t words,
+                                                     int words_per_row) {
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < words;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const uint32_t w = wq[idx];
+    const int64_t n = idx / words_per_row;
+    const int64_t slice = n * words_per_row +
+                          slice_of_stored_word((int)(idx - n * words_per_row), words_per_row);
     const uint32_t even = w & 0x0000FFFFu;  // k = 0, 2, 4, 6 in nibbles 0..3
     const uint32_t odd = w >> 16;           // k = 1, 3, 5, 7 in nibbles 4..7
     uint32_t lo = 0, hi = 0;                // bytes k = 0..3 and 4..7
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict_
       hi |= ((even >> (4 * i + 8)) & 0xFu) << (16 * i);
       hi |= ((odd >> (4 * i + 8)) & 0xFu) << (16 * i + 8);
     }
-    *reinterpret_cast<u32x2*>(q + idx * 8) = u32x2{lo, hi};
+    *reinterpret_cast<u32x2*>(q + slice * 8) = u32x2{lo, hi};
   }
 }
 
@@ -89,7 +94,7 @@ hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* 
 hipError_t launch_unpack(const int32_t* wq, uint8_t* q, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t words = N * (K >> 3);
   hipLaunchKernelGGL(unpack_kernel, grid_for(words, 256), 256, 0, stream,
-                     reinterpret_cast<const uint32_t*>(wq), q, words);
+                     reinterpret_cast<const uint32_t*>(wq), q, words, (int)(K >> 3));
   return hipGetLastError();
 }
 

@@ -5,12 +5,14 @@
 // small M that dequantises with the exponent-OR trick.  These kernels keep the
 // split-K idea and the trick, and re-plan the rest for CDNA4:
 //
-// * Work unit: 16 output rows (one MFMA column tile) x one 128-wide k-step.
-//   Lane (j = lane % 16, r = lane / 16) issues one 16-byte non-temporal load
-//   per k-step, chunk r (32 k) of row n0 + j.  A 4x4 dword transpose across
-//   the four 16-lane rows (permlane swaps) then leaves, in register t, word r
-//   of chunk t -- exactly the B operand layout of v_mfma_f32_16x16x32 for
-//   chunk t, so every MFMA covers 32 k of one quantisation group.
+// * Work unit: 16 output rows (one MFMA column tile) x one 128-wide k-step,
+//   i.e. one 128-k run of each row.  Lane (j = lane % 16, r = lane / 16)
+//   issues one 16-byte non-temporal load per k-step, stored words 4r..4r+3 of
+//   row n0 + j's run; the runs are stored as a 4x4 word transpose, so
+//   register t holds slice r of chunk t -- exactly the B operand layout of
+//   v_mfma_f32_16x16x32 for chunk t, and every MFMA covers 32 k of one
+//   quantisation group.  (An incomplete last run, stored in order, is
+//   transposed across the four 16-lane rows with permlane swaps instead.)
 // * The scale is factored out of the dot product: per group the wave forms
 //   sum_k x[m,k] * (q[n,k] - z[n,g]) in fp32 and adds s[n,g] times it to the
 //   accumulator; nothing is rounded to the activation dtype before the output.
@@ -58,6 +60,13 @@ struct GemvParams {
   int ksteps_per_split;
   int splits;
   int kpw;      // k-steps per wave (contiguous runs)
+  // staging geometry of one K range (M <= 16 kernel): 16-byte x segments per
+  // row and quantisation groups, with reciprocals floor(2^31 / d) + 1 for the
+  // index divisions: e / d == umulhi(2e, recip) whenever e * d < 2^31
+  int xsegs_per_row;
+  uint32_t xsegs_recip;
+  int groups_per_split;
+  uint32_t groups_recip;
 };
 
 // Store or hand over the reduced sums of one row tile: with one K range the
@@ -120,7 +129,6 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 template <int DT, int GS, bool ASYM, int KPW, int XPT>
 __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
-  constexpr int SEG_PER_GRP = GS / 8;   // 16-byte x segments per group (4, 8, 16)
   constexpr int SPT = (32 * KPW) / GS;  // scale loads per thread (see plan_gemv)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int last_flag;
@@ -137,26 +145,26 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   const int tile = blockIdx.x;
   const int split = blockIdx.y;
   const int n0 = tile * kGemvRowsPerTile;
-  const int n = n0 + col;
-  const int nc = min(n, p.N - 1);  // rows past N load row N-1; their outputs are dropped
+  const int nc = min(n0 + col, p.N - 1);  // rows past N read row N-1; their outputs are dropped
 
+  // Every workgroup stages a full-size K range (the last one may extend past
+  // K: those loads are clamped and the values never used), so the index maps
+  // below divide by per-launch constants, done with host-computed reciprocals.
   const int ks_begin = split * p.ksteps_per_split;
   const int ks_end = min(p.ksteps, ks_begin + p.ksteps_per_split);
   const int k0 = ks_begin * kGemvKStep;
-  const int kr = min(p.K, ks_end * kGemvKStep) - k0;  // a multiple of GS
   const int grp0 = k0 / GS;
-  const int ngr = kr / GS;
-  const int segs = kr >> 3;
-  const int xstride = kr + 8;  // padded LDS row of x, in halves
+  const int segs = p.xsegs_per_row;  // 16-byte x segments per row of the K range
+  const int ngr = p.groups_per_split;
+  const int xstride = segs * 8 + 8;  // padded LDS row of x, in halves
   const int my_first = ks_begin + wave * p.kpw;
   const int my_steps = max(0, min(p.kpw, ks_end - my_first));
 
-  // LDS layout (gemv_small_lds_bytes sizes it the same way)
-  float* red = reinterpret_cast<float*>(smem);                         // [nwaves][256]
-  uint16_t* xs = reinterpret_cast<uint16_t*>(red + nwaves * 256);      // [M][xstride]
-  float* xsum = reinterpret_cast<float*>(xs + p.M * xstride);          // [ngr][16]
-  uint16_t* sl = reinterpret_cast<uint16_t*>(xsum + ngr * 16);         // [16][ngr]
-  uint32_t* zl = reinterpret_cast<uint32_t*>(sl + 16 * ngr);             // [2][ngr]
+  // LDS layout (gemv_lds_bytes sizes it the same way)
+  float* red = reinterpret_cast<float*>(smem);                     // [nwaves][256]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(red + nwaves * 256);  // [M][xstride]
+  uint16_t* sl = xs + p.M * xstride;                               // [16][ngr]
+  uint32_t* zl = reinterpret_cast<uint32_t*>(sl + 16 * ngr);       // [2][ngr]
 
   // ---- 1. loads: x, scales and zero points (to be staged), then weights ----
   // Branch-free: addresses are clamped and results masked where used, so the
@@ -165,54 +173,50 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   u32x4 xr[XPT];
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    const int e = min(tid + j * nthr, xsegs - 1);
-    const int m = e / segs;
-    xr[j] = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + k0 + (e - m * segs) * 8);
+    const uint32_t e = (uint32_t)min(tid + j * nthr, xsegs - 1);
+    const uint32_t m = __umulhi(e << 1, p.xsegs_recip);
+    const int k = min(k0 + (int)(e - m * segs) * 8, p.K - 8);
+    xr[j] = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + k);
   }
   uint32_t sr[SPT];
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
-    const int e = min(tid + j * nthr, 16 * ngr - 1);
-    const int r = e / ngr;
-    sr[j] = p.scales[(size_t)min(n0 + r, p.N - 1) * p.G + grp0 + (e - r * ngr)];
+    const uint32_t e = (uint32_t)min(tid + j * nthr, 16 * ngr - 1);
+    const uint32_t r = __umulhi(e << 1, p.groups_recip);
+    const int g = min(grp0 + (int)(e - r * ngr), p.G - 1);
+    sr[j] = p.scales[(size_t)min(n0 + (int)r, p.N - 1) * p.G + g];
   }
   uint32_t zr = 0u;
   if constexpr (ASYM) {
     const int e = min(tid, 2 * ngr - 1);
-    const int rr = e / ngr;
-    zr = p.zp[(size_t)min((n0 >> 3) + rr, (p.N >> 3) - 1) * p.G + grp0 + (e - rr * ngr)];
+    const int rr = e >= ngr ? 1 : 0;
+    const int g = min(grp0 + e - rr * ngr, p.G - 1);
+    zr = p.zp[(size_t)min((n0 >> 3) + rr, (p.N >> 3) - 1) * p.G + g];
   }
   __builtin_amdgcn_sched_barrier(0);
-  const uint32_t* wrow = p.wq + (size_t)nc * (p.K >> 3);
+  // weights: a wave-uniform base per k-step plus one per-lane offset, so each
+  // load needs no vector address arithmetic
+  const uint32_t lane_off = (uint32_t)nc * (uint32_t)(p.K >> 1) + (uint32_t)row4 * 16u;
+  const int last_ks = ks_end - 1;
   u32x4 wv[KPW];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
-    const int ks = min(my_first + i, ks_end - 1);
-    const int c = min(ks * 4 + row4, p.nchunks - 1);
-    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (size_t)c * 4));
+    const int ks = min(my_first + i, last_ks);
+    const char* base = reinterpret_cast<const char*>(p.wq) + (size_t)ks * 64;
+    uint32_t off = lane_off;
+    // a partial last k-step (K not a multiple of 128): keep lanes in the row
+    if (ks * 4 + 4 > p.nchunks) off -= (uint32_t)max(0, ks * 4 + row4 - (p.nchunks - 1)) * 16u;
+    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. stage x, its group sums (bf16), scales and zero points in LDS ----
+  // ---- 2. stage x, scales and zero points in LDS ----
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    const int e = tid + j * nthr;
-    const int m = e / segs;
-    const int seg = e - m * segs;
-    if (e < xsegs) *reinterpret_cast<u32x4*>(xs + m * xstride + seg * 8) = xr[j];
-    if constexpr (DT == DT_BF16) {
-      // sum of this segment's 8 values, then over the SEG_PER_GRP consecutive
-      // lanes that hold one group (groups never straddle rows or the end)
-      float v = 0.f;
-      const uint32_t u[4] = {xr[j][0], xr[j][1], xr[j][2], xr[j][3]};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v += __builtin_bit_cast(float, u[q] << 16);
-        v += __builtin_bit_cast(float, u[q] & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int off = 1; off < SEG_PER_GRP; off <<= 1) v += __shfl_xor(v, off);
-      if (e < xsegs && (seg % SEG_PER_GRP) == 0) xsum[(seg / SEG_PER_GRP) * 16 + m] = v;
+    const uint32_t e = (uint32_t)(tid + j * nthr);
+    if (e < (uint32_t)xsegs) {
+      const uint32_t m = __umulhi(e << 1, p.xsegs_recip);
+      *reinterpret_cast<u32x4*>(xs + m * xstride + (e - m * segs) * 8) = xr[j];
     }
   }
 #pragma unroll
@@ -233,43 +237,48 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   const int zshift = 4 * (col & 7);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-  // one k-step (four 32-k chunks); FULL: all four chunks lie inside K, so no
-  // per-chunk checks (the common case; only a K that is not a multiple of 128
-  // has a partial last step, and groups never straddle it)
+  // one k-step (four 32-k chunks); FULL: all four chunks lie inside K
   auto kstep = [&](const u32x4 wraw, const int c0, auto full) {
     constexpr bool FULL = decltype(full)::value;
+    // a complete 128-k run is stored transposed, so register t already holds
+    // this lane's slice of chunk t; an incomplete last run is stored in
+    // order and is transposed across the 16-lane rows here
     u32x4 wt = wraw;
-    transpose_rows4(wt);
+    if constexpr (!FULL) transpose_rows4(wt);
+    // fp16: chains ch[0], ch[1] by chunk parity.  bf16: ch[0] collects
+    // x . (128 + q), ch[1] collects x . (-(128 + z)) from the second MFMA.
     f32x4 ch[2];
     uint32_t nmz = neg_magic_pair<DT>(8u);
+    u32x4 bcv = {nmz, nmz, nmz, nmz};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int c = c0 + t;
       if (!FULL && c >= p.nchunks) break;
       const int gl = c / CPG - grp0;  // group within this K range
-      if constexpr (DT == DT_F16 && ASYM) {
-        if (t % CPG == 0) nmz = neg_magic_pair<DT>((zrow_l[gl] >> zshift) & 0xFu);
+      if constexpr (ASYM) {
+        if (t % CPG == 0) {
+          nmz = neg_magic_pair<DT>((zrow_l[gl] >> zshift) & 0xFu);
+          if constexpr (DT == DT_BF16) bcv = u32x4{nmz, nmz, nmz, nmz};
+        }
       }
-      // fp16: B = q - z exactly; bf16: B = 128 + q
-      const u32x4 bq = (DT == DT_F16) ? qz_word_f16(wt[t], mask_v, nmz) : magic_word<DT>(wt[t], mask_v);
       const u32x4 a = *reinterpret_cast<const u32x4*>(xrow + (c * 32 - k0));
-      // two independent accumulation chains inside a group
-      if (t % CPG < 2)
-        ch[t & 1] = mfma16x16x32<DT>(a, bq, f32x4{0.f, 0.f, 0.f, 0.f});
-      else
-        ch[t & 1] = mfma16x16x32<DT>(a, bq, ch[t & 1]);
+      const bool fresh = (t % CPG) == 0;
+      if constexpr (DT == DT_F16) {
+        const u32x4 bq = qz_word_f16(wt[t], mask_v, nmz);  // q - z, exact
+        const int u = (t % CPG) & 1;
+        ch[u] = mfma16x16x32<DT>(a, bq, (t % CPG) < 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[u]);
+      } else {
+        const u32x4 bq = magic_word<DT>(wt[t], mask_v);     // 128 + q, exact
+        ch[0] = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[0]);
+        ch[1] = mfma16x16x32<DT>(a, bcv, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[1]);
+      }
       if (t % CPG == CPG - 1) {
-        const f32x4 g = (CPG == 1) ? ch[t & 1] : ch[0] + ch[1];
         const float s = act_to_f32<DT>(srow_l[gl]);
-        if constexpr (DT == DT_F16) {
-          acc += s * g;
+        if constexpr (DT == DT_F16 && CPG == 1) {
+          acc += s * ch[0];
         } else {
-          // subtract (128 + z) * sum_k x[m, k] for this lane's four rows m
-          const uint32_t z = ASYM ? (zrow_l[gl] >> zshift) & 0xFu : 8u;
-          const f32x4 xg = *reinterpret_cast<const f32x4*>(xsum + gl * 16 + 4 * row4);
-          const float sc = -s * (128.0f + (float)z);
-          acc += s * g;
-          acc += sc * xg;
+          acc += s * ch[0];
+          acc += s * ch[1];
         }
       }
     }
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
     if (i >= my_steps) break;
     const int c0 = (my_first + i) * 4;
     u32x4 wt = wv[i];
-    transpose_rows4(wt);
+    if (c0 + 4 > p.nchunks) transpose_rows4(wt);  // incomplete run: stored in order
     f32x4 tq[MT], tc[MT];
     uint32_t bc = neg_magic_pair<DT>(8u);
 #pragma unroll
@@ -397,7 +406,6 @@ size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int ksteps_per_split, in
   const size_t kr = (size_t)ksteps_per_split * kGemvKStep;
   const size_t ngr = kr / (size_t)group;
   return red + (size_t)M * (kr + 8) * sizeof(uint16_t)  // x
-         + ngr * 16 * sizeof(float)                     // group sums of x
          + 16 * ngr * sizeof(uint16_t)                  // scales
          + 2 * ngr * sizeof(uint32_t);                  // zero-point words
 }
@@ -513,6 +521,10 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
   prm.ksteps_per_split = plan.ksteps_per_split;
   prm.splits = plan.splits;
   prm.kpw = plan.kpw;
+  prm.xsegs_per_row = plan.ksteps_per_split * (kGemvKStep / 8);
+  prm.groups_per_split = plan.ksteps_per_split * kGemvKStep / a.group;
+  prm.xsegs_recip = (uint32_t)((1ull << 31) / (uint64_t)prm.xsegs_per_row + 1);
+  prm.groups_recip = (uint32_t)((1ull << 31) / (uint64_t)prm.groups_per_split + 1);
   return a.dtype == DT_F16 ? launch_m<DT_F16>(prm, a.group, plan, stream)
                            : launch_m<DT_BF16>(prm, a.group, plan, stream);
 }

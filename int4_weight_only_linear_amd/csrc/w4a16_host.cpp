@@ -150,6 +150,10 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
   if (p == W4A16_PATH_GEMV && M > W4A16_GEMV_MAX_M)
     return fail(W4A16_ERR_UNSUPPORTED, "the decode kernel takes M <= %d, got M=%lld",
                 W4A16_GEMV_MAX_M, (long long)M);
+  if (p == W4A16_PATH_GEMV && (uint64_t)N * (uint64_t)K / 2 > 0xFFFFFFFFull)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "the decode kernel addresses weights with 32-bit byte offsets: N*K/2 must be "
+                "below 4 GiB (N=%lld K=%lld)", (long long)N, (long long)K);
   const size_t need = workspace_for(M, N, K, group_size, p, dev->cu_count);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
@@ -191,6 +195,15 @@ const char* w4a16_last_error(void) { return g_last_error.c_str(); }
 // nibble t of a word holds k-offset (0,2,4,6,1,3,5,7)[t]; the inverse map:
 static const int kSlotOfKoff[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 
+// The 8-k slice held by stored word j of a row of J words: complete runs of
+// 16 words are stored as the 4x4 transpose (word 4r+t <-> slice 4t+r, its own
+// inverse); an incomplete last run is stored in order.
+static int64_t slice_of_stored_word(int64_t j, int64_t J) {
+  const int64_t run = j / 16, p = j % 16;
+  if ((run + 1) * 16 > J) return j;
+  return run * 16 + 4 * (p % 4) + p / 4;
+}
+
 w4a16_status w4a16_pack_weights(const uint8_t* q, int64_t N, int64_t K, int32_t* wq) {
   if (!q || !wq) return fail(W4A16_ERR_INVALID_ARG, "pack_weights: NULL pointer");
   if (N < 0 || K < 0 || K % 8) return fail(W4A16_ERR_INVALID_ARG, "pack_weights: need N >= 0, K >= 0, K %% 8 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
@@ -199,7 +212,7 @@ w4a16_status w4a16_pack_weights(const uint8_t* q, int64_t N, int64_t K, int32_t*
   const int64_t J = K / 8;
   for (int64_t n = 0; n < N; ++n)
     for (int64_t j = 0; j < J; ++j) {
-      const uint8_t* src = q + n * K + j * 8;
+      const uint8_t* src = q + n * K + slice_of_stored_word(j, J) * 8;
       uint32_t w = 0;
       for (int i = 0; i < 8; ++i) w |= (uint32_t)src[i] << (4 * kSlotOfKoff[i]);
       wq[n * J + j] = (int32_t)w;
@@ -214,7 +227,7 @@ w4a16_status w4a16_unpack_weights(const int32_t* wq, int64_t N, int64_t K, uint8
   for (int64_t n = 0; n < N; ++n)
     for (int64_t j = 0; j < J; ++j) {
       const uint32_t w = (uint32_t)wq[n * J + j];
-      uint8_t* dst = q + n * K + j * 8;
+      uint8_t* dst = q + n * K + slice_of_stored_word(j, J) * 8;
       for (int i = 0; i < 8; ++i) dst[i] = (uint8_t)((w >> (4 * kSlotOfKoff[i])) & 0xFu);
     }
   return ok();

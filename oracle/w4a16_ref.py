@@ -16,11 +16,17 @@ What it computes, and where each step comes from (pages by title):
   decode call takes (w_q, x_2d, w_s, cu_count, group_size, w_zp, bias); zero
   points are int32 or uint32 [N/8, groups], eight 4-bit values packed along
   dim 0.
-* Nibble order inside a weight word (the pages name an "AWQ-style packed
-  shuffle" / "ExLlama shuffle" but print no permutation).  Reading used here:
-  within word j of row n, the nibble at bit position 4*t holds the weight at
-  k = 8*j + KOFF_OF_NIBBLE[t], with KOFF_OF_NIBBLE = (0, 2, 4, 6, 1, 3, 5, 7).
-  Equivalently, k-offset i lives in nibble SLOT_OF_KOFF[i] = (0,4,1,5,2,6,3,7).
+* Word layout (the pages name an "AWQ-style packed shuffle" / "ExLlama
+  shuffle" layout [N, K/8] but print no permutation).  Reading used here, in
+  two levels:
+  - inside a word: the word holding the 8-k slice L of a row stores the
+    weight at k = 8*L + KOFF_OF_NIBBLE[t] in the nibble at bit 4*t, with
+    KOFF_OF_NIBBLE = (0, 2, 4, 6, 1, 3, 5, 7); equivalently k-offset i lives
+    in nibble SLOT_OF_KOFF[i] = (0, 4, 1, 5, 2, 6, 3, 7);
+  - across words: each complete run of 16 words (128 k) of a row is a 4x4
+    transpose of words -- stored word 4*r + t of the run holds slice 4*t + r
+    of the run; a final incomplete run (K not a multiple of 128) keeps its
+    slices in order.  ``slice_of_word`` spells the map out.
 * Zero-point packing: nibble i (bits 4i..4i+3) of word (r, grp) holds the
   zero point of row 8r + i ("packed 8x uint4 along dim 0").
 * Scales: [N, G] row-major in the activation dtype (G = K / group).
@@ -113,6 +119,28 @@ def f32_to_act_bits(v: np.ndarray, dtype: int) -> np.ndarray:
 # packing (the layout contract)
 # --------------------------------------------------------------------------
 
+WORDS_PER_RUN = 16  # 128 k
+
+
+def slice_of_word(j: int, words_per_row: int) -> int:
+    """Which 8-k slice of its row the stored word j holds.
+
+    Inside a complete run of 16 words the stored order is the 4x4 transpose
+    of the slice order (word 4*r + t <-> slice 4*t + r, an involution); an
+    incomplete last run is stored in order.
+    """
+    run, p = divmod(j, WORDS_PER_RUN)
+    if (run + 1) * WORDS_PER_RUN <= words_per_row:
+        r, t = divmod(p, 4)
+        return run * WORDS_PER_RUN + 4 * t + r
+    return j
+
+
+def _word_order(words_per_row: int) -> np.ndarray:
+    """order[j] = slice held by stored word j, for one row."""
+    return np.array([slice_of_word(j, words_per_row) for j in range(words_per_row)], dtype=np.int64)
+
+
 def pack_weights(q: np.ndarray) -> np.ndarray:
     """q uint8 [N, K] with values 0..15 -> int32 [N, K/8] in the word layout."""
     q = np.asarray(q)
@@ -122,19 +150,23 @@ def pack_weights(q: np.ndarray) -> np.ndarray:
     if q.size and (q.min() < 0 or q.max() > 15):
         raise ValueError("weights must lie in 0..15")
     q8 = q.astype(np.uint32).reshape(N, K // 8, 8)
-    word = np.zeros((N, K // 8), dtype=np.uint32)
+    by_slice = np.zeros((N, K // 8), dtype=np.uint32)
     for koff in range(8):
-        word |= q8[:, :, koff] << np.uint32(4 * SLOT_OF_KOFF[koff])
-    return word.view(np.int32)
+        by_slice |= q8[:, :, koff] << np.uint32(4 * SLOT_OF_KOFF[koff])
+    # stored word j holds slice order[j]
+    stored = by_slice[:, _word_order(K // 8)]
+    return np.ascontiguousarray(stored).view(np.int32)
 
 
 def unpack_weights(wq: np.ndarray) -> np.ndarray:
     """int32 (or uint32) [N, K/8] -> uint8 [N, K]; the bits are unsigned."""
     w = np.asarray(wq).view(np.uint32)
     N, J = w.shape
+    by_slice = np.empty_like(w)
+    by_slice[:, _word_order(J)] = w
     q = np.empty((N, J, 8), dtype=np.uint8)
     for koff in range(8):
-        q[:, :, koff] = (w >> np.uint32(4 * SLOT_OF_KOFF[koff])) & np.uint32(0xF)
+        q[:, :, koff] = (by_slice >> np.uint32(4 * SLOT_OF_KOFF[koff])) & np.uint32(0xF)
     return q.reshape(N, J * 8)
 
 

@@ -100,6 +100,32 @@ def test_worked_words_two_words_and_rows():
     assert w.tolist() == [[0, 0x3], [0, 0x50000000]]
 
 
+def test_worked_words_runs_of_128_k():
+    # a row of K = 128 is one complete run of 16 words, stored as the 4x4
+    # transpose of its slices: stored word 4*r + t holds slice 4*t + r.
+    def stored_words(k_hot, K=128, val=1):
+        q = np.zeros((1, K), dtype=np.uint8)
+        q[0, k_hot] = val
+        return O.pack_weights(q).view(np.uint32)[0].tolist()
+    w = stored_words(8)          # slice 1 = 4*0 + 1 -> t=0, r=1 -> word 4
+    assert [j for j, v in enumerate(w) if v] == [4] and w[4] == 0x1
+    w = stored_words(32)         # slice 4 = 4*1 + 0 -> t=1, r=0 -> word 1
+    assert [j for j, v in enumerate(w) if v] == [1] and w[1] == 0x1
+    w = stored_words(127, val=7)  # slice 15 stays at word 15; k-offset 7 -> nibble 7
+    assert [j for j, v in enumerate(w) if v] == [15] and w[15] == 0x70000000
+    w = stored_words(8 * 6 + 1, val=3)  # slice 6 = 4*1 + 2 -> word 4*2 + 1 = 9; k-offset 1 -> nibble 4
+    assert [j for j, v in enumerate(w) if v] == [9] and w[9] == 0x30000
+    # K = 160: one complete run and an incomplete one (4 words, stored in order)
+    w = stored_words(128 + 8 * 3 + 2, K=160, val=5)   # slice 19 -> word 19; k-offset 2 -> nibble 1
+    assert [j for j, v in enumerate(w) if v] == [19] and w[19] == 0x50
+    # the map itself: an involution on complete runs, the identity on the rest
+    for J in (16, 20, 48):
+        order = [O.slice_of_word(j, J) for j in range(J)]
+        assert sorted(order) == list(range(J))
+        assert all(O.slice_of_word(order[j], J) == j for j in range(J))
+    assert [O.slice_of_word(j, 20) for j in range(16, 20)] == [16, 17, 18, 19]
+
+
 def test_worked_words_zeros():
     z = np.arange(8, dtype=np.uint8).reshape(8, 1)
     assert int(O.pack_zeros(z).view(np.uint32)[0, 0]) == 0x76543210
