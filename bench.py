@@ -10,14 +10,15 @@ group 128, bf16 activations, M = 1).  Inputs are seeded synthetic tensors of
 those shapes (no checkpoint), resident in HBM before timing starts.  Each
 step reads a different copy of the weights from a pool larger than the
 256 MB Infinity Cache, so the weights stream from HBM as they do when
-consecutive layers differ.  The step's four launches are captured once per
-copy in a HIP graph and replayed, so the host's launch overhead is not
-measured.
+consecutive layers differ.  The steps are captured in HIP graphs of one
+step per weight copy and replayed, so the host's launch overhead is spread
+over many steps and the kernels run back to back, as in a decode loop.
 
 Printed: one JSON line with decode GB/s (algorithmic bytes / time), the
-roofline of the decode kernel (per-launch HIP-event durations over the timed
-steps), the prefill TFLOP/s at M = 1920 on the Llama-3.1-8B prefill layers,
-and the CPU oracle timed on a bounded sample on this host.
+roofline of the decode kernel (per-launch durations from HIP events around
+graphs of back-to-back launches of each layer), the prefill TFLOP/s at
+M = 1920 on the Llama-3.1-8B prefill layers, and the CPU oracle timed on a
+bounded sample on this host.
 """
 from __future__ import annotations
 
@@ -81,53 +82,67 @@ class Launcher:
         self.B._check(self.B.lib.w4a16_linear(*self.args, ws, nbytes, stream_ptr))
 
 
-def time_graphs(graphs, steps, warmup):
+def capture(launch_lists, stream):
+    """One graph replaying the given launch lists back to back."""
     import torch
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        sp = torch.cuda.current_stream().cuda_stream
+        for launches in launch_lists:
+            for fn in launches:
+                fn(sp)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(step_lists, steps, warmup, stream):
+    """Time exactly `steps` steps; step i runs step_lists[i % len(step_lists)].
+
+    The steps are captured in graphs of len(step_lists) consecutive steps
+    (plus one graph for the remainder), so the host's launch cost is spread
+    over many steps and the GPU runs them back to back.
+    """
+    import torch
+    C = len(step_lists)
+    full = capture(step_lists, stream)
+    rem = capture(step_lists[: steps % C], stream) if steps % C else None
+    for _ in range(max(1, warmup // C)):
+        full.replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for i in range(steps):
-        graphs[i % len(graphs)].replay()
+    for _ in range(steps // C):
+        full.replay()
+    if rem is not None:
+        rem.replay()
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
 
 
-def capture(launch_lists, stream):
+def per_launch_durations(step_lists, reps, stream):
+    """Mean duration of each launch position, from HIP events on the launch
+    stream around graphs of `len(step_lists)` back-to-back launches of that
+    position (one per weight copy), so event overhead is spread over many
+    launches and the kernels run as they do inside a step."""
     import torch
-    graphs = []
-    for launches in launch_lists:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            sp = torch.cuda.current_stream().cuda_stream
-            for fn in launches:
-                fn(sp)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    return graphs
-
-
-def per_launch_durations(launch_lists, steps):
-    """Each launch bracketed by HIP events on its own stream: ms per layer."""
-    import torch
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
-    nl = len(launch_lists[0])
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nl)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        launches = launch_lists[i % len(launch_lists)]
-        for j, fn in enumerate(launches):
-            ev[i][j][0].record(stream)
-            fn(sp)
-            ev[i][j][1].record(stream)
-    torch.cuda.synchronize()
-    return [float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
-            for j in range(nl)]
+    out = []
+    for j in range(len(step_lists[0])):
+        g = capture([[fns[j]] for fns in step_lists], stream)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / len(step_lists))
+        out.append(float(np.median(ts)))
+    return out
 
 
 def cpu_baseline(layers_host, budget_s=30.0):
@@ -198,13 +213,12 @@ def main():
         for fn in fns:
             fn(torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    graphs = capture(launch_lists, side)
-    ms_step = time_graphs(graphs, args.steps, args.warmup)
+    ms_step = time_steps(launch_lists, args.steps, args.warmup, side)
     step_bytes = sum(decode_bytes(1, l["N"], l["K"], GROUP) for l in layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # per-launch kernel durations (same launches, eager, HIP events on the launch stream)
-    durs = per_launch_durations(launch_lists, args.steps)
+    # per-launch kernel durations of each layer
+    durs = per_launch_durations(launch_lists, max(5, args.steps // copies), side)
     per_layer = []
     for l, d in zip(layers, durs):
         b = decode_bytes(1, l["N"], l["K"], GROUP)
@@ -216,7 +230,7 @@ def main():
     achieved = mean_bytes / (mean_ms * 1e-3) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="gemv_kernel<bf16, M-tiles 1, group 128, asym>",
+                    kernel="gemv_small_kernel<bf16, group 128, asym>",
                     mean_launch_us=round(mean_ms * 1e3, 3), bytes_per_launch=int(mean_bytes),
                     per_layer=per_layer)
 
@@ -227,9 +241,9 @@ def main():
         plaunch = [[Launcher(l, l["wq"], l["zp"], l["s"]) for l in players]]
         for fn in plaunch[0]:
             fn(torch.cuda.current_stream().cuda_stream)
-        pgraphs = capture(plaunch, side)
-        pms = time_graphs(pgraphs, args.prefill_steps, max(2, args.prefill_steps // 5))
-        pdurs = per_launch_durations(plaunch, args.prefill_steps)
+        torch.cuda.synchronize()
+        pms = time_steps(plaunch, args.prefill_steps, max(2, args.prefill_steps // 5), side)
+        pdurs = per_launch_durations(plaunch * 4, max(3, args.prefill_steps // 4), side)
         flops = sum(2 * 1920 * N * K for (K, N) in PREFILL_LAYERS)
         tflops = flops / (pms * 1e-3) / 1e12
         prefill = dict(workload="Llama-3.1-8B-shaped prefill, M=1920, layers (K,N) "
@@ -241,7 +255,7 @@ def main():
                        per_layer=[dict(K=K, N=N, us=round(d * 1e3, 2),
                                        tflops=round(2 * 1920 * N * K / (d * 1e-3) / 1e12, 1))
                                   for (K, N), d in zip(PREFILL_LAYERS, pdurs)])
-        del players, plaunch, pgraphs
+        del players, plaunch
 
     cpu = None
     if not args.no_cpu_baseline:

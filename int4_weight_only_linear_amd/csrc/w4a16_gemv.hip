@@ -60,13 +60,12 @@ struct GemvParams {
   int ksteps_per_split;
   int splits;
   int kpw;      // k-steps per wave (contiguous runs)
-  // staging geometry of one K range (M <= 16 kernel): 16-byte x segments per
-  // row and quantisation groups, with reciprocals floor(2^31 / d) + 1 for the
-  // index divisions: e / d == umulhi(2e, recip) whenever e * d < 2^31
-  int xsegs_per_row;
-  uint32_t xsegs_recip;
-  int groups_per_split;
-  uint32_t groups_recip;
+  // per-wave staging geometry (M <= 16 kernel): log2 of the 16-byte x
+  // segments per row and of the groups in one wave's run of kpw k-steps, and
+  // the bytes of one wave's LDS region
+  int lg_xsegs_per_wave;
+  int lg_groups_per_wave;
+  int wave_lds_bytes;
 };
 
 // Store or hand over the reduced sums of one row tile: with one K range the
@@ -126,20 +125,24 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // ---------------------------------------------------------------------------
 // M <= 16
 // ---------------------------------------------------------------------------
+// Each wave stages only what it reads -- x, scales and zero points of its own
+// run of k-steps -- in a private LDS region, so no wave waits for another
+// before its dot products; the only barrier is the final cross-wave sum.
+// All staging index maps are shifts and masks (the per-wave sizes are powers
+// of two), keeping the vector-ALU work in front of the weight loads small.
 template <int DT, int GS, bool ASYM, int KPW, int XPT>
 __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
-  constexpr int SPT = (32 * KPW) / GS;  // scale loads per thread (see plan_gemv)
+  constexpr int SPT = (32 * KPW) / GS;  // scale loads per lane for kpw = KPW
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
   const int lane = tid & 63;
   // wave index as a wave-uniform (scalar) value, so the per-wave k-step
   // bookkeeping below stays in SGPRs and its branches are scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nwaves = nthr >> 6;
+  const int nwaves = blockDim.x >> 6;
   const int col = lane & 15;   // MFMA column: output row within the tile
   const int row4 = lane >> 4;  // 16-lane row of the wave
   const int tile = blockIdx.x;
@@ -147,50 +150,49 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   const int n0 = tile * kGemvRowsPerTile;
   const int nc = min(n0 + col, p.N - 1);  // rows past N read row N-1; their outputs are dropped
 
-  // Every workgroup stages a full-size K range (the last one may extend past
-  // K: those loads are clamped and the values never used), so the index maps
-  // below divide by per-launch constants, done with host-computed reciprocals.
   const int ks_begin = split * p.ksteps_per_split;
   const int ks_end = min(p.ksteps, ks_begin + p.ksteps_per_split);
-  const int k0 = ks_begin * kGemvKStep;
-  const int grp0 = k0 / GS;
-  const int segs = p.xsegs_per_row;  // 16-byte x segments per row of the K range
-  const int ngr = p.groups_per_split;
-  const int xstride = segs * 8 + 8;  // padded LDS row of x, in halves
-  const int my_first = ks_begin + wave * p.kpw;
-  const int my_steps = max(0, min(p.kpw, ks_end - my_first));
+  const int kpw = p.kpw;                      // a power of two
+  const int my_first = ks_begin + wave * kpw;
+  const int my_steps = max(0, min(kpw, ks_end - my_first));
+  const int kw0 = my_first * kGemvKStep;      // first k of this wave's run
+  const int gw0 = kw0 / GS;                   // first group of this wave's run
+  const int ngw = kpw * (kGemvKStep / GS);    // groups per wave run (power of two)
+  const int lg_ngw = p.lg_groups_per_wave;
+  const int xsegs_row = kpw * (kGemvKStep / 8);  // 16-byte x segments per row of the run
+  const int lg_xsegs = p.lg_xsegs_per_wave;
+  const int xstride = xsegs_row * 8 + 8;      // padded LDS row of x, in halves
 
-  // LDS layout (gemv_lds_bytes sizes it the same way)
-  float* red = reinterpret_cast<float*>(smem);                     // [nwaves][256]
-  uint16_t* xs = reinterpret_cast<uint16_t*>(red + nwaves * 256);  // [M][xstride]
-  uint16_t* sl = xs + p.M * xstride;                               // [16][ngr]
-  uint32_t* zl = reinterpret_cast<uint32_t*>(sl + 16 * ngr);       // [2][ngr]
+  // LDS: the cross-wave sums, then one region per wave (gemv_lds_bytes)
+  float* red = reinterpret_cast<float*>(smem);  // [nwaves][256]
+  unsigned char* wreg = smem + (size_t)nwaves * 256 * sizeof(float) + (size_t)wave * p.wave_lds_bytes;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(wreg);   // [M][xstride]
+  uint16_t* sl = xs + p.M * xstride;                  // [16][ngw]
+  uint32_t* zl = reinterpret_cast<uint32_t*>(sl + 16 * ngw);  // [2][ngw]
 
-  // ---- 1. loads: x, scales and zero points (to be staged), then weights ----
-  // Branch-free: addresses are clamped and results masked where used, so the
-  // loads go out back to back and every wait has an exact count.
-  const int xsegs = p.M * segs;
+  // ---- 1. loads: x, scales and zero points of this wave's run, then weights ----
+  const int xsegs = p.M * xsegs_row;
   u32x4 xr[XPT];
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    const uint32_t e = (uint32_t)min(tid + j * nthr, xsegs - 1);
-    const uint32_t m = __umulhi(e << 1, p.xsegs_recip);
-    const int k = min(k0 + (int)(e - m * segs) * 8, p.K - 8);
+    const int e = min(lane + 64 * j, xsegs - 1);
+    const int m = e >> lg_xsegs;
+    const int k = min(kw0 + ((e & (xsegs_row - 1)) << 3), p.K - 8);
     xr[j] = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + k);
   }
   uint32_t sr[SPT];
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
-    const uint32_t e = (uint32_t)min(tid + j * nthr, 16 * ngr - 1);
-    const uint32_t r = __umulhi(e << 1, p.groups_recip);
-    const int g = min(grp0 + (int)(e - r * ngr), p.G - 1);
-    sr[j] = p.scales[(size_t)min(n0 + (int)r, p.N - 1) * p.G + g];
+    const int e = min(lane + 64 * j, 16 * ngw - 1);
+    const int r = e >> lg_ngw;
+    const int g = min(gw0 + (e & (ngw - 1)), p.G - 1);
+    sr[j] = p.scales[(size_t)min(n0 + r, p.N - 1) * p.G + g];
   }
   uint32_t zr = 0u;
   if constexpr (ASYM) {
-    const int e = min(tid, 2 * ngr - 1);
-    const int rr = e >= ngr ? 1 : 0;
-    const int g = min(grp0 + e - rr * ngr, p.G - 1);
+    const int e = min(lane, 2 * ngw - 1);
+    const int rr = e >> lg_ngw;
+    const int g = min(gw0 + (e & (ngw - 1)), p.G - 1);
     zr = p.zp[(size_t)min((n0 >> 3) + rr, (p.N >> 3) - 1) * p.G + g];
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -210,43 +212,43 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. stage x, scales and zero points in LDS ----
+  // ---- 2. stage them in this wave's LDS region (read back by the same wave) ----
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    const uint32_t e = (uint32_t)(tid + j * nthr);
-    if (e < (uint32_t)xsegs) {
-      const uint32_t m = __umulhi(e << 1, p.xsegs_recip);
-      *reinterpret_cast<u32x4*>(xs + m * xstride + (e - m * segs) * 8) = xr[j];
+    const int e = lane + 64 * j;
+    if (e < xsegs) {
+      const int m = e >> lg_xsegs;
+      *reinterpret_cast<u32x4*>(xs + m * xstride + ((e & (xsegs_row - 1)) << 3)) = xr[j];
     }
   }
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
-    const int e = tid + j * nthr;
-    if (e < 16 * ngr) sl[e] = (uint16_t)sr[j];
+    const int e = lane + 64 * j;
+    if (e < 16 * ngw) sl[e] = (uint16_t)sr[j];
   }
   if constexpr (ASYM) {
-    if (tid < 2 * ngr) zl[tid] = zr;
+    if (lane < 2 * ngw) zl[lane] = zr;
   }
-  __syncthreads();
 
   // ---- 3. dot products, one k-step at a time as its weights arrive ----
   const uint32_t mask_v = vgpr_const(0x000F000Fu);
   const uint16_t* xrow = xs + min(col, p.M - 1) * xstride + row4 * 8;  // rows >= M: any valid row
-  const uint16_t* srow_l = sl + col * ngr;
-  const uint32_t* zrow_l = zl + (col >> 3) * ngr;
+  const uint16_t* srow_l = sl + col * ngw;
+  const uint32_t* zrow_l = zl + (col >> 3) * ngw;
   const int zshift = 4 * (col & 7);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
   // one k-step (four 32-k chunks); FULL: all four chunks lie inside K
-  auto kstep = [&](const u32x4 wraw, const int c0, auto full) {
+  auto kstep = [&](const u32x4 wraw, const int i, auto full) {
     constexpr bool FULL = decltype(full)::value;
+    const int c0 = (my_first + i) * 4;
     // a complete 128-k run is stored transposed, so register t already holds
     // this lane's slice of chunk t; an incomplete last run is stored in
     // order and is transposed across the 16-lane rows here
     u32x4 wt = wraw;
     if constexpr (!FULL) transpose_rows4(wt);
-    // fp16: chains ch[0], ch[1] by chunk parity.  bf16: ch[0] collects
-    // x . (128 + q), ch[1] collects x . (-(128 + z)) from the second MFMA.
+    // fp16: two chains by chunk parity.  bf16: one chain collecting both
+    // x . (128 + q) and, from a second MFMA, x . (-(128 + z)).
     f32x4 ch[2];
     uint32_t nmz = neg_magic_pair<DT>(8u);
     u32x4 bcv = {nmz, nmz, nmz, nmz};
@@ -254,14 +256,14 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
     for (int t = 0; t < 4; ++t) {
       const int c = c0 + t;
       if (!FULL && c >= p.nchunks) break;
-      const int gl = c / CPG - grp0;  // group within this K range
+      const int gl = i * (4 / CPG) + t / CPG;  // group within this wave's run
       if constexpr (ASYM) {
         if (t % CPG == 0) {
           nmz = neg_magic_pair<DT>((zrow_l[gl] >> zshift) & 0xFu);
           if constexpr (DT == DT_BF16) bcv = u32x4{nmz, nmz, nmz, nmz};
         }
       }
-      const u32x4 a = *reinterpret_cast<const u32x4*>(xrow + (c * 32 - k0));
+      const u32x4 a = *reinterpret_cast<const u32x4*>(xrow + i * kGemvKStep + t * 32);
       const bool fresh = (t % CPG) == 0;
       if constexpr (DT == DT_F16) {
         const u32x4 bq = qz_word_f16(wt[t], mask_v, nmz);  // q - z, exact
@@ -270,16 +272,12 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
       } else {
         const u32x4 bq = magic_word<DT>(wt[t], mask_v);     // 128 + q, exact
         ch[0] = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[0]);
-        ch[1] = mfma16x16x32<DT>(a, bcv, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[1]);
+        ch[0] = mfma16x16x32<DT>(a, bcv, ch[0]);
       }
       if (t % CPG == CPG - 1) {
         const float s = act_to_f32<DT>(srow_l[gl]);
-        if constexpr (DT == DT_F16 && CPG == 1) {
-          acc += s * ch[0];
-        } else {
-          acc += s * ch[0];
-          acc += s * ch[1];
-        }
+        acc += s * ch[0];
+        if constexpr (DT == DT_F16 && CPG > 1) acc += s * ch[1];
       }
     }
   };
@@ -287,11 +285,10 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     if (i >= my_steps) break;
-    const int c0 = (my_first + i) * 4;
-    if (c0 + 4 <= p.nchunks)
-      kstep(wv[i], c0, std::true_type{});
+    if ((my_first + i) * 4 + 4 <= p.nchunks)
+      kstep(wv[i], i, std::true_type{});
     else
-      kstep(wv[i], c0, std::false_type{});
+      kstep(wv[i], i, std::false_type{});
   }
 
   // ---- 4. reduce the waves in order, then the K ranges ----
@@ -400,14 +397,20 @@ __global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
 // planning and launch
 // ---------------------------------------------------------------------------
 
-size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int ksteps_per_split, int group) {
+// one wave's staging region of the M <= 16 kernel: x rows of its run (padded
+// by 16 bytes), the scales of its 16 rows and groups, the zero-point words
+size_t gemv_wave_lds_bytes(int64_t M, int kpw, int group) {
+  const size_t kr = (size_t)kpw * kGemvKStep;
+  const size_t ngr = kr / (size_t)group;
+  const size_t b = (size_t)M * (kr + 8) * sizeof(uint16_t) + 16 * ngr * sizeof(uint16_t) +
+                   2 * ngr * sizeof(uint32_t);
+  return (b + 15) / 16 * 16;
+}
+
+size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int kpw, int group) {
   const size_t red = (size_t)waves * mtiles * 256 * sizeof(float);
   if (mtiles > 1) return red;
-  const size_t kr = (size_t)ksteps_per_split * kGemvKStep;
-  const size_t ngr = kr / (size_t)group;
-  return red + (size_t)M * (kr + 8) * sizeof(uint16_t)  // x
-         + 16 * ngr * sizeof(uint16_t)                  // scales
-         + 2 * ngr * sizeof(uint32_t);                  // zero-point words
+  return red + (size_t)waves * gemv_wave_lds_bytes(M, kpw, group);
 }
 
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
@@ -416,16 +419,14 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   p.ksteps = (int)((K + kGemvKStep - 1) / kGemvKStep);
   p.mtiles = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.xlds = p.mtiles == 1;
-  // k-steps per wave: at most kGemvStepsPerWave; with x staged, also few
-  // enough that a thread stages at most kGemvXSegsPerThread x segments
-  // (M * 16 segments per k-step, 64 threads per wave).  The scale and
-  // zero-point staging then needs at most 32 * kpw / group and 4 * kpw /
-  // group loads per thread, which the kernel's fixed counts cover.
+  // k-steps per wave: a power of two, at most kGemvStepsPerWave; with x
+  // staged, also small enough that a lane stages at most kGemvXSegsPerThread
+  // x segments (M * 16 * kpw segments per wave, 64 lanes): kpw <= 4 * XPT / M.
+  // The scale and zero-point staging then needs at most 32 * kpw / group and
+  // 4 * kpw / group loads per lane, which the kernel's fixed counts cover.
   int kpw = kGemvStepsPerWave;
-  if (p.xlds) {
-    const int cap = (int)((4 * kGemvXSegsPerThread) / M);
-    if (cap < kpw) kpw = cap < 1 ? 1 : cap;
-  }
+  if (p.xlds)
+    while (kpw > 1 && M * kpw > 4 * kGemvXSegsPerThread) kpw >>= 1;
   p.kpw = kpw;
   // split K until every row tile has enough workgroups to cover the CUs, a
   // workgroup has at most kGemvMaxWaves waves, and its LDS fits the budget
@@ -433,17 +434,17 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   if (p.tiles < cu_count) splits = (cu_count + p.tiles - 1) / p.tiles;
   for (;;) {
     if (splits > p.ksteps) splits = p.ksteps;
-    int kps = (p.ksteps + splits - 1) / splits;
+    const int kps = (p.ksteps + splits - 1) / splits;
     const int waves = (kps + kpw - 1) / kpw;
     if (splits == p.ksteps ||
-        (waves <= kGemvMaxWaves && gemv_lds_bytes(waves, p.mtiles, M, kps, group) <= kGemvLdsBudget))
+        (waves <= kGemvMaxWaves && gemv_lds_bytes(waves, p.mtiles, M, kpw, group) <= kGemvLdsBudget))
       break;
     ++splits;
   }
   p.ksteps_per_split = (p.ksteps + splits - 1) / splits;
   p.splits = (p.ksteps + p.ksteps_per_split - 1) / p.ksteps_per_split;
   p.waves = (p.ksteps_per_split + kpw - 1) / kpw;
-  p.lds_bytes = gemv_lds_bytes(p.waves, p.mtiles, M, p.ksteps_per_split, group);
+  p.lds_bytes = gemv_lds_bytes(p.waves, p.mtiles, M, kpw, group);
   return p;
 }
 
@@ -521,10 +522,15 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
   prm.ksteps_per_split = plan.ksteps_per_split;
   prm.splits = plan.splits;
   prm.kpw = plan.kpw;
-  prm.xsegs_per_row = plan.ksteps_per_split * (kGemvKStep / 8);
-  prm.groups_per_split = plan.ksteps_per_split * kGemvKStep / a.group;
-  prm.xsegs_recip = (uint32_t)((1ull << 31) / (uint64_t)prm.xsegs_per_row + 1);
-  prm.groups_recip = (uint32_t)((1ull << 31) / (uint64_t)prm.groups_per_split + 1);
+  {
+    int lg = 0;
+    while ((1 << lg) < plan.kpw * (kGemvKStep / 8)) ++lg;
+    prm.lg_xsegs_per_wave = lg;
+    lg = 0;
+    while ((1 << lg) < plan.kpw * kGemvKStep / a.group) ++lg;
+    prm.lg_groups_per_wave = lg;
+    prm.wave_lds_bytes = (int)gemv_wave_lds_bytes(a.M, plan.kpw, a.group);
+  }
   return a.dtype == DT_F16 ? launch_m<DT_F16>(prm, a.group, plan, stream)
                            : launch_m<DT_BF16>(prm, a.group, plan, stream);
 }

@@ -52,7 +52,8 @@ struct GemvPlan {
   size_t lds_bytes;      // dynamic LDS of one workgroup
 };
 
-size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int ksteps_per_split, int group);
+size_t gemv_wave_lds_bytes(int64_t M, int kpw, int group);
+size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int kpw, int group);
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N);
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& p, void* workspace,
