@@ -50,6 +50,29 @@ def decode_bytes(M, N, K, g, asym=True, bias=False):
     return b
 
 
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "gemv_small_kernel_llama8b_decode_M1_traffic.txt")
+DECODE_SOURCES = ("w4a16_gemv.hip", "w4a16_device.hpp", "w4a16_internal.h")
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (scaled by a copy of known size), or None when the decode
+    kernel's sources have changed since those counters were taken."""
+    import hashlib
+    try:
+        fields = dict(l.split(": ", 1) for l in open(TRAFFIC_PROFILE).read().splitlines() if ": " in l)
+        h = hashlib.sha256()
+        csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "int4_weight_only_linear_amd", "csrc")
+        for f in DECODE_SOURCES:
+            h.update(open(os.path.join(csrc, f), "rb").read())
+        if fields.get("kernel_source_sha256", "").strip() != h.hexdigest():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def build_layer(K, N, M, seed, device):
     import torch
     from synth import make_case
@@ -184,6 +207,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MB (for scaling PMC byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -199,6 +224,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     import int4_weight_only_linear_amd as L  # noqa: F401  (loads libw4a16; raises if missing)
+
+    if args.calibration_copy_mb:
+        # a plain copy of known size: reads and writes exactly n bytes, so the
+        # HBM byte counters of this dispatch give their scale on this device
+        n = args.calibration_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.bitwise_not(src, out=dst)  # one elementwise kernel: n bytes in, n out
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- decode: four layers at M = 1, weight copies rotated through HBM ----
     layers = [build_layer(K, N, 1, ("bench-decode", K, N), dev) for (K, N) in DECODE_LAYERS]
@@ -228,8 +264,10 @@ def main():
     mean_bytes = step_bytes / len(layers)
     mean_ms = float(np.mean(durs))
     achieved = mean_bytes / (mean_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    traffic_unit="bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                     kernel="gemv_small_kernel<bf16, group 128, asym>",
                     mean_launch_us=round(mean_ms * 1e3, 3), bytes_per_launch=int(mean_bytes),
                     per_layer=per_layer)
