@@ -144,6 +144,23 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   }
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 32x32x16 MFMA, fp32 accumulate.  Operand layout (per lane l of the wave):
+//   A[i][k]: i = l % 32, k = 8 * (l / 32) + e, e = 0..7 (the 8 packed values)
+//   B[k][j]: j = l % 32, same k
+//   D[i][j]: j = l % 32, i = 8 * (r / 4) + 4 * (l / 32) + r % 4, r = 0..15
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == DT_F16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+}
+
 // 4x4 transpose of dwords across the four 16-lane rows of a wave:
 // on entry lane row j holds v[t] = element (j, t); on exit it holds (t, j).
 // Two rounds of row swaps: rows {0,1} <-> {2,3}, then odd <-> even rows.
@@ -158,42 +175,57 @@ __device__ __forceinline__ void transpose_rows4(u32x4& v) {
   v[3] = d[1];
 }
 
+// v & 0x0F0F0F0F as one v_and_b32 the optimiser cannot see through
+__device__ __forceinline__ uint32_t mask_nibbles(uint32_t v) {
+  uint32_t r;
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
 // Exact dequantisation of one word (8 weights) to activation-dtype pairs:
-// out[i] holds k = 2i (low half) and 2i+1 (high half), each (q - z) * s
+// element i holds k = 2i (low half) and 2i+1 (high half), each (q - z) * s
 // rounded once to nearest even.
 //   fp16: (magic + q) - (magic + z) is exact in fp16 (|q - z| <= 15), the
 //         product with s is one correctly rounded fp16 multiply.
-//   bf16: fma(128 + q, s, -(128 + z) * s) in fp32 is exact (both products fit
-//         in 16 significant bits and the result is a multiple of ulp(s)), then
-//         one nearest-even conversion to bf16.
-// s_pair: the scale in both halves (fp16 path); s_f32 / c_f32 = s and
-// -(128 + z) * s (bf16 path); nmz_pair = -(magic + z) in both halves.
+//   bf16: the codes become fp32 through byte conversions (the even and odd
+//         nibbles masked into bytes), then fma(q, s, -z * s): q * s and z * s
+//         need at most 4 + 8 significant bits, so both and their difference
+//         (q - z) * s are exact in fp32, and one nearest-even conversion per
+//         pair rounds them to bf16.
+// s_pair: the scale in both halves and nmz_pair = -(magic + z) in both halves
+// (fp16); s_f32 = s and c_f32 = -z * s (bf16).
 template <int DT>
-__device__ __forceinline__ void dequant_word_exact(uint32_t w, uint32_t s_pair, uint32_t nmz_pair,
-                                                   float s_f32, float c_f32, uint32_t out[4]) {
+__device__ __forceinline__ u32x4 dequant_word(uint32_t w, uint32_t s_pair, uint32_t nmz_pair,
+                                              float s_f32, float c_f32) {
   if constexpr (DT == DT_F16) {
     const half2_t s2 = __builtin_bit_cast(half2_t, s_pair);
     const half2_t nmz = __builtin_bit_cast(half2_t, nmz_pair);
+    uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       half2_t v = __builtin_bit_cast(half2_t, magic_pair<DT_F16>(w, i));
       v = v + nmz;
       v = v * s2;
-      out[i] = __builtin_bit_cast(uint32_t, v);
+      o[i] = __builtin_bit_cast(uint32_t, v);
     }
+    return u32x4{o[0], o[1], o[2], o[3]};
   } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t t = w >> (4 * i);
-      const float lo = __builtin_bit_cast(float, ((t << 16) & 0x000F0000u) | 0x43000000u);
-      const float hi = __builtin_bit_cast(float, (t & 0x000F0000u) | 0x43000000u);
-      out[i] = f32x2_to_act_pair<DT_BF16>(__builtin_fmaf(lo, s_f32, c_f32),
-                                          __builtin_fmaf(hi, s_f32, c_f32));
-    }
+    // nibbles 0,2,4,6 (k = 0, 4, 1, 5) and 1,3,5,7 (k = 2, 6, 3, 7) in bytes;
+    // the masks are opaque to the compiler, which would otherwise fold each
+    // byte conversion back into a per-nibble bitfield extract
+    const uint32_t ev = mask_nibbles(w);
+    const uint32_t od = mask_nibbles(w >> 4);
+    auto f = [&](uint32_t v, int b) {
+      return __builtin_fmaf((float)((v >> (8 * b)) & 0xFFu), s_f32, c_f32);
+    };
+    return u32x4{f32x2_to_act_pair<DT_BF16>(f(ev, 0), f(ev, 2)),
+                 f32x2_to_act_pair<DT_BF16>(f(od, 0), f(od, 2)),
+                 f32x2_to_act_pair<DT_BF16>(f(ev, 1), f(ev, 3)),
+                 f32x2_to_act_pair<DT_BF16>(f(od, 1), f(od, 3))};
   }
 }
 
-// per (row, group) constants for dequant_word_exact
+// per (row, group) constants for dequant_word
 template <int DT>
 struct GroupConst {
   uint32_t s_pair;
@@ -208,8 +240,7 @@ __device__ __forceinline__ GroupConst<DT> group_const(uint16_t s_bits, uint32_t 
   g.s_pair = (uint32_t)s_bits | ((uint32_t)s_bits << 16);
   g.nmz_pair = neg_magic_pair<DT>(z);
   g.s_f32 = act_to_f32<DT>(s_bits);
-  // -(128 + z) * s is exact in fp32 (8 + 8 significant bits); used by bf16 only
-  g.c_f32 = -(128.0f + (float)z) * g.s_f32;
+  g.c_f32 = -(float)z * g.s_f32;  // exact: 4 + 8 significant bits (bf16 only)
   return g;
 }
 

@@ -27,10 +27,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
     const uint16_t sbits = scales[n * G + grp];
     const uint32_t z = ASYM ? zero_point(zp, (int)n, (int)G, (int)grp) : 8u;
     const GroupConst<DT> gc = group_const<DT>(sbits, z);
-    uint32_t o[4];
-    dequant_word_exact<DT>(__builtin_nontemporal_load(wq + idx), gc.s_pair, gc.nmz_pair, gc.s_f32,
-                           gc.c_f32, o);
-    *reinterpret_cast<u32x4*>(w + n * K + j * 8) = u32x4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<u32x4*>(w + n * K + j * 8) = dequant_word<DT>(
+        __builtin_nontemporal_load(wq + idx), gc.s_pair, gc.nmz_pair, gc.s_f32, gc.c_f32);
   }
 }
 

@@ -1,20 +1,31 @@
-// Prefill W4A16 GEMM for gfx950: dequantise weight tiles into LDS, multiply
-// with bf16/fp16 MFMA, accumulate in fp32.
+// Prefill W4A16 GEMM for gfx950: y = x . dequant(Wq)^T (+ bias) with fp16 /
+// bf16 MFMA and fp32 accumulation.
 //
 // The pages route M above the decode threshold to a fused dequantise-then-
 // GEMM kernel ("[ROCm][Kernel] Add HybridW4A16LinearKernel: Triton prefill +
-// HIP skinny decode", description).  Here that kernel is hand-written HIP:
+// HIP skinny decode", description).  Here it is hand-written for CDNA4:
 //
-// * Workgroup tile BM x BN = 128 x 128, k-tile BK = 128 (one stored 128-k run
-//   of each weight row), 256 threads (4 waves, each a 64 x 64 sub-tile of
-//   4 x 4 v_mfma_f32_16x16x32 tiles).
-// * Per k-tile each thread loads 128 B of x and two 16-byte pieces of one
-//   weight row's run, dequantises them exactly -- (q - z) * s rounded once to
-//   the activation dtype, the same value w4a16_dequant returns -- and stores
-//   both to LDS in k order.  The next k-tile's global loads are issued before
-//   the current one is multiplied.
-// * LDS rows are padded by 16 bytes so the 16 lanes that read one MFMA
-//   operand column hit different banks.
+// * A workgroup (4 waves) owns BM = 32*MB tokens by 256 output features; each
+//   wave owns 64 features (two 32-wide blocks) across all BM tokens, so every
+//   weight is dequantised exactly once per workgroup, by the wave that
+//   multiplies it.
+// * A k-step is one stored 128-k run of each weight row.  The weights are the
+//   MFMA A operand (v_mfma_f32_32x32x16): lane (j, h) needs 8 consecutive k of
+//   row j, i.e. one packed word, and the run's 4x4 word transpose puts the
+//   eight words a lane needs for the whole k-step into two 16-byte loads.
+//   They are dequantised in registers (the exact per-weight value that
+//   w4a16_dequant returns) and fed straight to the MFMA: no LDS round trip.
+// * The activations x are the B operand.  They are staged in LDS by direct
+//   global->LDS loads (global_load_lds_dwordx4), double buffered, with the
+//   16-byte pieces of each 256-byte row XOR-swizzled by (row mod 16) so the
+//   fragment reads of 16 consecutive lanes hit 16 different bank groups.
+// * The output tile of a wave is 64 features x BM tokens; in the MFMA result
+//   layout a lane holds 4 consecutive features of one token, and one
+//   permlane32 swap turns two such quads into 16 contiguous output bytes.
+// * Work units (tile, K split) are remapped so that consecutive units -- the
+//   same token rows, neighbouring features -- run on the same XCD and share
+//   its L2.  With more than one split, units store fp32 partial tiles and the
+//   last one to finish a tile adds them up in split order (deterministic).
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
 
@@ -22,14 +33,14 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 128;
-constexpr int LDK = BK + 8;  // padded LDS row, in 16-bit elements
 constexpr int kThreads = 256;
-constexpr int A_LOADS = BM * BK / 8 / kThreads;  // 16-byte x loads per thread (8)
-constexpr size_t kLdsBytes = (size_t)(BM + BN) * LDK * sizeof(uint16_t);
-static_assert(kLdsBytes <= 160 * 1024, "GEMM tiles exceed the 160 KiB of LDS per CU");
+constexpr int kBN = 256;         // output features per workgroup (64 per wave)
+constexpr int kBK = 128;         // k per step: one stored run of every row
+constexpr int kXRowBytes = 256;  // one staged x row: 128 k of 16-bit values
+constexpr int kXcds = 8;
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
 struct GemmParams {
   const uint16_t* x;
@@ -38,175 +49,442 @@ struct GemmParams {
   const uint32_t* zp;
   const uint16_t* bias;
   uint16_t* y;
+  float* partial;
+  uint32_t* counters;
   int M, N, K, G;
-  int nchunks;
+  int wpr;             // words per weight row, K / 8
+  int nsteps;          // ceil(K / 128)
+  int full_steps;      // K / 128: steps over complete (transposed) runs
+  int tiles_n;         // ceil(N / 256)
+  int units;           // tiles * splits = grid size
+  int splits;
+  int steps_per_split;
+  int vec_store;       // y rows are 16-byte aligned and N % 8 == 0
 };
 
-template <int DT, int GS, bool ASYM>
+// Workgroups are dispatched round-robin over the XCDs; give each XCD a
+// contiguous range of work units instead.
+__device__ __forceinline__ int xcd_unit(int b, int units) {
+  const int q = units / kXcds, r = units % kXcds;
+  const int xcd = b % kXcds, local = b / kXcds;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int DT, int GS, bool ASYM, int MB>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+  constexpr int BM = 32 * MB;
+  constexpr int XBUF = BM * kXRowBytes;  // bytes of one x buffer
+  constexpr int NDMA = BM / 16;          // 1 KiB global->LDS loads per wave and step
+  constexpr int GPS = kBK / GS;          // groups per k-step
+  // two separate arrays, so the compiler can tell that loads into one buffer
+  // never alias fragment reads of the other (no wait on the former before
+  // the latter)
+  __shared__ __attribute__((aligned(1024))) unsigned char xs0[XBUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char xs1[XBUF];
+  __shared__ uint32_t last_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
-  const int nkt = (p.K + BK - 1) / BK;
-  const int words_per_row = p.K >> 3;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31;
+  const int h = lane >> 5;
 
-  // weight loader: row b_row, 16-byte pieces b_q and b_q + 1 (stored words
-  // 4*b_q .. 4*b_q + 7 of the row's run)
-  const int b_row = tid >> 1;
-  const int b_q0 = (tid & 1) * 2;
-  const int b_n = n0 + b_row;
-  const bool b_nvalid = b_n < p.N;
-  const uint32_t* b_src = p.wq + (size_t)(b_nvalid ? b_n : 0) * words_per_row;
+  const int unit = xcd_unit(blockIdx.x, p.units);
+  const int tile = unit / p.splits;
+  const int split = unit - tile * p.splits;
+  const int mt = tile / p.tiles_n;
+  const int nt = tile - mt * p.tiles_n;
+  const int m0 = mt * BM;
+  const int nw0 = nt * kBN + wave * 64;  // first output feature of this wave
+  const int s_begin = split * p.steps_per_split;
+  const int s_end = min(p.nsteps, s_begin + p.steps_per_split);
+  const int s_full_end = min(s_end, p.full_steps);
 
-  u32x4 areg[A_LOADS];
-  u32x4 breg[2];
-  uint16_t b_s[2][4];
-  uint32_t b_z[2][4];
-
-  auto load_tile = [&](int kt) {
+  // ---- x staging: load d of this wave writes LDS rows row0 + 4d + lane/16;
+  // lane position (lane & 15) of a row holds the row's piece pos ^ (row & 15).
+  const int row0 = wave * (BM / 4);
+  uint32_t xoff[NDMA];
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int id = tid + kThreads * i;
-      const int row = id >> 4;  // 16 segments per 128-k row
-      const int seg = id & 15;
-      const int m = m0 + row;
-      const int k = kt * BK + seg * 8;
-      areg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (m < p.M && k < p.K) areg[i] = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + k);
-    }
-    const bool complete = (kt + 1) * BK <= p.K;
+  for (int d = 0; d < NDMA; ++d) {
+    const int row = row0 + 4 * d + (lane >> 4);
+    const int piece = (lane & 15) ^ (row & 15);
+    const int m = min(m0 + row, p.M - 1);
+    xoff[d] = ((uint32_t)m * (uint32_t)p.K + 8u * (uint32_t)piece) * 2u;
+  }
+  auto stage_x = [&](int s, lds_u8* buf, bool tail) {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(p.x) + (size_t)s * kXRowBytes;
+    const int kvalid = p.K - s * kBK;  // < 128 only on the last, incomplete run
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = b_q0 + h;  // piece within the run
-      breg[h] = u32x4{0u, 0u, 0u, 0u};
-      const int w0 = kt * 16 + q * 4;  // first stored word of the piece
-      if (b_nvalid && w0 < words_per_row) {
-        breg[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_src + w0));
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // word t of the piece holds slice 4t + q of a complete run, or
-          // slice 4q + t of an incomplete one (stored in order)
-          const int slice = kt * 16 + (complete ? 4 * t + q : 4 * q + t);
-          const int grp = min((slice * 8) / GS, p.G - 1);
-          b_s[h][t] = p.scales[(size_t)b_n * p.G + grp];
-          b_z[h][t] = ASYM ? zero_point(p.zp, b_n, p.G, grp) : 8u;
-        }
+    for (int d = 0; d < NDMA; ++d) {
+      uint32_t off = xoff[d];
+      if (tail) {
+        // pieces past K would read beyond the row (and the buffer, on the
+        // last row): point them at piece 0; their k-steps are never used
+        const int row = row0 + 4 * d + (lane >> 4);
+        const int piece = (lane & 15) ^ (row & 15);
+        if (8 * piece >= kvalid) off -= 16u * (uint32_t)piece;
       }
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off),
+                                       buf + (row0 + 4 * d) * kXRowBytes,
+                                       16, 0, 0);
     }
   };
 
-  auto store_tile = [&](int kt) {
+  // ---- weights: lane j of column block cb reads row n = nw0 + 32 cb + j
+  int nrow[2];
+  uint32_t woff[2];
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int id = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(&As[(id >> 4) * LDK + (id & 15) * 8]) = areg[i];
-    }
-    const bool complete = (kt + 1) * BK <= p.K;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = b_q0 + h;
-      const int w0 = kt * 16 + q * 4;
-      const bool valid = b_nvalid && w0 < words_per_row;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int ks = complete ? 4 * t + q : 4 * q + t;  // slice within the tile
-        u32x4 o4 = {0u, 0u, 0u, 0u};
-        if (valid && (complete || kt * 16 + ks < words_per_row)) {
-          const GroupConst<DT> gc = group_const<DT>(b_s[h][t], b_z[h][t]);
-          uint32_t o[4];
-          dequant_word_exact<DT>(breg[h][t], gc.s_pair, gc.nmz_pair, gc.s_f32, gc.c_f32, o);
-          o4 = u32x4{o[0], o[1], o[2], o[3]};
-        }
-        *reinterpret_cast<u32x4*>(&Bs[b_row * LDK + ks * 8]) = o4;
-      }
-    }
-  };
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  load_tile(0);
-  const int frag_row = lane & 15;
-  const int frag_k = (lane >> 4) * 8;
-  for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();  // the previous tile's MFMAs are done with the LDS
-    store_tile(kt);
-    __syncthreads();
-    if (kt + 1 < nkt) load_tile(kt + 1);  // in flight while this tile is multiplied
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      u32x4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(&As[(wm * 64 + i * 16 + frag_row) * LDK + kk + frag_k]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(&Bs[(wn * 64 + j * 16 + frag_row) * LDK + kk + frag_k]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32<DT>(af[i], bf[j], acc[i][j]);
-    }
+  for (int cb = 0; cb < 2; ++cb) {
+    nrow[cb] = min(nw0 + 32 * cb + j, p.N - 1);
+    woff[cb] = (uint32_t)nrow[cb] * (uint32_t)p.wpr * 4u + 16u * (uint32_t)h;
   }
 
-  // epilogue: + bias in fp32, one rounding to the activation dtype
+  struct StepRegs {
+    u32x4 w[2][2];        // [cb][piece]: word t of piece pc is k-sub 2t + pc
+    uint16_t s[2][GPS];   // scales of the step's groups
+    uint32_t z[2][GPS];   // packed zero-point words
+  };
+  // complete run: pieces h and h + 2 of the run's four 16-byte pieces
+  auto load_full = [&](int s, StepRegs& r) {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(p.wq) + (size_t)s * 64;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int nn = n0 + wn * 64 + j * 16 + (lane & 15);
-    if (nn >= p.N) continue;
-    const float b = p.bias ? act_to_f32<DT>(p.bias[nn]) : 0.f;
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int pc = 0; pc < 2; ++pc)
+        r.w[cb][pc] = *reinterpret_cast<const u32x4*>(base + woff[cb] + 32 * pc);
+  };
+  // incomplete run, stored in slice order: k-sub ks of half h is word 2 ks + h
+  auto load_tail = [&](int s, StepRegs& r) {
+    const int nks = (p.K - s * kBK) / 16;
+    const uint32_t* base = p.wq + (size_t)s * 16;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint32_t v = 0u;
+        if (ks < nks) v = base[(size_t)nrow[cb] * p.wpr + 2 * ks + h];
+        r.w[cb][ks & 1][ks >> 1] = v;
+      }
+  };
+  auto load_meta = [&](int s, StepRegs& r) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int gi = 0; gi < GPS; ++gi) {
+        const int g = min(s * GPS + gi, p.G - 1);
+        r.s[cb][gi] = p.scales[(size_t)nrow[cb] * p.G + g];
+        if constexpr (ASYM) r.z[cb][gi] = p.zp[(size_t)(nrow[cb] >> 3) * p.G + g];
+      }
+  };
+
+  // ---- x fragment reads: row 32 rb + j, piece 2 ks + h, at position
+  // (2 ks + h) ^ (j & 15) = 2 (ks ^ c2) + (h ^ c1)
+  const int c2 = (j & 15) >> 1;
+  const uint32_t xlane = (uint32_t)j * kXRowBytes + (uint32_t)((h ^ (j & 1)) << 4);
+
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rb][cb][e] = 0.f;
+
+  auto group_consts = [&](const StepRegs& r, GroupConst<DT> (&gc)[2][GPS]) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int gi = 0; gi < GPS; ++gi) {
+        const uint32_t z = ASYM ? (r.z[cb][gi] >> (4 * (nrow[cb] & 7))) & 0xFu : 8u;
+        gc[cb][gi] = group_const<DT>(r.s[cb][gi], z);
+      }
+  };
+  auto weights = [&](const StepRegs& r, const GroupConst<DT> (&gc)[2][GPS], int ks, u32x4 (&a)[2]) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const GroupConst<DT>& g = gc[cb][(16 * ks) / GS];
+      a[cb] = dequant_word<DT>(r.w[cb][ks & 1][ks >> 1], g.s_pair, g.nmz_pair, g.s_f32, g.c_f32);
+    }
+  };
+  auto xfrags = [&](const lds_u8* buf, int ks, u32x4 (&b)[MB]) {
+    const lds_u8* src = buf + xlane + (uint32_t)((ks ^ c2) << 5);
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) b[rb] = *(lds_u32x4*)(src + rb * 32 * kXRowBytes);
+  };
+  auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[MB]) {
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32x32x16<DT>(a[cb], b[rb], acc[rb][cb]);
+  };
+
+  // One complete k-step, software pipelined: the x fragments and dequantised
+  // weights of k-sub ks + 1 are produced while the MFMAs of ks run, and the
+  // scheduler is told to interleave them (per MFMA: a few VALU ops and at
+  // most one LDS read) so the matrix core never waits on either.
+  auto compute = [&](const lds_u8* buf, const StepRegs& r) {
+    GroupConst<DT> gc[2][GPS];
+    group_consts(r, gc);
+    u32x4 a[2][2], b[2][MB];
+    xfrags(buf, 0, b[0]);
+    weights(r, gc, 0, a[0]);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int c = ks & 1, nx = c ^ 1;
+      if (ks < 7) {
+        xfrags(buf, ks + 1, b[nx]);
+        weights(r, gc, ks + 1, a[nx]);
+      }
+      mfmas(a[c], b[c]);
+      if (ks < 7) {
+#pragma unroll
+        for (int i = 0; i < 2 * MB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          if (i < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, (48 + 2 * MB - 1) / (2 * MB), 0);  // VALU
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the incomplete last run: nks < 8 k-subs, not pipelined
+  auto compute_tail = [&](const lds_u8* buf, const StepRegs& r, int nks) {
+    GroupConst<DT> gc[2][GPS];
+    group_consts(r, gc);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < nks) {
+        u32x4 a[2], b[MB];
+        xfrags(buf, ks, b);
+        weights(r, gc, ks, a);
+        mfmas(a, b);
+      }
+    }
+  };
+
+  lds_u8* const buf0 = (lds_u8*)xs0;
+  lds_u8* const buf1 = (lds_u8*)xs1;
+
+  // ---- main loop over complete runs, two steps per iteration so that each
+  // LDS buffer and register set is a compile-time choice; the loop has no
+  // exit in its middle (an odd last step is peeled), which lets the
+  // accumulators stay in the same registers throughout
+  StepRegs ra, rb_;
+  int s = s_begin;
+  const int nfull = s_full_end - s_begin;
+  if (nfull > 0) {
+    stage_x(s, buf0, false);
+    load_full(s, ra);
+    load_meta(s, ra);
+    for (int it = 0; it < (nfull >> 1); ++it) {
+      __syncthreads();  // step s landed everywhere; buf1 is free
+      stage_x(s + 1, buf1, false);
+      load_full(s + 1, rb_);
+      load_meta(s + 1, rb_);
+      compute(buf0, ra);
+      ++s;
+      __syncthreads();
+      if (s + 1 < s_full_end) {
+        stage_x(s + 1, buf0, false);
+        load_full(s + 1, ra);
+        load_meta(s + 1, ra);
+      }
+      compute(buf1, rb_);
+      ++s;
+    }
+    if (nfull & 1) {
+      __syncthreads();
+      compute(buf0, ra);
+      ++s;
+    }
+  }
+  // ---- the incomplete last run (K % 128 != 0), unpipelined
+  if (s < s_end) {
+    __syncthreads();  // every wave is done with both buffers
+    stage_x(s, buf0, true);
+    load_tail(s, ra);
+    load_meta(s, ra);
+    wait_vm_all();
+    __syncthreads();
+    compute_tail(buf0, ra, (p.K - s * kBK) / 16);
+  }
+
+  // ---- split-K: store the partial tile; the last unit of the tile sums them
+  if (p.splits > 1) {
+    constexpr int NQ = MB * 2 * 4;  // float4 chunks per thread
+    const size_t slot = (size_t)BM * kBN;
+    float* mine = p.partial + (size_t)(tile * p.splits + split) * slot;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int q = (rb * 2 + cb) * 4 + a4;
+          *reinterpret_cast<f32x4*>(mine + ((size_t)q * kThreads + tid) * 4) =
+              f32x4{acc[rb][cb][4 * a4], acc[rb][cb][4 * a4 + 1], acc[rb][cb][4 * a4 + 2],
+                    acc[rb][cb][4 * a4 + 3]};
+        }
+    static_assert(NQ == MB * 8, "chunk count");
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = (prev == (uint32_t)(p.splits - 1));
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const float* first = p.partial + (size_t)tile * p.splits * slot;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int q = (rb * 2 + cb) * 4 + a4;
+          const size_t off = ((size_t)q * kThreads + tid) * 4;
+          const f32x4 own = f32x4{acc[rb][cb][4 * a4], acc[rb][cb][4 * a4 + 1],
+                                  acc[rb][cb][4 * a4 + 2], acc[rb][cb][4 * a4 + 3]};
+          f32x4 t = split == 0 ? own : *reinterpret_cast<const f32x4*>(first + off);
+          for (int sp = 1; sp < p.splits; ++sp)
+            t += sp == split ? own : *reinterpret_cast<const f32x4*>(first + sp * slot + off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rb][cb][4 * a4 + e] = t[e];
+        }
+    if (tid == 0) p.counters[tile] = 0u;  // ready for the next call
+  }
+
+  // ---- epilogue: + bias in fp32, one rounding, 16-byte stores
+  // acc[rb][cb][4a + e] is token m0 + 32 rb + j, feature nw0 + 32 cb + 8a + 4h + e
+  float bias_f[2][4][4];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = nw0 + 32 * cb + 8 * a + 4 * h + e;
+        bias_f[cb][a][e] = (p.bias && n < p.N) ? act_to_f32<DT>(p.bias[n]) : 0.f;
+      }
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    const int m = m0 + 32 * rb + j;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      uint32_t q[4][2];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x16& v = acc[rb][cb];
+        q[a][0] = f32x2_to_act_pair<DT>(v[4 * a] + bias_f[cb][a][0], v[4 * a + 1] + bias_f[cb][a][1]);
+        q[a][1] = f32x2_to_act_pair<DT>(v[4 * a + 2] + bias_f[cb][a][2], v[4 * a + 3] + bias_f[cb][a][3]);
+      }
+      // lanes h = 0 / 1 of quads (a, a + 1) hold features 8a + 0..3 / 8a + 4..7;
+      // after the swap lane h holds the 8 features 8(a + h) + 0..7
+#pragma unroll
+      for (int a = 0; a < 4; a += 2) {
+        const auto s0 = __builtin_amdgcn_permlane32_swap(q[a][0], q[a + 1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(q[a][1], q[a + 1][1], false, false);
+        const u32x4 out = u32x4{s0[0], s1[0], s0[1], s1[1]};
+        const int n = nw0 + 32 * cb + 8 * (a + h);
         if (m < p.M) {
-          float v = acc[i][j][r];
-          if (p.bias) v += b;
-          p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v);
+          uint16_t* dst = p.y + (size_t)m * p.N + n;
+          if (p.vec_store) {
+            if (n < p.N) *reinterpret_cast<u32x4*>(dst) = out;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < p.N) dst[e] = (uint16_t)(out[e >> 1] >> (16 * (e & 1)));
+          }
         }
       }
     }
   }
 }
 
-template <int DT, int GS, bool ASYM>
+template <int DT, int GS, bool ASYM, int MB>
 hipError_t launch_t(const GemmParams& prm, hipStream_t s) {
-  dim3 grid((prm.N + BN - 1) / BN, (prm.M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_kernel<DT, GS, ASYM>), grid, dim3(kThreads), 0, s, prm);
+  hipLaunchKernelGGL((gemm_kernel<DT, GS, ASYM, MB>), dim3(prm.units), dim3(kThreads), 0, s, prm);
   return hipGetLastError();
 }
 
+template <int DT, int GS, bool ASYM>
+hipError_t launch_mb(const GemmParams& prm, int mb, hipStream_t s) {
+  switch (mb) {
+    case 4: return launch_t<DT, GS, ASYM, 4>(prm, s);
+    case 6: return launch_t<DT, GS, ASYM, 6>(prm, s);
+    case 8: return launch_t<DT, GS, ASYM, 8>(prm, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int DT, int GS>
-hipError_t launch_z(const GemmParams& prm, hipStream_t s) {
-  return prm.zp ? launch_t<DT, GS, true>(prm, s) : launch_t<DT, GS, false>(prm, s);
+hipError_t launch_z(const GemmParams& prm, int mb, hipStream_t s) {
+  return prm.zp ? launch_mb<DT, GS, true>(prm, mb, s) : launch_mb<DT, GS, false>(prm, mb, s);
 }
 
 template <int DT>
-hipError_t launch_g(const GemmParams& prm, int group, hipStream_t s) {
+hipError_t launch_g(const GemmParams& prm, int group, int mb, hipStream_t s) {
   switch (group) {
-    case 32: return launch_z<DT, 32>(prm, s);
-    case 64: return launch_z<DT, 64>(prm, s);
-    case 128: return launch_z<DT, 128>(prm, s);
+    case 32: return launch_z<DT, 32>(prm, mb, s);
+    case 64: return launch_z<DT, 64>(prm, mb, s);
+    case 128: return launch_z<DT, 128>(prm, mb, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
+// Tile height and K split.  Cost model in cycles of one CU: a k-step of a
+// BM = 32 MB tile is 512 MB cycles of MFMA plus a fixed overhead; units run
+// in rounds of cu_count; a split unit also writes an fp32 partial tile and
+// the tile's last unit reads the others back, at the CU's share of HBM
+// bandwidth (~13 bytes per cycle).
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
+  GemmPlan best{};
+  double best_cost = 0.0;
+  const int nsteps = (int)((K + kBK - 1) / kBK);
+  const int64_t tiles_n = (N + kBN - 1) / kBN;
+  const int cus = cu_count > 0 ? cu_count : 256;
+  for (int mb : {8, 6, 4}) {
+    const int64_t bm = 32 * mb;
+    const int64_t tiles = ((M + bm - 1) / bm) * tiles_n;
+    for (int splits = 1; splits <= 16 && splits <= nsteps; ++splits) {
+      const int sps = (nsteps + splits - 1) / splits;
+      const int real_splits = (nsteps + sps - 1) / sps;
+      if (real_splits != splits) continue;
+      if (splits > 1 && tiles > kMaxCounters) break;
+      const int64_t units = tiles * splits;
+      const int64_t rounds = (units + cus - 1) / cus;
+      // per round, a split unit writes its fp32 partial tile and (on average)
+      // reads back almost as much
+      const double fixup = splits > 1 ? 2.0 * bm * kBN * 4 / 13.0 : 0.0;
+      const double cost = (double)rounds * (sps * (512.0 * mb + 700.0) + fixup);
+      if (best.units == 0 || cost < best_cost * 0.98) {
+        best_cost = cost;
+        best.mb = mb;
+        best.splits = splits;
+        best.steps_per_split = sps;
+        best.tiles_n = (int)tiles_n;
+        best.tiles = (int)tiles;
+        best.units = (int)units;
+      }
+    }
+  }
+  return best;
+}
 
-hipError_t launch_gemm(const LinearArgs& a, void*, int, hipStream_t stream) {
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cu_count) {
+  const GemmPlan p = plan_gemm(M, N, K, cu_count);
+  if (p.splits <= 1) return 0;
+  return kCounterBytes + (size_t)p.units * (size_t)(32 * p.mb) * kBN * sizeof(float);
+}
+
+hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipStream_t stream) {
+  const GemmPlan plan = plan_gemm(a.M, a.N, a.K, cu_count);
   GemmParams prm;
   prm.x = static_cast<const uint16_t*>(a.x);
   prm.wq = reinterpret_cast<const uint32_t*>(a.wq);
@@ -214,13 +492,27 @@ hipError_t launch_gemm(const LinearArgs& a, void*, int, hipStream_t stream) {
   prm.zp = reinterpret_cast<const uint32_t*>(a.zp);
   prm.bias = static_cast<const uint16_t*>(a.bias);
   prm.y = static_cast<uint16_t*>(a.y);
+  prm.counters = nullptr;
+  prm.partial = nullptr;
+  if (plan.splits > 1) {
+    if (workspace == nullptr) return hipErrorInvalidValue;
+    prm.counters = static_cast<uint32_t*>(workspace);
+    prm.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+  }
   prm.M = (int)a.M;
   prm.N = (int)a.N;
   prm.K = (int)a.K;
   prm.G = (int)(a.K / a.group);
-  prm.nchunks = (int)(a.K / 32);
-  return a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, stream)
-                           : launch_g<DT_BF16>(prm, a.group, stream);
+  prm.wpr = (int)(a.K / 8);
+  prm.nsteps = (int)((a.K + kBK - 1) / kBK);
+  prm.full_steps = (int)(a.K / kBK);
+  prm.tiles_n = plan.tiles_n;
+  prm.units = plan.units;
+  prm.splits = plan.splits;
+  prm.steps_per_split = plan.steps_per_split;
+  prm.vec_store = (a.N % 8 == 0) && (reinterpret_cast<uintptr_t>(a.y) % 16 == 0);
+  return a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, plan.mb, stream)
+                           : launch_g<DT_BF16>(prm, a.group, plan.mb, stream);
 }
 
 }  // namespace w4a16

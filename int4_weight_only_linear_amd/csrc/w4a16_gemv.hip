@@ -109,11 +109,7 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
     if (nn < p.N) {
       float v = 0.f;
       for (int s = 0; s < p.splits; ++s) {
-        float* src = p.partial + ((size_t)s * p.M + m) * p.N + nn;
-        v += *src;
-        // leave the whole workspace zero: a later call of another shape may
-        // place its counters where these partial sums were
-        *src = 0.f;
+        v += p.partial[((size_t)s * p.M + m) * p.N + nn];
       }
       if (p.bias) v += act_to_f32<DT>(p.bias[nn]);
       p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v);
@@ -431,7 +427,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   // split K until every row tile has enough workgroups to cover the CUs, a
   // workgroup has at most kGemvMaxWaves waves, and its LDS fits the budget
   int splits = 1;
-  if (p.tiles < cu_count) splits = (cu_count + p.tiles - 1) / p.tiles;
+  if (p.tiles < cu_count && p.tiles <= kMaxCounters) splits = (cu_count + p.tiles - 1) / p.tiles;
   for (;;) {
     if (splits > p.ksteps) splits = p.ksteps;
     const int kps = (p.ksteps + splits - 1) / splits;
@@ -448,12 +444,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   return p;
 }
 
-static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N) {
   if (p.splits <= 1) return 0;
-  return align_up((size_t)p.tiles * sizeof(uint32_t), 256) +
-         (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
+  return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
 template <int DT, int MT, int GS, bool ASYM>
@@ -510,8 +503,7 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
   prm.partial = nullptr;
   if (plan.splits > 1) {
     prm.counters = static_cast<uint32_t*>(workspace);
-    prm.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           align_up((size_t)plan.tiles * sizeof(uint32_t), 256));
+    prm.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
   }
   prm.M = (int)a.M;
   prm.N = (int)a.N;

@@ -154,6 +154,12 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
     return fail(W4A16_ERR_UNSUPPORTED,
                 "the decode kernel addresses weights with 32-bit byte offsets: N*K/2 must be "
                 "below 4 GiB (N=%lld K=%lld)", (long long)N, (long long)K);
+  if (p == W4A16_PATH_GEMM && ((uint64_t)N * (uint64_t)K / 2 > 0xFFFFFFFFull ||
+                               (uint64_t)M * (uint64_t)K * 2 > 0xFFFFFFFFull))
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "the prefill kernel addresses weights and activations with 32-bit byte "
+                "offsets: N*K/2 and M*K*2 must be below 4 GiB (M=%lld N=%lld K=%lld)",
+                (long long)M, (long long)N, (long long)K);
   const size_t need = workspace_for(M, N, K, group_size, p, dev->cu_count);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
@@ -174,10 +180,14 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
                    plan.splits, plan.waves);
     e = w4a16::launch_gemv(a, plan, workspace, s);
   } else {
-    if (log_enabled())
-      std::fprintf(stderr, "[w4a16] gemm M=%lld N=%lld K=%lld g=%d %s %s\n", (long long)M,
-                   (long long)N, (long long)K, group_size, dtype == W4A16_F16 ? "f16" : "bf16",
-                   zp ? "asym" : "sym");
+    if (log_enabled()) {
+      const w4a16::GemmPlan plan = w4a16::plan_gemm(M, N, K, dev->cu_count);
+      std::fprintf(stderr,
+                   "[w4a16] gemm M=%lld N=%lld K=%lld g=%d %s %s bm=%d splits=%d units=%d\n",
+                   (long long)M, (long long)N, (long long)K, group_size,
+                   dtype == W4A16_F16 ? "f16" : "bf16", zp ? "asym" : "sym", 32 * plan.mb,
+                   plan.splits, plan.units);
+    }
     e = w4a16::launch_gemm(a, workspace, dev->cu_count, s);
   }
   if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));

@@ -20,15 +20,24 @@ struct LinearArgs {
   int dtype;
 };
 
+// ---- workspace ---------------------------------------------------------------
+// Both kernels that split K keep one completion counter per output tile at the
+// start of the workspace and their fp32 partial sums after this fixed-size
+// counter region.  The last workgroup of a tile resets its counter, so the
+// region is zero again after every completed call; the partial sums are always
+// written in full before they are read, so their stale contents never matter,
+// whatever the shape of the previous call.
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int64_t kMaxCounters = (int64_t)(kCounterBytes / sizeof(uint32_t));
+
 // ---- skinny decode kernel ------------------------------------------------
 // One workgroup owns 16 output rows (one MFMA column tile) and one K range
 // ("split"); its waves take the 128-wide k-steps of that range in turn and
 // are reduced through LDS.  With more than one split, each workgroup stores
 // fp32 partial sums and the last one to finish a row tile adds them up in
-// split order (counter in the workspace), so results are deterministic.  That
-// workgroup also zeroes the partial sums it consumed and its counter, so a
-// completed call leaves the whole workspace zero for the next one, whatever
-// its shape.
+// split order (counter in the workspace), so results are deterministic.
+// Splitting only happens when there are fewer row tiles than CUs, so the
+// counters always fit the counter region.
 constexpr int kGemvRowsPerTile = 16;
 constexpr int kGemvKStep = 128;       // k per wave step: 4 chunks of 32
 constexpr int kGemvMaxWaves = 16;     // 1024 threads
@@ -60,6 +69,17 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& p, void* workspace,
                        hipStream_t stream);
 
 // ---- prefill GEMM ----------------------------------------------------------
+// A workgroup owns 32*mb tokens x 256 output features; `splits` K ranges of
+// `steps_per_split` 128-k steps each; units = tiles * splits workgroups.
+struct GemmPlan {
+  int mb;
+  int splits;
+  int steps_per_split;
+  int tiles_n;
+  int tiles;
+  int units;
+};
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cu_count);
 hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipStream_t stream);
 

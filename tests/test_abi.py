@@ -183,4 +183,8 @@ def test_workspace_size():
     tiles = 2560 // 16
     assert ws >= 256 * ((tiles * 4 + 255) // 256) + 2 * 4 * 2560 * 4
     assert L.w4a16_workspace_size(0, 2560, 9728, 128, 0, 0) == 0
-    assert L.w4a16_workspace_size(128, 4096, 4096, 128, 1, 1, L.PATH_GEMM) == 0
+    # the prefill GEMM: enough tiles to fill the CUs, no split
+    assert L.w4a16_workspace_size(1920, 28672, 4096, 128, 1, 1, L.PATH_GEMM) == 0
+    # a single 128-token tile row: K is split; counters region + fp32 partial tiles
+    ws = L.w4a16_workspace_size(128, 4096, 4096, 128, 1, 1, L.PATH_GEMM)
+    assert ws >= 64 * 1024 + 2 * 128 * 4096 * 4
