@@ -119,9 +119,12 @@ w4a16_path w4a16_select_path(int64_t M, int64_t N, int64_t K, int32_t group_size
                              int32_t dtype, int32_t has_zp);
 
 /* Workspace bytes w4a16_linear needs for this problem and path (AUTO allowed).
- * 0 means none.  The workspace must be zero-filled before its first use; every
- * completed call leaves it zero-filled again, so it can be reused by later
- * calls on the same stream.  Calls that overlap in time must not share one. */
+ * 0 means none; otherwise at least 64 KiB.  Layout: the first 64 KiB hold
+ * per-tile completion counters, the rest fp32 partial sums of a K split.  The
+ * workspace must be zero-filled before its first use; every completed call
+ * leaves the counter region zero again (the partial sums are always written
+ * before they are read), so one workspace serves later calls of any shape on
+ * the same stream.  Calls that overlap in time must not share one. */
 size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size,
                             int32_t dtype, int32_t has_zp, int32_t path);
 

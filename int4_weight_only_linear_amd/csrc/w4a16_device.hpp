@@ -244,6 +244,30 @@ __device__ __forceinline__ GroupConst<DT> group_const(uint16_t s_bits, uint32_t 
   return g;
 }
 
+// Cross-workgroup hand-off of fp32 partial sums (split K) without
+// cache-wide maintenance.  Every XCD has its own L2, so agent-scope
+// release/acquire fences write back and invalidate the whole L2 of the XCD
+// (buffer_wbl2 / buffer_inv); done by every split workgroup, that costs far
+// more than the hand-off and evicts the weights the other workgroups are
+// streaming.  Instead the partial sums themselves are written and read with
+// agent-scope relaxed atomic accesses (write-through to, and reads from, the
+// device-coherent level), and the order comes from the waits: a workgroup
+// barrier after the stores (it waits for them to complete) before the
+// completion counter is incremented, and the counter's result, shared
+// through LDS and a barrier, before the loads are issued.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_counter(uint32_t* counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ uint32_t zero_point(const uint32_t* zp, int n, int G, int grp) {
   return (zp[(size_t)(n >> 3) * G + grp] >> (4 * (n & 7))) & 0xFu;
 }

@@ -29,6 +29,9 @@
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
 
+#include <cstdio>
+#include <cstdlib>
+
 namespace w4a16 {
 
 namespace {
@@ -113,11 +116,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     const int m = min(m0 + row, p.M - 1);
     xoff[d] = ((uint32_t)m * (uint32_t)p.K + 8u * (uint32_t)piece) * 2u;
   }
-  auto stage_x = [&](int s, lds_u8* buf, bool tail) {
+  auto stage_x = [&](int s, lds_u8* buf, bool tail, int d0, int d1) {
     const unsigned char* base = reinterpret_cast<const unsigned char*>(p.x) + (size_t)s * kXRowBytes;
     const int kvalid = p.K - s * kBK;  // < 128 only on the last, incomplete run
 #pragma unroll
-    for (int d = 0; d < NDMA; ++d) {
+    for (int d = d0; d < d1; ++d) {
       uint32_t off = xoff[d];
       if (tail) {
         // pieces past K would read beyond the row (and the buffer, on the
@@ -220,31 +223,53 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
       for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32x32x16<DT>(a[cb], b[rb], acc[rb][cb]);
   };
 
+  // Pipeline state carried across k-steps: the operands of the k-sub about
+  // to be multiplied (by parity) and the current step's group constants.
+  u32x4 a[2][2], b[2][MB];
+  GroupConst<DT> gc[2][GPS];
+
+  // Own x pieces landed in LDS, own loads and LDS reads retired, then the
+  // workgroup barrier (no memory fence beyond that is needed: the x pieces
+  // reach LDS before their load counter drops).
+  auto step_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   // One complete k-step, software pipelined: the x fragments and dequantised
   // weights of k-sub ks + 1 are produced while the MFMAs of ks run, and the
   // scheduler is told to interleave them (per MFMA: a few VALU ops and at
-  // most one LDS read) so the matrix core never waits on either.
-  auto compute = [&](const lds_u8* buf, const StepRegs& r) {
-    GroupConst<DT> gc[2][GPS];
-    group_consts(r, gc);
-    u32x4 a[2][2], b[2][MB];
-    xfrags(buf, 0, b[0]);
-    weights(r, gc, 0, a[0]);
+  // most one LDS read) so the matrix core never waits on either.  The global
+  // loads of the next k-step are spread over k-subs 0..5 (issue(ks)).  The
+  // step's single barrier sits before its last k-sub: by then every wave's
+  // loads of the next step have landed and every wave has read its last
+  // fragments of this step, so the next step's first fragments (nbuf, nr)
+  // are produced while the last MFMAs of this one run.  On the last step
+  // nbuf / nr hold valid but unused data and the prefetch is simply wasted.
+  auto compute = [&](const lds_u8* buf, const StepRegs& r, const lds_u8* nbuf,
+                     const StepRegs& nr, auto&& issue) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int c = ks & 1, nx = c ^ 1;
       if (ks < 7) {
         xfrags(buf, ks + 1, b[nx]);
         weights(r, gc, ks + 1, a[nx]);
+      } else {
+        step_barrier();
+        group_consts(nr, gc);
+        xfrags(nbuf, 0, b[nx]);
+        weights(nr, gc, 0, a[nx]);
       }
+      const int nvm = issue(ks);
       mfmas(a[c], b[c]);
-      if (ks < 7) {
 #pragma unroll
-        for (int i = 0; i < 2 * MB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          if (i < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-          __builtin_amdgcn_sched_group_barrier(0x002, (48 + 2 * MB - 1) / (2 * MB), 0);  // VALU
-        }
+      for (int i = 0; i < 2 * MB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if (i < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, (48 + 2 * MB - 1) / (2 * MB), 0);  // VALU
+        if (i < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -267,43 +292,62 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   lds_u8* const buf0 = (lds_u8*)xs0;
   lds_u8* const buf1 = (lds_u8*)xs1;
 
+  // the next k-step's global loads, spread over k-subs 0..5 of the current
+  // one: weights first (k-sub 0), then metadata, then the x pieces
+  constexpr int kMetaLoads = 2 * GPS * (ASYM ? 2 : 1);
+  auto issue_next = [&](int ks, int sn, lds_u8* buf, StepRegs& r) -> int {
+    constexpr int DPK = (NDMA + 5) / 6;  // x loads per k-sub
+    int n = 0;
+    if (ks == 0) {
+      load_full(sn, r);
+      n += 4;
+    }
+    if (ks == 1) {
+      load_meta(sn, r);
+      n += kMetaLoads;
+    }
+    if (ks < 6) {
+      const int d0 = ks * DPK, d1 = min(NDMA, d0 + DPK);
+      if (d0 < d1) stage_x(sn, buf, false, d0, d1);
+      n += max(0, d1 - d0);
+    }
+    return n;
+  };
+  auto no_issue = [](int) -> int { return 0; };
+
   // ---- main loop over complete runs, two steps per iteration so that each
   // LDS buffer and register set is a compile-time choice; the loop has no
   // exit in its middle (an odd last step is peeled), which lets the
   // accumulators stay in the same registers throughout
-  StepRegs ra, rb_;
+  StepRegs ra = {}, rb_ = {};
   int s = s_begin;
   const int nfull = s_full_end - s_begin;
   if (nfull > 0) {
-    stage_x(s, buf0, false);
+    stage_x(s, buf0, false, 0, NDMA);
     load_full(s, ra);
     load_meta(s, ra);
+    __syncthreads();  // step s landed everywhere
+    group_consts(ra, gc);
+    xfrags(buf0, 0, b[0]);
+    weights(ra, gc, 0, a[0]);
     for (int it = 0; it < (nfull >> 1); ++it) {
-      __syncthreads();  // step s landed everywhere; buf1 is free
-      stage_x(s + 1, buf1, false);
-      load_full(s + 1, rb_);
-      load_meta(s + 1, rb_);
-      compute(buf0, ra);
+      compute(buf0, ra, buf1, rb_, [&](int ks) { return issue_next(ks, s + 1, buf1, rb_); });
       ++s;
-      __syncthreads();
-      if (s + 1 < s_full_end) {
-        stage_x(s + 1, buf0, false);
-        load_full(s + 1, ra);
-        load_meta(s + 1, ra);
-      }
-      compute(buf1, rb_);
+      // after the last pair there is no next step: load a valid one into the
+      // free buffer instead of branching (never used)
+      const int sn = min(s + 1, s_full_end - 1);
+      compute(buf1, rb_, buf0, ra, [&](int ks) { return issue_next(ks, sn, buf0, ra); });
       ++s;
     }
     if (nfull & 1) {
-      __syncthreads();
-      compute(buf0, ra);
+      compute(buf0, ra, buf1, rb_, no_issue);
       ++s;
     }
   }
   // ---- the incomplete last run (K % 128 != 0), unpipelined
   if (s < s_end) {
     __syncthreads();  // every wave is done with both buffers
-    stage_x(s, buf0, true);
+    stage_x(s, buf0, true, 0, NDMA);
     load_tail(s, ra);
     load_meta(s, ra);
     wait_vm_all();
@@ -312,8 +356,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   }
 
   // ---- split-K: store the partial tile; the last unit of the tile sums them
+  // in split order (cross-workgroup hand-off as described at store_coherent)
   if (p.splits > 1) {
-    constexpr int NQ = MB * 2 * 4;  // float4 chunks per thread
     const size_t slot = (size_t)BM * kBN;
     float* mine = p.partial + (size_t)(tile * p.splits + split) * slot;
 #pragma unroll
@@ -321,41 +365,40 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int q = (rb * 2 + cb) * 4 + a4;
-          *reinterpret_cast<f32x4*>(mine + ((size_t)q * kThreads + tid) * 4) =
-              f32x4{acc[rb][cb][4 * a4], acc[rb][cb][4 * a4 + 1], acc[rb][cb][4 * a4 + 2],
-                    acc[rb][cb][4 * a4 + 3]};
+        for (int e = 0; e < 16; ++e) {
+          const int q = (rb * 2 + cb) * 16 + e;
+          store_coherent(mine + (size_t)q * kThreads + tid, acc[rb][cb][e]);
         }
-    static_assert(NQ == MB * 8, "chunk count");
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_ACQ_REL,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      last_flag = (prev == (uint32_t)(p.splits - 1));
-    }
+    __syncthreads();  // every thread's partial sums are stored
+    if (tid == 0) last_flag = (arrive(p.counters + tile) == (uint32_t)(p.splits - 1));
     __syncthreads();
     if (!last_flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const float* first = p.partial + (size_t)tile * p.splits * slot;
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < 2; ++cb) {
+        // all splits' values of this 16-register block, loads first
+        float t[16];
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int q = (rb * 2 + cb) * 4 + a4;
-          const size_t off = ((size_t)q * kThreads + tid) * 4;
-          const f32x4 own = f32x4{acc[rb][cb][4 * a4], acc[rb][cb][4 * a4 + 1],
-                                  acc[rb][cb][4 * a4 + 2], acc[rb][cb][4 * a4 + 3]};
-          f32x4 t = split == 0 ? own : *reinterpret_cast<const f32x4*>(first + off);
-          for (int sp = 1; sp < p.splits; ++sp)
-            t += sp == split ? own : *reinterpret_cast<const f32x4*>(first + sp * slot + off);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[rb][cb][4 * a4 + e] = t[e];
+        for (int e = 0; e < 16; ++e) {
+          const size_t off = (size_t)((rb * 2 + cb) * 16 + e) * kThreads + tid;
+          t[e] = split == 0 ? acc[rb][cb][e] : load_coherent(first + off);
         }
-    if (tid == 0) p.counters[tile] = 0u;  // ready for the next call
+        for (int sp = 1; sp < p.splits; ++sp) {
+          float u[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const size_t off = (size_t)((rb * 2 + cb) * 16 + e) * kThreads + tid;
+            u[e] = sp == split ? acc[rb][cb][e] : load_coherent(first + sp * slot + off);
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) t[e] += u[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[rb][cb][e] = t[e];
+      }
+    if (tid == 0) reset_counter(p.counters + tile);  // ready for the next call
   }
 
   // ---- epilogue: + bias in fp32, one rounding, 16-byte stores
@@ -471,6 +514,23 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
         best.tiles_n = (int)tiles_n;
         best.tiles = (int)tiles;
         best.units = (int)units;
+      }
+    }
+  }
+  // tuning override "mb,splits" (tile height 32*mb, K ranges), e.g. for sweeps
+  if (const char* env = std::getenv("W4A16_GEMM_TILE")) {
+    int mb = 0, splits = 0;
+    if (std::sscanf(env, "%d,%d", &mb, &splits) == 2 && (mb == 4 || mb == 6 || mb == 8) &&
+        splits >= 1 && splits <= nsteps) {
+      const int sps = (nsteps + splits - 1) / splits;
+      const int64_t tiles = ((M + 32 * mb - 1) / (32 * mb)) * tiles_n;
+      if (splits == 1 || tiles <= kMaxCounters) {
+        best.mb = mb;
+        best.steps_per_split = sps;
+        best.splits = (nsteps + sps - 1) / sps;
+        best.tiles_n = (int)tiles_n;
+        best.tiles = (int)tiles;
+        best.units = (int)(tiles * best.splits);
       }
     }
   }

@@ -43,6 +43,8 @@
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
 
+#include <cstdlib>
+
 namespace w4a16 {
 
 struct GemvParams {
@@ -87,35 +89,28 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
         if (p.bias) v += act_to_f32<DT>(p.bias[nn]);
         p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v);
       } else {
-        p.partial[((size_t)split * p.M + m) * p.N + nn] = v;
+        store_coherent(p.partial + ((size_t)split * p.M + m) * p.N + nn, v);
       }
     }
   }
   if (p.splits == 1) return;
 
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    *last_flag = (prev == (uint32_t)(p.splits - 1));
-  }
+  __syncthreads();  // every thread's partial sums are stored
+  if (threadIdx.x == 0)
+    *last_flag = (arrive(p.counters + tile) == (uint32_t)(p.splits - 1));
   __syncthreads();
   if (!*last_flag) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   for (int e = threadIdx.x; e < 16 * p.M; e += blockDim.x) {
     const int m = e >> 4;
     const int nn = tile * kGemvRowsPerTile + (e & 15);
     if (nn < p.N) {
       float v = 0.f;
-      for (int s = 0; s < p.splits; ++s) {
-        v += p.partial[((size_t)s * p.M + m) * p.N + nn];
-      }
+      for (int s = 0; s < p.splits; ++s) v += load_coherent(p.partial + ((size_t)s * p.M + m) * p.N + nn);
       if (p.bias) v += act_to_f32<DT>(p.bias[nn]);
       p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v);
     }
   }
-  if (threadIdx.x == 0) p.counters[tile] = 0u;  // ready for the next call
+  if (threadIdx.x == 0) reset_counter(p.counters + tile);  // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -423,11 +418,21 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   int kpw = kGemvStepsPerWave;
   if (p.xlds)
     while (kpw > 1 && M * kpw > 4 * kGemvXSegsPerThread) kpw >>= 1;
+  // tuning overrides: k-steps per wave (a smaller power of two) and a
+  // minimum number of K splits
+  if (const char* env = std::getenv("W4A16_GEMV_KPW")) {
+    const int v = std::atoi(env);
+    if (v >= 1 && v <= kpw && (v & (v - 1)) == 0) kpw = v;
+  }
   p.kpw = kpw;
   // split K until every row tile has enough workgroups to cover the CUs, a
   // workgroup has at most kGemvMaxWaves waves, and its LDS fits the budget
   int splits = 1;
   if (p.tiles < cu_count && p.tiles <= kMaxCounters) splits = (cu_count + p.tiles - 1) / p.tiles;
+  if (const char* env = std::getenv("W4A16_GEMV_SPLITS")) {
+    const int v = std::atoi(env);
+    if (v > splits && p.tiles <= kMaxCounters) splits = v;
+  }
   for (;;) {
     if (splits > p.ksteps) splits = p.ksteps;
     const int kps = (p.ksteps + splits - 1) / splits;
