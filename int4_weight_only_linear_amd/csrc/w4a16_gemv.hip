@@ -124,7 +124,7 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 template <int DT, int GS, bool ASYM, int KPW, int XPT>
 __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
-  constexpr int SPT = (32 * KPW) / GS;  // scale loads per lane for kpw = KPW
+  constexpr int SPT = (32 * KPW) / GS > 0 ? (32 * KPW) / GS : 1;  // scale loads per lane
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int last_flag;
 
@@ -273,13 +273,63 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
     }
   };
 
+  if (my_steps == KPW && (my_first + KPW) * 4 <= p.nchunks) {
+    // Common case: the wave's whole run is complete 128-k runs.  Branch-free
+    // and software pipelined, two k-steps at a time: the x fragments of the
+    // next pair are read while this pair is multiplied, and the MFMAs of the
+    // two steps' q chains and zero-point chains (four independent
+    // accumulators) alternate, so no MFMA waits for the result of the one
+    // issued just before it.
+    constexpr int PAIR = KPW >= 2 ? 2 : 1;
+    u32x4 xa[2][PAIR][4];
+    auto load_x = [&](int i, u32x4 (&x)[PAIR][4]) {
 #pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    if (i >= my_steps) break;
-    if ((my_first + i) * 4 + 4 <= p.nchunks)
-      kstep(wv[i], i, std::true_type{});
-    else
-      kstep(wv[i], i, std::false_type{});
+      for (int s2 = 0; s2 < PAIR; ++s2)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          x[s2][t] = *reinterpret_cast<const u32x4*>(xrow + (i + s2) * kGemvKStep + t * 32);
+    };
+    load_x(0, xa[0]);
+#pragma unroll
+    for (int i = 0; i < KPW; i += PAIR) {
+      const int c = (i / PAIR) & 1;
+      if (i + PAIR < KPW) load_x(i + PAIR, xa[c ^ 1]);
+      f32x4 ch[PAIR], cz[PAIR];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int s2 = 0; s2 < PAIR; ++s2) {
+          const int ii = i + s2;
+          const int gl = ii * (4 / CPG) + t / CPG;  // group within this wave's run
+          const bool fresh = (t % CPG) == 0;
+          const uint32_t z = ASYM ? (zrow_l[gl] >> zshift) & 0xFu : 8u;
+          if constexpr (DT == DT_F16) {
+            const u32x4 bq = qz_word_f16(wv[ii][t], mask_v, neg_magic_pair<DT>(z));  // q - z, exact
+            ch[s2] = mfma16x16x32<DT>(xa[c][s2][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[s2]);
+          } else {
+            const u32x4 bq = magic_word<DT>(wv[ii][t], mask_v);  // 128 + q, exact
+            const uint32_t nmz = neg_magic_pair<DT>(z);           // -(128 + z)
+            ch[s2] = mfma16x16x32<DT>(xa[c][s2][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[s2]);
+            cz[s2] = mfma16x16x32<DT>(xa[c][s2][t], u32x4{nmz, nmz, nmz, nmz},
+                                      fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : cz[s2]);
+          }
+          if (t % CPG == CPG - 1) {
+            const float sc = act_to_f32<DT>(srow_l[gl]);
+            if constexpr (DT == DT_BF16) acc += sc * (ch[s2] + cz[s2]);
+            else acc += sc * ch[s2];
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      if (i >= my_steps) break;
+      if ((my_first + i) * 4 + 4 <= p.nchunks)
+        kstep(wv[i], i, std::true_type{});
+      else
+        kstep(wv[i], i, std::false_type{});
+    }
   }
 
   // ---- 4. reduce the waves in order, then the K ranges ----
@@ -459,10 +509,17 @@ static hipError_t launch_t(const GemvParams& prm, const GemvPlan& plan, hipStrea
   dim3 grid(plan.tiles, plan.splits);
   dim3 block(plan.waves * 64);
   constexpr int KPW = kGemvStepsPerWave;
-  if constexpr (MT == 1)
-    hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, KPW, kGemvXSegsPerThread>), grid, block,
-                       plan.lds_bytes, s, prm);
-  else
+  if constexpr (MT == 1) {
+    // the small kernel is instantiated per k-steps per wave, so that its
+    // branch-free path covers every wave whose run is complete
+    switch (plan.kpw) {
+      case 8: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, kGemvXSegsPerThread>), grid, block, plan.lds_bytes, s, prm); break;
+      case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, kGemvXSegsPerThread>), grid, block, plan.lds_bytes, s, prm); break;
+      case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, kGemvXSegsPerThread>), grid, block, plan.lds_bytes, s, prm); break;
+      case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, kGemvXSegsPerThread>), grid, block, plan.lds_bytes, s, prm); break;
+      default: return hipErrorInvalidConfiguration;
+    }
+  } else
     hipLaunchKernelGGL((gemv_wide_kernel<DT, MT, GS, ASYM, KPW>), grid, block, plan.lds_bytes, s, prm);
   return hipGetLastError();
 }
