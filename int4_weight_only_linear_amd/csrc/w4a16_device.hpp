@@ -84,6 +84,12 @@ __device__ __forceinline__ u32x4 qz_word_f16(uint32_t w, uint32_t mask_v, uint32
   return u32x4{add_f16x2(p0, nmz), add_f16x2(p1, nmz), add_f16x2(p2, nmz), add_f16x2(p3, nmz)};
 }
 
+// acc + (low half + high half) of a bf16 pair, in fp32
+__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
+                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
+}
+
 // The 8-k slice held by stored word j of a row of J words (see above).
 __device__ __forceinline__ int slice_of_stored_word(int j, int J) {
   const int run = j >> 4, p = j & 15;

@@ -160,6 +160,10 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   uint16_t* xs = reinterpret_cast<uint16_t*>(wreg);   // [M][xstride]
   uint16_t* sl = xs + p.M * xstride;                  // [16][ngw]
   uint32_t* zl = reinterpret_cast<uint32_t*>(sl + 16 * ngw);  // [2][ngw]
+  // bf16: 16-k partial sums of x, then x summed over each group, per token
+  float* xpart = reinterpret_cast<float*>(
+      wreg + ((((size_t)p.M * xstride + 16 * ngw) * sizeof(uint16_t) + 2 * ngw * sizeof(uint32_t) + 15) & ~(size_t)15));
+  float* xsum = xpart + p.M * kpw * 8;  // [ngw][16]
 
   // ---- 1. loads: x, scales and zero points of this wave's run, then weights ----
   const int xsegs = p.M * xsegs_row;
@@ -220,6 +224,38 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   if constexpr (ASYM) {
     if (lane < 2 * ngw) zl[lane] = zr;
   }
+  if constexpr (DT == DT_BF16) {
+    // sum of x over every group of the run, per token (zero past M): the
+    // magic offset and the zero point then cost one multiply-add per group,
+    // (128 + z) * xsum, instead of an MFMA with -(128 + z) per chunk
+    const int lg_parts = lg_xsegs - 1;  // kpw * 8 partials of 16 k per token
+    for (int it = lane; it < (p.M << lg_parts); it += 64) {
+      const uint16_t* src = xs + (it >> lg_parts) * xstride + ((it & ((1 << lg_parts) - 1)) << 4);
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + 8);
+      // named components, not v[e] in a loop: see add_f16x2 on bit casts of
+      // vector elements
+      float sum = sum_bf16x2(v0.x, 0.f);
+      sum = sum_bf16x2(v0.y, sum);
+      sum = sum_bf16x2(v0.z, sum);
+      sum = sum_bf16x2(v0.w, sum);
+      sum = sum_bf16x2(v1.x, sum);
+      sum = sum_bf16x2(v1.y, sum);
+      sum = sum_bf16x2(v1.z, sum);
+      sum = sum_bf16x2(v1.w, sum);
+      xpart[it] = sum;
+    }
+    constexpr int PPG = GS / 16;  // partials per group
+    for (int it = lane; it < 16 * ngw; it += 64) {
+      const int g = it >> 4, tok = it & 15;
+      float v = 0.f;
+      if (tok < p.M) {
+#pragma unroll
+        for (int q = 0; q < PPG; ++q) v += xpart[(tok << lg_parts) + g * PPG + q];
+      }
+      xsum[it] = v;
+    }
+  }
 
   // ---- 3. dot products, one k-step at a time as its weights arrive ----
   const uint32_t mask_v = vgpr_const(0x000F000Fu);
@@ -277,9 +313,9 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
     // Common case: the wave's whole run is complete 128-k runs.  Branch-free
     // and software pipelined, two k-steps at a time: the x fragments of the
     // next pair are read while this pair is multiplied, and the MFMAs of the
-    // two steps' q chains and zero-point chains (four independent
-    // accumulators) alternate, so no MFMA waits for the result of the one
-    // issued just before it.
+    // two steps' chains alternate, so no MFMA waits for the result of the one
+    // issued just before it.  bf16 multiplies x by 128 + q only; the offset
+    // and the zero point are removed per group with the x sums.
     constexpr int PAIR = KPW >= 2 ? 2 : 1;
     u32x4 xa[2][PAIR][4];
     auto load_x = [&](int i, u32x4 (&x)[PAIR][4]) {
@@ -294,7 +330,7 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
     for (int i = 0; i < KPW; i += PAIR) {
       const int c = (i / PAIR) & 1;
       if (i + PAIR < KPW) load_x(i + PAIR, xa[c ^ 1]);
-      f32x4 ch[PAIR], cz[PAIR];
+      f32x4 ch[PAIR];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -308,15 +344,18 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
             ch[s2] = mfma16x16x32<DT>(xa[c][s2][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[s2]);
           } else {
             const u32x4 bq = magic_word<DT>(wv[ii][t], mask_v);  // 128 + q, exact
-            const uint32_t nmz = neg_magic_pair<DT>(z);           // -(128 + z)
             ch[s2] = mfma16x16x32<DT>(xa[c][s2][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[s2]);
-            cz[s2] = mfma16x16x32<DT>(xa[c][s2][t], u32x4{nmz, nmz, nmz, nmz},
-                                      fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : cz[s2]);
           }
           if (t % CPG == CPG - 1) {
             const float sc = act_to_f32<DT>(srow_l[gl]);
-            if constexpr (DT == DT_BF16) acc += sc * (ch[s2] + cz[s2]);
-            else acc += sc * ch[s2];
+            if constexpr (DT == DT_BF16) {
+              // s * (x . (128 + q) - (128 + z) * xsum); -(128 + z) * s is exact
+              const float szc = -(128.0f + (float)z) * sc;
+              const f32x4 xs4 = *reinterpret_cast<const f32x4*>(xsum + gl * 16 + 4 * row4);
+              acc += sc * ch[s2] + szc * xs4;
+            } else {
+              acc += sc * ch[s2];
+            }
           }
         }
       }
@@ -443,8 +482,11 @@ __global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
 size_t gemv_wave_lds_bytes(int64_t M, int kpw, int group) {
   const size_t kr = (size_t)kpw * kGemvKStep;
   const size_t ngr = kr / (size_t)group;
-  const size_t b = (size_t)M * (kr + 8) * sizeof(uint16_t) + 16 * ngr * sizeof(uint16_t) +
-                   2 * ngr * sizeof(uint32_t);
+  size_t b = (size_t)M * (kr + 8) * sizeof(uint16_t) + 16 * ngr * sizeof(uint16_t) +
+             2 * ngr * sizeof(uint32_t);
+  b = (b + 15) / 16 * 16;
+  // per-token x sums: 16-k partials, then one per group and token (padded to 16)
+  b += (size_t)M * (kr / 16) * sizeof(float) + ngr * 16 * sizeof(float);
   return (b + 15) / 16 * 16;
 }
 
