@@ -198,6 +198,140 @@ def cpu_baseline(layers_host, budget_s=30.0):
                         f"decode step, layers {', '.join(done)} (K x N), single thread; packing not timed"))
 
 
+def _layer_tensors(case, device):
+    """Pack a synth case with the library and upload it."""
+    import torch
+    import int4_weight_only_linear_amd as L
+    act = torch.float16 if case.dtype == 0 else torch.bfloat16
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(act)
+    wq = torch.from_numpy(L.w4a16_pack_weights(case.q)).to(device)
+    zp = None if case.zp is None else torch.from_numpy(L.w4a16_pack_zeros(case.zp)).to(device)
+    bias = None if case.bias_bits is None else up(case.bias_bits)
+    return wq, zp, up(case.s_bits), up(case.x_bits), bias
+
+
+def time_point(x, pool, bias, y, M, N, K, g, dt, path, reps, stream):
+    """Mean per-launch time (ms) of w4a16_linear_path over a graph of one
+    launch per weight copy in `pool`, replayed `reps` times."""
+    import torch
+    import int4_weight_only_linear_amd as L
+    from int4_weight_only_linear_amd import _binding as B
+    need = L.w4a16_workspace_size(M, N, K, g, dt, pool[0][1] is not None, path)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=x.device) if need else None
+    wsp, wsn = (None, 0) if ws is None else (ws.data_ptr(), ws.numel())
+
+    def launch(wq, zp, s):
+        def fn(sp):
+            B._check(B.lib.w4a16_linear_path(
+                x.data_ptr(), wq.data_ptr(), s.data_ptr(), None if zp is None else zp.data_ptr(),
+                None if bias is None else bias.data_ptr(), y.data_ptr(), M, N, K, g, dt,
+                wsp, wsn, sp, path))
+        return fn
+    fns = [[launch(*w)] for w in pool]
+    fns[0][0](torch.cuda.current_stream().cuda_stream)  # first call outside capture
+    torch.cuda.synchronize()
+    graph = capture(fns, stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(pool))
+
+
+def run_report(path_prefix):
+    """Every point of the decode, prefill and dispatch-sweep workloads on both
+    paths: per-launch time, GB/s and % of HBM peak, TFLOP/s and % of the
+    dense MFMA peak, roofline fraction, and the dispatch crossover M* per
+    (shape, group, quantisation, dtype).  Writes <prefix>.md and <prefix>.json."""
+    import torch
+    import int4_weight_only_linear_amd as L
+    from synth import make_case
+    from synth.configs import CONFIGS
+    dev = torch.device("cuda:0")
+    side = torch.cuda.Stream()
+    rows = []
+    t_start = time.time()
+    for name in ("llama8b_decode", "qwen3_4b_decode", "llama8b_prefill", "sweep"):
+        cfg = CONFIGS[name]
+        mmax = max(cfg.Ms)
+        for layer in cfg.layers:
+            K, N = layer.K, layer.N
+            for g in cfg.groups:
+                for sym in cfg.symmetric:
+                    for dt in cfg.dtypes:
+                        for bias in cfg.bias:
+                            c = make_case(mmax, N, K, g, dt, sym, bias, seed=("report", name, K, N, g, sym, dt))
+                            wq, zp, s, x_all, b = _layer_tensors(c, dev)
+                            wbytes = wq.numel() * 4 + s.numel() * 2 + (0 if zp is None else zp.numel() * 4)
+                            copies = max(2, min(64, math.ceil((1 << 30) / wbytes)))
+                            pool = [(wq, zp, s)] + [(wq.clone(), None if zp is None else zp.clone(), s.clone())
+                                                    for _ in range(copies - 1)]
+                            for M in cfg.Ms:
+                                x = x_all[:M].contiguous()
+                                y = torch.empty((M, N), dtype=x.dtype, device=dev)
+                                for path in (L.PATH_GEMV, L.PATH_GEMM):
+                                    if path == L.PATH_GEMV and M > 64:
+                                        continue
+                                    reps = 20 if M >= 128 else 50
+                                    ms = time_point(x, pool, b, y, M, N, K, g, dt, path, reps, side)
+                                    nbytes = decode_bytes(M, N, K, g, asym=not sym, bias=bias)
+                                    flops = 2 * M * N * K
+                                    gbs = nbytes / (ms * 1e-3) / 1e9
+                                    tfl = flops / (ms * 1e-3) / 1e12
+                                    frac = max(gbs / HBM_PEAK_GBS, tfl / MFMA_BF16_PEAK_TFLOPS)
+                                    rows.append(dict(config=name, K=K, N=N, M=M, group=g,
+                                                     quant="uint4b8" if sym else "uint4+zp",
+                                                     dtype="fp16" if dt == 0 else "bf16", bias=bias,
+                                                     path="gemv" if path == L.PATH_GEMV else "gemm",
+                                                     auto=int(L.w4a16_select_path(M, N, K, g, dt, not sym)) == path,
+                                                     us=round(ms * 1e3, 3), GBs=round(gbs, 1),
+                                                     hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                                                     TFLOPs=round(tfl, 1),
+                                                     mfma_frac=round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                                                     roofline_frac=round(frac, 4)))
+                            print(f"[report] {name} K={K} N={N} g={g} {'sym' if sym else 'asym'} "
+                                  f"{'fp16' if dt == 0 else 'bf16'} bias={bias}: {len(cfg.Ms)} M values "
+                                  f"({time.time() - t_start:.0f}s)", file=sys.stderr, flush=True)
+                            del pool, wq, zp, s, x_all, b
+                            torch.cuda.empty_cache()
+    # dispatch crossover: the largest M at which the decode kernel is faster
+    cross = {}
+    for r in rows:
+        if r["config"] != "sweep":
+            continue
+        key = (r["K"], r["N"], r["group"], r["quant"], r["dtype"])
+        cross.setdefault(key, {}).setdefault(r["M"], {})[r["path"]] = r["us"]
+    mstar = []
+    for key, byM in sorted(cross.items()):
+        best = 0
+        for M in sorted(byM):
+            t = byM[M]
+            if "gemv" in t and t["gemv"] <= t["gemm"]:
+                best = M
+        mstar.append(dict(K=key[0], N=key[1], group=key[2], quant=key[3], dtype=key[4], Mstar=best))
+    with open(path_prefix + ".json", "w") as f:
+        json.dump(dict(rows=rows, mstar=mstar), f)
+    with open(path_prefix + ".md", "w") as f:
+        f.write("| config | K | N | M | g | quant | dtype | bias | path | auto | us | GB/s | %HBM | TFLOP/s | %MFMA |\n")
+        f.write("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| {r['config']} | {r['K']} | {r['N']} | {r['M']} | {r['group']} | {r['quant']} | "
+                    f"{r['dtype']} | {'y' if r['bias'] else 'n'} | {r['path']} | {'*' if r['auto'] else ''} | "
+                    f"{r['us']} | {r['GBs']} | {100 * r['hbm_frac']:.1f} | {r['TFLOPs']} | "
+                    f"{100 * r['mfma_frac']:.1f} |\n")
+        f.write("\n| K | N | g | quant | dtype | M* (largest M where the decode kernel is faster) |\n")
+        f.write("|---|---|---|---|---|---|\n")
+        for m in mstar:
+            f.write(f"| {m['K']} | {m['N']} | {m['group']} | {m['quant']} | {m['dtype']} | {m['Mstar']} |\n")
+    print(json.dumps(dict(report=path_prefix + ".md", points=len(rows), mstar=mstar)), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +343,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MB (for scaling PMC byte counters)")
+    ap.add_argument("--report", default="",
+                    help="instead of the bench line: time every point of the decode, prefill and "
+                         "dispatch-sweep workloads on both paths, write <REPORT>.md and .json")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -224,6 +361,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     import int4_weight_only_linear_amd as L  # noqa: F401  (loads libw4a16; raises if missing)
+    if args.report:
+        run_report(args.report)
+        return
 
     if args.calibration_copy_mb:
         # a plain copy of known size: reads and writes exactly n bytes, so the

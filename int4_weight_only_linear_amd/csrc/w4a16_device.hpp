@@ -267,6 +267,16 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_coherent_pair(uint64_t* p, float lo, float hi) {
+  const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) |
+                     ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void load_coherent_pair(const uint64_t* p, float& lo, float& hi) {
+  const uint64_t v = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lo = __builtin_bit_cast(float, (uint32_t)v);
+  hi = __builtin_bit_cast(float, (uint32_t)(v >> 32));
+}
 __device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

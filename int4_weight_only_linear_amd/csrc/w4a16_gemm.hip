@@ -356,48 +356,44 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   }
 
   // ---- split-K: store the partial tile; the last unit of the tile sums them
-  // in split order (cross-workgroup hand-off as described at store_coherent)
+  // in split order (cross-workgroup hand-off as described at store_coherent).
+  // Values travel in 8-byte pairs; thread tid's pair i of a partial tile sits
+  // at pair index i * kThreads + tid.  The sum runs over chunks of kChunk
+  // values: for each split in turn all of a chunk's loads are issued before
+  // any is used, so a chunk costs one memory round trip per split.
   if (p.splits > 1) {
-    const size_t slot = (size_t)BM * kBN;
-    float* mine = p.partial + (size_t)(tile * p.splits + split) * slot;
+    constexpr int NV = MB * 32;  // accumulator values per thread
+    constexpr int kChunk = 64;
+    static_assert(NV % kChunk == 0, "chunking");
+    const size_t slot = (size_t)BM * kBN / 2;  // pairs per partial tile
+    auto val = [&](int q) -> float { return acc[q >> 5][(q >> 4) & 1][q & 15]; };
+    uint64_t* mine = reinterpret_cast<uint64_t*>(p.partial) + (size_t)(tile * p.splits + split) * slot;
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int q = (rb * 2 + cb) * 16 + e;
-          store_coherent(mine + (size_t)q * kThreads + tid, acc[rb][cb][e]);
-        }
+    for (int i = 0; i < NV / 2; ++i) store_coherent_pair(mine + (size_t)i * kThreads + tid, val(2 * i), val(2 * i + 1));
     __syncthreads();  // every thread's partial sums are stored
     if (tid == 0) last_flag = (arrive(p.counters + tile) == (uint32_t)(p.splits - 1));
     __syncthreads();
     if (!last_flag) return;
-    const float* first = p.partial + (size_t)tile * p.splits * slot;
+    const uint64_t* first = reinterpret_cast<const uint64_t*>(p.partial) + (size_t)tile * p.splits * slot;
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
+    for (int c0 = 0; c0 < NV; c0 += kChunk) {
+      float t[kChunk];
+      for (int sp = 0; sp < p.splits; ++sp) {
+        float u[kChunk];
+        if (sp == split) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        // all splits' values of this 16-register block, loads first
-        float t[16];
+          for (int e = 0; e < kChunk; ++e) u[e] = val(c0 + e);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const size_t off = (size_t)((rb * 2 + cb) * 16 + e) * kThreads + tid;
-          t[e] = split == 0 ? acc[rb][cb][e] : load_coherent(first + off);
-        }
-        for (int sp = 1; sp < p.splits; ++sp) {
-          float u[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const size_t off = (size_t)((rb * 2 + cb) * 16 + e) * kThreads + tid;
-            u[e] = sp == split ? acc[rb][cb][e] : load_coherent(first + sp * slot + off);
-          }
-#pragma unroll
-          for (int e = 0; e < 16; ++e) t[e] += u[e];
+          for (int e = 0; e < kChunk; e += 2)
+            load_coherent_pair(first + sp * slot + (size_t)((c0 + e) / 2) * kThreads + tid, u[e], u[e + 1]);
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[rb][cb][e] = t[e];
+        for (int e = 0; e < kChunk; ++e) t[e] = sp == 0 ? u[e] : t[e] + u[e];
       }
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) acc[(c0 + e) >> 5][((c0 + e) >> 4) & 1][(c0 + e) & 15] = t[e];
+    }
     if (tid == 0) reset_counter(p.counters + tile);  // ready for the next call
   }
 
@@ -483,9 +479,7 @@ hipError_t launch_g(const GemmParams& prm, int group, int mb, hipStream_t s) {
 
 // Tile height and K split.  Cost model in cycles of one CU: a k-step of a
 // BM = 32 MB tile is 512 MB cycles of MFMA plus a fixed overhead; units run
-// in rounds of cu_count; a split unit also writes an fp32 partial tile and
-// the tile's last unit reads the others back, at the CU's share of HBM
-// bandwidth (~13 bytes per cycle).
+// in rounds of cu_count; splitting K adds the partial-tile hand-off.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
   GemmPlan best{};
   double best_cost = 0.0;
@@ -502,9 +496,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
       if (splits > 1 && tiles > kMaxCounters) break;
       const int64_t units = tiles * splits;
       const int64_t rounds = (units + cus - 1) / cus;
-      // per round, a split unit writes its fp32 partial tile and (on average)
-      // reads back almost as much
-      const double fixup = splits > 1 ? 2.0 * bm * kBN * 4 / 13.0 : 0.0;
+      // a split unit writes its fp32 partial tile; the tile's last unit then
+      // reads the others back, one memory round trip (~2500 cycles) per
+      // split and 64-value chunk, plus the bytes at the CU's share of HBM
+      const double fixup = splits > 1 ? 2.0 * bm * kBN * 4 / 13.0 +
+                                           2500.0 * splits * (32.0 * mb / 64.0) : 0.0;
       const double cost = (double)rounds * (sps * (512.0 * mb + 700.0) + fixup);
       if (best.units == 0 || cost < best_cost * 0.98) {
         best_cost = cost;
