@@ -318,6 +318,12 @@ def run_report(path_prefix):
     with open(path_prefix + ".json", "w") as f:
         json.dump(dict(rows=rows, mstar=mstar), f)
     with open(path_prefix + ".md", "w") as f:
+        f.write("# W4A16 linear on MI355X: every decode, prefill and crossover-sweep point on both kernels\n\n")
+        f.write(f"Command: python bench.py --report {path_prefix}\n\n")
+        f.write("Each point: mean time per launch over a HIP graph of back-to-back launches that rotate\n"
+                "through >= 1 GiB of weight copies (weights stream from HBM).  GB/s = algorithmic bytes\n"
+                "(weights, scales, zp, x, y, bias) / time; TFLOP/s = 2*M*N*K / time; peaks 8 TB/s and\n"
+                "2.5 PFLOP/s.  auto (*) marks the kernel W4A16_PATH_AUTO picks.\n\n")
         f.write("| config | K | N | M | g | quant | dtype | bias | path | auto | us | GB/s | %HBM | TFLOP/s | %MFMA |\n")
         f.write("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:
@@ -420,7 +426,8 @@ def main():
         for fn in plaunch[0]:
             fn(torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
-        pms = time_steps(plaunch, args.prefill_steps, max(2, args.prefill_steps // 5), side)
+        # five passes per graph, so graph launches do not separate the passes
+        pms = time_steps(plaunch * 5, args.prefill_steps, max(5, args.prefill_steps // 4), side)
         pdurs = per_launch_durations(plaunch * 4, max(3, args.prefill_steps // 4), side)
         flops = sum(2 * 1920 * N * K for (K, N) in PREFILL_LAYERS)
         tflops = flops / (pms * 1e-3) / 1e12

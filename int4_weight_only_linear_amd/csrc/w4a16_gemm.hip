@@ -477,9 +477,11 @@ hipError_t launch_g(const GemmParams& prm, int group, int mb, hipStream_t s) {
 
 }  // namespace
 
-// Tile height and K split.  Cost model in cycles of one CU: a k-step of a
-// BM = 32 MB tile is 512 MB cycles of MFMA plus a fixed overhead; units run
-// in rounds of cu_count; splitting K adds the partial-tile hand-off.
+// Tile height and K split.  Cost model in cycles of one CU, fitted to
+// measured k-step times (about 760 cycles per 32 tokens of the tile plus a
+// fixed 1000: MFMA issue, dequantisation and staging share one instruction
+// stream per SIMD); units run in rounds of cu_count; splitting K adds the
+// partial-tile hand-off.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
   GemmPlan best{};
   double best_cost = 0.0;
@@ -498,10 +500,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
       const int64_t rounds = (units + cus - 1) / cus;
       // a split unit writes its fp32 partial tile; the tile's last unit then
       // reads the others back, one memory round trip (~2500 cycles) per
-      // split and 64-value chunk, plus the bytes at the CU's share of HBM
-      const double fixup = splits > 1 ? 2.0 * bm * kBN * 4 / 13.0 +
+      // split and 64-value chunk, plus the bytes (mostly from L2 / MALL)
+      const double fixup = splits > 1 ? 2.0 * bm * kBN * 4 / 40.0 +
                                            2500.0 * splits * (32.0 * mb / 64.0) : 0.0;
-      const double cost = (double)rounds * (sps * (512.0 * mb + 700.0) + fixup);
+      const double cost = (double)rounds * (sps * (760.0 * mb + 1000.0) + fixup);
       if (best.units == 0 || cost < best_cost * 0.98) {
         best_cost = cost;
         best.mb = mb;

@@ -94,15 +94,16 @@ size_t act_bytes(int64_t n) { return (size_t)n * 2; }
 bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
 
 // Decode-kernel threshold.  The pages route M <= 5 to their skinny kernel
-// (on RDNA); on MI355X the skinny kernel stays on the HBM roofline further,
-// so the crossover is a measured table rather than the pages' constant.
+// (tuned on RDNA).  On MI355X the decode kernel beats the GEMM up to M = 16
+// at every shape, group, quantisation and dtype of the crossover sweep, and
+// the GEMM wins or ties from M = 32, so the constant is measured, not theirs.
 int64_t gemv_threshold(int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t has_zp) {
   (void)N; (void)K; (void)group; (void)dtype; (void)has_zp;
   if (const char* env = std::getenv("W4A16_M_THRESHOLD")) {
     const long v = std::strtol(env, nullptr, 10);
     if (v >= 0 && v <= W4A16_GEMV_MAX_M) return v;
   }
-  return 32;
+  return 16;
 }
 
 w4a16_path resolve_path(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,
