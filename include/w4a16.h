@@ -16,13 +16,21 @@
  * side is kept -- and it does NOT work here".
  *
  * Layout contract (all tensors contiguous, row-major):
- *   wq     int32  [N, K/8]  each word holds one 8-k slice of its row: the weight
- *                           at k = 8L + (0,2,4,6,1,3,5,7)[t] of slice L sits in
- *                           nibble t (bits 4t..4t+3).  Words are stored in slice
- *                           order except inside each complete run of 16 words
- *                           (128 k) of a row, which is stored as the 4x4
- *                           transpose: stored word 4r+t holds slice 4t+r of the
- *                           run.  A last, incomplete run stays in slice order.
+ *   wq     int32  [N, K/8]  N * K/8 words.  Each word holds one 8-k slice of
+ *                           a row: the weight at k = 8L + (0,2,4,6,1,3,5,7)[t]
+ *                           of slice L sits in nibble t (bits 4t..4t+3).  A
+ *                           row's words are in slice order except inside each
+ *                           complete run of 16 words (128 k), stored as the 4x4
+ *                           transpose: run word 4r+t holds slice 4t+r of the
+ *                           run; a last, incomplete run stays in slice order.
+ *                           Rows form tiles of 16.  A complete tile i occupies
+ *                           words [16i*K/8, 16(i+1)*K/8): for each complete run
+ *                           u, a block of 256 words at offset 256u whose word
+ *                           4(16r + j) + e is run word 4r+e of the tile's row j;
+ *                           after the blocks, the rows' incomplete runs, row
+ *                           after row.  A last, incomplete tile (N % 16 != 0)
+ *                           stores its rows one after another, K/8 words each.
+ *                           w4a16_pack_weights / w4a16_unpack_weights convert.
  *                           Bits are unsigned (int32 or uint32 storage).
  *   zp     int32  [N/8, G]  nibble i of word (r, j) is the zero point of row 8r+i
  *                           and group j.  NULL selects symmetric uint4b8 (z = 8).
@@ -57,7 +65,7 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 1
+#define W4A16_ABI_VERSION 2
 
 typedef enum w4a16_status {
   W4A16_OK = 0,

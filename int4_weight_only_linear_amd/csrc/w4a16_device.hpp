@@ -97,6 +97,34 @@ __device__ __forceinline__ int slice_of_stored_word(int j, int J) {
   return (run << 4) + 4 * (p & 3) + (p >> 2);
 }
 
+// Row n and 8-k slice of the word at flat index idx of the packed weights
+// (N rows of J words).  Complete 16-row tiles are stored tile-major: per
+// complete run a 256-word block whose 16-byte piece 16 r + row holds run
+// words 4r..4r+3 of that row, then the rows' incomplete runs row after row;
+// a final incomplete tile keeps its rows one after another.
+__device__ __forceinline__ void locate_word(int64_t idx, int64_t N, int J, int64_t& n, int& slice) {
+  const int64_t tile_words = 16 * (int64_t)J;
+  const int64_t tile = idx / tile_words;
+  if (tile >= (N >> 4)) {
+    n = idx / J;
+    slice = slice_of_stored_word((int)(idx - n * J), J);
+    return;
+  }
+  const int off = (int)(idx - tile * tile_words);
+  const int runs = J >> 4;
+  if (off < 256 * runs) {
+    const int piece = (off & 255) >> 2, e = off & 3;
+    n = tile * 16 + (piece & 15);
+    slice = ((off >> 8) << 4) + 4 * e + (piece >> 4);  // run word 4r+e holds slice 4e+r
+  } else {
+    const int tail = J - (runs << 4);
+    const int t = off - 256 * runs;
+    const int row = t / tail;
+    n = tile * 16 + row;
+    slice = (runs << 4) + (t - row * tail);
+  }
+}
+
 // -(magic + z) in both halves of a word
 template <int DT>
 __device__ __forceinline__ uint32_t neg_magic_pair(uint32_t z) {

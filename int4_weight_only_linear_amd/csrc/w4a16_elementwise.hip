@@ -21,13 +21,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   const int64_t G = K / group;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t n = idx / words_per_row;
-    const int64_t j = slice_of_stored_word((int)(idx - n * words_per_row), (int)words_per_row);
-    const int64_t grp = (j * 8) / group;
+    int64_t n;
+    int j;
+    locate_word(idx, N, (int)words_per_row, n, j);
+    const int64_t grp = ((int64_t)j * 8) / group;
     const uint16_t sbits = scales[n * G + grp];
     const uint32_t z = ASYM ? zero_point(zp, (int)n, (int)G, (int)grp) : 8u;
     const GroupConst<DT> gc = group_const<DT>(sbits, z);
-    *reinterpret_cast<u32x4*>(w + n * K + j * 8) = dequant_word<DT>(
+    *reinterpret_cast<u32x4*>(w + n * K + (int64_t)j * 8) = dequant_word<DT>(
         __builtin_nontemporal_load(wq + idx), gc.s_pair, gc.nmz_pair, gc.s_f32, gc.c_f32);
   }
 }
@@ -36,13 +37,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 // bytes in k order
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ wq,
                                                      uint8_t* __restrict__ q, int64_t words,
-                                                     int words_per_row) {
+                                                     int64_t N, int words_per_row) {
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < words;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const uint32_t w = wq[idx];
-    const int64_t n = idx / words_per_row;
-    const int64_t slice = n * words_per_row +
-                          slice_of_stored_word((int)(idx - n * words_per_row), words_per_row);
+    int64_t n;
+    int j;
+    locate_word(idx, N, words_per_row, n, j);
+    const int64_t slice = n * words_per_row + j;
     const uint32_t even = w & 0x0000FFFFu;  // k = 0, 2, 4, 6 in nibbles 0..3
     const uint32_t odd = w >> 16;           // k = 1, 3, 5, 7 in nibbles 4..7
     uint32_t lo = 0, hi = 0;                // bytes k = 0..3 and 4..7
@@ -92,7 +94,7 @@ hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* 
 hipError_t launch_unpack(const int32_t* wq, uint8_t* q, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t words = N * (K >> 3);
   hipLaunchKernelGGL(unpack_kernel, grid_for(words, 256), 256, 0, stream,
-                     reinterpret_cast<const uint32_t*>(wq), q, words, (int)(K >> 3));
+                     reinterpret_cast<const uint32_t*>(wq), q, words, N, (int)(K >> 3));
   return hipGetLastError();
 }
 

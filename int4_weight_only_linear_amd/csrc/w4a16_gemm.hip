@@ -135,13 +135,34 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     }
   };
 
-  // ---- weights: lane j of column block cb reads row n = nw0 + 32 cb + j
+  // ---- weights: lane j of column block cb reads row n = nw0 + 32 cb + j,
+  // pieces h and h + 2 (16 bytes each) of every run.  In a complete 16-row
+  // tile, run s is a 1 KiB block at tile start + 1024 s and piece pc of row
+  // n is its piece 16 pc + (n mod 16); a final incomplete tile keeps its
+  // rows one after another (64-byte runs).  The incomplete last run of a
+  // row (slice order) is tail_w[cb] words in, T = wpr - 16 full_steps words.
   int nrow[2];
-  uint32_t woff[2];
+  uint32_t woff[2][2];   // [cb][pc]: byte offset of piece h + 2 pc in run 0
+  uint32_t rshift[2];    // run s starts s << rshift bytes further
+  uint32_t tail_w[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    nrow[cb] = min(nw0 + 32 * cb + j, p.N - 1);
-    woff[cb] = (uint32_t)nrow[cb] * (uint32_t)p.wpr * 4u + 16u * (uint32_t)h;
+    const int n = min(nw0 + 32 * cb + j, p.N - 1);
+    nrow[cb] = n;
+    const int jj = n & 15;
+    const uint32_t t0 = (uint32_t)(n - jj) * (uint32_t)p.wpr;  // tile start, words
+    const int tail_words = p.wpr - 16 * p.full_steps;
+    if (n - jj + 16 <= p.N) {
+      woff[cb][0] = t0 * 4u + (uint32_t)(16 * h + jj) * 16u;
+      woff[cb][1] = woff[cb][0] + 512u;
+      rshift[cb] = 10u;
+      tail_w[cb] = t0 + 256u * (uint32_t)p.full_steps + (uint32_t)(jj * tail_words);
+    } else {
+      woff[cb][0] = (uint32_t)n * (uint32_t)p.wpr * 4u + 16u * (uint32_t)h;
+      woff[cb][1] = woff[cb][0] + 32u;
+      rshift[cb] = 6u;
+      tail_w[cb] = (uint32_t)n * (uint32_t)p.wpr + 16u * (uint32_t)p.full_steps;
+    }
   }
 
   struct StepRegs {
@@ -151,23 +172,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   };
   // complete run: pieces h and h + 2 of the run's four 16-byte pieces
   auto load_full = [&](int s, StepRegs& r) {
-    const unsigned char* base = reinterpret_cast<const unsigned char*>(p.wq) + (size_t)s * 64;
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(p.wq);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < 2; ++cb) {
+      const uint32_t run = (uint32_t)s << rshift[cb];
 #pragma unroll
       for (int pc = 0; pc < 2; ++pc)
-        r.w[cb][pc] = *reinterpret_cast<const u32x4*>(base + woff[cb] + 32 * pc);
+        r.w[cb][pc] = *reinterpret_cast<const u32x4*>(base + run + woff[cb][pc]);
+    }
   };
   // incomplete run, stored in slice order: k-sub ks of half h is word 2 ks + h
   auto load_tail = [&](int s, StepRegs& r) {
     const int nks = (p.K - s * kBK) / 16;
-    const uint32_t* base = p.wq + (size_t)s * 16;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         uint32_t v = 0u;
-        if (ks < nks) v = base[(size_t)nrow[cb] * p.wpr + 2 * ks + h];
+        if (ks < nks) v = p.wq[(size_t)tail_w[cb] + 2 * ks + h];
         r.w[cb][ks & 1][ks >> 1] = v;
       }
   };

@@ -7,12 +7,15 @@
 //
 // * Work unit: 16 output rows (one MFMA column tile) x one 128-wide k-step,
 //   i.e. one 128-k run of each row.  Lane (j = lane % 16, r = lane / 16)
-//   issues one 16-byte non-temporal load per k-step, stored words 4r..4r+3 of
-//   row n0 + j's run; the runs are stored as a 4x4 word transpose, so
-//   register t holds slice r of chunk t -- exactly the B operand layout of
+//   issues one 16-byte non-temporal load per k-step, run words 4r..4r+3 of
+//   row n0 + j; the runs are stored as a 4x4 word transpose, so register t
+//   holds slice r of chunk t -- exactly the B operand layout of
 //   v_mfma_f32_16x16x32 for chunk t, and every MFMA covers 32 k of one
-//   quantisation group.  (An incomplete last run, stored in order, is
-//   transposed across the four 16-lane rows with permlane swaps instead.)
+//   quantisation group.  The weights of a complete 16-row tile are stored
+//   tile-major, so the 64 lanes' pieces of one run are one contiguous 1 KiB
+//   block: whole cache lines, and each load's bytes come back together.  (An
+//   incomplete last run, stored in order, is transposed across the four
+//   16-lane rows with permlane swaps instead.)
 // * The scale is factored out of the dot product: per group the wave forms
 //   sum_k x[m,k] * (q[n,k] - z[n,g]) in fp32 and adds s[n,g] times it to the
 //   accumulator; nothing is rounded to the activation dtype before the output.
@@ -69,6 +72,46 @@ struct GemvParams {
   int lg_groups_per_wave;
   int wave_lds_bytes;
 };
+
+// Addresses of one lane's 16-byte weight pieces, run by run, for the row
+// tile starting at row n0: lane (r, j) needs run words 4r..4r+3 of row
+// n0 + j.  In a complete tile they are piece 16 r + j of the run's 1 KiB
+// block; in a final incomplete tile, bytes 16 r of the row's 64-byte run.
+// The incomplete last run (chunks 4R.. of K/32) is stored in slice order,
+// T = 4 * tail chunks words per row; lanes past it read its last chunk.
+struct WeightWalk {
+  const char* base;   // wave-uniform
+  uint32_t lane_off;  // complete runs: base + ks * run_bytes + lane_off
+  uint32_t run_bytes;
+  uint32_t tail_off;  // the incomplete last run: base + tail_off
+  int full_runs;
+  __device__ __forceinline__ const char* at(int ks) const {
+    return base + (ks < full_runs ? (size_t)ks * run_bytes + lane_off : (size_t)tail_off);
+  }
+};
+
+__device__ __forceinline__ WeightWalk weight_walk(const uint32_t* wq, int N, int K, int nchunks,
+                                                  int n0, int j, int r) {
+  WeightWalk w;
+  const uint32_t row_bytes = (uint32_t)(K >> 1);
+  const int full_runs = nchunks >> 2;
+  const int tail_chunks = nchunks - 4 * full_runs;
+  const uint32_t tail_piece = 16u * (uint32_t)max(0, min(r, tail_chunks - 1));
+  w.full_runs = full_runs;
+  if (n0 + kGemvRowsPerTile <= N) {
+    w.base = reinterpret_cast<const char*>(wq) + (size_t)n0 * row_bytes;
+    w.run_bytes = 1024u;
+    w.lane_off = (uint32_t)(16 * r + j) * 16u;
+    w.tail_off = (uint32_t)full_runs * 1024u + (uint32_t)j * (uint32_t)(16 * tail_chunks) + tail_piece;
+  } else {
+    const uint32_t n = (uint32_t)min(n0 + j, N - 1);
+    w.base = reinterpret_cast<const char*>(wq);
+    w.run_bytes = 64u;
+    w.lane_off = n * row_bytes + 16u * (uint32_t)r;
+    w.tail_off = n * row_bytes + (uint32_t)full_runs * 64u + tail_piece;
+  }
+  return w;
+}
 
 // Store or hand over the reduced sums of one row tile: with one K range the
 // output (+ bias, one rounding); otherwise the fp32 partial, and the last
@@ -139,7 +182,6 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   const int tile = blockIdx.x;
   const int split = blockIdx.y;
   const int n0 = tile * kGemvRowsPerTile;
-  const int nc = min(n0 + col, p.N - 1);  // rows past N read row N-1; their outputs are dropped
 
   const int ks_begin = split * p.ksteps_per_split;
   const int ks_end = min(p.ksteps, ks_begin + p.ksteps_per_split);
@@ -192,18 +234,17 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   }
   __builtin_amdgcn_sched_barrier(0);
   // weights: a wave-uniform base per k-step plus one per-lane offset, so each
-  // load needs no vector address arithmetic
-  const uint32_t lane_off = (uint32_t)nc * (uint32_t)(p.K >> 1) + (uint32_t)row4 * 16u;
+  // load needs no vector address arithmetic.  A complete row tile is stored
+  // tile-major: run ks of its 16 rows is one contiguous 1 KiB block and this
+  // lane's 16 bytes are its piece `lane` (r = row4, row = col).  The rows of
+  // a final incomplete tile are stored one after another, 64 bytes per run.
+  const WeightWalk ww = weight_walk(p.wq, p.N, p.K, p.nchunks, n0, col, row4);
   const int last_ks = ks_end - 1;
   u32x4 wv[KPW];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int ks = min(my_first + i, last_ks);
-    const char* base = reinterpret_cast<const char*>(p.wq) + (size_t)ks * 64;
-    uint32_t off = lane_off;
-    // a partial last k-step (K not a multiple of 128): keep lanes in the row
-    if (ks * 4 + 4 > p.nchunks) off -= (uint32_t)max(0, ks * 4 + row4 - (p.nchunks - 1)) * 16u;
-    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ww.at(ks)));
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -398,7 +439,7 @@ __global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
   const int split = blockIdx.y;
   const int n = tile * kGemvRowsPerTile + col;
   const int nc = min(n, p.N - 1);
-  const uint32_t* wrow = p.wq + (size_t)nc * (p.K >> 3);
+  const WeightWalk ww = weight_walk(p.wq, p.N, p.K, p.nchunks, tile * kGemvRowsPerTile, col, row4);
   const uint16_t* srow = p.scales + (size_t)nc * p.G;
 
   const int ks_begin = split * p.ksteps_per_split;
@@ -413,8 +454,7 @@ __global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int ks = min(my_first + i, ks_end - 1);
-    const int c = min(ks * 4 + row4, p.nchunks - 1);
-    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (size_t)c * 4));
+    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ww.at(ks)));
 #pragma unroll
     for (int h = 0; h < GPS; ++h) {
       const int grp = min((ks * 4 + h * CPG) / CPG, p.G - 1);

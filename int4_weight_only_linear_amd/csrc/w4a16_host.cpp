@@ -215,6 +215,23 @@ static int64_t slice_of_stored_word(int64_t j, int64_t J) {
   return run * 16 + 4 * (p % 4) + p / 4;
 }
 
+// Where stored word j of row n sits in the packed tensor.  Rows are grouped
+// in tiles of 16; a complete tile holds, for each complete run, one block of
+// 256 words whose 16-byte piece 16 r + (n mod 16) is the row's run words
+// 4r..4r+3, then the 16 rows' incomplete runs row after row.  The rows of a
+// final incomplete tile are stored one after another.
+static int64_t stored_position(int64_t n, int64_t j, int64_t N, int64_t J) {
+  const int64_t tile = n / 16, row = n % 16;
+  if ((tile + 1) * 16 > N) return n * J + j;
+  const int64_t runs = J / 16, tail = J - 16 * runs;
+  const int64_t base = tile * 16 * J;
+  if (j < 16 * runs) {
+    const int64_t run = j / 16, p = j % 16;
+    return base + 256 * run + 4 * (16 * (p / 4) + row) + p % 4;
+  }
+  return base + 256 * runs + tail * row + (j - 16 * runs);
+}
+
 w4a16_status w4a16_pack_weights(const uint8_t* q, int64_t N, int64_t K, int32_t* wq) {
   if (!q || !wq) return fail(W4A16_ERR_INVALID_ARG, "pack_weights: NULL pointer");
   if (N < 0 || K < 0 || K % 8) return fail(W4A16_ERR_INVALID_ARG, "pack_weights: need N >= 0, K >= 0, K %% 8 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
@@ -226,7 +243,7 @@ w4a16_status w4a16_pack_weights(const uint8_t* q, int64_t N, int64_t K, int32_t*
       const uint8_t* src = q + n * K + slice_of_stored_word(j, J) * 8;
       uint32_t w = 0;
       for (int i = 0; i < 8; ++i) w |= (uint32_t)src[i] << (4 * kSlotOfKoff[i]);
-      wq[n * J + j] = (int32_t)w;
+      wq[stored_position(n, j, N, J)] = (int32_t)w;
     }
   return ok();
 }
@@ -237,7 +254,7 @@ w4a16_status w4a16_unpack_weights(const int32_t* wq, int64_t N, int64_t K, uint8
   const int64_t J = K / 8;
   for (int64_t n = 0; n < N; ++n)
     for (int64_t j = 0; j < J; ++j) {
-      const uint32_t w = (uint32_t)wq[n * J + j];
+      const uint32_t w = (uint32_t)wq[stored_position(n, j, N, J)];
       uint8_t* dst = q + n * K + slice_of_stored_word(j, J) * 8;
       for (int i = 0; i < 8; ++i) dst[i] = (uint8_t)((w >> (4 * kSlotOfKoff[i])) & 0xFu);
     }

@@ -8,5 +8,6 @@ from .w4a16_ref import (  # noqa: F401
     f16_bits_to_f64, bf16_bits_to_f64, act_bits_to_f64,
     f32_to_f16_bits, f32_to_bf16_bits, f32_to_act_bits,
     pack_weights, unpack_weights, pack_zeros, unpack_zeros, slice_of_word, WORDS_PER_RUN,
+    word_position, TILE_ROWS,
     dequant_f32, dequant_act, linear_ref,
 )

@@ -26,7 +26,15 @@ What it computes, and where each step comes from (pages by title):
   - across words: each complete run of 16 words (128 k) of a row is a 4x4
     transpose of words -- stored word 4*r + t of the run holds slice 4*t + r
     of the run; a final incomplete run (K not a multiple of 128) keeps its
-    slices in order.  ``slice_of_word`` spells the map out.
+    slices in order.  ``slice_of_word`` spells the map out;
+  - across rows: the rows form tiles of 16 (rows 16*i .. 16*i + 15), and
+    every complete tile occupies the 16 * K/8 words starting at word
+    16*i * K/8, tile-major: run u of the 16 rows is one block of 256 words
+    at offset 256*u, whose word 4*(16*r + j) + e is word 4*r + e of row j's
+    run (so the 64 sixteen-byte pieces of a block are ordered (r, j)); the
+    incomplete last runs of the 16 rows follow the blocks, row after row.
+    A final incomplete tile (N not a multiple of 16) keeps its rows one
+    after another, K/8 words each.  ``word_position`` spells the map out.
 * Zero-point packing: nibble i (bits 4i..4i+3) of word (r, grp) holds the
   zero point of row 8r + i ("packed 8x uint4 along dim 0").
 * Scales: [N, G] row-major in the activation dtype (G = K / group).
@@ -141,6 +149,36 @@ def _word_order(words_per_row: int) -> np.ndarray:
     return np.array([slice_of_word(j, words_per_row) for j in range(words_per_row)], dtype=np.int64)
 
 
+TILE_ROWS = 16
+
+
+def word_position(n: int, j: int, N: int, words_per_row: int) -> int:
+    """Flat index, in the packed tensor, of stored word j of row n.
+
+    Rows of a complete 16-row tile are interleaved run by run (block of 256
+    words per run, piece order (r, row)); their incomplete runs follow the
+    blocks row after row.  Rows of a final incomplete tile are row-major.
+    """
+    J = words_per_row
+    tile, row = divmod(n, TILE_ROWS)
+    if (tile + 1) * TILE_ROWS > N:
+        return n * J + j
+    base = tile * TILE_ROWS * J
+    runs = J // WORDS_PER_RUN
+    run, p = divmod(j, WORDS_PER_RUN)
+    if run < runs:
+        r, e = divmod(p, 4)
+        return base + 256 * run + 4 * (TILE_ROWS * r + row) + e
+    tail = J - runs * WORDS_PER_RUN
+    return base + 256 * runs + tail * row + (j - runs * WORDS_PER_RUN)
+
+
+def _positions(N: int, words_per_row: int) -> np.ndarray:
+    """pos[n, j] = word_position(n, j, N, J), for every word."""
+    return np.array([[word_position(n, j, N, words_per_row) for j in range(words_per_row)]
+                     for n in range(N)], dtype=np.int64).reshape(N, words_per_row)
+
+
 def pack_weights(q: np.ndarray) -> np.ndarray:
     """q uint8 [N, K] with values 0..15 -> int32 [N, K/8] in the word layout."""
     q = np.asarray(q)
@@ -153,17 +191,21 @@ def pack_weights(q: np.ndarray) -> np.ndarray:
     by_slice = np.zeros((N, K // 8), dtype=np.uint32)
     for koff in range(8):
         by_slice |= q8[:, :, koff] << np.uint32(4 * SLOT_OF_KOFF[koff])
-    # stored word j holds slice order[j]
+    # stored word j of a row holds slice order[j]; the word then sits at
+    # its position in the row tiles
     stored = by_slice[:, _word_order(K // 8)]
-    return np.ascontiguousarray(stored).view(np.int32)
+    out = np.empty(N * (K // 8), dtype=np.uint32)
+    out[_positions(N, K // 8).ravel()] = stored.ravel()
+    return out.reshape(N, K // 8).view(np.int32)
 
 
 def unpack_weights(wq: np.ndarray) -> np.ndarray:
     """int32 (or uint32) [N, K/8] -> uint8 [N, K]; the bits are unsigned."""
     w = np.asarray(wq).view(np.uint32)
     N, J = w.shape
-    by_slice = np.empty_like(w)
-    by_slice[:, _word_order(J)] = w
+    stored = w.ravel()[_positions(N, J).ravel()].reshape(N, J)
+    by_slice = np.empty_like(stored)
+    by_slice[:, _word_order(J)] = stored
     q = np.empty((N, J, 8), dtype=np.uint8)
     for koff in range(8):
         q[:, :, koff] = (by_slice >> np.uint32(4 * SLOT_OF_KOFF[koff])) & np.uint32(0xF)

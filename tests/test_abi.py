@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert L.w4a16_abi_version() == 1
+    assert L.w4a16_abi_version() == L.ABI_VERSION == 2
     m = re.search(r"#define W4A16_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == L.w4a16_abi_version()
     m = re.search(r"#define W4A16_GEMV_MAX_M (\d+)", open(HEADER).read())
@@ -43,7 +43,7 @@ def test_abi_version():
 
 # ---- packing: the library's C++ against the oracle --------------------------
 
-@pytest.mark.parametrize("N,K", [(1, 8), (8, 32), (37, 96), (256, 256), (64, 4096)])
+@pytest.mark.parametrize("N,K", [(1, 8), (8, 32), (37, 96), (256, 256), (64, 4096), (40, 160), (17, 416), (48, 352)])
 def test_pack_weights_matches_oracle(N, K):
     q = np.random.default_rng(N * 7 + K).integers(0, 16, (N, K), dtype=np.uint8)
     wq = L.w4a16_pack_weights(q)
@@ -53,10 +53,11 @@ def test_pack_weights_matches_oracle(N, K):
 
 
 def test_unpack_weights_all_words_matches_oracle():
-    words = np.random.default_rng(3).integers(0, 2**32, (16, 64), dtype=np.uint64)
-    words = words.astype(np.uint32).view(np.int32)
-    assert np.array_equal(L.w4a16_unpack_weights(words), O.unpack_weights(words))
-    assert np.array_equal(L.w4a16_pack_weights(L.w4a16_unpack_weights(words)), words)
+    for shape in ((16, 64), (40, 52), (33, 12)):
+        words = np.random.default_rng(3).integers(0, 2**32, shape, dtype=np.uint64)
+        words = words.astype(np.uint32).view(np.int32)
+        assert np.array_equal(L.w4a16_unpack_weights(words), O.unpack_weights(words))
+        assert np.array_equal(L.w4a16_pack_weights(L.w4a16_unpack_weights(words)), words)
 
 
 @pytest.mark.parametrize("N,G", [(8, 1), (16, 3), (4096, 32)])

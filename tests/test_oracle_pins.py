@@ -126,6 +126,47 @@ def test_worked_words_runs_of_128_k():
     assert [O.slice_of_word(j, 20) for j in range(16, 20)] == [16, 17, 18, 19]
 
 
+def test_worked_words_row_tiles():
+    # rows form tiles of 16; a complete tile stores run u of its rows as one
+    # 256-word block, word 4*(16*r + j) + e = word 4*r + e of row j's run;
+    # incomplete runs follow row after row; a final incomplete tile is
+    # row-major.  Each case: one nonzero code, its flat word index and value.
+    def hot(N, K, n, k, val=1):
+        q = np.zeros((N, K), dtype=np.uint8)
+        q[n, k] = val
+        w = O.pack_weights(q).view(np.uint32).ravel()
+        nz = [i for i, v in enumerate(w) if v]
+        assert len(nz) == 1
+        return nz[0], int(w[nz[0]])
+    # N=16, K=128: one tile, one run
+    assert hot(16, 128, 3, 8) == (76, 0x1)          # slice 1 -> run word 4 (r=1, e=0) -> 4*(16+3)
+    assert hot(16, 128, 0, 32) == (1, 0x1)          # slice 4 -> run word 1 (r=0, e=1)
+    assert hot(16, 128, 15, 127, 7) == (255, 0x70000000)  # slice 15 -> run word 15 -> 4*(48+15)+3
+    assert hot(16, 128, 8, 49, 3) == (161, 0x30000)  # slice 6 -> run word 9 (r=2, e=1) -> 4*(32+8)+1
+    # N=16, K=160: the incomplete run (4 words a row) after the block
+    assert hot(16, 160, 5, 128 + 8 * 3 + 2, 5) == (279, 0x50)  # 256 + 4*5 + 3
+    # N=16, K=256: second run's block
+    assert hot(16, 256, 2, 128 + 8) == (328, 0x1)    # 256 + 4*(16*1 + 2)
+    # N=32, K=128: second tile starts at word 16*16
+    assert hot(32, 128, 16, 0) == (256, 0x1)
+    assert hot(32, 128, 17, 32) == (261, 0x1)       # 256 + 4*(0 + 1) + 1
+    # N=24, K=128: rows 16..23 are an incomplete tile, row-major
+    assert hot(24, 128, 17, 8) == (17 * 16 + 4, 0x1)
+    assert hot(24, 128, 0, 0) == (0, 0x1)
+    # a 16-byte piece of a block holds one row's slices r, 4+r, 8+r, 12+r
+    q = np.zeros((16, 128), dtype=np.uint8)
+    for sl in (2, 6, 10, 14):
+        q[7, 8 * sl] = 1 + sl // 4
+    w = O.pack_weights(q).view(np.uint32).ravel()
+    piece = 16 * 2 + 7
+    assert w[4 * piece:4 * piece + 4].tolist() == [1, 2, 3, 4]
+    assert int(np.count_nonzero(w)) == 4
+    # word_position is a bijection onto the tensor for ragged shapes too
+    for N, J in ((16, 16), (16, 20), (32, 44), (40, 28), (7, 20)):
+        pos = sorted(O.word_position(n, j, N, J) for n in range(N) for j in range(J))
+        assert pos == list(range(N * J))
+
+
 def test_worked_words_zeros():
     z = np.arange(8, dtype=np.uint8).reshape(8, 1)
     assert int(O.pack_zeros(z).view(np.uint32)[0, 0]) == 0x76543210

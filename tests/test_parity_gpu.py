@@ -56,6 +56,16 @@ def test_dequant_bit_exact(dt, sym, g, N, K):
     assert np.array_equal(w, ref)
 
 
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("N,K,g", [(24, 224, 32), (56, 320, 64), (48, 96, 32), (16, 1184, 32)])
+def test_dequant_bit_exact_incomplete_runs(dt, N, K, g):
+    c = make_case(1, N, K, g, dt, False, False, seed=("dqtail", N, K, g, dt))
+    d = DeviceCase(c)
+    w = device_to_bits(L.w4a16_dequant(d.wq, d.s, d.zp, group_size=g))
+    ref = O.dequant_act(O.pack_weights(c.q), c.s_bits, O.pack_zeros(c.zp), N, K, g, dt)
+    assert np.array_equal(w, ref)
+
+
 @pytest.mark.parametrize("name,dt,sym", [("llama", O.BF16, False), ("qwen", O.F16, True)])
 def test_dequant_bit_exact_full_layer(name, dt, sym):
     K, N = (4096, 4096) if name == "llama" else (2560, 6144)
@@ -93,6 +103,10 @@ GRID = [
     (1, 8, 128, 32), (1, 40, 384, 128), (3, 264, 1152, 64), (5, 128, 4096, 128),
     (16, 520, 640, 32), (17, 96, 512, 128), (40, 264, 1152, 64), (64, 136, 256, 32),
     (70, 264, 1152, 128), (130, 200, 640, 64), (257, 136, 384, 32),
+    # K not a multiple of 128 (an incomplete last run of 1, 2 or 3 chunks),
+    # with complete 16-row tiles and an incomplete last tile
+    (1, 48, 416, 32), (5, 40, 224, 32), (9, 24, 320, 64), (33, 56, 160, 32),
+    (130, 72, 608, 32), (200, 264, 1216, 64),
 ]
 
 
