@@ -15,6 +15,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace w4a16 {
@@ -95,6 +96,16 @@ __device__ __forceinline__ int slice_of_stored_word(int j, int J) {
   const int run = j >> 4, p = j & 15;
   if ((run + 1) * 16 > J) return j;
   return (run << 4) + 4 * (p & 3) + (p >> 2);
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time, so
+// register arrays indexed by I are never indexed dynamically
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Row n and 8-k slice of the word at flat index idx of the packed weights

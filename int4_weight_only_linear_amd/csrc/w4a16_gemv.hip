@@ -164,7 +164,9 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // before its dot products; the only barrier is the final cross-wave sum.
 // All staging index maps are shifts and masks (the per-wave sizes are powers
 // of two), keeping the vector-ALU work in front of the weight loads small.
-template <int DT, int GS, bool ASYM, int KPW, int XPT>
+// ONE: a single token (M == 1), whose sums are row 0 of each MFMA result
+// (lanes 0..15, register 0); the other rows are then never updated.
+template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE>
 __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
   constexpr int SPT = (32 * KPW) / GS > 0 ? (32 * KPW) / GS : 1;  // scale loads per lane
@@ -212,18 +214,37 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   u32x4 xr[XPT];
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    const int e = min(lane + 64 * j, xsegs - 1);
-    const int m = e >> lg_xsegs;
-    const int k = min(kw0 + ((e & (xsegs_row - 1)) << 3), p.K - 8);
-    xr[j] = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + k);
+    xr[j] = u32x4{0u, 0u, 0u, 0u};
+    if (64 * j < xsegs) {  // wave-uniform: only the loads that carry x
+      const int e = min(lane + 64 * j, xsegs - 1);
+      const int m = e >> lg_xsegs;
+      const int k = min(kw0 + ((e & (xsegs_row - 1)) << 3), p.K - 8);
+      xr[j] = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + k);
+    }
   }
+  // scales of the run: when each row's groups of the run are whole 16-byte
+  // pieces of the scale tensor, one 16-byte load per lane (lane = row *
+  // pieces per row + piece); otherwise one 2-byte load per scale
+  const bool svec = ngw >= 8 && (p.G & 7) == 0 && (gw0 & 7) == 0 && gw0 + ngw <= p.G &&
+                    (reinterpret_cast<uintptr_t>(p.scales) & 15) == 0;
+  u32x4 srv = {0u, 0u, 0u, 0u};
   uint32_t sr[SPT];
 #pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int e = min(lane + 64 * j, 16 * ngw - 1);
-    const int r = e >> lg_ngw;
-    const int g = min(gw0 + (e & (ngw - 1)), p.G - 1);
-    sr[j] = p.scales[(size_t)min(n0 + r, p.N - 1) * p.G + g];
+  for (int j = 0; j < SPT; ++j) sr[j] = 0u;
+  if (svec) {
+    const int lg_ppr = lg_ngw - 3;
+    const int e = min(lane, (16 << lg_ppr) - 1);
+    const int r = e >> lg_ppr;
+    srv = *reinterpret_cast<const u32x4*>(p.scales + (size_t)min(n0 + r, p.N - 1) * p.G + gw0 +
+                                          8 * (e & ((1 << lg_ppr) - 1)));
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int e = min(lane + 64 * j, 16 * ngw - 1);
+      const int r = e >> lg_ngw;
+      const int g = min(gw0 + (e & (ngw - 1)), p.G - 1);
+      sr[j] = p.scales[(size_t)min(n0 + r, p.N - 1) * p.G + g];
+    }
   }
   uint32_t zr = 0u;
   if constexpr (ASYM) {
@@ -257,10 +278,15 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
       *reinterpret_cast<u32x4*>(xs + m * xstride + ((e & (xsegs_row - 1)) << 3)) = xr[j];
     }
   }
+  if (svec) {
+    // lane = row * (ngw / 8) + piece holds scales row * ngw + 8 * piece ...
+    if (lane < 2 * ngw) *reinterpret_cast<u32x4*>(sl + 8 * lane) = srv;
+  } else {
 #pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int e = lane + 64 * j;
-    if (e < 16 * ngw) sl[e] = (uint16_t)sr[j];
+    for (int j = 0; j < SPT; ++j) {
+      const int e = lane + 64 * j;
+      if (e < 16 * ngw) sl[e] = (uint16_t)sr[j];
+    }
   }
   if constexpr (ASYM) {
     if (lane < 2 * ngw) zl[lane] = zr;
@@ -352,64 +378,69 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
 
   if (my_steps == KPW && (my_first + KPW) * 4 <= p.nchunks) {
     // Common case: the wave's whole run is complete 128-k runs.  Branch-free
-    // and software pipelined, two k-steps at a time: the x fragments of the
-    // next pair are read while this pair is multiplied, and the MFMAs of the
-    // two steps' chains alternate, so no MFMA waits for the result of the one
-    // issued just before it.  bf16 multiplies x by 128 + q only; the offset
-    // and the zero point are removed per group with the x sums.
-    constexpr int PAIR = KPW >= 2 ? 2 : 1;
-    u32x4 xa[2][PAIR][4];
-    auto load_x = [&](int i, u32x4 (&x)[PAIR][4]) {
+    // and software pipelined one k-step deep: the x fragments of step i + 1
+    // are read from LDS while step i is multiplied.  (Keeping only one step
+    // of fragments in flight keeps the register count low enough for many
+    // resident waves.)  bf16 multiplies x by 128 + q only; the offset and
+    // the zero point are removed per group with the x sums.
+    u32x4 xa[2][4];
+    auto load_x = [&](int i, u32x4 (&x)[4]) {
 #pragma unroll
-      for (int s2 = 0; s2 < PAIR; ++s2)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          x[s2][t] = *reinterpret_cast<const u32x4*>(xrow + (i + s2) * kGemvKStep + t * 32);
+      for (int t = 0; t < 4; ++t)
+        x[t] = *reinterpret_cast<const u32x4*>(xrow + i * kGemvKStep + t * 32);
     };
-    load_x(0, xa[0]);
+    {
+      constexpr int NR = ONE ? 1 : 4;  // accumulator rows in use
+      load_x(0, xa[0]);
 #pragma unroll
-    for (int i = 0; i < KPW; i += PAIR) {
-      const int c = (i / PAIR) & 1;
-      if (i + PAIR < KPW) load_x(i + PAIR, xa[c ^ 1]);
-      f32x4 ch[PAIR];
+      for (int i = 0; i < KPW; ++i) {
+        // keep each step's work after the wait for its own weights: left
+        // free, the scheduler hoists later steps' unpacking to the top, and
+        // the first MFMA then waits for every load of the run
+        __builtin_amdgcn_sched_barrier(0);
+        const int c = i & 1;
+        if (i + 1 < KPW) load_x(i + 1, xa[c ^ 1]);
+        f32x4 ch;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int s2 = 0; s2 < PAIR; ++s2) {
-          const int ii = i + s2;
-          const int gl = ii * (4 / CPG) + t / CPG;  // group within this wave's run
+        for (int t = 0; t < 4; ++t) {
+          const int gl = i * (4 / CPG) + t / CPG;  // group within this wave's run
           const bool fresh = (t % CPG) == 0;
           const uint32_t z = ASYM ? (zrow_l[gl] >> zshift) & 0xFu : 8u;
           if constexpr (DT == DT_F16) {
-            const u32x4 bq = qz_word_f16(wv[ii][t], mask_v, neg_magic_pair<DT>(z));  // q - z, exact
-            ch[s2] = mfma16x16x32<DT>(xa[c][s2][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[s2]);
+            const u32x4 bq = qz_word_f16(wv[i][t], mask_v, neg_magic_pair<DT>(z));  // q - z, exact
+            ch = mfma16x16x32<DT>(xa[c][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
           } else {
-            const u32x4 bq = magic_word<DT>(wv[ii][t], mask_v);  // 128 + q, exact
-            ch[s2] = mfma16x16x32<DT>(xa[c][s2][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch[s2]);
+            const u32x4 bq = magic_word<DT>(wv[i][t], mask_v);  // 128 + q, exact
+            ch = mfma16x16x32<DT>(xa[c][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
           }
           if (t % CPG == CPG - 1) {
             const float sc = act_to_f32<DT>(srow_l[gl]);
             if constexpr (DT == DT_BF16) {
               // s * (x . (128 + q) - (128 + z) * xsum); -(128 + z) * s is exact
               const float szc = -(128.0f + (float)z) * sc;
-              const f32x4 xs4 = *reinterpret_cast<const f32x4*>(xsum + gl * 16 + 4 * row4);
-              acc += sc * ch[s2] + szc * xs4;
+              const float* xs = xsum + gl * 16 + 4 * row4;
+#pragma unroll
+              for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], __builtin_fmaf(szc, xs[r], acc[r]));
             } else {
-              acc += sc * ch[s2];
+#pragma unroll
+              for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], acc[r]);
             }
           }
         }
       }
     }
   } else {
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      if (i >= my_steps) break;
+    // unrolled at compile time, so that wv[] is never indexed dynamically
+    // (which would put it in scratch memory)
+    static_for<0, KPW>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (i >= my_steps) return;
+      __builtin_amdgcn_sched_barrier(0);  // this step's work after its own wait
       if ((my_first + i) * 4 + 4 <= p.nchunks)
         kstep(wv[i], i, std::true_type{});
       else
         kstep(wv[i], i, std::false_type{});
-    }
+    });
   }
 
   // ---- 4. reduce the waves in order, then the K ranges ----
@@ -472,6 +503,7 @@ __global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     if (i >= my_steps) break;
+    __builtin_amdgcn_sched_barrier(0);  // this step's work after its own wait
     const int c0 = (my_first + i) * 4;
     u32x4 wt = wv[i];
     if (c0 + 4 > p.nchunks) transpose_rows4(wt);  // incomplete run: stored in order
@@ -595,10 +627,15 @@ static hipError_t launch_t(const GemvParams& prm, const GemvPlan& plan, hipStrea
     // the small kernel is instantiated per k-steps per wave, so that its
     // branch-free path covers every wave whose run is complete
     switch (plan.kpw) {
-      case 8: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, kGemvXSegsPerThread>), grid, block, plan.lds_bytes, s, prm); break;
-      case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, kGemvXSegsPerThread>), grid, block, plan.lds_bytes, s, prm); break;
-      case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, kGemvXSegsPerThread>), grid, block, plan.lds_bytes, s, prm); break;
-      case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, kGemvXSegsPerThread>), grid, block, plan.lds_bytes, s, prm); break;
+      case 8:
+        if (prm.M == 1)
+          hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, kGemvXSegsPerThread, true>), grid, block, plan.lds_bytes, s, prm);
+        else
+          hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, kGemvXSegsPerThread, false>), grid, block, plan.lds_bytes, s, prm);
+        break;
+      case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, kGemvXSegsPerThread, false>), grid, block, plan.lds_bytes, s, prm); break;
+      case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, kGemvXSegsPerThread, false>), grid, block, plan.lds_bytes, s, prm); break;
+      case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, kGemvXSegsPerThread, false>), grid, block, plan.lds_bytes, s, prm); break;
       default: return hipErrorInvalidConfiguration;
     }
   } else
