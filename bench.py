@@ -144,26 +144,29 @@ def time_steps(step_lists, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps
 
 
-def per_launch_durations(step_lists, reps, stream):
+def per_launch_durations(step_lists, reps, stream, passes=5, replays=4):
     """Mean duration of each launch position, from HIP events on the launch
-    stream around graphs of `len(step_lists)` back-to-back launches of that
-    position (one per weight copy), so event overhead is spread over many
-    launches and the kernels run as they do inside a step."""
+    stream around `replays` back-to-back replays of a graph holding `passes`
+    rounds of that position's launches (one per weight copy), so the graph
+    and event overheads are spread over hundreds of launches and the kernels
+    run back to back as they do inside a step.  Median over `reps`."""
     import torch
     out = []
     for j in range(len(step_lists[0])):
-        g = capture([[fns[j]] for fns in step_lists], stream)
+        g = capture([[fns[j]] for _ in range(passes) for fns in step_lists], stream)
         g.replay()
         torch.cuda.synchronize()
+        n = passes * len(step_lists) * replays
         ts = []
         for _ in range(reps):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            g.replay()
+            for _ in range(replays):
+                g.replay()
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) / len(step_lists))
+            ts.append(e0.elapsed_time(e1) / n)
         out.append(float(np.median(ts)))
     return out
 
@@ -428,7 +431,7 @@ def main():
         torch.cuda.synchronize()
         # five passes per graph, so graph launches do not separate the passes
         pms = time_steps(plaunch * 5, args.prefill_steps, max(5, args.prefill_steps // 4), side)
-        pdurs = per_launch_durations(plaunch * 4, max(3, args.prefill_steps // 4), side)
+        pdurs = per_launch_durations(plaunch * 4, max(3, args.prefill_steps // 4), side, passes=1, replays=2)
         flops = sum(2 * 1920 * N * K for (K, N) in PREFILL_LAYERS)
         tflops = flops / (pms * 1e-3) / 1e12
         prefill = dict(workload="Llama-3.1-8B-shaped prefill, M=1920, layers (K,N) "

@@ -174,9 +174,21 @@ def word_position(n: int, j: int, N: int, words_per_row: int) -> int:
 
 
 def _positions(N: int, words_per_row: int) -> np.ndarray:
-    """pos[n, j] = word_position(n, j, N, J), for every word."""
-    return np.array([[word_position(n, j, N, words_per_row) for j in range(words_per_row)]
-                     for n in range(N)], dtype=np.int64).reshape(N, words_per_row)
+    """pos[n, j] = word_position(n, j, N, J) for every word, the same cases
+    written with whole-array operations."""
+    J = words_per_row
+    n = np.arange(N, dtype=np.int64)[:, None]
+    j = np.arange(J, dtype=np.int64)[None, :]
+    tile, row = n // TILE_ROWS, n % TILE_ROWS
+    runs = J // WORDS_PER_RUN
+    tail = J - runs * WORDS_PER_RUN
+    base = tile * TILE_ROWS * J
+    run, p = j // WORDS_PER_RUN, j % WORDS_PER_RUN
+    in_run = base + 256 * run + 4 * (TILE_ROWS * (p // 4) + row) + p % 4
+    in_tail = base + 256 * runs + tail * row + (j - runs * WORDS_PER_RUN)
+    tiled = np.where(j < runs * WORDS_PER_RUN, in_run, in_tail)
+    complete = (tile + 1) * TILE_ROWS <= N
+    return np.where(complete, tiled, n * J + j)
 
 
 def pack_weights(q: np.ndarray) -> np.ndarray:

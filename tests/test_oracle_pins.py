@@ -161,10 +161,13 @@ def test_worked_words_row_tiles():
     piece = 16 * 2 + 7
     assert w[4 * piece:4 * piece + 4].tolist() == [1, 2, 3, 4]
     assert int(np.count_nonzero(w)) == 4
-    # word_position is a bijection onto the tensor for ragged shapes too
-    for N, J in ((16, 16), (16, 20), (32, 44), (40, 28), (7, 20)):
-        pos = sorted(O.word_position(n, j, N, J) for n in range(N) for j in range(J))
-        assert pos == list(range(N * J))
+    # word_position is a bijection onto the tensor for ragged shapes too, and
+    # the whole-array map the packer uses agrees with it word for word
+    from oracle.w4a16_ref import _positions
+    for N, J in ((16, 16), (16, 20), (32, 44), (40, 28), (7, 20), (48, 4), (33, 64)):
+        pos = [O.word_position(n, j, N, J) for n in range(N) for j in range(J)]
+        assert sorted(pos) == list(range(N * J))
+        assert _positions(N, J).ravel().tolist() == pos
 
 
 def test_worked_words_zeros():
