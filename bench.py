@@ -247,6 +247,44 @@ def time_point(x, pool, bias, y, M, N, K, g, dt, path, reps, stream):
     return e0.elapsed_time(e1) / (reps * len(pool))
 
 
+def dense_comparator(players, stream, steps):
+    """The dequantised prefill copy on the same layers: w4a16_dequant once,
+    then w4a16_linear_dense per call (dense product on the matrix cores).
+    Times the dense call alone, like the W4A16 GEMM, plus the one-off
+    dequantisation, and states the memory the copy costs."""
+    import torch
+    import int4_weight_only_linear_amd as L
+    from int4_weight_only_linear_amd import _binding as B
+    rows = []
+    for l in players:
+        K, N, M = l["K"], l["N"], l["M"]
+        w = L.w4a16_dequant(l["wq"], l["s"], l["zp"], group_size=GROUP)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.w4a16_dequant(l["wq"], l["s"], l["zp"], group_size=GROUP, out=w)
+        e1.record()
+        torch.cuda.synchronize()
+        deq_us = e0.elapsed_time(e1) * 1e3
+        ws = torch.empty(L.w4a16_dense_workspace_size(M, N, K, L.W4A16_BF16, False),
+                         dtype=torch.uint8, device=w.device)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=w.device)
+
+        def fn(sp, x=l["x"], w=w, y=y, ws=ws, M=M, N=N, K=K):
+            B._check(B.lib.w4a16_linear_dense(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), M, N, K,
+                                              L.W4A16_BF16, ws.data_ptr(), ws.numel(), sp))
+        fn(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        ms = time_steps([[fn]] * 4, max(8, steps), 4, stream)
+        rows.append(dict(K=K, N=N, us=round(ms * 1e3, 2),
+                         tflops=round(2 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                         dequant_once_us=round(deq_us, 1), copy_bytes=N * K * 2))
+        del w, ws, y
+    return dict(what="w4a16_dequant once (kept resident, 4x the packed bytes), then "
+                     "w4a16_linear_dense (rocBLAS gemm_ex bf16, fp32 accumulation) per call",
+                per_layer=rows)
+
+
 def run_report(path_prefix):
     """Every point of the decode, prefill and dispatch-sweep workloads on both
     paths: per-launch time, GB/s and % of HBM peak, TFLOP/s and % of the
@@ -349,6 +387,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies in the rotation pool (0: >= 1 GiB)")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dequantised-copy (dense) comparator of the prefill layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MB (for scaling PMC byte counters)")
@@ -443,6 +483,8 @@ def main():
                        per_layer=[dict(K=K, N=N, us=round(d * 1e3, 2),
                                        tflops=round(2 * 1920 * N * K / (d * 1e-3) / 1e12, 1))
                                   for (K, N), d in zip(PREFILL_LAYERS, pdurs)])
+        if not args.no_dense:
+            prefill["dequantised_copy"] = dense_comparator(players, side, args.prefill_steps)
         del players, plaunch
 
     cpu = None

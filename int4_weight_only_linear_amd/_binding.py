@@ -48,6 +48,9 @@ SIGNATURES = {
                                    _c_i32, _vp, _c_sz, _vp, _c_i32]),
     "w4a16_dequant": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i32, _c_i32, _vp]),
     "w4a16_unpack_device": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp]),
+    "w4a16_linear_dense": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32, _vp, _c_sz,
+                                    _vp]),
+    "w4a16_dense_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
 }
 
 
@@ -305,4 +308,37 @@ def w4a16_unpack_device(wq, out=None):
     stream = torch.cuda.current_stream(wq.device).cuda_stream
     with torch.cuda.device(wq.device):
         _check(lib.w4a16_unpack_device(wq.data_ptr(), out.data_ptr(), N, K, stream))
+    return out
+
+
+def w4a16_dense_workspace_size(M, N, K, dtype, has_bias) -> int:
+    return int(lib.w4a16_dense_workspace_size(M, N, K, dtype, int(bool(has_bias))))
+
+
+def w4a16_linear_dense(x, w, bias=None, *, out=None, workspace=None):
+    """y = x . w^T (+ bias) with w the dequantised weights [N, K] (w4a16_dequant),
+    on x's device and current stream."""
+    torch = _torch()
+    dt = _act_code(x)
+    if x.dim() != 2 or w.dim() != 2 or w.shape[1] != x.shape[1]:
+        raise ValueError(f"x must be [M, K] and w [N, K], got {tuple(x.shape)} and {tuple(w.shape)}")
+    if w.dtype != x.dtype or (bias is not None and bias.dtype != x.dtype):
+        raise TypeError("x, w and bias must share one dtype")
+    M, K = x.shape
+    N = w.shape[0]
+    if bias is not None and tuple(bias.shape) != (N,):
+        raise ValueError(f"bias must be [{N}]")
+    for t, name in ((x, "x"), (w, "w"), (bias, "bias")):
+        _require_device(t, name, x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        need = w4a16_dense_workspace_size(M, N, K, dt, bias is not None)
+        if workspace is None:
+            workspace = _workspace(x.device, stream, need)
+        ws_ptr = None if workspace is None else workspace.data_ptr()
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib.w4a16_linear_dense(x.data_ptr(), w.data_ptr(), _ptr(bias), out.data_ptr(), M, N, K,
+                                      dt, ws_ptr, ws_bytes, stream))
     return out

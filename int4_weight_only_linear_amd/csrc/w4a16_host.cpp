@@ -375,6 +375,58 @@ w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t*
   return ok();
 }
 
+size_t w4a16_dense_workspace_size(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t has_bias) {
+  (void)K;
+  (void)dtype;
+  if (M <= 0 || N <= 0) return 0;
+  size_t b = w4a16::kDenseBlasWorkspace;
+  if (has_bias) b += ((size_t)M * (size_t)N * sizeof(float) + 255) / 256 * 256;
+  return b;
+}
+
+w4a16_status w4a16_linear_dense(const void* x, const void* w, const void* bias, void* y, int64_t M,
+                                int64_t N, int64_t K, int32_t dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+    return fail(W4A16_ERR_INVALID_ARG, "activation dtype must be fp16 (0) or bf16 (1), got %d", (int)dtype);
+  if (M < 0 || N < 1 || K < 1)
+    return fail(W4A16_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1 (M=%lld N=%lld K=%lld)",
+                (long long)M, (long long)N, (long long)K);
+  if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
+    return fail(W4A16_ERR_UNSUPPORTED, "the dense path takes M, N and K below 2^31");
+  if (M == 0) return ok();
+  if (!x || !w || !y) return fail(W4A16_ERR_INVALID_ARG, "x, w and y must not be NULL");
+  if (!aligned(x, 2) || !aligned(w, 2) || !aligned(y, 2) || (bias && !aligned(bias, 2)))
+    return fail(W4A16_ERR_ALIGNMENT, "x, w, bias and y must be 2-byte aligned");
+  const size_t ny = act_bytes(M * N);
+  if (overlap(y, ny, x, act_bytes(M * K)) || overlap(y, ny, w, act_bytes(N * K)) ||
+      overlap(y, ny, bias, bias ? act_bytes(N) : 0))
+    return fail(W4A16_ERR_INVALID_ARG, "y must not overlap x, w or bias");
+  const size_t need = w4a16_dense_workspace_size(M, N, K, dtype, bias != nullptr);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (!aligned(workspace, 256)) return fail(W4A16_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (overlap(workspace, need, y, ny) || overlap(workspace, need, x, act_bytes(M * K)) ||
+      overlap(workspace, need, w, act_bytes(N * K)))
+    return fail(W4A16_ERR_INVALID_ARG, "the workspace must not overlap x, w or y");
+  const DeviceInfo* dev = nullptr;
+  w4a16_status st = device_info(&dev);
+  if (st != W4A16_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* acc = bias ? reinterpret_cast<float*>(ws + w4a16::kDenseBlasWorkspace) : nullptr;
+  std::string why;
+  if (!w4a16::dense_gemm(x, w, bias ? static_cast<void*>(acc) : y, bias != nullptr, M, N, K, dtype,
+                         ws, w4a16::kDenseBlasWorkspace, s, &why))
+    return fail(W4A16_ERR_UNSUPPORTED, "dense path: %s", why.c_str());
+  if (bias) {
+    hipError_t e = w4a16::launch_bias_round(acc, bias, y, M, N, dtype, s);
+    if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
 w4a16_status w4a16_unpack_device(const int32_t* wq, uint8_t* q, int64_t N, int64_t K, void* stream) {
   if (N < 0 || K < 0 || K % 8) return fail(W4A16_ERR_INVALID_ARG, "need N >= 0, K >= 0, K %% 8 == 0");
   if (N == 0 || K == 0) return ok();

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <string>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -86,6 +88,14 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
 // ---- elementwise -----------------------------------------------------------
 hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* zp, void* w,
                           int64_t N, int64_t K, int group, int dtype, hipStream_t stream);
+// Dequantised prefill copy: bytes of BLAS workspace the dense path hands to
+// the BLAS (the fp32 sums, when there is a bias, follow them).
+constexpr size_t kDenseBlasWorkspace = 32u << 20;
+bool dense_gemm(const void* x, const void* w, void* d, bool d_f32, int64_t M, int64_t N, int64_t K,
+                int dtype, void* blas_ws, size_t blas_ws_bytes, hipStream_t stream,
+                std::string* why);
+hipError_t launch_bias_round(const float* acc, const void* bias, void* y, int64_t M, int64_t N,
+                             int dtype, hipStream_t stream);
 hipError_t launch_unpack(const int32_t* wq, uint8_t* q, int64_t N, int64_t K,
                          hipStream_t stream);
 

@@ -189,3 +189,17 @@ def test_workspace_size():
     # a single 128-token tile row: K is split; counters region + fp32 partial tiles
     ws = L.w4a16_workspace_size(128, 4096, 4096, 128, 1, 1, L.PATH_GEMM)
     assert ws >= 64 * 1024 + 2 * 128 * 4096 * 4
+
+
+def test_dense_workspace_size_and_argument_checks():
+    mb = 1 << 20
+    assert L.w4a16_dense_workspace_size(0, 4096, 4096, L.W4A16_BF16, 1) == 0
+    assert L.w4a16_dense_workspace_size(1920, 4096, 4096, L.W4A16_BF16, 0) == 32 * mb
+    assert L.w4a16_dense_workspace_size(1920, 4096, 4096, L.W4A16_BF16, 1) == 32 * mb + 1920 * 4096 * 4
+    assert L.w4a16_dense_workspace_size(3, 5, 8, L.W4A16_F16, 1) == 32 * mb + 256
+    # rejected before any device is touched
+    st = B.lib.w4a16_linear_dense(None, None, None, None, 4, 8, 8, 7, None, 0, None)
+    assert st == 1 and "dtype" in L.w4a16_last_error()
+    st = B.lib.w4a16_linear_dense(None, None, None, None, 4, 8, 8, L.W4A16_BF16, None, 0, None)
+    assert st == 1 and "NULL" in L.w4a16_last_error()
+    assert B.lib.w4a16_linear_dense(None, None, None, None, 0, 8, 8, L.W4A16_BF16, None, 0, None) == 0

@@ -272,3 +272,28 @@ def test_config_full_size(name, li, K, N, g, sym, dt, bias):
         for path in (AUTO,) + paths_for(M):
             y = d.run(path)
             assert_close(y[:, rows], ref, dt, f"M={M} path={path}")
+
+
+# ---- dequantised prefill copy: dense product over w4a16_dequant's weights -----
+
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("M,N,K,g,sym,bias", [
+    (1, 64, 256, 32, True, False), (130, 200, 640, 64, False, True),
+    (257, 136, 416, 32, False, False), (1920, 512, 1024, 128, False, True),
+])
+def test_dense_prefill_copy(dt, M, N, K, g, sym, bias):
+    c = make_case(M, N, K, g, dt, sym, bias, seed=("dense", M, N, K, g, dt, sym, bias))
+    d = DeviceCase(c)
+    w = L.w4a16_dequant(d.wq, d.s, d.zp, group_size=g)
+    y = L.w4a16_linear_dense(d.x, w, d.bias)
+    torch.cuda.synchronize()
+    # the reference multiplies the same rounded weights, exactly (float64)
+    zpk = None if sym else O.pack_zeros(c.zp)
+    W = O.act_bits_to_f64(O.dequant_act(O.pack_weights(c.q), c.s_bits, zpk, N, K, g, dt), dt)
+    ref = O.act_bits_to_f64(c.x_bits, dt) @ W.T
+    if bias:
+        ref = ref + O.act_bits_to_f64(c.bias_bits, dt)[None, :]
+    got = device_to_bits(y)
+    assert_close(got, ref, dt, "dense copy")
+    # and the W4A16 prefill GEMM, which multiplies the same rounded weights
+    assert_close(d.run(GEMM), ref, dt, "prefill GEMM vs the same weights")
