@@ -112,8 +112,9 @@ w4a16_status w4a16_pack_zeros(const uint8_t* z, int64_t N, int64_t G, int32_t* z
 w4a16_status w4a16_unpack_zeros(const int32_t* zpk, int64_t N, int64_t G, uint8_t* z);
 
 /* Validates the arguments of w4a16_linear without touching any device.
- * Rules: group_size in {32, 64, 128} (the pages' accept set); K >= group_size
- * and K % group_size == 0; N >= 1; N % 8 == 0 when zp != NULL; M >= 0;
+ * Rules: group_size in {32, 64, 128} (the pages' accept set), or
+ * group_size == K with K % 32 == 0 (per-channel: one scale and zero point per
+ * row, scales [N, 1], zp [N/8, 1]); K >= group_size and K % group_size == 0; N >= 1; N % 8 == 0 when zp != NULL; M >= 0;
  * dtype is W4A16_F16 or W4A16_BF16; x, wq, scales, y non-NULL when M > 0;
  * x and wq 16-byte aligned, scales/bias/y 2-byte aligned, zp 4-byte aligned;
  * y must not overlap x, wq, scales, zp or bias. */

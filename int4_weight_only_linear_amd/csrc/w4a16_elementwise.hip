@@ -15,18 +15,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
                                                       const uint16_t* __restrict__ scales,
                                                       const uint32_t* __restrict__ zp,
                                                       uint16_t* __restrict__ w, int64_t N,
-                                                      int64_t K, int group) {
+                                                      int64_t K, int group, int sG, int gmul) {
   const int64_t words_per_row = K >> 3;
   const int64_t total = N * words_per_row;
-  const int64_t G = K / group;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     int64_t n;
     int j;
     locate_word(idx, N, (int)words_per_row, n, j);
     const int64_t grp = ((int64_t)j * 8) / group;
-    const uint16_t sbits = scales[n * G + grp];
-    const uint32_t z = ASYM ? zero_point(zp, (int)n, (int)G, (int)grp) : 8u;
+    const uint16_t sbits = scales[n * sG + grp * gmul];
+    const uint32_t z = ASYM ? zero_point(zp, (int)n, sG, (int)grp * gmul) : 8u;
     const GroupConst<DT> gc = group_const<DT>(sbits, z);
     *reinterpret_cast<u32x4*>(w + n * K + (int64_t)j * 8) = dequant_word<DT>(
         __builtin_nontemporal_load(wq + idx), gc.s_pair, gc.nmz_pair, gc.s_f32, gc.c_f32);
@@ -84,7 +83,7 @@ int grid_for(int64_t items, int threads) {
 
 }  // namespace
 
-hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* zp, void* w,
+hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* zp, int sG, int gmul, void* w,
                           int64_t N, int64_t K, int group, int dtype, hipStream_t stream) {
   const int64_t words = N * (K >> 3);
   const int blocks = grid_for(words, 256);
@@ -94,14 +93,14 @@ hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* 
   uint16_t* out = static_cast<uint16_t*>(w);
   if (dtype == DT_F16) {
     if (zp)
-      hipLaunchKernelGGL((dequant_kernel<DT_F16, true>), blocks, 256, 0, stream, wqu, s, zpu, out, N, K, group);
+      hipLaunchKernelGGL((dequant_kernel<DT_F16, true>), blocks, 256, 0, stream, wqu, s, zpu, out, N, K, group, sG, gmul);
     else
-      hipLaunchKernelGGL((dequant_kernel<DT_F16, false>), blocks, 256, 0, stream, wqu, s, zpu, out, N, K, group);
+      hipLaunchKernelGGL((dequant_kernel<DT_F16, false>), blocks, 256, 0, stream, wqu, s, zpu, out, N, K, group, sG, gmul);
   } else {
     if (zp)
-      hipLaunchKernelGGL((dequant_kernel<DT_BF16, true>), blocks, 256, 0, stream, wqu, s, zpu, out, N, K, group);
+      hipLaunchKernelGGL((dequant_kernel<DT_BF16, true>), blocks, 256, 0, stream, wqu, s, zpu, out, N, K, group, sG, gmul);
     else
-      hipLaunchKernelGGL((dequant_kernel<DT_BF16, false>), blocks, 256, 0, stream, wqu, s, zpu, out, N, K, group);
+      hipLaunchKernelGGL((dequant_kernel<DT_BF16, false>), blocks, 256, 0, stream, wqu, s, zpu, out, N, K, group, sG, gmul);
   }
   return hipGetLastError();
 }

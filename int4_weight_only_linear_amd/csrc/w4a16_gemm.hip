@@ -55,6 +55,7 @@ struct GemmParams {
   float* partial;
   uint32_t* counters;
   int M, N, K, G;
+  int sG, gmul;        // scale / zero-point index of (row n, group g): n * sG + g * gmul
   int wpr;             // words per weight row, K / 8
   int nsteps;          // ceil(K / 128)
   int full_steps;      // K / 128: steps over complete (transposed) runs
@@ -199,8 +200,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int gi = 0; gi < GPS; ++gi) {
         const int g = min(s * GPS + gi, p.G - 1);
-        r.s[cb][gi] = p.scales[(size_t)nrow[cb] * p.G + g];
-        if constexpr (ASYM) r.z[cb][gi] = p.zp[(size_t)(nrow[cb] >> 3) * p.G + g];
+        r.s[cb][gi] = p.scales[(size_t)nrow[cb] * p.sG + g * p.gmul];
+        if constexpr (ASYM) r.z[cb][gi] = p.zp[(size_t)(nrow[cb] >> 3) * p.sG + g * p.gmul];
       }
   };
 
@@ -583,6 +584,8 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
   prm.N = (int)a.N;
   prm.K = (int)a.K;
   prm.G = (int)(a.K / a.group);
+  prm.sG = a.sG;
+  prm.gmul = a.gmul;
   prm.wpr = (int)(a.K / 8);
   prm.nsteps = (int)((a.K + kBK - 1) / kBK);
   prm.full_steps = (int)(a.K / kBK);

@@ -60,6 +60,7 @@ struct GemvParams {
   float* partial;      // [splits][M][N] when splits > 1
   uint32_t* counters;  // [tiles] when splits > 1; zero between calls
   int M, N, K, G;
+  int sG, gmul;  // scale / zero-point index of (row n, group g): n * sG + g * gmul
   int nchunks;  // K / 32
   int ksteps;   // ceil(nchunks / 4)
   int ksteps_per_split;
@@ -225,8 +226,8 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
   // scales of the run: when each row's groups of the run are whole 16-byte
   // pieces of the scale tensor, one 16-byte load per lane (lane = row *
   // pieces per row + piece); otherwise one 2-byte load per scale
-  const bool svec = ngw >= 8 && (p.G & 7) == 0 && (gw0 & 7) == 0 && gw0 + ngw <= p.G &&
-                    (reinterpret_cast<uintptr_t>(p.scales) & 15) == 0;
+  const bool svec = ngw >= 8 && p.gmul == 1 && (p.sG & 7) == 0 && (gw0 & 7) == 0 &&
+                    gw0 + ngw <= p.G && (reinterpret_cast<uintptr_t>(p.scales) & 15) == 0;
   u32x4 srv = {0u, 0u, 0u, 0u};
   uint32_t sr[SPT];
 #pragma unroll
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
     const int lg_ppr = lg_ngw - 3;
     const int e = min(lane, (16 << lg_ppr) - 1);
     const int r = e >> lg_ppr;
-    srv = *reinterpret_cast<const u32x4*>(p.scales + (size_t)min(n0 + r, p.N - 1) * p.G + gw0 +
+    srv = *reinterpret_cast<const u32x4*>(p.scales + (size_t)min(n0 + r, p.N - 1) * p.sG + gw0 +
                                           8 * (e & ((1 << lg_ppr) - 1)));
   } else {
 #pragma unroll
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
       const int e = min(lane + 64 * j, 16 * ngw - 1);
       const int r = e >> lg_ngw;
       const int g = min(gw0 + (e & (ngw - 1)), p.G - 1);
-      sr[j] = p.scales[(size_t)min(n0 + r, p.N - 1) * p.G + g];
+      sr[j] = p.scales[(size_t)min(n0 + r, p.N - 1) * p.sG + g * p.gmul];
     }
   }
   uint32_t zr = 0u;
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
     const int e = min(lane, 2 * ngw - 1);
     const int rr = e >> lg_ngw;
     const int g = min(gw0 + (e & (ngw - 1)), p.G - 1);
-    zr = p.zp[(size_t)min((n0 >> 3) + rr, (p.N >> 3) - 1) * p.G + g];
+    zr = p.zp[(size_t)min((n0 >> 3) + rr, (p.N >> 3) - 1) * p.sG + g * p.gmul];
   }
   __builtin_amdgcn_sched_barrier(0);
   // weights: a wave-uniform base per k-step plus one per-lane offset, so each
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
   const int n = tile * kGemvRowsPerTile + col;
   const int nc = min(n, p.N - 1);
   const WeightWalk ww = weight_walk(p.wq, p.N, p.K, p.nchunks, tile * kGemvRowsPerTile, col, row4);
-  const uint16_t* srow = p.scales + (size_t)nc * p.G;
+  const uint16_t* srow = p.scales + (size_t)nc * p.sG;
 
   const int ks_begin = split * p.ksteps_per_split;
   const int ks_end = min(p.ksteps, ks_begin + p.ksteps_per_split);
@@ -489,8 +490,8 @@ __global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
 #pragma unroll
     for (int h = 0; h < GPS; ++h) {
       const int grp = min((ks * 4 + h * CPG) / CPG, p.G - 1);
-      sv[i][h] = srow[grp];
-      zw[i][h] = ASYM ? p.zp[(size_t)(nc >> 3) * p.G + grp] : 0u;
+      sv[i][h] = srow[grp * p.gmul];
+      zw[i][h] = ASYM ? p.zp[(size_t)(nc >> 3) * p.sG + grp * p.gmul] : 0u;
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -690,6 +691,8 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
   prm.N = (int)a.N;
   prm.K = (int)a.K;
   prm.G = (int)(a.K / a.group);
+  prm.sG = a.sG;
+  prm.gmul = a.gmul;
   prm.nchunks = (int)(a.K / 32);
   prm.ksteps = plan.ksteps;
   prm.ksteps_per_split = plan.ksteps_per_split;

@@ -93,6 +93,22 @@ size_t act_bytes(int64_t n) { return (size_t)n * 2; }
 
 bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
 
+// Group sizes: the pages' accept set {32, 64, 128}, and per-channel scales
+// (group_size == K, one scale and zero point per row) for K a multiple of 32.
+bool group_ok(int32_t g, int64_t K) { return valid_group(g) || (g == K && K % 32 == 0); }
+
+// The kernels' group for a group size: itself, or for per-channel scales the
+// largest of 128, 64, 32 dividing K, every group of a row then reading the
+// row's one scale (gmul = 0, row stride sG = 1).
+struct GroupMap {
+  int kgroup, sG, gmul;
+};
+GroupMap group_map(int32_t g, int64_t K) {
+  if (valid_group(g)) return {g, (int)(K / g), 1};
+  const int kg = K % 128 == 0 ? 128 : (K % 64 == 0 ? 64 : 32);
+  return {kg, 1, 0};
+}
+
 // Decode-kernel threshold.  The pages route M <= 5 to their skinny kernel
 // (tuned on RDNA).  On MI355X the decode kernel beats the GEMM up to M = 16
 // at every shape, group, quantisation and dtype of the crossover sweep, and
@@ -141,6 +157,8 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
                          size_t workspace_bytes, void* stream, int32_t path) {
   w4a16_status st = w4a16_check_args(x, wq, scales, zp, bias, y, M, N, K, group_size, dtype);
   if (st != W4A16_OK) return st;
+  const GroupMap gm = group_map(group_size, K);
+  group_size = gm.kgroup;  // from here on, the kernels' group
   if (path < W4A16_PATH_AUTO || path > W4A16_PATH_GEMM)
     return fail(W4A16_ERR_INVALID_ARG, "unknown path %d", (int)path);
   if (M == 0) return ok();
@@ -168,7 +186,7 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
   if (need > 0 && !aligned(workspace, 256))
     return fail(W4A16_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
 
-  w4a16::LinearArgs a{x, wq, scales, zp, bias, y, M, N, K, group_size, dtype};
+  w4a16::LinearArgs a{x, wq, scales, zp, bias, y, M, N, K, group_size, dtype, gm.sG, gm.gmul};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p == W4A16_PATH_GEMV) {
@@ -291,8 +309,10 @@ w4a16_status w4a16_check_args(const void* x, const int32_t* wq, const void* scal
                               int64_t N, int64_t K, int32_t group_size, int32_t dtype) {
   if (dtype != W4A16_F16 && dtype != W4A16_BF16)
     return fail(W4A16_ERR_INVALID_ARG, "activation dtype must be fp16 (0) or bf16 (1), got %d", (int)dtype);
-  if (!valid_group(group_size))
-    return fail(W4A16_ERR_UNSUPPORTED, "group size must be 32, 64 or 128, got %d", (int)group_size);
+  if (!group_ok(group_size, K))
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "group size must be 32, 64, 128 or K (per-channel, K %% 32 == 0), got %d (K=%lld)",
+                (int)group_size, (long long)K);
   if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M must be >= 0, got %lld", (long long)M);
   if (N < 1) return fail(W4A16_ERR_INVALID_ARG, "N must be >= 1, got %lld", (long long)N);
   if (K < group_size || K % group_size)
@@ -326,8 +346,9 @@ w4a16_path w4a16_select_path(int64_t M, int64_t N, int64_t K, int32_t group_size
 
 size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t dtype,
                             int32_t has_zp, int32_t path) {
-  if (M <= 0 || N <= 0 || K <= 0 || !valid_group(group_size)) return 0;
-  const w4a16_path p = resolve_path(M, N, K, group_size, dtype, has_zp, path);
+  if (M <= 0 || N <= 0 || K <= 0 || !group_ok(group_size, K) || K % group_size) return 0;
+  const int kgroup = group_map(group_size, K).kgroup;
+  const w4a16_path p = resolve_path(M, N, K, kgroup, dtype, has_zp, path);
   int cus = kPlanningCUs;
   int dev = -1;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
@@ -335,7 +356,7 @@ size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size,
     if (device_info(&d) == W4A16_OK) cus = d->cu_count;
     g_last_error.clear();
   }
-  return workspace_for(M, N, K, group_size, p, cus);
+  return workspace_for(M, N, K, kgroup, p, cus);
 }
 
 w4a16_status w4a16_linear(const void* x, const int32_t* wq, const void* scales, const int32_t* zp,
@@ -358,8 +379,10 @@ w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t*
                            int64_t N, int64_t K, int32_t group_size, int32_t dtype, void* stream) {
   if (dtype != W4A16_F16 && dtype != W4A16_BF16)
     return fail(W4A16_ERR_INVALID_ARG, "activation dtype must be fp16 (0) or bf16 (1), got %d", (int)dtype);
-  if (!valid_group(group_size))
-    return fail(W4A16_ERR_UNSUPPORTED, "group size must be 32, 64 or 128, got %d", (int)group_size);
+  if (!group_ok(group_size, K))
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "group size must be 32, 64, 128 or K (per-channel, K %% 32 == 0), got %d (K=%lld)",
+                (int)group_size, (long long)K);
   if (N < 1 || K < group_size || K % group_size)
     return fail(W4A16_ERR_INVALID_ARG, "need N >= 1 and K a positive multiple of the group size");
   if (zp && N % 8) return fail(W4A16_ERR_INVALID_ARG, "packed zero points need N %% 8 == 0");
@@ -369,7 +392,8 @@ w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t*
   const DeviceInfo* dev = nullptr;
   w4a16_status st = device_info(&dev);
   if (st != W4A16_OK) return st;
-  hipError_t e = w4a16::launch_dequant(wq, scales, zp, w, N, K, group_size, dtype,
+  const GroupMap gm = group_map(group_size, K);
+  hipError_t e = w4a16::launch_dequant(wq, scales, zp, gm.sG, gm.gmul, w, N, K, gm.kgroup, dtype,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -18,8 +18,10 @@ struct LinearArgs {
   const void* bias;   // may be NULL
   void* y;
   int64_t M, N, K;
-  int group;
+  int group;  // the kernels' group: 32, 64 or 128 (a divisor of K for per-channel scales)
   int dtype;
+  int sG;     // scale / zero-point row stride, in groups: K / group_size
+  int gmul;   // 1, or 0 for per-channel scales (every group of a row reads column 0)
 };
 
 // ---- workspace ---------------------------------------------------------------
@@ -86,7 +88,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cu_count);
 hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipStream_t stream);
 
 // ---- elementwise -----------------------------------------------------------
-hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* zp, void* w,
+hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* zp, int sG, int gmul, void* w,
                           int64_t N, int64_t K, int group, int dtype, hipStream_t stream);
 // Dequantised prefill copy: bytes of BLAS workspace the dense path hands to
 // the BLAS (the fp32 sums, when there is a bias, follow them).

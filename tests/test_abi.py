@@ -111,7 +111,7 @@ def test_check_args_accepts_valid():
 
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(g=16), 2, "group size"),
-    (dict(g=256), 2, "group size"),
+    (dict(g=256, K=512), 2, "group size"),     # neither the accept set nor K
     (dict(K=200), 1, "multiple of the group"),
     (dict(K=64, g=128), 1, "multiple of the group"),
     (dict(N=0), 1, "N must be"),
@@ -203,3 +203,15 @@ def test_dense_workspace_size_and_argument_checks():
     st = B.lib.w4a16_linear_dense(None, None, None, None, 4, 8, 8, L.W4A16_BF16, None, 0, None)
     assert st == 1 and "NULL" in L.w4a16_last_error()
     assert B.lib.w4a16_linear_dense(None, None, None, None, 0, 8, 8, L.W4A16_BF16, None, 0, None) == 0
+
+
+def test_per_channel_group_accept_set():
+    ok = lambda M, N, K, g, zp=0: B.lib.w4a16_check_args(
+        1024, 1024, 1024, 1024 if zp else None, None, 1 << 30, M, N, K, g, L.W4A16_BF16)
+    assert ok(1, 64, 4096, 4096, 1) == 0      # per-channel, K a multiple of 128
+    assert ok(1, 64, 320, 320) == 0            # per-channel, K a multiple of 64
+    assert ok(1, 64, 96, 96) == 0              # per-channel, K a multiple of 32
+    assert ok(1, 64, 40, 40) == 2              # K not a multiple of 32
+    assert ok(1, 64, 512, 256) == 2            # neither the accept set nor K
+    assert "per-channel" in L.w4a16_last_error()
+    assert L.w4a16_workspace_size(1, 64, 4096, 4096, L.W4A16_BF16, True) >= 0

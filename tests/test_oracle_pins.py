@@ -478,6 +478,28 @@ def test_row_permutation_equivariance():
     assert np.array_equal(_oracle_y(case), y[:, p])
 
 
+def test_per_channel_equals_groups_with_one_scale_per_row():
+    # group = K (one scale and zero point per row) is the same layer as any
+    # smaller group whose scales and zero points repeat along the row
+    for dt, sym in ((O.BF16, False), (O.F16, True)):
+        c = make_case(3, 16, 384, 384, dt, sym, True, seed=("perchan", dt, sym))
+        zpk = None if sym else O.pack_zeros(c.zp)
+        y1 = O.linear_ref(c.x_bits, O.pack_weights(c.q), c.s_bits, zpk, c.bias_bits,
+                          3, 16, 384, 384, dt)
+        s3 = np.repeat(c.s_bits, 3, axis=1)
+        z3 = None if sym else O.pack_zeros(np.repeat(c.zp, 3, axis=1))
+        y3 = O.linear_ref(c.x_bits, O.pack_weights(c.q), s3, z3, c.bias_bits, 3, 16, 384, 128, dt)
+        assert np.array_equal(y1, y3)
+        # and a changed scale moves every weight of its row, nowhere else
+        s_b = c.s_bits.copy()
+        s_b[5, 0] = O.f32_to_act_bits(np.float32(2.0) * O.act_bits_to_f64(s_b[5:6, 0], dt).astype(np.float32), dt)[0]
+        W0 = O.dequant_f32(O.pack_weights(c.q), c.s_bits, zpk, 16, 384, 384, dt)
+        W1 = O.dequant_f32(O.pack_weights(c.q), s_b, zpk, 16, 384, 384, dt)
+        changed = np.argwhere(W0 != W1)
+        assert set(changed[:, 0].tolist()) <= {5}
+        assert np.array_equal(W1[5], 2.0 * W0[5])
+
+
 def test_dequant_rejects_bad_group():
     with pytest.raises(ValueError):
         O.dequant_f32(np.zeros((8, 5), np.int32), np.zeros((8, 1), np.uint16), None, 8, 40, 32, O.F16)

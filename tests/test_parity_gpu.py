@@ -297,3 +297,21 @@ def test_dense_prefill_copy(dt, M, N, K, g, sym, bias):
     assert_close(got, ref, dt, "dense copy")
     # and the W4A16 prefill GEMM, which multiplies the same rounded weights
     assert_close(d.run(GEMM), ref, dt, "prefill GEMM vs the same weights")
+
+
+# ---- per-channel scales: group_size == K (one scale and zero point per row) ----
+
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("M,N,K,sym,bias", [
+    (1, 64, 4096, False, False), (5, 40, 320, True, True), (33, 24, 96, False, True),
+    (130, 72, 1152, False, False), (2, 200, 416, False, True),
+])
+def test_per_channel_scales(dt, M, N, K, sym, bias):
+    c = make_case(M, N, K, K, dt, sym, bias, seed=("perchan", M, N, K, dt, sym, bias))
+    d = DeviceCase(c)
+    ref = oracle_rows(c)
+    for path in paths_for(M):
+        assert_close(d.run(path), ref, dt, f"per-channel path {path}")
+    w = device_to_bits(L.w4a16_dequant(d.wq, d.s, d.zp, group_size=K))
+    zpk = None if sym else O.pack_zeros(c.zp)
+    assert np.array_equal(w, O.dequant_act(O.pack_weights(c.q), c.s_bits, zpk, N, K, K, dt))
