@@ -9,5 +9,5 @@ from .w4a16_ref import (  # noqa: F401
     f32_to_f16_bits, f32_to_bf16_bits, f32_to_act_bits,
     pack_weights, unpack_weights, pack_zeros, unpack_zeros, slice_of_word, WORDS_PER_RUN,
     word_position, TILE_ROWS,
-    dequant_f32, dequant_act, linear_ref,
+    dequant_f32, dequant_act, linear_ref, moe_linear_ref,
 )

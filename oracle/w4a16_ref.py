@@ -298,3 +298,43 @@ def linear_ref(x_bits, wq, scale_bits, zpk, bias_bits, M: int, N: int, K: int,
         y = y + act_bits_to_f64(np.asarray(bias_bits).reshape(N), dtype)[None, :]
     return y
 
+
+
+# --------------------------------------------------------------------------
+# expert-indexed product (fused MoE skinny GEMM)
+# --------------------------------------------------------------------------
+
+def moe_linear_ref(x_bits, wq, scale_bits, zpk, bias_bits, topk_ids, topk_weights,
+                   M: int, topk: int, E: int, N: int, K: int, group: int, dtype: int,
+                   x_per_slot: bool = False) -> np.ndarray:
+    """Expert-indexed product, one output row per (token, slot), float64.
+
+    The pages name a fused-MoE variant of the skinny kernel (an expert-indexed
+    W4A16 GEMM; "Upstream sync 67/N: merge 382bbd5144 HybridW4A16LinearKernel
+    (conflict)", conflict table) without printing its contract.  Reading used:
+    slot s = m * topk + j of token m uses expert e = topk_ids[m, j], whose
+    weights, scales, zero points and bias are slice e of stacks [E, ...] in the
+    linear layer's layouts, and
+        y[s] = topk_weights[m, j] * (x_row . W_e^T + b_e)
+    with x_row = x[m] (x of shape [M, K]) or x[s] (x of shape [M*topk, K]);
+    no weights means 1.  An id outside [0, E) gives a zero row.
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(M, topk)
+    x = np.asarray(x_bits).reshape(M * topk if x_per_slot else M, K)
+    wq = np.asarray(wq).reshape(E, N, K // 8)
+    s = np.asarray(scale_bits).reshape(E, N, K // group)
+    z = None if zpk is None else np.asarray(zpk).reshape(E, N // 8, K // group)
+    b = None if bias_bits is None else np.asarray(bias_bits).reshape(E, N)
+    y = np.zeros((M * topk, N), dtype=np.float64)
+    for m in range(M):
+        for j in range(topk):
+            slot = m * topk + j
+            e = int(ids[m, j])
+            if not 0 <= e < E:
+                continue
+            row = x[slot if x_per_slot else m][None, :]
+            y[slot] = linear_ref(row, wq[e], s[e], None if z is None else z[e],
+                                 None if b is None else b[e], 1, N, K, group, dtype)[0]
+            if topk_weights is not None:
+                y[slot] *= float(np.asarray(topk_weights, dtype=np.float32).reshape(M, topk)[m, j])
+    return y

@@ -503,3 +503,65 @@ def test_per_channel_equals_groups_with_one_scale_per_row():
 def test_dequant_rejects_bad_group():
     with pytest.raises(ValueError):
         O.dequant_f32(np.zeros((8, 5), np.int32), np.zeros((8, 1), np.uint16), None, 8, 40, 32, O.F16)
+
+
+# --------------------------------------------------------------------------
+# expert-indexed product
+# --------------------------------------------------------------------------
+
+def _moe_stack(E, N, K, g, dt, sym, bias, seed):
+    """E independent layers, and their stacks [E, ...] in the layer layouts."""
+    cases = [make_case(1, N, K, g, dt, sym, bias, seed=(seed, e)) for e in range(E)]
+    wq = np.stack([O.pack_weights(c.q) for c in cases])
+    s = np.stack([c.s_bits for c in cases])
+    z = None if sym else np.stack([O.pack_zeros(c.zp) for c in cases])
+    b = np.stack([c.bias_bits for c in cases]) if bias else None
+    return cases, wq, s, z, b
+
+
+def test_moe_single_expert_is_the_linear_layer():
+    cases, wq, s, z, b = _moe_stack(1, 16, 256, 64, O.BF16, False, True, "moe1")
+    x = make_case(3, 16, 256, 64, O.BF16, False, False, seed="moe1x").x_bits
+    ids = np.zeros((3, 2), dtype=np.int32)
+    y = O.moe_linear_ref(x, wq, s, z, b, ids, None, 3, 2, 1, 16, 256, 64, O.BF16)
+    ref = O.linear_ref(x, wq[0], s[0], z[0], b[0], 3, 16, 256, 64, O.BF16)
+    assert np.array_equal(y[0::2], ref) and np.array_equal(y[1::2], ref)
+
+
+def test_moe_slot_uses_its_own_expert_slice():
+    E, N, K = 4, 16, 128
+    cases, wq, s, z, b = _moe_stack(E, N, K, 32, O.F16, False, True, "moe2")
+    x = make_case(2, N, K, 32, O.F16, False, False, seed="moe2x").x_bits
+    ids = np.array([[3, 0], [1, 3]], dtype=np.int32)
+    y = O.moe_linear_ref(x, wq, s, z, b, ids, None, 2, 2, E, N, K, 32, O.F16)
+    for m in range(2):
+        for j in range(2):
+            e = ids[m, j]
+            c = cases[e]
+            ref = O.linear_ref(x[m:m + 1], O.pack_weights(c.q), c.s_bits, O.pack_zeros(c.zp),
+                               c.bias_bits, 1, N, K, 32, O.F16)[0]
+            assert np.array_equal(y[m * 2 + j], ref)
+    # relabelling the experts (stacks permuted, ids mapped) changes nothing
+    perm = np.array([2, 0, 3, 1])
+    inv = np.argsort(perm)
+    y2 = O.moe_linear_ref(x, wq[perm], s[perm], z[perm], b[perm], inv[ids], None,
+                          2, 2, E, N, K, 32, O.F16)
+    assert np.array_equal(y2, y)
+
+
+def test_moe_weights_ids_and_slot_rows():
+    E, N, K = 3, 8, 64
+    cases, wq, s, z, b = _moe_stack(E, N, K, 32, O.BF16, True, False, "moe3")
+    x = make_case(2, N, K, 32, O.BF16, True, False, seed="moe3x").x_bits
+    ids = np.array([[0, 2], [1, 7]], dtype=np.int32)   # 7 is not an expert
+    y = O.moe_linear_ref(x, wq, s, None, None, ids, None, 2, 2, E, N, K, 32, O.BF16)
+    assert np.all(y[3] == 0.0) and np.any(y[2] != 0.0)
+    w = np.array([[2.0, 0.0], [0.25, 1.0]], dtype=np.float32)
+    yw = O.moe_linear_ref(x, wq, s, None, None, ids, w, 2, 2, E, N, K, 32, O.BF16)
+    assert np.array_equal(yw[0], 2.0 * y[0]) and np.all(yw[1] == 0.0)
+    assert np.array_equal(yw[2], 0.25 * y[2])
+    # one x row per slot, equal to its token's row, is the shared-x product
+    xs = np.repeat(np.asarray(x).reshape(2, K), 2, axis=0)
+    ys = O.moe_linear_ref(xs, wq, s, None, None, ids, None, 2, 2, E, N, K, 32, O.BF16,
+                          x_per_slot=True)
+    assert np.array_equal(ys, y)
