@@ -166,6 +166,30 @@ w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t*
                            void* w, int64_t N, int64_t K, int32_t group_size,
                            int32_t dtype, void* stream);
 
+/* Expert-indexed decode (the fused-MoE skinny W4A16 GEMM the page "Upstream
+ * sync 67/N: merge 382bbd5144 HybridW4A16LinearKernel (conflict)" lists in its
+ * conflict table beside the linear kernel).  For token m and slot j of its
+ * top-k experts, slot s = m * topk + j, expert e = topk_ids[m, j]:
+ *   y[s, :] = topk_weights[m, j] * (x_row . dequant(W_e)^T + bias_e)
+ * rounded once to the activation dtype; x_row = x[m] (x_per_slot == 0, x is
+ * [M, K]) or x[s] (x_per_slot != 0, x is [M * topk, K]).
+ *   wq     int32 [E, N, K/8]  expert e's [N, K/8] block in the wq layout above
+ *   scales act   [E, N, G]    zp int32 [E, N/8, G] or NULL; bias act [E, N] or NULL
+ *   topk_ids int32 [M, topk]  device; an id outside [0, E) gives a zero row
+ *   topk_weights fp32 [M, topk] or NULL (1)
+ *   y      act   [M * topk, N]
+ * Groups as for w4a16_linear.  Every slot is one decode-kernel problem with
+ * M = 1 and one K range, so no workspace is used; M * topk <= 65535 and one
+ * expert's N*K/2 below 4 GiB.  Device pointers, caller-owned; asynchronous on
+ * `stream`.  Alignment: x and wq 16 bytes; zp, topk_ids, topk_weights 4;
+ * scales, bias, y 2.  y must not overlap any input.  Errors as w4a16_linear;
+ * W4A16_ERR_UNSUPPORTED when K needs more than one workgroup per slot. */
+w4a16_status w4a16_moe_linear(const void* x, const int32_t* wq, const void* scales,
+                              const int32_t* zp, const void* bias, const int32_t* topk_ids,
+                              const float* topk_weights, void* y, int64_t M, int64_t topk,
+                              int64_t E, int64_t N, int64_t K, int32_t group_size,
+                              int32_t dtype, int32_t x_per_slot, void* stream);
+
 /* Dequantised prefill copy ("Converge the two W4A16 linear kernels onto the
  * upstream shell", "What this does": the optional dequantized prefill cache).
  * A caller that keeps w = w4a16_dequant(...) resident (N*K activation-dtype

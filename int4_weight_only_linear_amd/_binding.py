@@ -51,6 +51,8 @@ SIGNATURES = {
     "w4a16_linear_dense": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32, _vp, _c_sz,
                                     _vp]),
     "w4a16_dense_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
+    "w4a16_moe_linear": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
+                                  _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _vp]),
 }
 
 
@@ -341,4 +343,45 @@ def w4a16_linear_dense(x, w, bias=None, *, out=None, workspace=None):
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check(lib.w4a16_linear_dense(x.data_ptr(), w.data_ptr(), _ptr(bias), out.data_ptr(), M, N, K,
                                       dt, ws_ptr, ws_bytes, stream))
+    return out
+
+
+def w4a16_moe_linear(x, wq, scales, topk_ids, zp=None, bias=None, topk_weights=None, *,
+                     group_size: int, x_per_slot: bool = False, out=None):
+    """Expert-indexed decode: y[m*topk + j] = topk_weights[m, j] * (x_row . W_e^T + b_e),
+    e = topk_ids[m, j], with stacks wq [E, N, K/8], scales [E, N, G], zp [E, N/8, G],
+    bias [E, N]; x is [M, K] (or [M*topk, K] with x_per_slot).  Returns [M*topk, N]."""
+    torch = _torch()
+    dt = _act_code(x)
+    if wq.dim() != 3:
+        raise ValueError("wq must be [E, N, K/8]")
+    E, N, K = wq.shape[0], wq.shape[1], wq.shape[2] * 8
+    if topk_ids.dim() != 2 or topk_ids.dtype != torch.int32:
+        raise TypeError("topk_ids must be int32 [M, topk]")
+    M, topk = topk_ids.shape
+    if x.dim() != 2 or x.shape[1] != K or x.shape[0] != (M * topk if x_per_slot else M):
+        raise ValueError(f"x is {tuple(x.shape)}, expected [{M * topk if x_per_slot else M}, {K}]")
+    if group_size <= 0 or K % group_size:
+        raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
+    G = K // group_size
+    if scales.dtype != x.dtype or tuple(scales.shape) != (E, N, G):
+        raise ValueError(f"scales must be {x.dtype} {(E, N, G)}")
+    if zp is not None and (zp.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32))
+                           or tuple(zp.shape) != (E, N // 8, G)):
+        raise ValueError(f"zp must be int32 {(E, N // 8, G)}")
+    if bias is not None and (bias.dtype != x.dtype or tuple(bias.shape) != (E, N)):
+        raise ValueError(f"bias must be {x.dtype} {(E, N)}")
+    if topk_weights is not None and (topk_weights.dtype != torch.float32
+                                     or tuple(topk_weights.shape) != (M, topk)):
+        raise ValueError(f"topk_weights must be float32 {(M, topk)}")
+    for t, name in ((x, "x"), (wq, "wq"), (scales, "scales"), (zp, "zp"), (bias, "bias"),
+                    (topk_ids, "topk_ids"), (topk_weights, "topk_weights")):
+        _require_device(t, name, x.device)
+    if out is None:
+        out = torch.empty((M * topk, N), dtype=x.dtype, device=x.device)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        _check(lib.w4a16_moe_linear(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), _ptr(zp), _ptr(bias),
+                                    topk_ids.data_ptr(), _ptr(topk_weights), out.data_ptr(), M, topk, E,
+                                    N, K, group_size, dt, int(bool(x_per_slot)), stream))
     return out

@@ -72,7 +72,33 @@ struct GemvParams {
   int lg_xsegs_per_wave;
   int lg_groups_per_wave;
   int wave_lds_bytes;
+  float yscale;  // multiplies each sum after the bias (1; an expert slot's router weight)
+  // expert-indexed mode (moe_ids != NULL): workgroup z handles slot z, whose
+  // expert moe_ids[z] selects slice e of the weight / scale / zp / bias stacks
+  const int32_t* moe_ids;
+  const float* moe_weights;  // [slots] or NULL
+  int topk, experts, x_per_slot;
+  size_t w_estride, s_estride, z_estride;  // words / halves / words per expert
+  int slots;  // workgroups along z: 1, or the expert slots
 };
+
+// The expert slot of this workgroup (expert-indexed mode): its expert's
+// slices, its x row and output row.  False for an id outside [0, experts),
+// whose row is zero.
+__device__ __forceinline__ bool select_slot(GemvParams& p) {
+  const int slot = blockIdx.z;
+  const int e = p.moe_ids[slot];
+  const size_t xrow = (size_t)(p.x_per_slot ? slot : slot / p.topk);
+  p.y += (size_t)slot * p.N;
+  if (e < 0 || e >= p.experts) return false;
+  p.wq += (size_t)e * p.w_estride;
+  p.scales += (size_t)e * p.s_estride;
+  if (p.zp) p.zp += (size_t)e * p.z_estride;
+  if (p.bias) p.bias += (size_t)e * p.N;
+  p.x += xrow * p.K;
+  if (p.moe_weights) p.yscale = p.moe_weights[slot];
+  return true;
+}
 
 // Addresses of one lane's 16-byte weight pieces, run by run, for the row
 // tile starting at row n0: lane (r, j) needs run words 4r..4r+3 of row
@@ -131,7 +157,7 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
       for (int w = 0; w < nwaves; ++w) v += red[w * nel + e];
       if (p.splits == 1) {
         if (p.bias) v += act_to_f32<DT>(p.bias[nn]);
-        p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v);
+        p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v * p.yscale);
       } else {
         store_coherent(p.partial + ((size_t)split * p.M + m) * p.N + nn, v);
       }
@@ -151,7 +177,7 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
       float v = 0.f;
       for (int s = 0; s < p.splits; ++s) v += load_coherent(p.partial + ((size_t)s * p.M + m) * p.N + nn);
       if (p.bias) v += act_to_f32<DT>(p.bias[nn]);
-      p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v);
+      p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v * p.yscale);
     }
   }
   if (threadIdx.x == 0) reset_counter(p.counters + tile);  // ready for the next call
@@ -168,7 +194,7 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // ONE: a single token (M == 1), whose sums are row 0 of each MFMA result
 // (lanes 0..15, register 0); the other rows are then never updated.
 template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE>
-__global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
+__global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams params) {
   constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
   constexpr int SPT = (32 * KPW) / GS > 0 ? (32 * KPW) / GS : 1;  // scale loads per lane
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -176,6 +202,13 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  GemvParams p = params;
+  if (p.moe_ids && !select_slot(p)) {
+    // not an expert: a zero row (the whole workgroup leaves here)
+    const int n = blockIdx.x * kGemvRowsPerTile + tid;
+    if (tid < kGemvRowsPerTile && n < p.N) p.y[n] = 0;
+    return;
+  }
   // wave index as a wave-uniform (scalar) value, so the per-wave k-step
   // bookkeeping below stays in SGPRs and its branches are scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -621,7 +654,7 @@ size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N) {
 
 template <int DT, int MT, int GS, bool ASYM>
 static hipError_t launch_t(const GemvParams& prm, const GemvPlan& plan, hipStream_t s) {
-  dim3 grid(plan.tiles, plan.splits);
+  dim3 grid(plan.tiles, plan.splits, prm.slots);
   dim3 block(plan.waves * 64);
   constexpr int KPW = kGemvStepsPerWave;
   if constexpr (MT == 1) {
@@ -670,11 +703,32 @@ static hipError_t launch_m(const GemvParams& prm, int group, const GemvPlan& pla
 }
 
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspace,
-                       hipStream_t stream) {
+                       hipStream_t stream, const MoeArgs* moe) {
   if (plan.waves < 1 || plan.waves > kGemvMaxWaves || plan.lds_bytes > kGemvLdsBudget ||
       plan.kpw < 1 || plan.kpw > kGemvStepsPerWave)
     return hipErrorInvalidConfiguration;
+  // expert-indexed: one M = 1 product per slot, one K range
+  if (moe && (a.M != 1 || plan.splits != 1 || plan.mtiles != 1 || moe->slots < 1 ||
+              moe->slots > kMaxGridZ))
+    return hipErrorInvalidConfiguration;
   GemvParams prm;
+  prm.yscale = 1.0f;
+  prm.moe_ids = nullptr;
+  prm.moe_weights = nullptr;
+  prm.topk = prm.experts = prm.x_per_slot = 0;
+  prm.w_estride = prm.s_estride = prm.z_estride = 0;
+  prm.slots = 1;
+  if (moe) {
+    prm.moe_ids = moe->ids;
+    prm.moe_weights = moe->weights;
+    prm.topk = (int)moe->topk;
+    prm.experts = (int)moe->experts;
+    prm.x_per_slot = moe->x_per_slot ? 1 : 0;
+    prm.w_estride = (size_t)a.N * (size_t)(a.K / 8);
+    prm.s_estride = (size_t)a.N * (size_t)a.sG;
+    prm.z_estride = (size_t)(a.N / 8) * (size_t)a.sG;
+    prm.slots = (int)moe->slots;
+  }
   prm.x = static_cast<const uint16_t*>(a.x);
   prm.wq = reinterpret_cast<const uint32_t*>(a.wq);
   prm.scales = static_cast<const uint16_t*>(a.scales);

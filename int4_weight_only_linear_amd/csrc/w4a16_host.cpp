@@ -399,6 +399,62 @@ w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t*
   return ok();
 }
 
+w4a16_status w4a16_moe_linear(const void* x, const int32_t* wq, const void* scales,
+                              const int32_t* zp, const void* bias, const int32_t* topk_ids,
+                              const float* topk_weights, void* y, int64_t M, int64_t topk,
+                              int64_t E, int64_t N, int64_t K, int32_t group_size, int32_t dtype,
+                              int32_t x_per_slot, void* stream) {
+  if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+    return fail(W4A16_ERR_INVALID_ARG, "activation dtype must be fp16 (0) or bf16 (1), got %d", (int)dtype);
+  if (!group_ok(group_size, K))
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "group size must be 32, 64, 128 or K (per-channel, K %% 32 == 0), got %d (K=%lld)",
+                (int)group_size, (long long)K);
+  if (M < 0 || topk < 1 || E < 1 || N < 1)
+    return fail(W4A16_ERR_INVALID_ARG, "need M >= 0, topk >= 1, E >= 1, N >= 1");
+  if (K < group_size || K % group_size)
+    return fail(W4A16_ERR_INVALID_ARG, "K must be a positive multiple of the group size %d, got K=%lld",
+                (int)group_size, (long long)K);
+  if (zp && N % 8)
+    return fail(W4A16_ERR_INVALID_ARG, "packed zero points need N %% 8 == 0, got N=%lld", (long long)N);
+  if (M * topk > w4a16::kMaxGridZ || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX)
+    return fail(W4A16_ERR_UNSUPPORTED, "M * topk must be at most %lld", (long long)w4a16::kMaxGridZ);
+  if ((uint64_t)N * (uint64_t)K / 2 > 0xFFFFFFFFull)
+    return fail(W4A16_ERR_UNSUPPORTED, "one expert's weights must be below 4 GiB (N*K/2)");
+  if (M == 0) return ok();
+  if (!x || !wq || !scales || !topk_ids || !y)
+    return fail(W4A16_ERR_INVALID_ARG, "x, wq, scales, topk_ids and y must not be NULL");
+  if (!aligned(x, 16) || !aligned(wq, 16))
+    return fail(W4A16_ERR_ALIGNMENT, "x and wq must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(y, 2) || (bias && !aligned(bias, 2)) || !aligned(topk_ids, 4) ||
+      (topk_weights && !aligned(topk_weights, 4)) || (zp && !aligned(zp, 4)))
+    return fail(W4A16_ERR_ALIGNMENT, "scales, bias and y must be 2-byte aligned; zp, topk_ids and "
+                "topk_weights 4-byte aligned");
+  const int64_t slots = M * topk;
+  const int64_t G = K / group_size;
+  const size_t ybytes = act_bytes(slots * N);
+  if (overlap(y, ybytes, x, act_bytes((x_per_slot ? slots : M) * K)) ||
+      overlap(y, ybytes, wq, (size_t)E * N * (K / 8) * 4) || overlap(y, ybytes, scales, act_bytes(E * N * G)) ||
+      (zp && overlap(y, ybytes, zp, (size_t)E * (N / 8) * G * 4)) ||
+      (bias && overlap(y, ybytes, bias, act_bytes(E * N))) || overlap(y, ybytes, topk_ids, (size_t)slots * 4) ||
+      (topk_weights && overlap(y, ybytes, topk_weights, (size_t)slots * 4)))
+    return fail(W4A16_ERR_INVALID_ARG, "y must not overlap any input");
+  const DeviceInfo* dev = nullptr;
+  w4a16_status st = device_info(&dev);
+  if (st != W4A16_OK) return st;
+  const GroupMap gm = group_map(group_size, K);
+  // one K range per slot (the slots fill the device): planned as if for one CU
+  const w4a16::GemvPlan plan = w4a16::plan_gemv(1, N, K, gm.kgroup, 1);
+  if (plan.splits != 1)
+    return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is too large for one decode workgroup per slot",
+                (long long)K);
+  w4a16::LinearArgs a{x, wq, scales, zp, bias, y, 1, N, K, gm.kgroup, dtype, gm.sG, gm.gmul};
+  w4a16::MoeArgs moe{topk_ids, topk_weights, topk, E, slots, x_per_slot != 0};
+  hipError_t e = w4a16::launch_gemv(a, plan, nullptr, static_cast<hipStream_t>(stream), &moe);
+  if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t w4a16_dense_workspace_size(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t has_bias) {
   (void)K;
   (void)dtype;

@@ -69,8 +69,18 @@ size_t gemv_wave_lds_bytes(int64_t M, int kpw, int group);
 size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int kpw, int group);
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N);
+// Expert-indexed decode: slots = M * topk products of one token row with the
+// expert topk_ids[slot]'s slice of [E, ...] stacks (see w4a16_moe_linear).
+struct MoeArgs {
+  const int32_t* ids;
+  const float* weights;  // NULL: 1
+  int64_t topk, experts, slots;
+  bool x_per_slot;
+};
+constexpr int64_t kMaxGridZ = 65535;
+
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& p, void* workspace,
-                       hipStream_t stream);
+                       hipStream_t stream, const MoeArgs* moe = nullptr);
 
 // ---- prefill GEMM ----------------------------------------------------------
 // A workgroup owns 32*mb tokens x 256 output features; `splits` K ranges of

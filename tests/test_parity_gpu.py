@@ -315,3 +315,69 @@ def test_per_channel_scales(dt, M, N, K, sym, bias):
     w = device_to_bits(L.w4a16_dequant(d.wq, d.s, d.zp, group_size=K))
     zpk = None if sym else O.pack_zeros(c.zp)
     assert np.array_equal(w, O.dequant_act(O.pack_weights(c.q), c.s_bits, zpk, N, K, K, dt))
+
+
+# ---- expert-indexed decode (fused-MoE skinny GEMM) ------------------------------
+
+def _moe_case(E, topk, M, N, K, g, dt, sym, bias, weights, x_per_slot, seed, invalid=True):
+    cases = [make_case(1, N, K, g, dt, sym, bias, seed=(seed, "expert", e)) for e in range(E)]
+    rng = np.random.default_rng(abs(hash((seed, E, topk, M))) % (2**32))
+    ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(M)]).astype(np.int32)
+    if invalid and M * topk >= 3:
+        ids.flat[1] = -1
+        ids.flat[M * topk - 1] = E
+    w = rng.random((M, topk)).astype(np.float32) if weights else None
+    xc = make_case(M * topk if x_per_slot else M, N, K, g, dt, sym, False, seed=(seed, "x"))
+    host = dict(
+        wq=np.stack([L.w4a16_pack_weights(c.q) for c in cases]),
+        s=np.stack([c.s_bits for c in cases]),
+        zp=None if sym else np.stack([L.w4a16_pack_zeros(c.zp) for c in cases]),
+        bias=np.stack([c.bias_bits for c in cases]) if bias else None,
+        x=xc.x_bits, ids=ids, w=w)
+    return host
+
+
+def _moe_device(h, dt):
+    from gpu_util import bits_to_device
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return dict(wq=t(h["wq"]), s=bits_to_device(h["s"], dt, "cuda:0"),
+                zp=t(h["zp"]), bias=None if h["bias"] is None else bits_to_device(h["bias"], dt, "cuda:0"),
+                x=bits_to_device(h["x"], dt, "cuda:0"), ids=t(h["ids"]), w=t(h["w"]))
+
+
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("E,topk,M,N,K,g,sym,bias,weights,xps", [
+    (8, 2, 3, 48, 256, 64, False, True, True, False),
+    (16, 4, 2, 40, 416, 32, True, False, False, True),
+    (4, 1, 5, 24, 4096, 128, False, False, True, False),
+    (6, 3, 1, 200, 320, 320, False, True, False, False),   # per-channel scales
+])
+def test_moe_linear(dt, E, topk, M, N, K, g, sym, bias, weights, xps):
+    h = _moe_case(E, topk, M, N, K, g, dt, sym, bias, weights, xps, seed=("moe", E, topk, M, N, K, g))
+    d = _moe_device(h, dt)
+    y = L.w4a16_moe_linear(d["x"], d["wq"], d["s"], d["ids"], d["zp"], d["bias"], d["w"],
+                           group_size=g, x_per_slot=xps)
+    torch.cuda.synchronize()
+    ref = O.moe_linear_ref(h["x"], h["wq"].view(np.int32).reshape(E * N, K // 8).reshape(E, N, K // 8),
+                           h["s"], h["zp"], h["bias"], h["ids"], h["w"], M, topk, E, N, K, g, dt,
+                           x_per_slot=xps)
+    got = device_to_bits(y)
+    assert_close(got, ref, dt, "moe")
+    bad = [i for i, e in enumerate(h["ids"].ravel()) if not 0 <= e < E]
+    assert np.all(got[bad] == 0)
+
+
+def test_moe_linear_full_size_sampled():
+    # Qwen3-30B-A3B-shaped experts (hidden 2048, expert intermediate 768, gate and
+    # up fused: N = 1536), 128 experts, top-8, 4 tokens; 8 slots checked
+    E, topk, M, N, K, g, dt = 128, 8, 4, 1536, 2048, 128, O.BF16
+    h = _moe_case(E, topk, M, N, K, g, dt, False, False, True, False, seed="moefull", invalid=False)
+    d = _moe_device(h, dt)
+    y = device_to_bits(L.w4a16_moe_linear(d["x"], d["wq"], d["s"], d["ids"], d["zp"], None, d["w"],
+                                          group_size=g))
+    for slot in (0, 5, 9, 14, 19, 22, 27, 31):
+        m, j = divmod(slot, topk)
+        e = int(h["ids"][m, j])
+        ref = O.linear_ref(h["x"][m:m + 1], h["wq"][e], h["s"][e], h["zp"][e], None, 1, N, K, g, dt)[0]
+        ref = ref * float(h["w"][m, j])
+        assert_close(y[slot:slot + 1], ref[None, :], dt, f"moe slot {slot}")
