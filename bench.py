@@ -289,6 +289,70 @@ def dense_comparator(players, stream, steps):
                 per_layer=rows)
 
 
+MOE_LAYERS = (("gate_up", 1536, 2048, False), ("down", 2048, 768, True))  # (name, N, K, x per slot)
+MOE_EXPERTS, MOE_TOPK = 128, 8
+
+
+def moe_measure(stream, reps=20):
+    """Expert-indexed decode on Qwen3-30B-A3B-shaped experts (128 experts,
+    top-8, hidden 2048, expert intermediate 768; gate and up fused), bf16,
+    asymmetric uint4, group 128, synthetic routing (distinct random experts
+    per token, random router weights).  GB/s counts each distinct expert's
+    weights, scales and zero points once per launch, plus x and y.  Timed over
+    a graph of launches rotating through >= 1 GiB of stack copies."""
+    import torch
+    import int4_weight_only_linear_amd as L
+    from int4_weight_only_linear_amd import _binding as B
+    from synth import make_case
+    dev = torch.device("cuda:0")
+    E, topk, g = MOE_EXPERTS, MOE_TOPK, GROUP
+    rows = []
+    for name, N, K, xps in MOE_LAYERS:
+        G = K // g
+        c = make_case(1, N, K, g, 1, False, False, seed=("bench-moe", name))
+        wq1 = torch.from_numpy(L.w4a16_pack_weights(c.q)).to(dev)
+        zp1 = torch.from_numpy(L.w4a16_pack_zeros(c.zp)).to(dev)
+        s1 = torch.from_numpy(c.s_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        # E experts: the one packed expert perturbed per expert (distinct bytes)
+        wq = wq1.unsqueeze(0).repeat(E, 1, 1) ^ torch.arange(E, device=dev, dtype=torch.int32).view(E, 1, 1)
+        zp = zp1.unsqueeze(0).repeat(E, 1, 1)
+        s = s1.unsqueeze(0).repeat(E, 1, 1).contiguous()
+        per_expert = N * K // 2 + N * G * 2 + (N // 8) * G * 4
+        copies = max(2, min(16, -(-(1 << 30) // (E * per_expert))))
+        stacks = [(wq, zp, s)] + [(wq.clone(), zp.clone(), s.clone()) for _ in range(copies - 1)]
+        for M in (1, 4):
+            rng = np.random.default_rng(hash((name, M)) % (2**32))
+            ids_h = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(M)]).astype(np.int32)
+            ids = torch.from_numpy(ids_h).to(dev)
+            w = torch.from_numpy(rng.random((M, topk)).astype(np.float32)).to(dev)
+            xr = M * topk if xps else M
+            x = torch.from_numpy(make_case(xr, N, K, g, 1, False, False, seed=("bench-moe-x", name, M))
+                                 .x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            y = torch.empty((M * topk, N), dtype=torch.bfloat16, device=dev)
+
+            def launch(st):
+                def fn(sp, st=st):
+                    B._check(B.lib.w4a16_moe_linear(x.data_ptr(), st[0].data_ptr(), st[2].data_ptr(),
+                                                    st[1].data_ptr(), None, ids.data_ptr(), w.data_ptr(),
+                                                    y.data_ptr(), M, topk, E, N, K, g, L.W4A16_BF16,
+                                                    int(xps), sp))
+                return fn
+            fns = [[launch(st)] for st in stacks]
+            fns[0][0](torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            ms = time_steps(fns * 4, reps * len(fns), len(fns), stream)
+            nbytes = len(set(ids_h.ravel().tolist())) * per_expert + xr * K * 2 + M * topk * N * 2
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            rows.append(dict(layer=name, N=N, K=K, M=M, us=round(ms * 1e3, 2), GBs=round(gbs, 1),
+                             frac=round(gbs / HBM_PEAK_GBS, 4)))
+        del stacks, wq, zp, s
+        torch.cuda.empty_cache()
+    return dict(workload=f"Qwen3-30B-A3B-shaped expert layers: {E} experts, top-{topk}, "
+                         "gate_up 2048 -> 1536 (x per token), down 768 -> 2048 (x per slot); "
+                         "asym uint4 g128 bf16; synthetic routing",
+                per_layer=rows)
+
+
 def run_report(path_prefix):
     """Every point of the decode, prefill and dispatch-sweep workloads on both
     paths: per-launch time, GB/s and % of HBM peak, TFLOP/s and % of the
@@ -391,6 +455,7 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies in the rotation pool (0: >= 1 GiB)")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-moe", action="store_true", help="skip the expert-indexed decode measurement")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dequantised-copy (dense) comparator of the prefill layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -493,6 +558,10 @@ def main():
             prefill["dequantised_copy"] = dense_comparator(players, side, args.prefill_steps)
         del players, plaunch
 
+    moe = None
+    if not args.no_moe:
+        moe = moe_measure(side)
+
     cpu = None
     if not args.no_cpu_baseline:
         host_layers = [(l["K"], l["N"], l["case"]) for l in layers]
@@ -525,6 +594,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "moe_decode": moe,
     }
     print(json.dumps(out), flush=True)
 
