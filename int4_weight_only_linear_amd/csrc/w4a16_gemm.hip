@@ -64,6 +64,8 @@ struct GemmParams {
   int splits;
   int steps_per_split;
   int vec_store;       // y rows are 16-byte aligned and N % 8 == 0
+  int two_pass;        // K split: store plain partials [split][M][np], summed by a second kernel
+  int np;              // partial row stride: N rounded up to 8
 };
 
 // Workgroups are dispatched round-robin over the XCDs; give each XCD a
@@ -384,6 +386,30 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   // at pair index i * kThreads + tid.  The sum runs over chunks of kChunk
   // values: for each split in turn all of a chunk's loads are issued before
   // any is used, so a chunk costs one memory round trip per split.
+  // (compiled for the 128-token tile only: in the taller tiles' kernels this
+  // block costs the accumulators their registers, and the planner uses the
+  // two-pass form at small M only)
+  if constexpr (MB == 4) if (p.splits > 1 && p.two_pass) {
+    // plain fp32 partial sums, row-major [split][M][np]; splitk_reduce_kernel
+    // adds the splits in order.  acc[rb][cb][4a + e] is token m0 + 32 rb + j,
+    // feature nw0 + 32 cb + 8a + 4h + e: four consecutive features, 16 bytes.
+    float* part = p.partial + (size_t)split * p.M * p.np;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      const int m = m0 + 32 * rb + j;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int n = nw0 + 32 * cb + 8 * a + 4 * h;
+          if (m < p.M && n < p.np)
+            *reinterpret_cast<f32x4*>(part + (size_t)m * p.np + n) =
+                f32x4{acc[rb][cb][4 * a], acc[rb][cb][4 * a + 1], acc[rb][cb][4 * a + 2],
+                      acc[rb][cb][4 * a + 3]};
+        }
+    }
+    return;
+  }
   if (p.splits > 1) {
     constexpr int NV = MB * 32;  // accumulator values per thread
     constexpr int kChunk = 64;
@@ -467,6 +493,31 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   }
 }
 
+// The K split's second pass: y = sum of the splits' fp32 partials, in split
+// order, + bias in fp32, one rounding.  One thread per row and 4 consecutive
+// features.
+template <int DT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
+                                                            const uint16_t* __restrict__ bias,
+                                                            uint16_t* __restrict__ y, int M, int N,
+                                                            int np, int splits) {
+  const int qpr = np >> 2;
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= (int64_t)M * qpr) return;
+  const int m = (int)(q / qpr), n = (int)(q % qpr) * 4;
+  const size_t plane = (size_t)M * np;
+  const float* src = partial + (size_t)m * np + n;
+  f32x4 s = *reinterpret_cast<const f32x4*>(src);
+  for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4*>(src + sp * plane);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (n + e < N) {
+      float v = s[e];
+      if (bias) v += act_to_f32<DT>(bias[n + e]);
+      y[(size_t)m * N + n + e] = f32_to_act<DT>(v);
+    }
+}
+
 template <int DT, int GS, bool ASYM, int MB>
 hipError_t launch_t(const GemmParams& prm, hipStream_t s) {
   hipLaunchKernelGGL((gemm_kernel<DT, GS, ASYM, MB>), dim3(prm.units), dim3(kThreads), 0, s, prm);
@@ -518,7 +569,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
       const int sps = (nsteps + splits - 1) / splits;
       const int real_splits = (nsteps + sps - 1) / sps;
       if (real_splits != splits) continue;
-      if (splits > 1 && tiles > kMaxCounters) break;
+
       const int64_t units = tiles * splits;
       const int64_t rounds = (units + cus - 1) / cus;
       // a split unit writes its fp32 partial tile; the tile's last unit then
@@ -526,26 +577,39 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
       // split and 64-value chunk, plus the bytes (mostly from L2 / MALL)
       const double fixup = splits > 1 ? 2.0 * bm * kBN * 4 / 40.0 +
                                            2500.0 * splits * (32.0 * mb / 64.0) : 0.0;
-      const double cost = (double)rounds * (sps * (760.0 * mb + 1000.0) + fixup);
-      if (best.units == 0 || cost < best_cost * 0.98) {
-        best_cost = cost;
-        best.mb = mb;
-        best.splits = splits;
-        best.steps_per_split = sps;
-        best.tiles_n = (int)tiles_n;
-        best.tiles = (int)tiles;
-        best.units = (int)units;
+      const double loop = sps * (760.0 * mb + 1000.0);
+      const double cost = (double)rounds * (loop + fixup);
+      // two passes: each unit stores its partial tile (~64 bytes a cycle),
+      // then a second kernel reads all partials (mostly from the last-level
+      // cache, taken as 5 TB/s at 2.1 GHz) plus its launch
+      const double np = (double)((N + 7) / 8 * 8);
+      const double cost2 = (double)rounds * (loop + bm * kBN * 4 / 64.0) +
+                           (splits * (double)M * np * 4.0 + (double)M * N * 2.0) * (2.1e9 / 5e12) + 3000.0;
+      for (int tp = 0; tp < (splits > 1 && mb == 4 ? 2 : 1); ++tp) {
+        const double c = tp ? cost2 : cost;
+        if (tp == 0 && splits > 1 && tiles > kMaxCounters) continue;
+        if (best.units == 0 || c < best_cost * 0.98) {
+          best_cost = c;
+          best.mb = mb;
+          best.splits = splits;
+          best.steps_per_split = sps;
+          best.tiles_n = (int)tiles_n;
+          best.tiles = (int)tiles;
+          best.units = (int)units;
+          best.two_pass = tp == 1;
+        }
       }
     }
   }
   // tuning override "mb,splits" (tile height 32*mb, K ranges), e.g. for sweeps
   if (const char* env = std::getenv("W4A16_GEMM_TILE")) {
-    int mb = 0, splits = 0;
-    if (std::sscanf(env, "%d,%d", &mb, &splits) == 2 && (mb == 4 || mb == 6 || mb == 8) &&
-        splits >= 1 && splits <= nsteps) {
+    int mb = 0, splits = 0, tp = 0;
+    if (std::sscanf(env, "%d,%d,%d", &mb, &splits, &tp) >= 2 && (mb == 4 || mb == 6 || mb == 8) &&
+        splits >= 1 && splits <= nsteps && (tp == 0 || mb == 4)) {
       const int sps = (nsteps + splits - 1) / splits;
       const int64_t tiles = ((M + 32 * mb - 1) / (32 * mb)) * tiles_n;
-      if (splits == 1 || tiles <= kMaxCounters) {
+      if (splits == 1 || tp == 1 || tiles <= kMaxCounters) {
+        best.two_pass = splits > 1 && tp == 1;
         best.mb = mb;
         best.steps_per_split = sps;
         best.splits = (nsteps + sps - 1) / sps;
@@ -561,6 +625,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cu_count) {
   const GemmPlan p = plan_gemm(M, N, K, cu_count);
   if (p.splits <= 1) return 0;
+  if (p.two_pass)
+    return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)((N + 7) / 8 * 8) * sizeof(float);
   return kCounterBytes + (size_t)p.units * (size_t)(32 * p.mb) * kBN * sizeof(float);
 }
 
@@ -594,8 +660,21 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
   prm.splits = plan.splits;
   prm.steps_per_split = plan.steps_per_split;
   prm.vec_store = (a.N % 8 == 0) && (reinterpret_cast<uintptr_t>(a.y) % 16 == 0);
-  return a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, plan.mb, stream)
-                           : launch_g<DT_BF16>(prm, a.group, plan.mb, stream);
+  prm.two_pass = plan.splits > 1 && plan.two_pass;
+  if (prm.two_pass && plan.mb != 4) return hipErrorInvalidConfiguration;
+  prm.np = (int)((a.N + 7) / 8 * 8);
+  hipError_t e = a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, plan.mb, stream)
+                                   : launch_g<DT_BF16>(prm, a.group, plan.mb, stream);
+  if (e != hipSuccess || !prm.two_pass) return e;
+  const int64_t quads = (int64_t)prm.M * (prm.np / 4);
+  const int blocks = (int)((quads + 255) / 256);
+  if (a.dtype == DT_F16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<DT_F16>, dim3(blocks), dim3(256), 0, stream, prm.partial,
+                       prm.bias, prm.y, prm.M, prm.N, prm.np, prm.splits);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<DT_BF16>, dim3(blocks), dim3(256), 0, stream, prm.partial,
+                       prm.bias, prm.y, prm.M, prm.N, prm.np, prm.splits);
+  return hipGetLastError();
 }
 
 }  // namespace w4a16

@@ -92,6 +92,9 @@ struct GemmPlan {
   int tiles_n;
   int tiles;
   int units;
+  // K split summed by a second kernel from plain fp32 partials (small M,
+  // many splits) instead of by the tile's last workgroup
+  bool two_pass;
 };
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cu_count);

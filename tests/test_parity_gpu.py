@@ -381,3 +381,18 @@ def test_moe_linear_full_size_sampled():
         ref = O.linear_ref(h["x"][m:m + 1], h["wq"][e], h["s"][e], h["zp"][e], None, 1, N, K, g, dt)[0]
         ref = ref * float(h["w"][m, j])
         assert_close(y[slot:slot + 1], ref[None, :], dt, f"moe slot {slot}")
+
+
+# ---- GEMM K split: last-workgroup hand-off and the two-pass form ----------------
+
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("tile", ["4,3,0", "4,3,1", "6,5,0", "8,2,0", "4,7,1"])
+@pytest.mark.parametrize("M,N,K,g,bias", [(130, 200, 640, 64, True), (128, 264, 1216, 32, False),
+                                          (300, 56, 2048, 128, True)])
+def test_gemm_k_split_forms(monkeypatch, dt, tile, M, N, K, g, bias):
+    monkeypatch.setenv("W4A16_GEMM_TILE", tile)
+    c = make_case(M, N, K, g, dt, False, bias, seed=("ksplit", M, N, K, g, dt, bias))
+    d = DeviceCase(c)
+    y1 = d.run(GEMM)
+    assert_close(y1, oracle_rows(c), dt, f"GEMM tile {tile}")
+    assert np.array_equal(d.run(GEMM), y1), "split-K result changed between runs"
