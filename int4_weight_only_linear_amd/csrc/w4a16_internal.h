@@ -47,11 +47,12 @@ constexpr int kGemvKStep = 128;       // k per wave step: 4 chunks of 32
 constexpr int kGemvMaxWaves = 16;     // 1024 threads
 constexpr int kGemvMaxMTiles = 4;     // M <= 64
 constexpr int kGemvStepsPerWave = 8;  // k-steps whose loads a wave keeps in flight
-constexpr int kGemvXSegsPerThread = 4;  // 16-byte x loads per thread when x is staged
+constexpr int kGemvXSegsPerThread = 8;  // 16-byte x loads per thread when x is staged
 // Dynamic LDS per decode workgroup (cross-wave reduction + staged x).  The
 // kernel's LDS layout and the host's plan both size it with gemv_lds_bytes,
-// and the plan splits K until it fits this budget.
-constexpr size_t kGemvLdsBudget = 64 * 1024;
+// and the plan splits K until it fits this budget (gfx950 has 160 KiB of LDS
+// per CU; a K split costs a partial-sum hand-off, so the budget is generous).
+constexpr size_t kGemvLdsBudget = 128 * 1024;
 
 struct GemvPlan {
   int tiles;             // ceil(N / 16)
