@@ -178,7 +178,12 @@ def test_select_path_env_override(monkeypatch):
 def test_workspace_size():
     # enough row tiles for every CU: no split, no workspace
     assert L.w4a16_workspace_size(1, 28672, 4096, 128, 1, 1) == 0
-    # fewer row tiles than CUs: K is split and the workspace holds counters + partials
+    # 160 row tiles: not split (a split costs more than the idle CUs)
+    assert L.w4a16_workspace_size(1, 2560, 4096, 128, 0, 0) == 0
+    # 3 row tiles: split across the CUs
+    assert L.w4a16_workspace_size(1, 40, 4096, 128, 1, 1) > 0
+    # more k-steps than one workgroup's waves take (M = 4: 4 steps a wave, 76
+    # steps): K is split and the workspace holds counters + partials
     ws = L.w4a16_workspace_size(4, 2560, 9728, 128, 0, 0)
     assert ws > 0
     tiles = 2560 // 16

@@ -229,14 +229,15 @@ def test_workspace_reuse_across_shapes():
 
 
 def test_workspace_errors():
-    c = make_case(1, 2560, 9728, 128, O.BF16, False, False, seed=("ws",))
+    # 40 rows are 3 row tiles: the decode kernel splits K and needs a workspace
+    c = make_case(1, 40, 9728, 128, O.BF16, False, False, seed=("ws",))
     d = DeviceCase(c)
-    need = L.w4a16_workspace_size(1, 2560, 9728, 128, O.BF16, True, GEMV)
+    need = L.w4a16_workspace_size(1, 40, 9728, 128, O.BF16, True, GEMV)
     assert need > 0
-    y = torch.empty((1, 2560), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((1, 40), dtype=torch.bfloat16, device="cuda")
     from int4_weight_only_linear_amd import _binding as B
     st = B.lib.w4a16_linear_path(d.x.data_ptr(), d.wq.data_ptr(), d.s.data_ptr(), d.zp.data_ptr(),
-                                 None, y.data_ptr(), 1, 2560, 9728, 128, O.BF16, None, 0,
+                                 None, y.data_ptr(), 1, 40, 9728, 128, O.BF16, None, 0,
                                  torch.cuda.current_stream().cuda_stream, GEMV)
     assert st == 6 and "workspace" in L.w4a16_last_error()
 
