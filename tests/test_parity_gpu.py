@@ -397,3 +397,64 @@ def test_gemm_k_split_forms(monkeypatch, dt, tile, M, N, K, g, bias):
     y1 = d.run(GEMM)
     assert_close(y1, oracle_rows(c), dt, f"GEMM tile {tile}")
     assert np.array_equal(d.run(GEMM), y1), "split-K result changed between runs"
+
+
+# ---- graph capture: every entry point replays to its eager result --------------
+
+def _graph_replays_match(run_eager, run_captured, reps=3):
+    eager = run_eager()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            out = run_captured()
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        run_eager()                         # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,N,K,g,path,tile", [
+    (1, 4096, 4096, 128, GEMV, None),        # decode, no split
+    (3, 40, 4096, 64, GEMV, None),           # decode, K split (workspace counters)
+    (130, 200, 640, 64, GEMM, "4,3,0"),      # GEMM, last-workgroup hand-off
+    (128, 264, 1216, 32, GEMM, "4,4,1"),     # GEMM, two-pass split
+    (300, 520, 1024, 128, GEMM, None),       # GEMM, no split
+])
+def test_graph_capture_linear(monkeypatch, M, N, K, g, path, tile):
+    if tile:
+        monkeypatch.setenv("W4A16_GEMM_TILE", tile)
+    c = make_case(M, N, K, g, O.BF16, False, True, seed=("graph", M, N, K, g, path))
+    d = DeviceCase(c)
+    need = L.w4a16_workspace_size(M, N, K, g, O.BF16, True, path)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda") if need else None
+    y_cap = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def run(out=None):
+        return L.w4a16_linear_path(d.x, d.wq, d.s, d.zp, d.bias, group_size=g, path=path, out=out,
+                                   workspace=ws)
+    _graph_replays_match(lambda: run(), lambda: run(y_cap))
+
+
+def test_graph_capture_dense_and_moe():
+    c = make_case(128, 136, 512, 64, O.F16, False, True, seed=("graphdense",))
+    d = DeviceCase(c)
+    w = L.w4a16_dequant(d.wq, d.s, d.zp, group_size=64)
+    ws = torch.zeros(L.w4a16_dense_workspace_size(128, 136, 512, O.F16, True), dtype=torch.uint8,
+                     device="cuda")
+    y_cap = torch.empty((128, 136), dtype=torch.float16, device="cuda")
+    _graph_replays_match(lambda: L.w4a16_linear_dense(d.x, w, d.bias, workspace=ws),
+                         lambda: L.w4a16_linear_dense(d.x, w, d.bias, out=y_cap, workspace=ws))
+    h = _moe_case(8, 2, 3, 48, 256, 64, O.BF16, False, True, True, False, seed="graphmoe")
+    m = _moe_device(h, O.BF16)
+    y_moe = torch.empty((6, 48), dtype=torch.bfloat16, device="cuda")
+    run = lambda out=None: L.w4a16_moe_linear(m["x"], m["wq"], m["s"], m["ids"], m["zp"], m["bias"],
+                                              m["w"], group_size=64, out=out)
+    _graph_replays_match(lambda: run(), lambda: run(y_moe))
