@@ -614,10 +614,10 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   // The scale and zero-point staging then needs at most 32 * kpw / group and
   // 4 * kpw / group loads per lane, which the kernel's fixed counts cover.
   // measured on the decode layers: 8 k-steps per wave for M <= 2, 4 for
-  // M <= 8 (deeper waves are slower there), then as many as the staging allows
+  // M <= 8, 1 above (deeper waves are slower there)
   int kpw = kGemvStepsPerWave;
   if (p.xlds)
-    while (kpw > 1 && (M * kpw > 4 * kGemvXSegsPerThread || (kpw > 4 && M > 2))) kpw >>= 1;
+    while (kpw > 1 && (M * kpw > 4 * kGemvXSegsPerThread || (kpw > 4 && M > 2) || M > 8)) kpw >>= 1;
   // tuning overrides: k-steps per wave (a smaller power of two) and a
   // minimum number of K splits
   if (const char* env = std::getenv("W4A16_GEMV_KPW")) {

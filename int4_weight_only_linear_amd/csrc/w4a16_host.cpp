@@ -110,16 +110,17 @@ GroupMap group_map(int32_t g, int64_t K) {
 }
 
 // Decode-kernel threshold.  The pages route M <= 5 to their skinny kernel
-// (tuned on RDNA).  On MI355X the decode kernel beats the GEMM up to M = 16
+// (tuned on RDNA).  On MI355X the decode kernel beats the GEMM up to M = 8
 // at every shape, group, quantisation and dtype of the crossover sweep, and
-// the GEMM wins or ties from M = 32, so the constant is measured, not theirs.
+// the GEMM (with its two-pass K split at small M) wins from M = 16 in 23 of
+// the 24, so the constant is measured, not theirs.
 int64_t gemv_threshold(int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t has_zp) {
   (void)N; (void)K; (void)group; (void)dtype; (void)has_zp;
   if (const char* env = std::getenv("W4A16_M_THRESHOLD")) {
     const long v = std::strtol(env, nullptr, 10);
     if (v >= 0 && v <= W4A16_GEMV_MAX_M) return v;
   }
-  return 16;
+  return 8;
 }
 
 w4a16_path resolve_path(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,
