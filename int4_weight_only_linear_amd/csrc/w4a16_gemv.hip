@@ -636,12 +636,13 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
     const int v = std::atoi(env);
     if (v >= 1 && (v == 1 || p.tiles <= kMaxCounters)) splits = v;  // raised below if it must be
   }
+  const size_t budget = p.tiles <= cu_count ? kGemvLdsBudget : kGemvLdsBudgetShared;
   for (;;) {
     if (splits > p.ksteps) splits = p.ksteps;
     const int kps = (p.ksteps + splits - 1) / splits;
     const int waves = (kps + kpw - 1) / kpw;
     if (splits == p.ksteps ||
-        (waves <= kGemvMaxWaves && gemv_lds_bytes(waves, p.mtiles, M, kpw, group) <= kGemvLdsBudget))
+        (waves <= kGemvMaxWaves && gemv_lds_bytes(waves, p.mtiles, M, kpw, group) <= budget))
       break;
     ++splits;
   }

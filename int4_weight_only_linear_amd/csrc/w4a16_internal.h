@@ -50,9 +50,12 @@ constexpr int kGemvStepsPerWave = 8;  // k-steps whose loads a wave keeps in fli
 constexpr int kGemvXSegsPerThread = 8;  // 16-byte x loads per thread when x is staged
 // Dynamic LDS per decode workgroup (cross-wave reduction + staged x).  The
 // kernel's LDS layout and the host's plan both size it with gemv_lds_bytes,
-// and the plan splits K until it fits this budget (gfx950 has 160 KiB of LDS
-// per CU; a K split costs a partial-sum hand-off, so the budget is generous).
-constexpr size_t kGemvLdsBudget = 128 * 1024;
+// and the plan splits K until it fits the budget.  gfx950 has 160 KiB of LDS
+// per CU: with at most one row tile per CU a workgroup may take 128 KiB (a K
+// split costs a partial-sum hand-off); with more tiles than CUs, 64 KiB, so
+// that several workgroups are resident on a CU at once.
+constexpr size_t kGemvLdsBudget = 128 * 1024;       // the most any plan uses
+constexpr size_t kGemvLdsBudgetShared = 64 * 1024;  // more row tiles than CUs
 
 struct GemvPlan {
   int tiles;             // ceil(N / 16)
