@@ -66,6 +66,7 @@ struct GemvParams {
   int ksteps_per_split;
   int splits;
   int kpw;      // k-steps per wave (contiguous runs)
+  int waves;    // waves per workgroup
   // per-wave staging geometry (M <= 16 kernel): log2 of the 16-byte x
   // segments per row and of the groups in one wave's run of kpw k-steps, and
   // the bytes of one wave's LDS region
@@ -193,7 +194,9 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // of two), keeping the vector-ALU work in front of the weight loads small.
 // ONE: a single token (M == 1), whose sums are row 0 of each MFMA result
 // (lanes 0..15, register 0); the other rows are then never updated.
-template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE>
+// MOE: expert-indexed mode (a separate instance, so that the plain layer has
+// no branch in front of its parameter loads and they arrive in one batch).
+template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE, bool MOE>
 __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams params) {
   constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
   constexpr int SPT = (32 * KPW) / GS > 0 ? (32 * KPW) / GS : 1;  // scale loads per lane
@@ -203,16 +206,18 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams param
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   GemvParams p = params;
-  if (p.moe_ids && !select_slot(p)) {
-    // not an expert: a zero row (the whole workgroup leaves here)
-    const int n = blockIdx.x * kGemvRowsPerTile + tid;
-    if (tid < kGemvRowsPerTile && n < p.N) p.y[n] = 0;
-    return;
+  if constexpr (MOE) {
+    if (!select_slot(p)) {
+      // not an expert: a zero row (the whole workgroup leaves here)
+      const int n = blockIdx.x * kGemvRowsPerTile + tid;
+      if (tid < kGemvRowsPerTile && n < p.N) p.y[n] = 0;
+      return;
+    }
   }
   // wave index as a wave-uniform (scalar) value, so the per-wave k-step
   // bookkeeping below stays in SGPRs and its branches are scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nwaves = blockDim.x >> 6;
+  const int nwaves = p.waves;
   const int col = lane & 15;   // MFMA column: output row within the tile
   const int row4 = lane >> 4;  // 16-lane row of the wave
   const int tile = blockIdx.x;
@@ -261,10 +266,12 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams param
   // pieces per row + piece); otherwise one 2-byte load per scale
   const bool svec = ngw >= 8 && p.gmul == 1 && (p.sG & 7) == 0 && (gw0 & 7) == 0 &&
                     gw0 + ngw <= p.G && (reinterpret_cast<uintptr_t>(p.scales) & 15) == 0;
-  u32x4 srv = {0u, 0u, 0u, 0u};
+  // (srv and sr are filled only on their own branch and read only on it:
+  // giving them a value on the other branch would make that branch write a
+  // register with a load in flight on this one, and the compiler then waits
+  // for every earlier load -- x -- before the weights are issued)
+  u32x4 srv;
   uint32_t sr[SPT];
-#pragma unroll
-  for (int j = 0; j < SPT; ++j) sr[j] = 0u;
   if (svec) {
     const int lg_ppr = lg_ngw - 3;
     const int e = min(lane, (16 << lg_ppr) - 1);
@@ -658,29 +665,39 @@ size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N) {
   return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
+// the small kernel is instantiated per k-steps per wave, so that its
+// branch-free path covers every wave whose run is complete
+template <int DT, int GS, bool ASYM, bool MOE>
+static hipError_t launch_small(const GemvParams& prm, const GemvPlan& plan, dim3 grid, dim3 block,
+                               hipStream_t s) {
+  constexpr int XPT = kGemvXSegsPerThread;
+  switch (plan.kpw) {
+    case 8:
+      if (prm.M == 1)
+        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, XPT, true, MOE>), grid, block, plan.lds_bytes, s, prm);
+      else
+        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, XPT, false, MOE>), grid, block, plan.lds_bytes, s, prm);
+      break;
+    case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, XPT, false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
+    case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, XPT, false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
+    case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, XPT, false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
+    default: return hipErrorInvalidConfiguration;
+  }
+  return hipGetLastError();
+}
+
 template <int DT, int MT, int GS, bool ASYM>
 static hipError_t launch_t(const GemvParams& prm, const GemvPlan& plan, hipStream_t s) {
   dim3 grid(plan.tiles, plan.splits, prm.slots);
   dim3 block(plan.waves * 64);
   constexpr int KPW = kGemvStepsPerWave;
   if constexpr (MT == 1) {
-    // the small kernel is instantiated per k-steps per wave, so that its
-    // branch-free path covers every wave whose run is complete
-    switch (plan.kpw) {
-      case 8:
-        if (prm.M == 1)
-          hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, kGemvXSegsPerThread, true>), grid, block, plan.lds_bytes, s, prm);
-        else
-          hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, kGemvXSegsPerThread, false>), grid, block, plan.lds_bytes, s, prm);
-        break;
-      case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, kGemvXSegsPerThread, false>), grid, block, plan.lds_bytes, s, prm); break;
-      case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, kGemvXSegsPerThread, false>), grid, block, plan.lds_bytes, s, prm); break;
-      case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, kGemvXSegsPerThread, false>), grid, block, plan.lds_bytes, s, prm); break;
-      default: return hipErrorInvalidConfiguration;
-    }
-  } else
+    return prm.moe_ids ? launch_small<DT, GS, ASYM, true>(prm, plan, grid, block, s)
+                       : launch_small<DT, GS, ASYM, false>(prm, plan, grid, block, s);
+  } else {
     hipLaunchKernelGGL((gemv_wide_kernel<DT, MT, GS, ASYM, KPW>), grid, block, plan.lds_bytes, s, prm);
-  return hipGetLastError();
+    return hipGetLastError();
+  }
 }
 
 template <int DT, int MT, int GS>
@@ -758,6 +775,7 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
   prm.ksteps_per_split = plan.ksteps_per_split;
   prm.splits = plan.splits;
   prm.kpw = plan.kpw;
+  prm.waves = plan.waves;
   {
     int lg = 0;
     while ((1 << lg) < plan.kpw * (kGemvKStep / 8)) ++lg;
