@@ -115,6 +115,7 @@ w4a16_status w4a16_unpack_zeros(const int32_t* zpk, int64_t N, int64_t G, uint8_
  * Rules: group_size in {32, 64, 128} (the pages' accept set), or
  * group_size == K with K % 32 == 0 (per-channel: one scale and zero point per
  * row, scales [N, 1], zp [N/8, 1]); K >= group_size and K % group_size == 0; N >= 1; N % 8 == 0 when zp != NULL; M >= 0;
+ * K <= 2^24 (W4A16_ERR_UNSUPPORTED above: the kernels use 32-bit offsets);
  * dtype is W4A16_F16 or W4A16_BF16; x, wq, scales, y non-NULL when M > 0;
  * x and wq 16-byte aligned, scales/bias/y 2-byte aligned, zp 4-byte aligned;
  * y must not overlap x, wq, scales, zp or bias. */

@@ -107,14 +107,18 @@ __device__ __forceinline__ bool select_slot(GemvParams& p) {
 // block; in a final incomplete tile, bytes 16 r of the row's 64-byte run.
 // The incomplete last run (chunks 4R.. of K/32) is stored in slice order,
 // T = 4 * tail chunks words per row; lanes past it read its last chunk.
+// Every address is a wave-uniform base (scalar registers) plus a 32-bit
+// per-lane byte offset, the form the loads take without vector address
+// arithmetic.
 struct WeightWalk {
-  const char* base;   // wave-uniform
+  const char* base;   // wave-uniform: row n0 of the tile
   uint32_t lane_off;  // complete runs: base + ks * run_bytes + lane_off
   uint32_t run_bytes;
   uint32_t tail_off;  // the incomplete last run: base + tail_off
   int full_runs;
   __device__ __forceinline__ const char* at(int ks) const {
-    return base + (ks < full_runs ? (size_t)ks * run_bytes + lane_off : (size_t)tail_off);
+    const bool full = ks < full_runs;  // wave-uniform
+    return base + (full ? (size_t)ks * run_bytes : 0) + (size_t)(full ? lane_off : tail_off);
   }
 };
 
@@ -126,17 +130,16 @@ __device__ __forceinline__ WeightWalk weight_walk(const uint32_t* wq, int N, int
   const int tail_chunks = nchunks - 4 * full_runs;
   const uint32_t tail_piece = 16u * (uint32_t)max(0, min(r, tail_chunks - 1));
   w.full_runs = full_runs;
+  w.base = reinterpret_cast<const char*>(wq) + (size_t)n0 * row_bytes;
   if (n0 + kGemvRowsPerTile <= N) {
-    w.base = reinterpret_cast<const char*>(wq) + (size_t)n0 * row_bytes;
     w.run_bytes = 1024u;
     w.lane_off = (uint32_t)(16 * r + j) * 16u;
     w.tail_off = (uint32_t)full_runs * 1024u + (uint32_t)j * (uint32_t)(16 * tail_chunks) + tail_piece;
   } else {
-    const uint32_t n = (uint32_t)min(n0 + j, N - 1);
-    w.base = reinterpret_cast<const char*>(wq);
+    const uint32_t dn = (uint32_t)(min(n0 + j, N - 1) - n0);
     w.run_bytes = 64u;
-    w.lane_off = n * row_bytes + 16u * (uint32_t)r;
-    w.tail_off = n * row_bytes + (uint32_t)full_runs * 64u + tail_piece;
+    w.lane_off = __umul24(dn, row_bytes) + 16u * (uint32_t)r;
+    w.tail_off = __umul24(dn, row_bytes) + (uint32_t)full_runs * 64u + tail_piece;
   }
   return w;
 }
@@ -197,7 +200,7 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // MOE: expert-indexed mode (a separate instance, so that the plain layer has
 // no branch in front of its parameter loads and they arrive in one batch).
 template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE, bool MOE>
-__global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams params) {
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void gemv_small_kernel(const GemvParams params) {
   constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
   constexpr int SPT = (32 * KPW) / GS > 0 ? (32 * KPW) / GS : 1;  // scale loads per lane
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -249,16 +252,21 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams param
   float* xsum = xpart + p.M * kpw * 8;  // [ngw][16]
 
   // ---- 1. loads: x, scales and zero points of this wave's run, then weights ----
+  // (each a wave-uniform base plus a 32-bit per-lane byte offset)
   const int xsegs = p.M * xsegs_row;
-  u32x4 xr[XPT];
+  const int xk0 = min(kw0, p.K - 8);  // k of the x base; lanes read k = min(kw0 + 8 seg, K - 8)
+  const char* xbase = reinterpret_cast<const char*>(p.x + xk0);
+  // (the per-lane products below take 24-bit operands: a row index below 16
+  // times a stride or K below 2^24, and a group index times 0 or 1)
+  u32x4 xr[XPT];  // only the loads that carry x are filled, and only they are staged
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    xr[j] = u32x4{0u, 0u, 0u, 0u};
     if (64 * j < xsegs) {  // wave-uniform: only the loads that carry x
       const int e = min(lane + 64 * j, xsegs - 1);
       const int m = e >> lg_xsegs;
       const int k = min(kw0 + ((e & (xsegs_row - 1)) << 3), p.K - 8);
-      xr[j] = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + k);
+      const uint32_t off = 2u * (__umul24(m, p.K) + (uint32_t)(k - xk0));
+      xr[j] = *reinterpret_cast<const u32x4*>(xbase + off);
     }
   }
   // scales of the run: when each row's groups of the run are whole 16-byte
@@ -272,19 +280,22 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams param
   // for every earlier load -- x -- before the weights are issued)
   u32x4 srv;
   uint32_t sr[SPT];
+  const char* sbase = reinterpret_cast<const char*>(p.scales + (size_t)n0 * p.sG);  // row n0
+  const int last_dr = p.N - 1 - n0;  // rows past N read row N - 1
   if (svec) {
     const int lg_ppr = lg_ngw - 3;
     const int e = min(lane, (16 << lg_ppr) - 1);
     const int r = e >> lg_ppr;
-    srv = *reinterpret_cast<const u32x4*>(p.scales + (size_t)min(n0 + r, p.N - 1) * p.sG + gw0 +
-                                          8 * (e & ((1 << lg_ppr) - 1)));
+    const uint32_t off = 2u * (__umul24(min(r, last_dr), p.sG) + (uint32_t)(gw0 + 8 * (e & ((1 << lg_ppr) - 1))));
+    srv = *reinterpret_cast<const u32x4*>(sbase + off);
   } else {
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int e = min(lane + 64 * j, 16 * ngw - 1);
       const int r = e >> lg_ngw;
       const int g = min(gw0 + (e & (ngw - 1)), p.G - 1);
-      sr[j] = p.scales[(size_t)min(n0 + r, p.N - 1) * p.sG + g * p.gmul];
+      const uint32_t off = 2u * (__umul24(min(r, last_dr), p.sG) + __umul24(g, p.gmul));
+      sr[j] = *reinterpret_cast<const uint16_t*>(sbase + off);
     }
   }
   uint32_t zr = 0u;
@@ -292,7 +303,9 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams param
     const int e = min(lane, 2 * ngw - 1);
     const int rr = e >> lg_ngw;
     const int g = min(gw0 + (e & (ngw - 1)), p.G - 1);
-    zr = p.zp[(size_t)min((n0 >> 3) + rr, (p.N >> 3) - 1) * p.sG + g * p.gmul];
+    const char* zbase = reinterpret_cast<const char*>(p.zp + (size_t)(n0 >> 3) * p.sG);
+    const uint32_t off = 4u * (__umul24(min(rr, (p.N >> 3) - 1 - (n0 >> 3)), p.sG) + __umul24(g, p.gmul));
+    zr = *reinterpret_cast<const uint32_t*>(zbase + off);
   }
   __builtin_amdgcn_sched_barrier(0);
   // weights: a wave-uniform base per k-step plus one per-lane offset, so each
@@ -419,54 +432,51 @@ __global__ __launch_bounds__(1024) void gemv_small_kernel(const GemvParams param
 
   if (my_steps == KPW && (my_first + KPW) * 4 <= p.nchunks) {
     // Common case: the wave's whole run is complete 128-k runs.  Branch-free
-    // and software pipelined one k-step deep: the x fragments of step i + 1
-    // are read from LDS while step i is multiplied.  (Keeping only one step
-    // of fragments in flight keeps the register count low enough for many
-    // resident waves.)  bf16 multiplies x by 128 + q only; the offset and
-    // the zero point are removed per group with the x sums.
-    u32x4 xa[2][4];
-    auto load_x = [&](int i, u32x4 (&x)[4]) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        x[t] = *reinterpret_cast<const u32x4*>(xrow + i * kGemvKStep + t * 32);
+    // and software pipelined by 32-k chunks: the x fragment of chunk q + XD
+    // is read from LDS while chunk q is multiplied (a ring of XD + 1
+    // fragments, few registers, so that many waves stay resident).  bf16
+    // multiplies x by 128 + q only; the offset and the zero point are
+    // removed per group with the x sums.
+    constexpr int XD = ONE ? 2 : 1;  // measured best on the decode layers
+    constexpr int NQ = 4 * KPW;  // chunks of the run
+    u32x4 xa[XD + 1];
+    auto load_x = [&](int q) {
+      return *reinterpret_cast<const u32x4*>(xrow + (q >> 2) * kGemvKStep + (q & 3) * 32);
     };
-    {
-      constexpr int NR = ONE ? 1 : 4;  // accumulator rows in use
-      load_x(0, xa[0]);
+    constexpr int NR = ONE ? 1 : 4;  // accumulator rows in use
 #pragma unroll
-      for (int i = 0; i < KPW; ++i) {
-        // keep each step's work after the wait for its own weights: left
-        // free, the scheduler hoists later steps' unpacking to the top, and
-        // the first MFMA then waits for every load of the run
-        __builtin_amdgcn_sched_barrier(0);
-        const int c = i & 1;
-        if (i + 1 < KPW) load_x(i + 1, xa[c ^ 1]);
-        f32x4 ch;
+    for (int q = 0; q < XD; ++q) xa[q] = load_x(q);
+    f32x4 ch;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int gl = i * (4 / CPG) + t / CPG;  // group within this wave's run
-          const bool fresh = (t % CPG) == 0;
-          const uint32_t z = ASYM ? (zrow_l[gl] >> zshift) & 0xFu : 8u;
-          if constexpr (DT == DT_F16) {
-            const u32x4 bq = qz_word_f16(wv[i][t], mask_v, neg_magic_pair<DT>(z));  // q - z, exact
-            ch = mfma16x16x32<DT>(xa[c][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
-          } else {
-            const u32x4 bq = magic_word<DT>(wv[i][t], mask_v);  // 128 + q, exact
-            ch = mfma16x16x32<DT>(xa[c][t], bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
-          }
-          if (t % CPG == CPG - 1) {
-            const float sc = act_to_f32<DT>(srow_l[gl]);
-            if constexpr (DT == DT_BF16) {
-              // s * (x . (128 + q) - (128 + z) * xsum); -(128 + z) * s is exact
-              const float szc = -(128.0f + (float)z) * sc;
-              const float* xs = xsum + gl * 16 + 4 * row4;
+    for (int q = 0; q < NQ; ++q) {
+      const int i = q >> 2, t = q & 3;
+      // keep each step's work after the wait for its own weights: left
+      // free, the scheduler hoists later steps' unpacking to the top, and
+      // the first MFMA then waits for every load of the run
+      if (t == 0) __builtin_amdgcn_sched_barrier(0);
+      if (q + XD < NQ) xa[(q + XD) % (XD + 1)] = load_x(q + XD);
+      const u32x4 a = xa[q % (XD + 1)];
+      const int gl = i * (4 / CPG) + t / CPG;  // group within this wave's run
+      const bool fresh = (t % CPG) == 0;
+      const uint32_t z = ASYM ? (zrow_l[gl] >> zshift) & 0xFu : 8u;
+      if constexpr (DT == DT_F16) {
+        const u32x4 bq = qz_word_f16(wv[i][t], mask_v, neg_magic_pair<DT>(z));  // q - z, exact
+        ch = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
+      } else {
+        const u32x4 bq = magic_word<DT>(wv[i][t], mask_v);  // 128 + q, exact
+        ch = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
+      }
+      if (t % CPG == CPG - 1) {
+        const float sc = act_to_f32<DT>(srow_l[gl]);
+        if constexpr (DT == DT_BF16) {
+          // s * (x . (128 + q) - (128 + z) * xsum); -(128 + z) * s is exact
+          const float szc = -(128.0f + (float)z) * sc;
+          const float* xs = xsum + gl * 16 + 4 * row4;
 #pragma unroll
-              for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], __builtin_fmaf(szc, xs[r], acc[r]));
-            } else {
+          for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], __builtin_fmaf(szc, xs[r], acc[r]));
+        } else {
 #pragma unroll
-              for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], acc[r]);
-            }
-          }
+          for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], acc[r]);
         }
       }
     }
@@ -665,22 +675,31 @@ size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N) {
   return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
+// x loads per lane an instance stages: the plan gives M <= 2 at 8 k-steps per
+// wave (1 for the single-token instance) and M <= 16 at one k-step, so these
+// cover the M * 16 * kpw segments of a wave's run with no spare registers
+constexpr int small_xpt(int kpw, bool one) {
+  return one ? 2 : (kpw == 8 || kpw == 1 ? 4 : kGemvXSegsPerThread);
+}
+
 // the small kernel is instantiated per k-steps per wave, so that its
 // branch-free path covers every wave whose run is complete
 template <int DT, int GS, bool ASYM, bool MOE>
 static hipError_t launch_small(const GemvParams& prm, const GemvPlan& plan, dim3 grid, dim3 block,
                                hipStream_t s) {
-  constexpr int XPT = kGemvXSegsPerThread;
+  const bool one = plan.kpw == 8 && prm.M == 1;
+  const int xpt = one ? small_xpt(8, true) : small_xpt(plan.kpw, false);
+  if ((int64_t)prm.M * 16 * plan.kpw > 64 * xpt) return hipErrorInvalidConfiguration;
   switch (plan.kpw) {
     case 8:
-      if (prm.M == 1)
-        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, XPT, true, MOE>), grid, block, plan.lds_bytes, s, prm);
+      if (one)
+        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, true), true, MOE>), grid, block, plan.lds_bytes, s, prm);
       else
-        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, XPT, false, MOE>), grid, block, plan.lds_bytes, s, prm);
+        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, false), false, MOE>), grid, block, plan.lds_bytes, s, prm);
       break;
-    case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, XPT, false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
-    case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, XPT, false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
-    case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, XPT, false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
+    case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, small_xpt(4, false), false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
+    case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, small_xpt(2, false), false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
+    case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, small_xpt(1, false), false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
     default: return hipErrorInvalidConfiguration;
   }
   return hipGetLastError();

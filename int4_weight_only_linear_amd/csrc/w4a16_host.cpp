@@ -321,6 +321,9 @@ w4a16_status w4a16_check_args(const void* x, const int32_t* wq, const void* scal
                 (int)group_size, (long long)K);
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || M * K > INT64_MAX / 2 || N * K > INT64_MAX / 2)
     return fail(W4A16_ERR_INVALID_ARG, "problem too large");
+  if (K > w4a16::kMaxK)
+    return fail(W4A16_ERR_UNSUPPORTED, "K above %lld is not supported (the kernels' 32-bit offsets), got K=%lld",
+                (long long)w4a16::kMaxK, (long long)K);
   if (zp && N % 8)
     return fail(W4A16_ERR_INVALID_ARG, "packed zero points need N %% 8 == 0, got N=%lld", (long long)N);
   if (M == 0) return ok();
@@ -422,6 +425,9 @@ w4a16_status w4a16_moe_linear(const void* x, const int32_t* wq, const void* scal
     return fail(W4A16_ERR_UNSUPPORTED, "M * topk must be at most %lld", (long long)w4a16::kMaxGridZ);
   if ((uint64_t)N * (uint64_t)K / 2 > 0xFFFFFFFFull)
     return fail(W4A16_ERR_UNSUPPORTED, "one expert's weights must be below 4 GiB (N*K/2)");
+  if (K > w4a16::kMaxK)
+    return fail(W4A16_ERR_UNSUPPORTED, "K above %lld is not supported (the kernels' 32-bit offsets), got K=%lld",
+                (long long)w4a16::kMaxK, (long long)K);
   if (M == 0) return ok();
   if (!x || !wq || !scales || !topk_ids || !y)
     return fail(W4A16_ERR_INVALID_ARG, "x, wq, scales, topk_ids and y must not be NULL");

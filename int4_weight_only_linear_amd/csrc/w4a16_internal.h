@@ -47,6 +47,9 @@ constexpr int kGemvKStep = 128;       // k per wave step: 4 chunks of 32
 constexpr int kGemvMaxWaves = 16;     // 1024 threads
 constexpr int kGemvMaxMTiles = 4;     // M <= 64
 constexpr int kGemvStepsPerWave = 8;  // k-steps whose loads a wave keeps in flight
+// K bound: per-lane byte offsets within a row tile, and products of a row
+// index below 16 with K or a stride, stay in 24-bit / 32-bit arithmetic
+constexpr int64_t kMaxK = int64_t(1) << 24;
 constexpr int kGemvXSegsPerThread = 8;  // 16-byte x loads per thread when x is staged
 // Dynamic LDS per decode workgroup (cross-wave reduction + staged x).  The
 // kernel's LDS layout and the host's plan both size it with gemv_lds_bytes,

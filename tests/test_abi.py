@@ -113,6 +113,8 @@ def test_check_args_accepts_valid():
     (dict(g=16), 2, "group size"),
     (dict(g=256, K=512), 2, "group size"),     # neither the accept set nor K
     (dict(K=200), 1, "multiple of the group"),
+    (dict(K=(1 << 24) + 128), 2, "K above"),
+    (dict(K=1 << 25, g=1 << 25), 2, "K above"),  # per-channel
     (dict(K=64, g=128), 1, "multiple of the group"),
     (dict(N=0), 1, "N must be"),
     (dict(M=-1), 1, "M must be"),
