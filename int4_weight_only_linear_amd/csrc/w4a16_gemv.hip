@@ -495,6 +495,21 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
   }
 
   // ---- 4. reduce the waves in order, then the K ranges ----
+  if constexpr (ONE) {
+    if (p.splits == 1) {
+      // one token, one K range: the sums are register 0 of lanes 0..15
+      red[wave * 256 + lane] = acc[0];
+      __syncthreads();
+      const int nn = n0 + tid;
+      if (tid < kGemvRowsPerTile && nn < p.N) {
+        float v = 0.f;
+        for (int w = 0; w < nwaves; ++w) v += red[w * 256 + tid];
+        if (p.bias) v += act_to_f32<DT>(p.bias[nn]);
+        p.y[nn] = f32_to_act<DT>(v * p.yscale);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave * 256 + r * 64 + lane] = acc[r];
   __syncthreads();
