@@ -83,6 +83,18 @@ struct GemvParams {
   int slots;  // workgroups along z: 1, or the expert slots
 };
 
+// One 16-byte global->LDS load per active lane: lane l reads base + off and
+// writes LDS bytes lds + 16 l .. lds + 16 l + 15 (lds wave-uniform).  M0
+// holds the LDS address for the load (one wait state after it is written) and
+// is given back its value afterwards.
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, unsigned char* lds) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(off), "s"(base) : "memory");
+}
+
 // The expert slot of this workgroup (expert-indexed mode): its expert's
 // slices, its x row and output row.  False for an id outside [0, experts),
 // whose row is zero.
@@ -199,12 +211,25 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // (lanes 0..15, register 0); the other rows are then never updated.
 // MOE: expert-indexed mode (a separate instance, so that the plain layer has
 // no branch in front of its parameter loads and they arrive in one batch).
-template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE, bool MOE>
+// WGSZ (single token, bf16, groups of 128, every wave a full run of 8 k-steps,
+// one K range): the workgroup's scales and zero points are fetched once for
+// all its waves, by a few 1 KiB global->LDS loads issued first, instead of two
+// small loads per wave; every load instruction costs a CU about the same issue
+// time whatever its size, and on the large layers that issue time paces the
+// weight stream.  Each group's sum is kept in a register and scaled after the
+// run, behind one workgroup barrier.
+// At most 72 VGPRs (seven waves per SIMD, which runs the largest decode layers'
+// workgroups in one round); every instance fits without spilling.
+template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE, bool MOE, bool WGSZ>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void gemv_small_kernel(const GemvParams params) {
   constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
   constexpr int SPT = (32 * KPW) / GS > 0 ? (32 * KPW) / GS : 1;  // scale loads per lane
+  static_assert(!WGSZ || (ONE && DT == DT_BF16 && GS == 128 && KPW == 8), "WGSZ instance");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int last_flag;
+  // WGSZ: the workgroup's scales [group piece][16 rows][8 groups] (bf16), then
+  // its zero points [group quad][2 row blocks][4 groups] (packed words)
+  __shared__ __attribute__((aligned(16))) unsigned char wgsz[WGSZ ? kGemvWgSzBytes : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -253,6 +278,30 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
 
   // ---- 1. loads: x, scales and zero points of this wave's run, then weights ----
   // (each a wave-uniform base plus a 32-bit per-lane byte offset)
+  const int gwg = nwaves * ngw;  // WGSZ: groups of the workgroup's K range, 8 per wave
+  if constexpr (WGSZ) {
+    // 16-byte pieces straight to LDS: scale piece c * 16 + r is groups
+    // 8c..8c+7 of row n0 + r (one piece per wave and row), zero-point piece
+    // c * 2 + b is groups 4c..4c+3 of row block n0 / 8 + b
+    const int gw0_wg = ks_begin * (kGemvKStep / GS);
+    const int np_s = 2 * gwg, np_z = gwg / 2;
+    const int wz = min((np_s + 63) >> 6, nwaves - 1);  // the wave that loads the zero points
+    // (written as assembly, so the compiler does not take these LDS writes
+    // for possible aliases of the x staging and wait for every later load
+    // before it; they are the wave's oldest loads, so its own waits for later
+    // loads cover them, and the run's end waits for them explicitly)
+    if (64 * wave < np_s) {
+      const int pc = 64 * wave + lane;
+      if (pc < np_s) {
+        const uint32_t off = 2u * (__umul24(min(pc & 15, p.N - 1 - n0), p.sG) + (uint32_t)(gw0_wg + 8 * (pc >> 4)));
+        lds_dma16(reinterpret_cast<const char*>(p.scales + (size_t)n0 * p.sG), off, wgsz + 1024 * wave);
+      }
+    }
+    if (ASYM && wave == wz && lane < np_z) {
+      const uint32_t off = 4u * (__umul24(min(lane & 1, (p.N >> 3) - 1 - (n0 >> 3)), p.sG) + (uint32_t)(gw0_wg + 4 * (lane >> 1)));
+      lds_dma16(reinterpret_cast<const char*>(p.zp + (size_t)(n0 >> 3) * p.sG), off, wgsz + 32 * gwg);
+    }
+  }
   const int xsegs = p.M * xsegs_row;
   const int xk0 = min(kw0, p.K - 8);  // k of the x base; lanes read k = min(kw0 + 8 seg, K - 8)
   const char* xbase = reinterpret_cast<const char*>(p.x + xk0);
@@ -280,6 +329,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
   // for every earlier load -- x -- before the weights are issued)
   u32x4 srv;
   uint32_t sr[SPT];
+  uint32_t zr = 0u;
+  if constexpr (!WGSZ) {
   const char* sbase = reinterpret_cast<const char*>(p.scales + (size_t)n0 * p.sG);  // row n0
   const int last_dr = p.N - 1 - n0;  // rows past N read row N - 1
   if (svec) {
@@ -298,7 +349,6 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
       sr[j] = *reinterpret_cast<const uint16_t*>(sbase + off);
     }
   }
-  uint32_t zr = 0u;
   if constexpr (ASYM) {
     const int e = min(lane, 2 * ngw - 1);
     const int rr = e >> lg_ngw;
@@ -306,6 +356,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
     const char* zbase = reinterpret_cast<const char*>(p.zp + (size_t)(n0 >> 3) * p.sG);
     const uint32_t off = 4u * (__umul24(min(rr, (p.N >> 3) - 1 - (n0 >> 3)), p.sG) + __umul24(g, p.gmul));
     zr = *reinterpret_cast<const uint32_t*>(zbase + off);
+  }
   }
   __builtin_amdgcn_sched_barrier(0);
   // weights: a wave-uniform base per k-step plus one per-lane offset, so each
@@ -332,18 +383,20 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
       *reinterpret_cast<u32x4*>(xs + m * xstride + ((e & (xsegs_row - 1)) << 3)) = xr[j];
     }
   }
-  if (svec) {
-    // lane = row * (ngw / 8) + piece holds scales row * ngw + 8 * piece ...
-    if (lane < 2 * ngw) *reinterpret_cast<u32x4*>(sl + 8 * lane) = srv;
-  } else {
+  if constexpr (!WGSZ) {
+    if (svec) {
+      // lane = row * (ngw / 8) + piece holds scales row * ngw + 8 * piece ...
+      if (lane < 2 * ngw) *reinterpret_cast<u32x4*>(sl + 8 * lane) = srv;
+    } else {
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-      const int e = lane + 64 * j;
-      if (e < 16 * ngw) sl[e] = (uint16_t)sr[j];
+      for (int j = 0; j < SPT; ++j) {
+        const int e = lane + 64 * j;
+        if (e < 16 * ngw) sl[e] = (uint16_t)sr[j];
+      }
     }
-  }
-  if constexpr (ASYM) {
-    if (lane < 2 * ngw) zl[lane] = zr;
+    if constexpr (ASYM) {
+      if (lane < 2 * ngw) zl[lane] = zr;
+    }
   }
   if constexpr (DT == DT_BF16) {
     // sum of x over every group of the run, per token (zero past M): the
@@ -430,7 +483,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
     }
   };
 
-  if (my_steps == KPW && (my_first + KPW) * 4 <= p.nchunks) {
+  // (a WGSZ launch has only such waves: the host checks that K is a whole
+  // number of 8-step runs of 128 and that there is one K range)
+  if (WGSZ || (my_steps == KPW && (my_first + KPW) * 4 <= p.nchunks)) {
     // Common case: the wave's whole run is complete 128-k runs.  Branch-free
     // and software pipelined by 32-k chunks: the x fragment of chunk q + XD
     // is read from LDS while chunk q is multiplied (a ring of XD + 1
@@ -447,6 +502,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
 #pragma unroll
     for (int q = 0; q < XD; ++q) xa[q] = load_x(q);
     f32x4 ch;
+    constexpr int NG = WGSZ ? 4 * KPW / CPG : 1;
+    float chg[NG];  // WGSZ: each group's sum x . (128 + q), scaled after the run
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int i = q >> 2, t = q & 3;
@@ -458,7 +515,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
       const u32x4 a = xa[q % (XD + 1)];
       const int gl = i * (4 / CPG) + t / CPG;  // group within this wave's run
       const bool fresh = (t % CPG) == 0;
-      const uint32_t z = ASYM ? (zrow_l[gl] >> zshift) & 0xFu : 8u;
+      const uint32_t z = (ASYM && !WGSZ) ? (zrow_l[gl] >> zshift) & 0xFu : 8u;
       if constexpr (DT == DT_F16) {
         const u32x4 bq = qz_word_f16(wv[i][t], mask_v, neg_magic_pair<DT>(z));  // q - z, exact
         ch = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
@@ -467,17 +524,40 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
         ch = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
       }
       if (t % CPG == CPG - 1) {
-        const float sc = act_to_f32<DT>(srow_l[gl]);
-        if constexpr (DT == DT_BF16) {
-          // s * (x . (128 + q) - (128 + z) * xsum); -(128 + z) * s is exact
-          const float szc = -(128.0f + (float)z) * sc;
-          const float* xs = xsum + gl * 16 + 4 * row4;
-#pragma unroll
-          for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], __builtin_fmaf(szc, xs[r], acc[r]));
+        if constexpr (WGSZ) {
+          chg[gl] = ch[0];
         } else {
+          const float sc = act_to_f32<DT>(srow_l[gl]);
+          if constexpr (DT == DT_BF16) {
+            // s * (x . (128 + q) - (128 + z) * xsum); -(128 + z) * s is exact
+            const float szc = -(128.0f + (float)z) * sc;
+            const float* xs = xsum + gl * 16 + 4 * row4;
 #pragma unroll
-          for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], acc[r]);
+            for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], __builtin_fmaf(szc, xs[r], acc[r]));
+          } else {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(sc, ch[r], acc[r]);
+          }
         }
+      }
+    }
+    if constexpr (WGSZ) {
+      // the workgroup's scales and zero points have landed (every wave waits
+      // for its own global->LDS loads, then the barrier); then the groups in
+      // run order, the same operations in the same order as applying each
+      // group at its end
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* ssh = reinterpret_cast<const uint16_t*>(wgsz) + (wave * 16 + col) * 8;
+      const uint32_t* zsh = reinterpret_cast<const uint32_t*>(wgsz + 32 * gwg);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float sc = act_to_f32<DT>(ssh[g]);
+        const int gw = wave * NG + g;  // group within the workgroup's range
+        const uint32_t z = ASYM ? (zsh[((gw >> 2) * 2 + (col >> 3)) * 4 + (gw & 3)] >> zshift) & 0xFu : 8u;
+        const float szc = -(128.0f + (float)z) * sc;
+        acc[0] = __builtin_fmaf(sc, chg[g], __builtin_fmaf(szc, xsum[g * 16 + 4 * row4], acc[0]));
       }
     }
   } else {
@@ -705,16 +785,31 @@ static hipError_t launch_small(const GemvParams& prm, const GemvPlan& plan, dim3
   const bool one = plan.kpw == 8 && prm.M == 1;
   const int xpt = one ? small_xpt(8, true) : small_xpt(plan.kpw, false);
   if ((int64_t)prm.M * 16 * plan.kpw > 64 * xpt) return hipErrorInvalidConfiguration;
+  // the workgroup-shared scale / zero-point instance: every wave a full run
+  // of 8 k-steps in one K range, and 16-byte pieces of scales and zero points
+  const auto aligned16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool wgsz = DT == DT_BF16 && GS == 128 && one && plan.splits == 1 && prm.gmul == 1 &&
+                    plan.ksteps == 8 * plan.waves && plan.waves <= kGemvMaxWaves &&
+                    (prm.sG & 7) == 0 && aligned16(prm.scales) && (!prm.zp || aligned16(prm.zp)) &&
+                    (!MOE || ((prm.s_estride & 7) == 0 && (prm.z_estride & 3) == 0)) &&
+                    std::getenv("W4A16_GEMV_NO_WGSZ") == nullptr;
   switch (plan.kpw) {
     case 8:
-      if (one)
-        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, true), true, MOE>), grid, block, plan.lds_bytes, s, prm);
-      else
-        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, false), false, MOE>), grid, block, plan.lds_bytes, s, prm);
+      if (one) {
+        if constexpr (DT == DT_BF16 && GS == 128) {
+          if (wgsz) {
+            hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, true), true, MOE, true>), grid, block, plan.lds_bytes, s, prm);
+            break;
+          }
+        }
+        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, true), true, MOE, false>), grid, block, plan.lds_bytes, s, prm);
+      } else {
+        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm);
+      }
       break;
-    case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, small_xpt(4, false), false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
-    case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, small_xpt(2, false), false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
-    case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, small_xpt(1, false), false, MOE>), grid, block, plan.lds_bytes, s, prm); break;
+    case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, small_xpt(4, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm); break;
+    case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, small_xpt(2, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm); break;
+    case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, small_xpt(1, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm); break;
     default: return hipErrorInvalidConfiguration;
   }
   return hipGetLastError();

@@ -46,7 +46,10 @@ constexpr int kGemvRowsPerTile = 16;
 constexpr int kGemvKStep = 128;       // k per wave step: 4 chunks of 32
 constexpr int kGemvMaxWaves = 16;     // 1024 threads
 constexpr int kGemvMaxMTiles = 4;     // M <= 64
-constexpr int kGemvStepsPerWave = 8;  // k-steps whose loads a wave keeps in flight
+constexpr int kGemvStepsPerWave = 8;
+// decode, single token bf16 g128: the workgroup's scales (16 rows x 8 groups
+// per wave, bf16) and packed zero points (2 row blocks x 8 groups per wave)
+constexpr int kGemvWgSzBytes = kGemvMaxWaves * (16 * 8 * 2 + 2 * 8 * 4);  // k-steps whose loads a wave keeps in flight
 // K bound: per-lane byte offsets within a row tile, and products of a row
 // index below 16 with K or a stride, stay in 24-bit / 32-bit arithmetic
 constexpr int64_t kMaxK = int64_t(1) << 24;

@@ -121,6 +121,26 @@ def test_linear_grid(M, N, K, g, dt, sym, bias):
         assert_close(d.run(path), ref, dt, f"path {path}")
 
 
+@pytest.mark.parametrize("N,K,sym,bias", [
+    (1032, 1024, False, True),    # one wave per workgroup, incomplete last row tile
+    (1024, 4096, False, False),   # four waves
+    (1048, 14336, True, True),    # fourteen waves, incomplete last row tile
+    (1024, 16384, False, False),  # sixteen waves, the most a workgroup has
+])
+def test_decode_workgroup_scales(monkeypatch, N, K, sym, bias):
+    # one token, bf16, groups of 128, K a whole number of 8-step runs and one
+    # K range: the instance whose workgroup fetches all its waves' scales and
+    # zero points at once.  Same arithmetic in the same order as the per-wave
+    # instance (bit-identical), and within tolerance of the oracle.
+    c = make_case(1, N, K, 128, O.BF16, sym, bias, seed=("wgsz", N, K, sym, bias))
+    d = DeviceCase(c)
+    y_shared = d.run(GEMV)
+    monkeypatch.setenv("W4A16_GEMV_NO_WGSZ", "1")
+    y_wave = d.run(GEMV)
+    assert np.array_equal(y_shared, y_wave)
+    assert_close(y_shared, oracle_rows(c), O.BF16, "workgroup scales")
+
+
 def test_ragged_n_not_multiple_of_eight_symmetric():
     # symmetric weights allow any N; N = 13 leaves a partial row tile
     for dt in (O.F16, O.BF16):
