@@ -4,7 +4,8 @@
 
 Every translation unit is compiled in parallel to an object under ``_build/``
 and linked into ``int4_weight_only_linear_amd/libw4a16.so``.  All device
-code is compiled without packed-fp32 instruction selection.
+code is compiled without packed-fp32 instruction selection; the decode kernels
+with kernel-argument preloading.
 """
 from __future__ import annotations
 
@@ -30,6 +31,8 @@ COMMON = [
 ]
 SOURCES = ["w4a16_host.cpp", "w4a16_gemv.hip", "w4a16_gemm.hip", "w4a16_elementwise.hip",
            "w4a16_blas.cpp"]
+# the decode kernel takes its first ten arguments preloaded into SGPRs
+EXTRA = {"w4a16_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
 
 
 def _hipcc() -> str:
@@ -41,7 +44,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

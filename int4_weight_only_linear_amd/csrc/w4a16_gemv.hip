@@ -220,8 +220,16 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // run, behind one workgroup barrier.
 // At most 72 VGPRs (seven waves per SIMD, which runs the largest decode layers'
 // workgroups in one round); every instance fits without spilling.
+// The leading scalar arguments are everything the loads in front of the run
+// need; this file is compiled with kernel-argument preloading, so they arrive
+// in SGPRs when the wave starts instead of after a scalar load from the
+// argument segment (gfx950 preloads plain arguments, not the parameter
+// struct).  The other fields that the loads need are derived from them.
 template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE, bool MOE, bool WGSZ>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void gemv_small_kernel(const GemvParams params) {
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void gemv_small_kernel(const uint16_t* a_x, const uint32_t* a_wq,
+                                                          const uint16_t* a_scales, const uint32_t* a_zp,
+                                                          int a_M, int a_N, int a_K, int a_sG, int a_gmul,
+                                                          int a_kps, const GemvParams params) {
   constexpr int CPG = GS / 32;          // 32-k chunks per group (1, 2, 4)
   constexpr int SPT = (32 * KPW) / GS > 0 ? (32 * KPW) / GS : 1;  // scale loads per lane
   static_assert(!WGSZ || (ONE && DT == DT_BF16 && GS == 128 && KPW == 8), "WGSZ instance");
@@ -234,6 +242,25 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   GemvParams p = params;
+  p.x = a_x;
+  p.wq = a_wq;
+  p.scales = a_scales;
+  p.zp = a_zp;
+  p.M = a_M;
+  p.N = a_N;
+  p.K = a_K;
+  p.sG = a_sG;
+  p.gmul = a_gmul;
+  p.ksteps_per_split = a_kps;
+  // as the host sets them (the plan's k-steps per wave is KPW)
+  p.G = a_K / GS;
+  p.nchunks = a_K >> 5;
+  p.ksteps = (p.nchunks + 3) >> 2;
+  p.kpw = KPW;
+  p.waves = (a_kps + KPW - 1) / KPW;
+  p.lg_xsegs_per_wave = __builtin_ctz(KPW * (kGemvKStep / 8));
+  p.lg_groups_per_wave = __builtin_ctz(KPW * kGemvKStep / GS > 0 ? KPW * kGemvKStep / GS : 1);
+  p.wave_lds_bytes = gemv_wave_lds_bytes(a_M, KPW, GS);
   if constexpr (MOE) {
     if (!select_slot(p)) {
       // not an expert: a zero row (the whole workgroup leaves here)
@@ -697,21 +724,10 @@ __global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
 
 // one wave's staging region of the M <= 16 kernel: x rows of its run (padded
 // by 16 bytes), the scales of its 16 rows and groups, the zero-point words
-size_t gemv_wave_lds_bytes(int64_t M, int kpw, int group) {
-  const size_t kr = (size_t)kpw * kGemvKStep;
-  const size_t ngr = kr / (size_t)group;
-  size_t b = (size_t)M * (kr + 8) * sizeof(uint16_t) + 16 * ngr * sizeof(uint16_t) +
-             2 * ngr * sizeof(uint32_t);
-  b = (b + 15) / 16 * 16;
-  // per-token x sums: 16-k partials, then one per group and token (padded to 16)
-  b += (size_t)M * (kr / 16) * sizeof(float) + ngr * 16 * sizeof(float);
-  return (b + 15) / 16 * 16;
-}
-
 size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int kpw, int group) {
   const size_t red = (size_t)waves * mtiles * 256 * sizeof(float);
   if (mtiles > 1) return red;
-  return red + (size_t)waves * gemv_wave_lds_bytes(M, kpw, group);
+  return red + (size_t)waves * (size_t)gemv_wave_lds_bytes((int)M, kpw, group);
 }
 
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
@@ -798,18 +814,18 @@ static hipError_t launch_small(const GemvParams& prm, const GemvPlan& plan, dim3
       if (one) {
         if constexpr (DT == DT_BF16 && GS == 128) {
           if (wgsz) {
-            hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, true), true, MOE, true>), grid, block, plan.lds_bytes, s, prm);
+            hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, true), true, MOE, true>), grid, block, plan.lds_bytes, s, prm.x, prm.wq, prm.scales, prm.zp, prm.M, prm.N, prm.K, prm.sG, prm.gmul, prm.ksteps_per_split, prm);
             break;
           }
         }
-        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, true), true, MOE, false>), grid, block, plan.lds_bytes, s, prm);
+        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, true), true, MOE, false>), grid, block, plan.lds_bytes, s, prm.x, prm.wq, prm.scales, prm.zp, prm.M, prm.N, prm.K, prm.sG, prm.gmul, prm.ksteps_per_split, prm);
       } else {
-        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm);
+        hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm.x, prm.wq, prm.scales, prm.zp, prm.M, prm.N, prm.K, prm.sG, prm.gmul, prm.ksteps_per_split, prm);
       }
       break;
-    case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, small_xpt(4, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm); break;
-    case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, small_xpt(2, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm); break;
-    case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, small_xpt(1, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm); break;
+    case 4: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 4, small_xpt(4, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm.x, prm.wq, prm.scales, prm.zp, prm.M, prm.N, prm.K, prm.sG, prm.gmul, prm.ksteps_per_split, prm); break;
+    case 2: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 2, small_xpt(2, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm.x, prm.wq, prm.scales, prm.zp, prm.M, prm.N, prm.K, prm.sG, prm.gmul, prm.ksteps_per_split, prm); break;
+    case 1: hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 1, small_xpt(1, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm.x, prm.wq, prm.scales, prm.zp, prm.M, prm.N, prm.K, prm.sG, prm.gmul, prm.ksteps_per_split, prm); break;
     default: return hipErrorInvalidConfiguration;
   }
   return hipGetLastError();
@@ -912,7 +928,7 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
     lg = 0;
     while ((1 << lg) < plan.kpw * kGemvKStep / a.group) ++lg;
     prm.lg_groups_per_wave = lg;
-    prm.wave_lds_bytes = (int)gemv_wave_lds_bytes(a.M, plan.kpw, a.group);
+    prm.wave_lds_bytes = gemv_wave_lds_bytes((int)a.M, plan.kpw, a.group);
   }
   return a.dtype == DT_F16 ? launch_m<DT_F16>(prm, a.group, plan, stream)
                            : launch_m<DT_BF16>(prm, a.group, plan, stream);

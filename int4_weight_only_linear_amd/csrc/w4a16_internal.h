@@ -75,7 +75,18 @@ struct GemvPlan {
   size_t lds_bytes;      // dynamic LDS of one workgroup
 };
 
-size_t gemv_wave_lds_bytes(int64_t M, int kpw, int group);
+// LDS bytes of one wave's staging region (M <= 16 kernel): x [M][kpw*128 + 8]
+// halves, scales [16][groups] halves, zero points [2][groups] words, then
+// fp32 x partial sums (16 k each) and per-group x sums [groups][16].  The
+// kernel recomputes it from M, kpw and the group, so host and device share it.
+__host__ __device__ inline int gemv_wave_lds_bytes(int M, int kpw, int group) {
+  const int kr = kpw * kGemvKStep;
+  const int ngr = kr / group;
+  int b = M * (kr + 8) * 2 + 16 * ngr * 2 + 2 * ngr * 4;
+  b = (b + 15) / 16 * 16;
+  b += M * (kr / 16) * 4 + ngr * 16 * 4;
+  return (b + 15) / 16 * 16;
+}
 size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int kpw, int group);
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N);
