@@ -617,6 +617,21 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
       return;
     }
   }
+  if (p.splits == 1 && p.M <= 4) {
+    // up to four tokens, one K range: token m's sums are register m of lanes
+    // 0..15 (the general path's order: waves in order, then bias, rounding)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave * 256 + r * 64 + lane] = acc[r];
+    __syncthreads();
+    const int m = tid >> 4, nn = n0 + (tid & 15);
+    if (tid < 16 * p.M && nn < p.N) {
+      float v = 0.f;
+      for (int w = 0; w < nwaves; ++w) v += red[w * 256 + m * 64 + (tid & 15)];
+      if (p.bias) v += act_to_f32<DT>(p.bias[nn]);
+      p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v * p.yscale);
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave * 256 + r * 64 + lane] = acc[r];
   __syncthreads();
