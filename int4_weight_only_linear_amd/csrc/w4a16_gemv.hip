@@ -768,13 +768,12 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
     if (v >= 1 && v <= kpw && (v & (v - 1)) == 0) kpw = v;
   }
   p.kpw = kpw;
-  // A K split costs a partial-sum hand-off (~2 us of memory round trips), more
-  // than it saves by filling idle CUs: measured on 160-tile layers, no split
-  // is 30-40 % faster.  So K is split only when fewer than a quarter of the
-  // CUs would get a row tile, or (below) when a workgroup's waves or LDS
-  // demand it (at most kGemvMaxWaves waves, LDS within the budget).
+  // A K split costs a partial-sum hand-off (2-4 us of coherent memory round
+  // trips), more than it saves by filling idle CUs: measured at M = 1 on
+  // 16-160-tile layers (K = 2560-14336), no split is 10-70 % faster.  So K is
+  // split only (below) when a workgroup's waves or LDS demand it (at most
+  // kGemvMaxWaves waves, LDS within the budget).
   int splits = 1;
-  if (4 * p.tiles < cu_count && p.tiles <= kMaxCounters) splits = (cu_count + p.tiles - 1) / p.tiles;
   if (const char* env = std::getenv("W4A16_GEMV_SPLITS")) {
     const int v = std::atoi(env);
     if (v >= 1 && (v == 1 || p.tiles <= kMaxCounters)) splits = v;  // raised below if it must be

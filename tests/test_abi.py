@@ -182,8 +182,10 @@ def test_workspace_size():
     assert L.w4a16_workspace_size(1, 28672, 4096, 128, 1, 1) == 0
     # 160 row tiles: not split (a split costs more than the idle CUs)
     assert L.w4a16_workspace_size(1, 2560, 4096, 128, 0, 0) == 0
-    # 3 row tiles: split across the CUs
-    assert L.w4a16_workspace_size(1, 40, 4096, 128, 1, 1) > 0
+    # 3 row tiles: not split either (the hand-off costs more than idle CUs)
+    assert L.w4a16_workspace_size(1, 40, 4096, 128, 1, 1) == 0
+    # more k-steps than 16 waves of 8 take (K = 20480: 160 steps): K is split
+    assert L.w4a16_workspace_size(1, 40, 20480, 128, 1, 1) > 0
     # more k-steps than one workgroup's waves take (M = 4: 4 steps a wave, 76
     # steps): K is split and the workspace holds counters + partials
     ws = L.w4a16_workspace_size(4, 2560, 9728, 128, 0, 0)

@@ -226,7 +226,8 @@ def test_power_of_two_scaling_is_exact(path):
 
 
 def test_determinism_with_split_k():
-    # N = 2560 gives fewer row tiles than CUs, so K is split across workgroups
+    # M = 4 takes 4 k-steps a wave: K = 9728 (76 steps) needs more than 16
+    # waves, so K is split across two workgroups
     c = make_case(4, 2560, 9728, 128, O.BF16, False, False, seed=("det",))
     d = DeviceCase(c)
     a = d.run(GEMV)
@@ -238,7 +239,8 @@ def test_determinism_with_split_k():
 def test_workspace_reuse_across_shapes():
     # one workspace shared by split-K calls of different shapes, in an order
     # where a later call's counters sit where an earlier call's partial sums were
-    shapes = [(5, 264, 4096, 128), (4, 2560, 9728, 128), (2, 40, 1024, 64), (3, 1024, 4096, 32)]
+    # (every shape needs more than 16 waves for one K range, so each is split)
+    shapes = [(5, 264, 9728, 128), (4, 2560, 9728, 128), (2, 40, 20480, 64), (3, 1024, 12288, 32)]
     cases = [make_case(M, N, K, g, O.BF16, False, False, seed=("reuse", M, N, K, g))
              for (M, N, K, g) in shapes]
     devs = [DeviceCase(c) for c in cases]
@@ -249,15 +251,16 @@ def test_workspace_reuse_across_shapes():
 
 
 def test_workspace_errors():
-    # 40 rows are 3 row tiles: the decode kernel splits K and needs a workspace
-    c = make_case(1, 40, 9728, 128, O.BF16, False, False, seed=("ws",))
+    # K = 20480 needs more than 16 waves of 8 k-steps: the decode kernel splits
+    # K and needs a workspace
+    c = make_case(1, 40, 20480, 128, O.BF16, False, False, seed=("ws",))
     d = DeviceCase(c)
-    need = L.w4a16_workspace_size(1, 40, 9728, 128, O.BF16, True, GEMV)
+    need = L.w4a16_workspace_size(1, 40, 20480, 128, O.BF16, True, GEMV)
     assert need > 0
     y = torch.empty((1, 40), dtype=torch.bfloat16, device="cuda")
     from int4_weight_only_linear_amd import _binding as B
     st = B.lib.w4a16_linear_path(d.x.data_ptr(), d.wq.data_ptr(), d.s.data_ptr(), d.zp.data_ptr(),
-                                 None, y.data_ptr(), 1, 40, 9728, 128, O.BF16, None, 0,
+                                 None, y.data_ptr(), 1, 40, 20480, 128, O.BF16, None, 0,
                                  torch.cuda.current_stream().cuda_stream, GEMV)
     assert st == 6 and "workspace" in L.w4a16_last_error()
 
@@ -443,7 +446,7 @@ def _graph_replays_match(run_eager, run_captured, reps=3):
 
 @pytest.mark.parametrize("M,N,K,g,path,tile", [
     (1, 4096, 4096, 128, GEMV, None),        # decode, no split
-    (3, 40, 4096, 64, GEMV, None),           # decode, K split (workspace counters)
+    (3, 40, 9728, 64, GEMV, None),           # decode, K split (workspace counters)
     (130, 200, 640, 64, GEMM, "4,3,0"),      # GEMM, last-workgroup hand-off
     (128, 264, 1216, 32, GEMM, "4,4,1"),     # GEMM, two-pass split
     (300, 520, 1024, 128, GEMM, None),       # GEMM, no split
