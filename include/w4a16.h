@@ -125,9 +125,10 @@ w4a16_status w4a16_check_args(const void* x, const int32_t* wq, const void* scal
                               int32_t dtype);
 
 /* The path W4A16_PATH_AUTO resolves to for this problem (host only): the
- * decode kernel for M <= 8, the GEMM above (the crossover measured on
- * MI355X).  Environment overrides: W4A16_M_THRESHOLD=<m> moves the bound,
- * W4A16_FORCE_PATH=gemv|gemm forces one path. */
+ * decode kernel for M <= 16 when K <= 4096 and for M <= 8 otherwise, the GEMM
+ * above (the crossover measured on MI355X).  Environment overrides:
+ * W4A16_M_THRESHOLD=<m> moves the bound, W4A16_FORCE_PATH=gemv|gemm forces
+ * one path. */
 w4a16_path w4a16_select_path(int64_t M, int64_t N, int64_t K, int32_t group_size,
                              int32_t dtype, int32_t has_zp);
 

@@ -110,17 +110,20 @@ GroupMap group_map(int32_t g, int64_t K) {
 }
 
 // Decode-kernel threshold.  The pages route M <= 5 to their skinny kernel
-// (tuned on RDNA).  On MI355X the decode kernel beats the GEMM up to M = 8
-// at every shape, group, quantisation and dtype of the crossover sweep, and
-// the GEMM (with its two-pass K split at small M) wins from M = 16 in 23 of
-// the 24, so the constant is measured, not theirs.
+// (tuned on RDNA).  On MI355X (crossover sweep: 4096x14336 and 28672x4096,
+// groups 32/64/128, symmetric and asymmetric, fp16 and bf16) the decode
+// kernel beats the GEMM up to M = 8 at every point but one (a 1 % tie); at
+// M = 16 it still wins in 10 of the 12 K = 4096 combinations (by up to 22 %;
+// it loses bf16 g128 by 1-3 %) but in only 1 of the 12 K = 28672 ones; from
+// M = 32 the GEMM wins everywhere.  So the bound is 16 for K <= 4096 and 8
+// above, measured, not the pages'.
 int64_t gemv_threshold(int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t has_zp) {
-  (void)N; (void)K; (void)group; (void)dtype; (void)has_zp;
+  (void)N; (void)group; (void)dtype; (void)has_zp;
   if (const char* env = std::getenv("W4A16_M_THRESHOLD")) {
     const long v = std::strtol(env, nullptr, 10);
     if (v >= 0 && v <= W4A16_GEMV_MAX_M) return v;
   }
-  return 8;
+  return K <= 4096 ? 16 : 8;
 }
 
 w4a16_path resolve_path(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,

@@ -164,10 +164,15 @@ def test_zero_point_dtype_message_is_the_pages():
 # ---- path selection and workspace sizing (host logic) -----------------------
 
 def test_select_path_by_m():
-    for M in (1, 2, 5, 8):
+    # K <= 4096: the decode kernel up to M = 16; larger K: up to M = 8
+    for M in (1, 2, 5, 8, 9, 16):
         assert L.w4a16_select_path(M, 4096, 4096, 128, 1, 1) == L.PATH_GEMV
-    for M in (9, 16, 32, 65, 128, 1920):
+    for M in (17, 32, 65, 128, 1920):
         assert L.w4a16_select_path(M, 4096, 4096, 128, 1, 1) == L.PATH_GEMM
+    for M in (1, 5, 8):
+        assert L.w4a16_select_path(M, 4096, 14336, 128, 1, 1) == L.PATH_GEMV
+    for M in (9, 16, 32, 1920):
+        assert L.w4a16_select_path(M, 4096, 14336, 128, 1, 1) == L.PATH_GEMM
 
 
 def test_select_path_env_override(monkeypatch):
