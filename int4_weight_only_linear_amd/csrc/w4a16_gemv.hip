@@ -28,12 +28,16 @@
 //   contiguous runs of k-steps and issue every load up front, x and the
 //   per-group scales and zero points first (staged in LDS, coalesced), then
 //   the weights; each k-step waits only for its own weights, so the dot
-//   products of early k-steps overlap the arrival of later ones.
-// * The host splits K across workgroups when there are fewer row tiles than
-//   CUs, or when a K range would not fit the LDS budget; so there is no limit
-//   on K * M (the pages' converged kernel likewise streams the overflow from
-//   global, "[ROCm] Converge the two W4A16 linear kernels onto the upstream
-//   shell", "What this does").
+//   products of early k-steps overlap the arrival of later ones.  Every CU
+//   pays roughly the same issue time per load instruction whatever its size,
+//   so the loads are few and wide: 1 KiB weight and x loads, and (single
+//   token, bf16, groups of 128) one workgroup-wide fetch of the scales and
+//   zero points instead of two small loads per wave.
+// * The host splits K across workgroups only when a K range needs more than
+//   16 waves or the LDS budget: the partial-sum hand-off costs more than idle
+//   CUs.  So there is no limit on K * M (the pages' converged kernel likewise
+//   streams the overflow from global, "[ROCm] Converge the two W4A16 linear
+//   kernels onto the upstream shell", "What this does").
 // * Waves are reduced through LDS in wave order; with several K ranges per
 //   row tile the partial sums go through the workspace and the last workgroup
 //   to arrive adds them in range order.  Results do not depend on scheduling.
