@@ -215,6 +215,10 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // (lanes 0..15, register 0); the other rows are then never updated.
 // MOE: expert-indexed mode (a separate instance, so that the plain layer has
 // no branch in front of its parameter loads and they arrive in one batch).
+constexpr int small_waves_per_simd(int kpw, bool one, int gs) {
+  return kpw == 8 && !one && gs == 32 ? 6 : 7;
+}
+
 // WGSZ (single token, bf16, groups of 128, every wave a full run of 8 k-steps,
 // one K range): the workgroup's scales and zero points are fetched once for
 // all its waves, by a few 1 KiB global->LDS loads issued first, instead of two
@@ -223,14 +227,15 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // weight stream.  Each group's sum is kept in a register and scaled after the
 // run, behind one workgroup barrier.
 // At most 72 VGPRs (seven waves per SIMD, which runs the largest decode layers'
-// workgroups in one round); every instance fits without spilling.
+// workgroups in one round), 80 for the two-token g32 instance, which spills
+// at 72; every instance fits without spilling.
 // The leading scalar arguments are everything the loads in front of the run
 // need; this file is compiled with kernel-argument preloading, so they arrive
 // in SGPRs when the wave starts instead of after a scalar load from the
 // argument segment (gfx950 preloads plain arguments, not the parameter
 // struct).  The other fields that the loads need are derived from them.
 template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE, bool MOE, bool WGSZ>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void gemv_small_kernel(const uint16_t* a_x, const uint32_t* a_wq,
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_waves_per_simd(KPW, ONE, GS)))) void gemv_small_kernel(const uint16_t* a_x, const uint32_t* a_wq,
                                                           const uint16_t* a_scales, const uint32_t* a_zp,
                                                           int a_M, int a_N, int a_K, int a_sG, int a_gmul,
                                                           int a_kps, const GemvParams params) {
