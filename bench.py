@@ -467,8 +467,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: libw4a16 has no multi-GPU path in this build "
-              "(the row- and column-parallel sharding of the layer is described, not built). "
+        print("bench.py measures one GPU only: libw4a16 has no multi-GPU path (row- and "
+              "column-parallel sharding of the layer is a design, not code). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
