@@ -43,6 +43,10 @@
  * (q - z) * s, accumulates in fp32, adds the bias in fp32 and rounds each
  * output once, to nearest-even, to the activation dtype.  w4a16_dequant
  * returns (q - z) * s rounded once, to nearest-even, to the activation dtype.
+ * Range: with bf16, the prefill GEMM (the path taken above the decode
+ * threshold) forms q * s as (q * 2^-9) * (s * 2^9), so it needs
+ * |s| < 2^119 (s * 2^9 finite); a larger scale gives a non-finite output
+ * there.  Every other path, and w4a16_dequant, takes any finite scale.
  *
  * Conventions shared by every entry point:
  *   - The caller owns every buffer.  The library keeps no pointer after a

@@ -25,6 +25,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -237,9 +238,17 @@ __device__ __forceinline__ uint32_t mask_nibbles(uint32_t v) {
 //         need at most 4 + 8 significant bits, so both and their difference
 //         (q - z) * s are exact in fp32, and one nearest-even conversion per
 //         pair rounds them to bf16.
+//   bf16, FP8Q: the masked bytes are read as OCP e4m3 numbers instead: a
+//         byte b in [0, 15] is exactly b * 2^-9 (b < 8 are the subnormals,
+//         b >= 8 the lowest normal binade, both spaced 2^-9), and one
+//         v_cvt_pk_f32_fp8 converts two of them, where the byte form takes
+//         one instruction per code (19 VALU per word instead of 23).  With
+//         s_f32 = s * 2^9 the fma's exact product is again q * s, so the
+//         result is bit-identical as long as s * 2^9 is finite (|s| < 2^119).
 // s_pair: the scale in both halves and nmz_pair = -(magic + z) in both halves
-// (fp16); s_f32 = s and c_f32 = -z * s (bf16).
-template <int DT>
+// (fp16); s_f32 = s (s * 2^9 with FP8Q) and c_f32 = -z * s (bf16); the
+// constants come from group_const<DT, FP8Q>.
+template <int DT, bool FP8Q = false>
 __device__ __forceinline__ u32x4 dequant_word(uint32_t w, uint32_t s_pair, uint32_t nmz_pair,
                                               float s_f32, float c_f32) {
   if constexpr (DT == DT_F16) {
@@ -260,13 +269,26 @@ __device__ __forceinline__ u32x4 dequant_word(uint32_t w, uint32_t s_pair, uint3
     // byte conversion back into a per-nibble bitfield extract
     const uint32_t ev = mask_nibbles(w);
     const uint32_t od = mask_nibbles(w >> 4);
-    auto f = [&](uint32_t v, int b) {
-      return __builtin_fmaf((float)((v >> (8 * b)) & 0xFFu), s_f32, c_f32);
-    };
-    return u32x4{f32x2_to_act_pair<DT_BF16>(f(ev, 0), f(ev, 2)),
-                 f32x2_to_act_pair<DT_BF16>(f(od, 0), f(od, 2)),
-                 f32x2_to_act_pair<DT_BF16>(f(ev, 1), f(ev, 3)),
-                 f32x2_to_act_pair<DT_BF16>(f(od, 1), f(od, 3))};
+    if constexpr (!FP8Q) {
+      auto f = [&](uint32_t v, int b) {
+        return __builtin_fmaf((float)((v >> (8 * b)) & 0xFFu), s_f32, c_f32);
+      };
+      return u32x4{f32x2_to_act_pair<DT_BF16>(f(ev, 0), f(ev, 2)),
+                   f32x2_to_act_pair<DT_BF16>(f(od, 0), f(od, 2)),
+                   f32x2_to_act_pair<DT_BF16>(f(ev, 1), f(ev, 3)),
+                   f32x2_to_act_pair<DT_BF16>(f(od, 1), f(od, 3))};
+    } else {
+      // bytes (0, 1) and (2, 3) of each masked word
+      const f32x2 e0 = __builtin_amdgcn_cvt_pk_f32_fp8(ev, false);
+      const f32x2 e1 = __builtin_amdgcn_cvt_pk_f32_fp8(ev, true);
+      const f32x2 o0 = __builtin_amdgcn_cvt_pk_f32_fp8(od, false);
+      const f32x2 o1 = __builtin_amdgcn_cvt_pk_f32_fp8(od, true);
+      auto f = [&](float q) { return __builtin_fmaf(q, s_f32, c_f32); };
+      return u32x4{f32x2_to_act_pair<DT_BF16>(f(e0[0]), f(e1[0])),
+                   f32x2_to_act_pair<DT_BF16>(f(o0[0]), f(o1[0])),
+                   f32x2_to_act_pair<DT_BF16>(f(e0[1]), f(e1[1])),
+                   f32x2_to_act_pair<DT_BF16>(f(o0[1]), f(o1[1]))};
+    }
   }
 }
 
@@ -279,13 +301,14 @@ struct GroupConst {
   float c_f32;
 };
 
-template <int DT>
+template <int DT, bool FP8Q = false>
 __device__ __forceinline__ GroupConst<DT> group_const(uint16_t s_bits, uint32_t z) {
   GroupConst<DT> g;
   g.s_pair = (uint32_t)s_bits | ((uint32_t)s_bits << 16);
   g.nmz_pair = neg_magic_pair<DT>(z);
   g.s_f32 = act_to_f32<DT>(s_bits);
   g.c_f32 = -(float)z * g.s_f32;  // exact: 4 + 8 significant bits (bf16 only)
+  if constexpr (FP8Q && DT == DT_BF16) g.s_f32 *= 512.0f;  // undoes the codes' 2^-9
   return g;
 }
 

@@ -226,14 +226,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int gi = 0; gi < GPS; ++gi) {
         const uint32_t z = ASYM ? (r.z[cb][gi] >> (4 * (nrow[cb] & 7))) & 0xFu : 8u;
-        gc[cb][gi] = group_const<DT>(r.s[cb][gi], z);
+        gc[cb][gi] = group_const<DT, true>(r.s[cb][gi], z);
       }
   };
   auto weights = [&](const StepRegs& r, const GroupConst<DT> (&gc)[2][GPS], int ks, u32x4 (&a)[2]) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const GroupConst<DT>& g = gc[cb][(16 * ks) / GS];
-      a[cb] = dequant_word<DT>(r.w[cb][ks & 1][ks >> 1], g.s_pair, g.nmz_pair, g.s_f32, g.c_f32);
+      a[cb] = dequant_word<DT, true>(r.w[cb][ks & 1][ks >> 1], g.s_pair, g.nmz_pair, g.s_f32, g.c_f32);
     }
   };
   auto xfrags = [&](const lds_u8* buf, int ks, u32x4 (&b)[MB]) {

@@ -187,6 +187,33 @@ def test_one_hot_x_reproduces_dequantised_weight(dt, g):
             assert np.array_equal(y[0], W[:, k]), f"k={k} path={path}"
 
 
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("sym,g", [(True, 128), (False, 32)])
+def test_gemm_operands_are_the_dequantised_weights(dt, sym, g):
+    # x = identity (M = K tokens): y[k, n] = w[n, k] exactly, so every MFMA
+    # operand the GEMM builds is compared bit for bit with the oracle's
+    # dequantised weight, over scales spanning the format (bf16 up to 2^118:
+    # the GEMM reads the codes as e4m3 numbers b * 2^-9 and multiplies by
+    # s * 2^9, exact while that stays finite)
+    N, K = 40, 256
+    c = make_case(1, N, K, g, dt, sym, False, seed=("gemmop", dt, sym, g))
+    rng = np.random.default_rng(13)
+    lo, hi = (-14, 10) if dt == O.F16 else (-60, 118)
+    sgn = np.where(rng.random(c.s_bits.shape) < 0.5, -1.0, 1.0)
+    c.s_bits = O.f32_to_act_bits((sgn * 2.0 ** rng.uniform(lo, hi, c.s_bits.shape)).astype(np.float32), dt)
+    c.s_bits[0, 0] = O.f32_to_act_bits(np.array([2.0 ** hi], np.float32), dt)[0]
+    d = DeviceCase(c)
+    zpk = None if sym else O.pack_zeros(c.zp)
+    W = O.dequant_act(O.pack_weights(c.q), c.s_bits, zpk, N, K, g, dt)
+    one = 0x3C00 if dt == O.F16 else 0x3F80
+    d.set_x((np.eye(K) * one).astype(np.uint16))
+    y = d.run(GEMM)
+    # a zero weight (q = z) with a negative scale is -0; the fp32 sum that
+    # starts from +0 returns +0, so the sign of zero is not compared
+    nz = lambda a: np.where(a == 0x8000, 0, a)
+    assert np.array_equal(nz(y), nz(W.T))
+
+
 @pytest.mark.parametrize("path", [GEMV, GEMM])
 @pytest.mark.parametrize("dt", [O.F16, O.BF16])
 def test_all_eights_symmetric_gives_bias(path, dt):
