@@ -7,5 +7,5 @@ of the method's arithmetic: no packing, no dequantisation, no product.  Both
 the CPU oracle side and the GPU side of every test take their inputs from
 here; half-precision values are handed over as raw uint16 bit patterns.
 """
-from .gen import Case, make_case, to_act_bits, stream_seed  # noqa: F401
+from .gen import Case, make_case, to_act_bits, stream_seed, stored_words  # noqa: F401
 from .configs import CONFIGS, Layer, config_cases  # noqa: F401

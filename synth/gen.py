@@ -80,3 +80,12 @@ def make_case(M: int, N: int, K: int, group: int, dtype: int, symmetric: bool,
     xrng = np.random.default_rng(stream_seed("x", seed if x_seed is None else x_seed, M))
     x_bits = to_act_bits(xrng.normal(0.0, 1.0, size=(M, K)).astype(np.float32), dtype)
     return Case(M, N, K, group, dtype, q, zp, s_bits, x_bits, bias_bits)
+
+
+def stored_words(seed, first_row: int, rows: int, words_per_row: int) -> np.ndarray:
+    """Uniform random uint32 words for rows [first_row, first_row + rows) of a
+    packed tensor, drawn in the stored layout itself: uniform words are
+    uniform 4-bit codes whatever the nibble order, so a layer too large to
+    draw code by code is drawn word by word (one stream per row block)."""
+    rng = np.random.default_rng(stream_seed("words", seed, first_row))
+    return rng.integers(0, 1 << 32, size=(rows, words_per_row), dtype=np.uint32)

@@ -565,3 +565,17 @@ def test_moe_weights_ids_and_slot_rows():
     ys = O.moe_linear_ref(xs, wq, s, None, None, ids, None, 2, 2, E, N, K, 32, O.BF16,
                           x_per_slot=True)
     assert np.array_equal(ys, y)
+
+
+def test_complete_tiles_are_self_contained():
+    # the rows of a complete 16-row tile (K a multiple of 128) hold exactly
+    # that tile's codes: slicing the packed tensor at tile boundaries equals
+    # packing the slice, and a tile's words unpack on their own
+    rng = np.random.default_rng(5)
+    N, K = 64, 512
+    q = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    wq = O.pack_weights(q)
+    for t in range(N // 16):
+        rows = slice(16 * t, 16 * t + 16)
+        assert np.array_equal(wq[rows], O.pack_weights(q[rows]))
+        assert np.array_equal(O.unpack_weights(wq[rows]), q[rows])
