@@ -303,7 +303,7 @@ def moe_measure(stream, reps=20):
     import torch
     import int4_weight_only_linear_amd as L
     from int4_weight_only_linear_amd import _binding as B
-    from synth import make_case
+    from synth import make_case, stream_seed
     dev = torch.device("cuda:0")
     E, topk, g = MOE_EXPERTS, MOE_TOPK, GROUP
     rows = []
@@ -321,7 +321,7 @@ def moe_measure(stream, reps=20):
         copies = max(2, min(16, -(-(1 << 30) // (E * per_expert))))
         stacks = [(wq, zp, s)] + [(wq.clone(), zp.clone(), s.clone()) for _ in range(copies - 1)]
         for M in (1, 4):
-            rng = np.random.default_rng(hash((name, M)) % (2**32))
+            rng = np.random.default_rng(stream_seed("bench-moe-ids", name, M))
             ids_h = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(M)]).astype(np.int32)
             ids = torch.from_numpy(ids_h).to(dev)
             w = torch.from_numpy(rng.random((M, topk)).astype(np.float32)).to(dev)

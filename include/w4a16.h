@@ -189,7 +189,9 @@ w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t*
  * expert's N*K/2 below 4 GiB.  Device pointers, caller-owned; asynchronous on
  * `stream`.  Alignment: x and wq 16 bytes; zp, topk_ids, topk_weights 4;
  * scales, bias, y 2.  y must not overlap any input.  Errors as w4a16_linear;
- * W4A16_ERR_UNSUPPORTED when K needs more than one workgroup per slot. */
+ * W4A16_ERR_UNSUPPORTED when K needs more than one workgroup per slot: with
+ * N > 16 that is K above 15360, 13312 or 9216 for groups of 128, 64 or 32
+ * (per-channel scales count as the largest of these dividing K). */
 w4a16_status w4a16_moe_linear(const void* x, const int32_t* wq, const void* scales,
                               const int32_t* zp, const void* bias, const int32_t* topk_ids,
                               const float* topk_weights, void* y, int64_t M, int64_t topk,

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from synth import make_case, CONFIGS
+from synth import make_case, stream_seed, CONFIGS
 from gpu_util import DeviceCase, assert_close, device_to_bits, note, oracle_rows, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -372,7 +372,7 @@ def test_per_channel_scales(dt, M, N, K, sym, bias):
 
 def _moe_case(E, topk, M, N, K, g, dt, sym, bias, weights, x_per_slot, seed, invalid=True):
     cases = [make_case(1, N, K, g, dt, sym, bias, seed=(seed, "expert", e)) for e in range(E)]
-    rng = np.random.default_rng(abs(hash((seed, E, topk, M))) % (2**32))
+    rng = np.random.default_rng(stream_seed("moe-ids", seed, E, topk, M))
     ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(M)]).astype(np.int32)
     if invalid and M * topk >= 3:
         ids.flat[1] = -1
@@ -432,6 +432,26 @@ def test_moe_linear_full_size_sampled():
         ref = O.linear_ref(h["x"][m:m + 1], h["wq"][e], h["s"][e], h["zp"][e], None, 1, N, K, g, dt)[0]
         ref = ref * float(h["w"][m, j])
         assert_close(y[slot:slot + 1], ref[None, :], dt, f"moe slot {slot}")
+
+
+@pytest.mark.parametrize("g,kmax", [(128, 15360), (64, 13312), (32, 9216)])
+def test_moe_linear_k_bound(g, kmax):
+    # one workgroup per slot: the largest K the header states runs (against
+    # the oracle), the next multiple of 128 is refused before any launch
+    E, topk, M, N, dt = 2, 1, 1, 32, O.BF16
+    h = _moe_case(E, topk, M, N, kmax, g, dt, False, False, False, False, seed=("moek", g), invalid=False)
+    d = _moe_device(h, dt)
+    y = device_to_bits(L.w4a16_moe_linear(d["x"], d["wq"], d["s"], d["ids"], d["zp"], None, None, group_size=g))
+    e = int(h["ids"][0, 0])
+    ref = O.linear_ref(h["x"][0:1], h["wq"][e], h["s"][e], h["zp"][e], None, 1, N, kmax, g, dt)
+    assert_close(y, ref, dt, f"moe K={kmax}")
+    K2 = kmax + 128
+    wq2 = torch.zeros((E, N, K2 // 8), dtype=torch.int32, device="cuda:0")
+    s2 = torch.zeros((E, N, K2 // g), dtype=torch.bfloat16, device="cuda:0")
+    zp2 = torch.zeros((E, N // 8, K2 // g), dtype=torch.int32, device="cuda:0")
+    x2 = torch.zeros((M, K2), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(L.W4A16Error, match="too large for one decode workgroup"):
+        L.w4a16_moe_linear(x2, wq2, s2, d["ids"], zp2, None, None, group_size=g)
 
 
 # ---- GEMM K split: last-workgroup hand-off and the two-pass form ----------------

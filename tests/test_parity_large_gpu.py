@@ -72,3 +72,45 @@ def test_weights_just_under_4gib():
                                None, M, 16, K, GS, O.BF16)
             assert_close(yb[:, r], ref, O.BF16, f"path={path} M={M} tile={t}")
         del x, y
+
+
+@pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
+def test_expert_stack_past_4gib():
+    # 68 experts of N 16384 x K 8192 (64 MiB packed each, 4.25 GiB in all):
+    # expert 64 starts at byte 2^32 of the stack.  Slots routed to experts on
+    # both sides of it; three 16-row tiles of each slot's output are compared
+    # with the oracle.
+    dev = torch.device("cuda:0")
+    E, Ne, Ke, topk, M = 68, 16384, 8192, 4, 4
+    wpr, Ge = Ke // 8, Ke // GS
+    ids = np.array([[0, 63, 64, 67], [65, 1, 66, 62], [64, 67, 2, 33], [63, 65, 10, 50]], dtype=np.int32)
+    tiles = (0, 257, Ne // 16 - 1)
+    note(f"[gpu] large: drawing and uploading {E * Ne * Ke / 2 / 2**30:.2f} GiB of expert weights")
+    wq = torch.empty((E, Ne, wpr), dtype=torch.int32, device=dev)
+    tile_words = {}
+    for e in range(E):
+        words = stored_words("large-moe-w", e * Ne, Ne, wpr)
+        wq[e].copy_(torch.from_numpy(words.view(np.int32)))
+        if e in ids:
+            for t in tiles:
+                tile_words[e, t] = words[16 * t:16 * t + 16].copy()
+        del words
+    zpk = stored_words("large-moe-z", 0, E * Ne // 8, Ge).reshape(E, Ne // 8, Ge)
+    rng = np.random.default_rng(stream_seed("large-moe-s"))
+    s_bits = to_act_bits(np.abs(rng.normal(0.0, 0.02, size=(E, Ne, Ge))).astype(np.float32) + 1e-3, O.BF16)
+    x_bits = to_act_bits(rng.normal(0.0, 1.0, size=(M, Ke)).astype(np.float32), O.BF16)
+    tw = rng.random((M, topk)).astype(np.float32)
+    y = L.w4a16_moe_linear(bits_to_device(x_bits, O.BF16, dev), wq, bits_to_device(s_bits, O.BF16, dev),
+                           torch.from_numpy(ids).to(dev), torch.from_numpy(zpk.view(np.int32)).to(dev),
+                           None, torch.from_numpy(tw).to(dev), group_size=GS)
+    torch.cuda.synchronize()
+    yb = device_to_bits(y)
+    for m in range(M):
+        for j in range(topk):
+            e, slot = int(ids[m, j]), m * topk + j
+            for t in tiles:
+                r = slice(16 * t, 16 * t + 16)
+                ref = O.linear_ref(x_bits[m:m + 1], tile_words[e, t].view(np.int32), s_bits[e, r],
+                                   zpk[e, 2 * t:2 * t + 2].view(np.int32), None, 1, 16, Ke, GS, O.BF16)
+                assert_close(yb[slot:slot + 1, r], ref * float(tw[m, j]), O.BF16,
+                             f"slot {slot} expert {e} tile {t}")
