@@ -86,7 +86,7 @@ typedef enum w4a16_dtype { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype;
 typedef enum w4a16_path {
   W4A16_PATH_AUTO = 0,  /* pick by M, N, K, group and dtype */
   W4A16_PATH_GEMV = 1,  /* skinny split-K decode kernel (M <= W4A16_GEMV_MAX_M) */
-  W4A16_PATH_GEMM = 2   /* dequantise-into-LDS MFMA GEMM */
+  W4A16_PATH_GEMM = 2   /* prefill MFMA GEMM (weights dequantised in registers) */
 } w4a16_path;
 
 /* Largest M the skinny decode kernel accepts. */
