@@ -175,8 +175,9 @@ def per_launch_durations(step_lists, reps, stream, passes=5, replays=4):
     return out
 
 
-def cpu_baseline(layers_host, budget_s=30.0):
-    """The oracle (untuned) on this host: one decode step over the layers, 1 thread."""
+def cpu_baseline(layers_host, min_s=10.0):
+    """The oracle (untuned) on this host, 1 thread: whole M=1 decode steps over
+    the layers, repeated until at least `min_s` seconds of oracle work."""
     import contextlib
     import oracle as O
     try:
@@ -184,25 +185,21 @@ def cpu_baseline(layers_host, budget_s=30.0):
         ctx = threadpool_limits(limits=1)
     except ImportError:  # pragma: no cover
         ctx = contextlib.nullcontext()
-    total_bytes = 0
-    t_total = 0.0
-    done = []
+    packed = [(K, N, c, O.pack_weights(c.q), O.pack_zeros(c.zp)) for (K, N, c) in layers_host]
+    total_bytes, t_total, steps = 0, 0.0, 0
     with ctx:
-        for (K, N, c) in layers_host:
-            zpk = O.pack_zeros(c.zp)
-            wq = O.pack_weights(c.q)
-            t0 = time.perf_counter()
-            O.linear_ref(c.x_bits, wq, c.s_bits, zpk, None, c.M, N, K, GROUP, 1)
-            t_total += time.perf_counter() - t0
-            total_bytes += decode_bytes(c.M, N, K, GROUP)
-            done.append(f"{K}x{N}")
-            del wq, zpk
-            if t_total > budget_s:
-                break
+        while t_total < min_s:
+            for (K, N, c, wq, zpk) in packed:
+                t0 = time.perf_counter()
+                O.linear_ref(c.x_bits, wq, c.s_bits, zpk, None, c.M, N, K, GROUP, 1)
+                t_total += time.perf_counter() - t0
+                total_bytes += decode_bytes(c.M, N, K, GROUP)
+            steps += 1
+    layers = ", ".join(f"{K}x{N}" for (K, N, _c) in layers_host)
     return dict(value=total_bytes / t_total / 1e9, unit="GB/s", cores=1, kind="oracle",
                 seconds=round(t_total, 3),
-                sample=("oracle linear_ref (unpack + exact fp32 dequant + fp64 GEMV) over one M=1 "
-                        f"decode step, layers {', '.join(done)} (K x N), single thread; packing not timed"))
+                sample=(f"oracle linear_ref (unpack + exact fp32 dequant + fp64 GEMV) over {steps} M=1 "
+                        f"decode step(s), layers {layers} (K x N), single thread; packing not timed"))
 
 
 def _layer_tensors(case, device):
