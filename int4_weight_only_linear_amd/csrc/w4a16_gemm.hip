@@ -37,7 +37,6 @@ namespace w4a16 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBN = 256;         // output features per workgroup (64 per wave)
 constexpr int kBK = 128;         // k per step: one stored run of every row
 constexpr int kXRowBytes = 256;  // one staged x row: 128 k of 16-bit values
 constexpr int kXcds = 8;
@@ -59,7 +58,7 @@ struct GemmParams {
   int wpr;             // words per weight row, K / 8
   int nsteps;          // ceil(K / 128)
   int full_steps;      // K / 128: steps over complete (transposed) runs
-  int tiles_n;         // ceil(N / 256)
+  int tiles_n;         // ceil(N / (128 * CB))
   int units;           // tiles * splits = grid size
   int splits;
   int steps_per_split;
@@ -78,9 +77,10 @@ __device__ __forceinline__ int xcd_unit(int b, int units) {
 
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int DT, int GS, bool ASYM, int MB>
+template <int DT, int GS, bool ASYM, int MB, int CB>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   constexpr int BM = 32 * MB;
+  constexpr int BN = 128 * CB;           // output features: 32 CB per wave
   constexpr int XBUF = BM * kXRowBytes;  // bytes of one x buffer
   constexpr int NDMA = BM / 16;          // 1 KiB global->LDS loads per wave and step
   constexpr int GPS = kBK / GS;          // groups per k-step
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   const int mt = tile / p.tiles_n;
   const int nt = tile - mt * p.tiles_n;
   const int m0 = mt * BM;
-  const int nw0 = nt * kBN + wave * 64;  // first output feature of this wave
+  const int nw0 = nt * BN + wave * 32 * CB;  // first output feature of this wave
   const int s_begin = split * p.steps_per_split;
   const int s_end = min(p.nsteps, s_begin + p.steps_per_split);
   const int s_full_end = min(s_end, p.full_steps);
@@ -144,12 +144,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   // n is its piece 16 pc + (n mod 16); a final incomplete tile keeps its
   // rows one after another (64-byte runs).  The incomplete last run of a
   // row (slice order) is tail_w[cb] words in, T = wpr - 16 full_steps words.
-  int nrow[2];
-  uint32_t woff[2][2];   // [cb][pc]: byte offset of piece h + 2 pc in run 0
-  uint32_t rshift[2];    // run s starts s << rshift bytes further
-  uint32_t tail_w[2];
+  int nrow[CB];
+  uint32_t woff[CB][2];   // [cb][pc]: byte offset of piece h + 2 pc in run 0
+  uint32_t rshift[CB];    // run s starts s << rshift bytes further
+  uint32_t tail_w[CB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     const int n = min(nw0 + 32 * cb + j, p.N - 1);
     nrow[cb] = n;
     const int jj = n & 15;
@@ -169,15 +169,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   }
 
   struct StepRegs {
-    u32x4 w[2][2];        // [cb][piece]: word t of piece pc is k-sub 2t + pc
-    uint16_t s[2][GPS];   // scales of the step's groups
-    uint32_t z[2][GPS];   // packed zero-point words
+    u32x4 w[CB][2];       // [cb][piece]: word t of piece pc is k-sub 2t + pc
+    uint16_t s[CB][GPS];  // scales of the step's groups
+    uint32_t z[CB][GPS];  // packed zero-point words
   };
   // complete run: pieces h and h + 2 of the run's four 16-byte pieces
   auto load_full = [&](int s, StepRegs& r) {
     const unsigned char* base = reinterpret_cast<const unsigned char*>(p.wq);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       const uint32_t run = (uint32_t)s << rshift[cb];
 #pragma unroll
       for (int pc = 0; pc < 2; ++pc)
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   auto load_tail = [&](int s, StepRegs& r) {
     const int nks = (p.K - s * kBK) / 16;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         uint32_t v = 0u;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   };
   auto load_meta = [&](int s, StepRegs& r) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int gi = 0; gi < GPS; ++gi) {
         const int g = min(s * GPS + gi, p.G - 1);
@@ -212,26 +212,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   const int c2 = (j & 15) >> 1;
   const uint32_t xlane = (uint32_t)j * kXRowBytes + (uint32_t)((h ^ (j & 1)) << 4);
 
-  f32x16 acc[MB][2];
+  f32x16 acc[MB][CB];
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[rb][cb][e] = 0.f;
 
-  auto group_consts = [&](const StepRegs& r, GroupConst<DT> (&gc)[2][GPS]) {
+  auto group_consts = [&](const StepRegs& r, GroupConst<DT> (&gc)[CB][GPS]) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int gi = 0; gi < GPS; ++gi) {
         const uint32_t z = ASYM ? (r.z[cb][gi] >> (4 * (nrow[cb] & 7))) & 0xFu : 8u;
         gc[cb][gi] = group_const<DT, true>(r.s[cb][gi], z);
       }
   };
-  auto weights = [&](const StepRegs& r, const GroupConst<DT> (&gc)[2][GPS], int ks, u32x4 (&a)[2]) {
+  auto weights = [&](const StepRegs& r, const GroupConst<DT> (&gc)[CB][GPS], int ks, u32x4 (&a)[CB]) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       const GroupConst<DT>& g = gc[cb][(16 * ks) / GS];
       a[cb] = dequant_word<DT, true>(r.w[cb][ks & 1][ks >> 1], g.s_pair, g.nmz_pair, g.s_f32, g.c_f32);
     }
@@ -241,17 +241,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) b[rb] = *(lds_u32x4*)(src + rb * 32 * kXRowBytes);
   };
-  auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[MB]) {
+  auto mfmas = [&](const u32x4 (&a)[CB], const u32x4 (&b)[MB]) {
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32x32x16<DT>(a[cb], b[rb], acc[rb][cb]);
+      for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mfma32x32x16<DT>(a[cb], b[rb], acc[rb][cb]);
   };
 
   // Pipeline state carried across k-steps: the operands of the k-sub about
   // to be multiplied (by parity) and the current step's group constants.
-  u32x4 a[2][2], b[2][MB];
-  GroupConst<DT> gc[2][GPS];
+  u32x4 a[2][CB], b[2][MB];
+  GroupConst<DT> gc[CB][GPS];
 
   // Own x pieces landed in LDS, own loads and LDS reads retired, then the
   // workgroup barrier (no memory fence beyond that is needed: the x pieces
@@ -290,10 +290,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
       const int nvm = issue(ks);
       mfmas(a[c], b[c]);
 #pragma unroll
-      for (int i = 0; i < 2 * MB; ++i) {
+      for (int i = 0; i < CB * MB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         if (i < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, (48 + 2 * MB - 1) / (2 * MB), 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, (24 * CB + CB * MB - 1) / (CB * MB), 0);  // VALU
         if (i < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -301,12 +301,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   };
   // the incomplete last run: nks < 8 k-subs, not pipelined
   auto compute_tail = [&](const lds_u8* buf, const StepRegs& r, int nks) {
-    GroupConst<DT> gc[2][GPS];
+    GroupConst<DT> gc[CB][GPS];
     group_consts(r, gc);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       if (ks < nks) {
-        u32x4 a[2], b[MB];
+        u32x4 a[CB], b[MB];
         xfrags(buf, ks, b);
         weights(r, gc, ks, a);
         mfmas(a, b);
@@ -319,13 +319,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 
   // the next k-step's global loads, spread over k-subs 0..5 of the current
   // one: weights first (k-sub 0), then metadata, then the x pieces
-  constexpr int kMetaLoads = 2 * GPS * (ASYM ? 2 : 1);
+  constexpr int kMetaLoads = CB * GPS * (ASYM ? 2 : 1);
   auto issue_next = [&](int ks, int sn, lds_u8* buf, StepRegs& r) -> int {
     constexpr int DPK = (NDMA + 5) / 6;  // x loads per k-sub
     int n = 0;
     if (ks == 0) {
       load_full(sn, r);
-      n += 4;
+      n += 2 * CB;
     }
     if (ks == 1) {
       load_meta(sn, r);
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     for (int rb = 0; rb < MB; ++rb) {
       const int m = m0 + 32 * rb + j;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const int n = nw0 + 32 * cb + 8 * a + 4 * h;
@@ -411,11 +411,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     return;
   }
   if (p.splits > 1) {
-    constexpr int NV = MB * 32;  // accumulator values per thread
+    constexpr int NV = MB * CB * 16;  // accumulator values per thread
     constexpr int kChunk = 64;
     static_assert(NV % kChunk == 0, "chunking");
-    const size_t slot = (size_t)BM * kBN / 2;  // pairs per partial tile
-    auto val = [&](int q) -> float { return acc[q >> 5][(q >> 4) & 1][q & 15]; };
+    const size_t slot = (size_t)BM * BN / 2;  // pairs per partial tile
+    auto val = [&](int q) -> float { return acc[q / (16 * CB)][(q / 16) % CB][q % 16]; };
     uint64_t* mine = reinterpret_cast<uint64_t*>(p.partial) + (size_t)(tile * p.splits + split) * slot;
 #pragma unroll
     for (int i = 0; i < NV / 2; ++i) store_coherent_pair(mine + (size_t)i * kThreads + tid, val(2 * i), val(2 * i + 1));
@@ -441,16 +441,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
         for (int e = 0; e < kChunk; ++e) t[e] = sp == 0 ? u[e] : t[e] + u[e];
       }
 #pragma unroll
-      for (int e = 0; e < kChunk; ++e) acc[(c0 + e) >> 5][((c0 + e) >> 4) & 1][(c0 + e) & 15] = t[e];
+      for (int e = 0; e < kChunk; ++e) acc[(c0 + e) / (16 * CB)][((c0 + e) / 16) % CB][(c0 + e) % 16] = t[e];
     }
     if (tid == 0) reset_counter(p.counters + tile);  // ready for the next call
   }
 
   // ---- epilogue: + bias in fp32, one rounding, 16-byte stores
   // acc[rb][cb][4a + e] is token m0 + 32 rb + j, feature nw0 + 32 cb + 8a + 4h + e
-  float bias_f[2][4][4];
+  float bias_f[CB][4][4];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   for (int rb = 0; rb < MB; ++rb) {
     const int m = m0 + 32 * rb + j;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       uint32_t q[4][2];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
@@ -518,99 +518,116 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
-template <int DT, int GS, bool ASYM, int MB>
+template <int DT, int GS, bool ASYM, int MB, int CB>
 hipError_t launch_t(const GemmParams& prm, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<DT, GS, ASYM, MB>), dim3(prm.units), dim3(kThreads), 0, s, prm);
+  hipLaunchKernelGGL((gemm_kernel<DT, GS, ASYM, MB, CB>), dim3(prm.units), dim3(kThreads), 0, s, prm);
   return hipGetLastError();
 }
 
+// tile shapes: 32 mb tokens x 128 cb features; cb = 1 only for mb 4 and 8
 template <int DT, int GS, bool ASYM>
-hipError_t launch_mb(const GemmParams& prm, int mb, hipStream_t s) {
+hipError_t launch_mb(const GemmParams& prm, int mb, int cb, hipStream_t s) {
+  if (cb == 1) {
+    switch (mb) {
+      case 4: return launch_t<DT, GS, ASYM, 4, 1>(prm, s);
+      case 8: return launch_t<DT, GS, ASYM, 8, 1>(prm, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (mb) {
-    case 4: return launch_t<DT, GS, ASYM, 4>(prm, s);
-    case 6: return launch_t<DT, GS, ASYM, 6>(prm, s);
-    case 8: return launch_t<DT, GS, ASYM, 8>(prm, s);
+    case 4: return launch_t<DT, GS, ASYM, 4, 2>(prm, s);
+    case 6: return launch_t<DT, GS, ASYM, 6, 2>(prm, s);
+    case 8: return launch_t<DT, GS, ASYM, 8, 2>(prm, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DT, int GS>
-hipError_t launch_z(const GemmParams& prm, int mb, hipStream_t s) {
-  return prm.zp ? launch_mb<DT, GS, true>(prm, mb, s) : launch_mb<DT, GS, false>(prm, mb, s);
+hipError_t launch_z(const GemmParams& prm, int mb, int cb, hipStream_t s) {
+  return prm.zp ? launch_mb<DT, GS, true>(prm, mb, cb, s) : launch_mb<DT, GS, false>(prm, mb, cb, s);
 }
 
 template <int DT>
-hipError_t launch_g(const GemmParams& prm, int group, int mb, hipStream_t s) {
+hipError_t launch_g(const GemmParams& prm, int group, int mb, int cb, hipStream_t s) {
   switch (group) {
-    case 32: return launch_z<DT, 32>(prm, mb, s);
-    case 64: return launch_z<DT, 64>(prm, mb, s);
-    case 128: return launch_z<DT, 128>(prm, mb, s);
+    case 32: return launch_z<DT, 32>(prm, mb, cb, s);
+    case 64: return launch_z<DT, 64>(prm, mb, cb, s);
+    case 128: return launch_z<DT, 128>(prm, mb, cb, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-// Tile height and K split.  Cost model in cycles of one CU, fitted to
-// measured k-step times (about 760 cycles per 32 tokens of the tile plus a
-// fixed 1000: MFMA issue, dequantisation and staging share one instruction
-// stream per SIMD); units run in rounds of cu_count; splitting K adds the
-// partial-tile hand-off.
+// Tile shape and K split.  Cost model in cycles of one CU, fitted to
+// measured k-step times (about 380 cycles per 32 tokens and 128 features of
+// the tile plus a fixed 1000: MFMA issue, dequantisation and staging share
+// one instruction stream per SIMD); units run in rounds of cu_count; splitting
+// K adds the partial-tile hand-off.  Narrow tiles (128 features, one column
+// block per wave) double the tile count at small M, where 256-feature tiles
+// leave CUs idle or need K splits whose partial sums outweigh the weights.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count) {
   GemmPlan best{};
   double best_cost = 0.0;
   const int nsteps = (int)((K + kBK - 1) / kBK);
-  const int64_t tiles_n = (N + kBN - 1) / kBN;
   const int cus = cu_count > 0 ? cu_count : 256;
-  for (int mb : {8, 6, 4}) {
-    const int64_t bm = 32 * mb;
-    const int64_t tiles = ((M + bm - 1) / bm) * tiles_n;
-    for (int splits = 1; splits <= 16 && splits <= nsteps; ++splits) {
-      const int sps = (nsteps + splits - 1) / splits;
-      const int real_splits = (nsteps + sps - 1) / sps;
-      if (real_splits != splits) continue;
+  for (int cb : {2, 1}) {
+    const int64_t bn = 128 * cb;
+    const int64_t tiles_n = (N + bn - 1) / bn;
+    for (int mb : {8, 6, 4}) {
+      if (cb == 1 && mb == 6) continue;
+      const int64_t bm = 32 * mb;
+      const int64_t tiles = ((M + bm - 1) / bm) * tiles_n;
+      for (int splits = 1; splits <= 16 && splits <= nsteps; ++splits) {
+        const int sps = (nsteps + splits - 1) / splits;
+        const int real_splits = (nsteps + sps - 1) / sps;
+        if (real_splits != splits) continue;
 
-      const int64_t units = tiles * splits;
-      const int64_t rounds = (units + cus - 1) / cus;
-      // a split unit writes its fp32 partial tile; the tile's last unit then
-      // reads the others back, one memory round trip (~2500 cycles) per
-      // split and 64-value chunk, plus the bytes (mostly from L2 / MALL)
-      const double fixup = splits > 1 ? 2.0 * bm * kBN * 4 / 40.0 +
-                                           2500.0 * splits * (32.0 * mb / 64.0) : 0.0;
-      const double loop = sps * (760.0 * mb + 1000.0);
-      const double cost = (double)rounds * (loop + fixup);
-      // two passes: each unit stores its partial tile (~64 bytes a cycle),
-      // then a second kernel reads all partials (mostly from the last-level
-      // cache, taken as 5 TB/s at 2.1 GHz) plus its launch
-      const double np = (double)((N + 7) / 8 * 8);
-      const double cost2 = (double)rounds * (loop + bm * kBN * 4 / 64.0) +
-                           (splits * (double)M * np * 4.0 + (double)M * N * 2.0) * (2.1e9 / 5e12) + 3000.0;
-      for (int tp = 0; tp < (splits > 1 && mb == 4 ? 2 : 1); ++tp) {
-        const double c = tp ? cost2 : cost;
-        if (tp == 0 && splits > 1 && tiles > kMaxCounters) continue;
-        if (best.units == 0 || c < best_cost * 0.98) {
-          best_cost = c;
-          best.mb = mb;
-          best.splits = splits;
-          best.steps_per_split = sps;
-          best.tiles_n = (int)tiles_n;
-          best.tiles = (int)tiles;
-          best.units = (int)units;
-          best.two_pass = tp == 1;
+        const int64_t units = tiles * splits;
+        const int64_t rounds = (units + cus - 1) / cus;
+        // a split unit writes its fp32 partial tile; the tile's last unit then
+        // reads the others back, one memory round trip (~2500 cycles) per
+        // split and 64-value chunk, plus the bytes (mostly from L2 / MALL)
+        const double fixup = splits > 1 ? 2.0 * bm * bn * 4 / 40.0 +
+                                             2500.0 * splits * (16.0 * cb * mb / 64.0) : 0.0;
+        const double loop = sps * (380.0 * cb * mb + 1000.0);
+        const double cost = (double)rounds * (loop + fixup);
+        // two passes: each unit stores its partial tile (~64 bytes a cycle),
+        // then a second kernel reads all partials (mostly from the last-level
+        // cache, taken as 5 TB/s at 2.1 GHz) plus its launch
+        const double np = (double)((N + 7) / 8 * 8);
+        const double cost2 = (double)rounds * (loop + bm * bn * 4 / 64.0) +
+                             (splits * (double)M * np * 4.0 + (double)M * N * 2.0) * (2.1e9 / 5e12) + 3000.0;
+        for (int tp = 0; tp < (splits > 1 && mb == 4 ? 2 : 1); ++tp) {
+          const double c = tp ? cost2 : cost;
+          if (tp == 0 && splits > 1 && tiles > kMaxCounters) continue;
+          if (best.units == 0 || c < best_cost * 0.98) {
+            best_cost = c;
+            best.mb = mb;
+            best.cb = cb;
+            best.splits = splits;
+            best.steps_per_split = sps;
+            best.tiles_n = (int)tiles_n;
+            best.tiles = (int)tiles;
+            best.units = (int)units;
+            best.two_pass = tp == 1;
+          }
         }
       }
     }
   }
-  // tuning override "mb,splits" (tile height 32*mb, K ranges), e.g. for sweeps
+  // tuning override "mb,splits[,two_pass[,cb]]" (tile 32*mb x 128*cb, K ranges), e.g. for sweeps
   if (const char* env = std::getenv("W4A16_GEMM_TILE")) {
-    int mb = 0, splits = 0, tp = 0;
-    if (std::sscanf(env, "%d,%d,%d", &mb, &splits, &tp) >= 2 && (mb == 4 || mb == 6 || mb == 8) &&
-        splits >= 1 && splits <= nsteps && (tp == 0 || mb == 4)) {
+    int mb = 0, splits = 0, tp = 0, cb = 2;
+    if (std::sscanf(env, "%d,%d,%d,%d", &mb, &splits, &tp, &cb) >= 2 && (mb == 4 || mb == 6 || mb == 8) &&
+        (cb == 2 || (cb == 1 && mb != 6)) && splits >= 1 && splits <= nsteps && (tp == 0 || mb == 4)) {
       const int sps = (nsteps + splits - 1) / splits;
+      const int64_t tiles_n = (N + 128 * cb - 1) / (128 * cb);
       const int64_t tiles = ((M + 32 * mb - 1) / (32 * mb)) * tiles_n;
       if (splits == 1 || tp == 1 || tiles <= kMaxCounters) {
         best.two_pass = splits > 1 && tp == 1;
         best.mb = mb;
+        best.cb = cb;
         best.steps_per_split = sps;
         best.splits = (nsteps + sps - 1) / sps;
         best.tiles_n = (int)tiles_n;
@@ -627,7 +644,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cu_count) {
   if (p.splits <= 1) return 0;
   if (p.two_pass)
     return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)((N + 7) / 8 * 8) * sizeof(float);
-  return kCounterBytes + (size_t)p.units * (size_t)(32 * p.mb) * kBN * sizeof(float);
+  return kCounterBytes + (size_t)p.units * (size_t)(32 * p.mb) * (size_t)(128 * p.cb) * sizeof(float);
 }
 
 hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipStream_t stream) {
@@ -663,8 +680,8 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
   prm.two_pass = plan.splits > 1 && plan.two_pass;
   if (prm.two_pass && plan.mb != 4) return hipErrorInvalidConfiguration;
   prm.np = (int)((a.N + 7) / 8 * 8);
-  hipError_t e = a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, plan.mb, stream)
-                                   : launch_g<DT_BF16>(prm, a.group, plan.mb, stream);
+  hipError_t e = a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, plan.mb, plan.cb, stream)
+                                   : launch_g<DT_BF16>(prm, a.group, plan.mb, plan.cb, stream);
   if (e != hipSuccess || !prm.two_pass) return e;
   const int64_t quads = (int64_t)prm.M * (prm.np / 4);
   const int blocks = (int)((quads + 255) / 256);

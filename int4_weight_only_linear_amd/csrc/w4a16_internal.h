@@ -107,7 +107,8 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& p, void* workspace,
 // A workgroup owns 32*mb tokens x 256 output features; `splits` K ranges of
 // `steps_per_split` 128-k steps each; units = tiles * splits workgroups.
 struct GemmPlan {
-  int mb;
+  int mb;                // tile height 32 * mb tokens
+  int cb;                // tile width 128 * cb features (cb column blocks of 32 per wave)
   int splits;
   int steps_per_split;
   int tiles_n;

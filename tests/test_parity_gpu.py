@@ -457,7 +457,8 @@ def test_moe_linear_k_bound(g, kmax):
 # ---- GEMM K split: last-workgroup hand-off and the two-pass form ----------------
 
 @pytest.mark.parametrize("dt", [O.F16, O.BF16])
-@pytest.mark.parametrize("tile", ["4,3,0", "4,3,1", "6,5,0", "8,2,0", "4,7,1"])
+@pytest.mark.parametrize("tile", ["4,3,0", "4,3,1", "6,5,0", "8,2,0", "4,7,1",
+                                  "4,1,0,1", "4,3,0,1", "4,3,1,1", "8,1,0,1", "8,2,0,1"])
 @pytest.mark.parametrize("M,N,K,g,bias", [(130, 200, 640, 64, True), (128, 264, 1216, 32, False),
                                           (300, 56, 2048, 128, True)])
 def test_gemm_k_split_forms(monkeypatch, dt, tile, M, N, K, g, bias):
