@@ -10,6 +10,7 @@ with kernel-argument preloading.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import json
 import os
 import shutil
 import subprocess
@@ -42,14 +43,42 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; libw4a16 needs ROCm's hipcc to build")
 
 
+_REMARK = "kernel-resource-usage"
+
+
+def _resources(text: str) -> dict:
+    """Per-kernel register use from hipcc's resource-usage remarks."""
+    res, name = {}, None
+    for line in text.splitlines():
+        if _REMARK not in line or "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split("[-R", 1)[0].strip()
+        key, _, val = body.partition(":")
+        if key == "Function Name":
+            name = val.strip()
+            res[name] = {}
+        elif name is not None and val.strip().lstrip("-").isdigit():
+            res[name][key.strip()] = int(val)
+    return res
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".hip"):
+        cmd.append(f"-Rpass-analysis={_REMARK}")
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
+    text = r.stdout + r.stderr
+    out = "\n".join(l for l in text.splitlines()
+                    if "packed-fp32-ops" not in l and _REMARK not in l and not l.lstrip().startswith(("|", "^"))
+                    and not l.lstrip()[:1].isdigit())
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{out}")
+        raise RuntimeError(f"hipcc failed on {src}:\n{text}")
+    if src.endswith(".hip"):
+        # register and scratch use of every kernel instance, kept beside the
+        # object (the GEMM planner's tile table is checked against it)
+        with open(obj + ".resources.json", "w") as f:
+            json.dump(_resources(text), f, indent=1, sort_keys=True)
     if out.strip():
         print(out, file=sys.stderr)
     return obj

@@ -138,13 +138,14 @@ w4a16_path resolve_path(int64_t M, int64_t N, int64_t K, int32_t group, int32_t 
 
 constexpr int kPlanningCUs = 256;  // MI355X; the launch plan uses the device's own count
 
-size_t workspace_for(int64_t M, int64_t N, int64_t K, int32_t group, w4a16_path path, int cu_count) {
+size_t workspace_for(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype, bool asym,
+                     w4a16_path path, int cu_count) {
   if (M <= 0) return 0;
   if (path == W4A16_PATH_GEMV) {
     const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, group, cu_count);
     return w4a16::gemv_workspace_bytes(plan, M, N);
   }
-  return w4a16::gemm_workspace_bytes(M, N, K, cu_count);
+  return w4a16::gemm_workspace_bytes(M, N, K, group, dtype, asym, cu_count);
 }
 
 bool log_enabled() {
@@ -183,7 +184,7 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
                 "the prefill kernel addresses weights and activations with 32-bit byte "
                 "offsets: N*K/2 and M*K*2 must be below 4 GiB (M=%lld N=%lld K=%lld)",
                 (long long)M, (long long)N, (long long)K);
-  const size_t need = workspace_for(M, N, K, group_size, p, dev->cu_count);
+  const size_t need = workspace_for(M, N, K, group_size, dtype, zp != nullptr, p, dev->cu_count);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
                 workspace_bytes, workspace ? "" : " (NULL)");
@@ -204,12 +205,12 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
     e = w4a16::launch_gemv(a, plan, workspace, s);
   } else {
     if (log_enabled()) {
-      const w4a16::GemmPlan plan = w4a16::plan_gemm(M, N, K, dev->cu_count);
+      const w4a16::GemmPlan plan = w4a16::plan_gemm(M, N, K, group_size, dtype, zp != nullptr, dev->cu_count);
       std::fprintf(stderr,
-                   "[w4a16] gemm M=%lld N=%lld K=%lld g=%d %s %s bm=%d splits=%d units=%d\n",
+                   "[w4a16] gemm M=%lld N=%lld K=%lld g=%d %s %s bm=%d bn=%d splits=%d units=%d\n",
                    (long long)M, (long long)N, (long long)K, group_size,
                    dtype == W4A16_F16 ? "f16" : "bf16", zp ? "asym" : "sym", 32 * plan.mb,
-                   plan.splits, plan.units);
+                   128 * plan.cb, plan.splits, plan.units);
     }
     e = w4a16::launch_gemm(a, workspace, dev->cu_count, s);
   }
@@ -363,7 +364,7 @@ size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size,
     if (device_info(&d) == W4A16_OK) cus = d->cu_count;
     g_last_error.clear();
   }
-  return workspace_for(M, N, K, kgroup, p, cus);
+  return workspace_for(M, N, K, kgroup, dtype, has_zp != 0, p, cus);
 }
 
 w4a16_status w4a16_linear(const void* x, const int32_t* wq, const void* scales, const int32_t* zp,

@@ -118,8 +118,9 @@ struct GemmPlan {
   // many splits) instead of by the tile's last workgroup
   bool two_pass;
 };
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cu_count);
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int cu_count);
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym, int cu_count);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym,
+                            int cu_count);
 hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipStream_t stream);
 
 // ---- elementwise -----------------------------------------------------------

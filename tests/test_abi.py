@@ -229,3 +229,24 @@ def test_per_channel_group_accept_set():
     assert ok(1, 64, 512, 256) == 2            # neither the accept set nor K
     assert "per-channel" in L.w4a16_last_error()
     assert L.w4a16_workspace_size(1, 64, 4096, 4096, L.W4A16_BF16, True) >= 0
+
+
+def test_gemm_planner_skips_exactly_the_spilling_tiles():
+    # The planner leaves out the 192- and 256-token x 256-feature tiles for
+    # fp16 with groups of 32 (either quantisation) or asymmetric groups of 64,
+    # and bf16 with symmetric groups of 32 (wide_tall_tile_spills in
+    # w4a16_gemm.hip): those must be exactly the GEMM instances the compiler
+    # spills registers for, read from the build's resource-usage record.
+    import json
+    path = os.path.join(ROOT, "_build", "w4a16_gemm.hip.o.resources.json")
+    if not os.path.exists(path):
+        pytest.skip("no build record here")
+    with open(path) as f:
+        res = json.load(f)
+    spilling = set()
+    for name, r in res.items():
+        m = re.search(r"gemm_kernelILi(\d)ELi(\d+)ELb(\d)ELi(\d)ELi(\d)E", name)
+        if m and r.get("VGPRs Spill", 0) > 16:
+            spilling.add(tuple(int(v) for v in m.groups()))
+    excluded = {(0, 32, 0), (0, 32, 1), (0, 64, 1), (1, 32, 0)}  # (dtype, group, asym)
+    assert spilling == {(dt, g, a, mb, 2) for (dt, g, a) in excluded for mb in (6, 8)}
