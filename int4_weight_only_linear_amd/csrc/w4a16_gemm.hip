@@ -607,11 +607,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool a
         const double loop = sps * (380.0 * cb * mb + 1000.0);
         const double cost = (double)rounds * (loop + fixup);
         // two passes: each unit stores its partial tile (~64 bytes a cycle),
-        // then a second kernel reads all partials (mostly from the last-level
-        // cache, taken as 5 TB/s at 2.1 GHz) plus its launch
+        // then a second kernel reads all partials plus its launch; the
+        // partials' round trip is taken as 3 TB/s at 2.1 GHz (fitted to every
+        // plan timed at M = 128-512 on 4096x6144, 4096x28672 and 14336x4096)
         const double np = (double)((N + 7) / 8 * 8);
         const double cost2 = (double)rounds * (loop + bm * bn * 4 / 64.0) +
-                             (splits * (double)M * np * 4.0 + (double)M * N * 2.0) * (2.1e9 / 5e12) + 3000.0;
+                             (splits * (double)M * np * 4.0 + (double)M * N * 2.0) * (2.1e9 / 3e12) + 3000.0;
         for (int tp = 0; tp < (splits > 1 && mb == 4 ? 2 : 1); ++tp) {
           const double c = tp ? cost2 : cost;
           if (tp == 0 && splits > 1 && tiles > kMaxCounters) continue;
