@@ -765,11 +765,15 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   // x segments (M * 16 * kpw segments per wave, 64 lanes): kpw <= 4 * XPT / M.
   // The scale and zero-point staging then needs at most 32 * kpw / group and
   // 4 * kpw / group loads per lane, which the kernel's fixed counts cover.
-  // measured on the decode layers: 8 k-steps per wave for M <= 2, 4 for
-  // M <= 8, 1 above (deeper waves are slower there)
+  // measured on the decode layers: 8 k-steps per wave for one token, 4 for
+  // up to 8 tokens, 1 above (deeper waves are slower there); two tokens keep
+  // 8 only where 4 would need more than kGemvMaxWaves waves and so a K split
+  // (M = 2 with 4: 6-13 % faster on K = 2560-4096 layers, 28 % slower on
+  // K = 9728, where it splits)
   int kpw = kGemvStepsPerWave;
+  const bool deep = M == 1 || (M == 2 && p.ksteps > 4 * kGemvMaxWaves);
   if (p.xlds)
-    while (kpw > 1 && (M * kpw > 4 * kGemvXSegsPerThread || (kpw > 4 && M > 2) || M > 8)) kpw >>= 1;
+    while (kpw > 1 && (M * kpw > 4 * kGemvXSegsPerThread || (kpw > 4 && !deep) || M > 8)) kpw >>= 1;
   // tuning overrides: k-steps per wave (a smaller power of two) and a
   // minimum number of K splits
   if (const char* env = std::getenv("W4A16_GEMV_KPW")) {
