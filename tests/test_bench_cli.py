@@ -1,0 +1,33 @@
+"""bench.py host logic (no GPU): the single-GPU refusal and the algorithmic
+byte count the decode roofline divides by."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def test_decode_bytes_counts_each_operand_once():
+    # Llama-3.1-8B gate/up projection, one token, asymmetric g128: packed codes
+    # N*K/2, bf16 scales 2*N*G, packed zero points 4*(N/8)*G, x 2*K, y 2*N
+    N, K, g = 28672, 4096, 128
+    G = K // g
+    assert bench.decode_bytes(1, N, K, g) == N * K // 2 + 2 * N * G + 4 * (N // 8) * G + 2 * K + 2 * N
+    # symmetric: no zero points; bias adds one act-dtype value per row; M scales x and y only
+    assert bench.decode_bytes(1, N, K, g, asym=False) == N * K // 2 + 2 * N * G + 2 * K + 2 * N
+    assert bench.decode_bytes(4, N, K, g, asym=False, bias=True) == \
+        N * K // 2 + 2 * N * G + 4 * 2 * K + 4 * 2 * N + 2 * N
+    # the four decode layers' mean: the per-launch figure the roofline uses
+    total = sum(bench.decode_bytes(1, n, k, g) for (k, n) in bench.DECODE_LAYERS)
+    assert total // len(bench.DECODE_LAYERS) == 28362752
