@@ -215,8 +215,8 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
 // (lanes 0..15, register 0); the other rows are then never updated.
 // MOE: expert-indexed mode (a separate instance, so that the plain layer has
 // no branch in front of its parameter loads and they arrive in one batch).
-constexpr int small_waves_per_simd(int kpw, bool one, int gs) {
-  return kpw == 8 && !one && gs == 32 ? 6 : 7;
+constexpr int small_waves_per_simd(int kpw, bool one, int gs, int xpt) {
+  return kpw == 8 && xpt == 8 ? 4 : (kpw == 8 && !one && gs == 32 ? 6 : 7);
 }
 
 // WGSZ (single token, bf16, groups of 128, every wave a full run of 8 k-steps,
@@ -235,7 +235,7 @@ constexpr int small_waves_per_simd(int kpw, bool one, int gs) {
 // argument segment (gfx950 preloads plain arguments, not the parameter
 // struct).  The other fields that the loads need are derived from them.
 template <int DT, int GS, bool ASYM, int KPW, int XPT, bool ONE, bool MOE, bool WGSZ>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_waves_per_simd(KPW, ONE, GS)))) void gemv_small_kernel(const uint16_t* a_x, const uint32_t* a_wq,
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_waves_per_simd(KPW, ONE, GS, XPT)))) void gemv_small_kernel(const uint16_t* a_x, const uint32_t* a_wq,
                                                           const uint16_t* a_scales, const uint32_t* a_zp,
                                                           int a_M, int a_N, int a_K, int a_sG, int a_gmul,
                                                           int a_kps, const GemvParams params) {
@@ -766,12 +766,12 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   // The scale and zero-point staging then needs at most 32 * kpw / group and
   // 4 * kpw / group loads per lane, which the kernel's fixed counts cover.
   // measured on the decode layers: 8 k-steps per wave for one token, 4 for
-  // up to 8 tokens, 1 above (deeper waves are slower there); two tokens keep
-  // 8 only where 4 would need more than kGemvMaxWaves waves and so a K split
-  // (M = 2 with 4: 6-13 % faster on K = 2560-4096 layers, 28 % slower on
-  // K = 9728, where it splits)
+  // up to 8 tokens, 1 above (deeper waves are slower there); two to four
+  // tokens keep 8 only where 4 would need more than kGemvMaxWaves waves and
+  // so a K split (M = 2 with 4: 6-13 % faster on K = 2560-4096 layers, 28 %
+  // slower on K = 9728, where it splits)
   int kpw = kGemvStepsPerWave;
-  const bool deep = M == 1 || (M == 2 && p.ksteps > 4 * kGemvMaxWaves);
+  const bool deep = M == 1 || (M <= 4 && p.ksteps > 4 * kGemvMaxWaves);
   if (p.xlds)
     while (kpw > 1 && (M * kpw > 4 * kGemvXSegsPerThread || (kpw > 4 && !deep) || M > 8)) kpw >>= 1;
   // tuning overrides: k-steps per wave (a smaller power of two) and a
@@ -826,7 +826,10 @@ template <int DT, int GS, bool ASYM, bool MOE>
 static hipError_t launch_small(const GemvParams& prm, const GemvPlan& plan, dim3 grid, dim3 block,
                                hipStream_t s) {
   const bool one = plan.kpw == 8 && prm.M == 1;
-  const int xpt = one ? small_xpt(8, true) : small_xpt(plan.kpw, false);
+  // three or four tokens at 8 k-steps (K too long for 4 without a split)
+  // stage up to 8 x segments per lane
+  const bool x8 = !MOE && plan.kpw == 8 && prm.M > 2;
+  const int xpt = one ? small_xpt(8, true) : (x8 ? 8 : small_xpt(plan.kpw, false));
   if ((int64_t)prm.M * 16 * plan.kpw > 64 * xpt) return hipErrorInvalidConfiguration;
   // the workgroup-shared scale / zero-point instance: every wave a full run
   // of 8 k-steps in one K range, and 16-byte pieces of scales and zero points
@@ -846,6 +849,9 @@ static hipError_t launch_small(const GemvParams& prm, const GemvPlan& plan, dim3
           }
         }
         hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, true), true, MOE, false>), grid, block, plan.lds_bytes, s, prm.x, prm.wq, prm.scales, prm.zp, prm.M, prm.N, prm.K, prm.sG, prm.gmul, prm.ksteps_per_split, prm);
+      } else if (x8) {
+        if constexpr (!MOE)
+          hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, 8, false, MOE, false>), grid, block, plan.lds_bytes, s, prm.x, prm.wq, prm.scales, prm.zp, prm.M, prm.N, prm.K, prm.sG, prm.gmul, prm.ksteps_per_split, prm);
       } else {
         hipLaunchKernelGGL((gemv_small_kernel<DT, GS, ASYM, 8, small_xpt(8, false), false, MOE, false>), grid, block, plan.lds_bytes, s, prm.x, prm.wq, prm.scales, prm.zp, prm.M, prm.N, prm.K, prm.sG, prm.gmul, prm.ksteps_per_split, prm);
       }

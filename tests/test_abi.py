@@ -191,12 +191,15 @@ def test_workspace_size():
     assert L.w4a16_workspace_size(1, 40, 4096, 128, 1, 1) == 0
     # more k-steps than 16 waves of 8 take (K = 20480: 160 steps): K is split
     assert L.w4a16_workspace_size(1, 40, 20480, 128, 1, 1) > 0
-    # more k-steps than one workgroup's waves take (M = 4: 4 steps a wave, 76
+    # two to four tokens take 8 steps a wave where 4 would need more than 16
+    # waves (76 steps), so K stays whole
+    assert L.w4a16_workspace_size(4, 2560, 9728, 128, 0, 0) == 0
+    # more k-steps than one workgroup's waves take (M = 5: 4 steps a wave, 76
     # steps): K is split and the workspace holds counters + partials
-    ws = L.w4a16_workspace_size(4, 2560, 9728, 128, 0, 0)
+    ws = L.w4a16_workspace_size(5, 2560, 9728, 128, 0, 0)
     assert ws > 0
     tiles = 2560 // 16
-    assert ws >= 256 * ((tiles * 4 + 255) // 256) + 2 * 4 * 2560 * 4
+    assert ws >= 256 * ((tiles * 4 + 255) // 256) + 2 * 5 * 2560 * 4
     assert L.w4a16_workspace_size(0, 2560, 9728, 128, 0, 0) == 0
     # the prefill GEMM: enough tiles to fill the CUs, no split
     assert L.w4a16_workspace_size(1920, 28672, 4096, 128, 1, 1, L.PATH_GEMM) == 0

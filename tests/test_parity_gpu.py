@@ -253,9 +253,9 @@ def test_power_of_two_scaling_is_exact(path):
 
 
 def test_determinism_with_split_k():
-    # M = 4 takes 4 k-steps a wave: K = 9728 (76 steps) needs more than 16
+    # M = 5 takes 4 k-steps a wave: K = 9728 (76 steps) needs more than 16
     # waves, so K is split across two workgroups
-    c = make_case(4, 2560, 9728, 128, O.BF16, False, False, seed=("det",))
+    c = make_case(5, 2560, 9728, 128, O.BF16, False, False, seed=("det",))
     d = DeviceCase(c)
     a = d.run(GEMV)
     for _ in range(3):
@@ -263,11 +263,22 @@ def test_determinism_with_split_k():
     assert_close(a, oracle_rows(c), O.BF16, "split-K")
 
 
+@pytest.mark.parametrize("M,N,K,g,sym", [(3, 2560, 9728, 128, True), (4, 2560, 9728, 128, False),
+                                         (4, 264, 9728, 128, False), (3, 40, 9728, 64, False)])
+def test_decode_three_four_tokens_long_k_unsplit(M, N, K, g, sym):
+    # three or four tokens where 4 k-steps a wave would need more than 16
+    # waves: 8 k-steps a wave, 8 x segments per lane, one K range
+    assert L.w4a16_workspace_size(M, N, K, g, O.BF16, not sym, GEMV) == 0
+    c = make_case(M, N, K, g, O.BF16, sym, True, seed=("x8", M, N, K, g, sym))
+    assert_close(DeviceCase(c).run(GEMV), oracle_rows(c), O.BF16, "3-4 tokens, long K")
+
+
 def test_workspace_reuse_across_shapes():
     # one workspace shared by split-K calls of different shapes, in an order
     # where a later call's counters sit where an earlier call's partial sums were
     # (every shape needs more than 16 waves for one K range, so each is split)
-    shapes = [(5, 264, 9728, 128), (4, 2560, 9728, 128), (2, 40, 20480, 64), (3, 1024, 12288, 32)]
+    # (or, at M <= 4 and 8 k-steps a wave, more LDS than one workgroup holds)
+    shapes = [(5, 264, 9728, 128), (4, 2560, 14336, 128), (2, 40, 20480, 64), (3, 1024, 12288, 32)]
     cases = [make_case(M, N, K, g, O.BF16, False, False, seed=("reuse", M, N, K, g))
              for (M, N, K, g) in shapes]
     devs = [DeviceCase(c) for c in cases]
@@ -494,7 +505,7 @@ def _graph_replays_match(run_eager, run_captured, reps=3):
 
 @pytest.mark.parametrize("M,N,K,g,path,tile", [
     (1, 4096, 4096, 128, GEMV, None),        # decode, no split
-    (3, 40, 9728, 64, GEMV, None),           # decode, K split (workspace counters)
+    (5, 40, 9728, 64, GEMV, None),           # decode, K split (workspace counters)
     (130, 200, 640, 64, GEMM, "4,3,0"),      # GEMM, last-workgroup hand-off
     (128, 264, 1216, 32, GEMM, "4,4,1"),     # GEMM, two-pass split
     (300, 520, 1024, 128, GEMM, None),       # GEMM, no split
