@@ -581,10 +581,14 @@ bool wide_tall_tile_spills(int group, int dtype, bool asym) {
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym, int cu_count) {
   GemmPlan best{};
   const bool tall_wide_ok = !wide_tall_tile_spills(group, dtype, asym);
+  // where the tall wide tiles are left out, narrow tiles are tried first, so
+  // that near-ties go to them: at M = 1920 on 6144x4096 they beat the
+  // 128-token wide tile by 1-20 % for those combinations
+  const int cb_order[2] = {tall_wide_ok ? 2 : 1, tall_wide_ok ? 1 : 2};
   double best_cost = 0.0;
   const int nsteps = (int)((K + kBK - 1) / kBK);
   const int cus = cu_count > 0 ? cu_count : 256;
-  for (int cb : {2, 1}) {
+  for (int cb : cb_order) {
     const int64_t bn = 128 * cb;
     const int64_t tiles_n = (N + bn - 1) / bn;
     for (int mb : {8, 6, 4}) {
