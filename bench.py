@@ -382,7 +382,7 @@ def run_report(path_prefix):
                                 x = x_all[:M].contiguous()
                                 y = torch.empty((M, N), dtype=x.dtype, device=dev)
                                 for path in (L.PATH_GEMV, L.PATH_GEMM):
-                                    if path == L.PATH_GEMV and M > 64:
+                                    if path == L.PATH_GEMV and M > L.GEMV_MAX_M:
                                         continue
                                     reps = 20 if M >= 128 else 50
                                     ms = time_point(x, pool, b, y, M, N, K, g, dt, path, reps, side)

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 2
+#define W4A16_ABI_VERSION 3
 
 typedef enum w4a16_status {
   W4A16_OK = 0,
@@ -89,11 +89,24 @@ typedef enum w4a16_path {
   W4A16_PATH_GEMM = 2   /* prefill MFMA GEMM (weights dequantised in registers) */
 } w4a16_path;
 
-/* Largest M the skinny decode kernel accepts. */
-#define W4A16_GEMV_MAX_M 64
+/* Largest M the skinny decode kernel accepts (one MFMA tile of tokens; above
+ * it the prefill GEMM is faster at every measured shape). */
+#define W4A16_GEMV_MAX_M 16
 
 /* ABI version of the loaded library (W4A16_ABI_VERSION it was built with). */
 int w4a16_abi_version(void);
+
+/* Re-reads the tuning environment variables (host only).  The library reads
+ * them once, at the first call that needs them, so that a launch makes no
+ * getenv call; a process that changes them afterwards (a sweep, a test) calls
+ * this.  None of them is needed for correct results:
+ *   W4A16_FORCE_PATH=gemv|gemm, W4A16_M_THRESHOLD=<m>  path selection
+ *   W4A16_GEMM_TILE=mb,splits[,two_pass[,cb]]        prefill tile and K split
+ *   W4A16_GEMV_KPW=<k>, W4A16_GEMV_SPLITS=<s>         decode k-steps per wave, K splits
+ *   W4A16_GEMV_NO_WGSZ=1                              decode: per-wave scale loads
+ *   W4A16_LOG=1                                       one line per call on stderr
+ * Must not run concurrently with other library calls. */
+void w4a16_reload_tuning(void);
 
 /* Message describing the last failing call on this thread ("" after success).
  * Valid until the next library call on the same thread. */
@@ -116,6 +129,10 @@ w4a16_status w4a16_pack_zeros(const uint8_t* z, int64_t N, int64_t G, int32_t* z
 w4a16_status w4a16_unpack_zeros(const int32_t* zpk, int64_t N, int64_t G, uint8_t* z);
 
 /* Validates the arguments of w4a16_linear without touching any device.
+ * The accept set is the one the page "Upstream sync 67/N: merge 382bbd5144
+ * HybridW4A16LinearKernel (conflict)" re-tests in its reviewer's item 2: the
+ * quantisation types (uint4b8 when zp == NULL, uint4 with zero points), the
+ * activation dtypes fp16 / bf16, the group sizes and K divisibility.
  * Rules: group_size in {32, 64, 128} (the pages' accept set), or
  * group_size == K with K % 32 == 0 (per-channel: one scale and zero point per
  * row, scales [N, 1], zp [N/8, 1]); K >= group_size and K % group_size == 0; N >= 1; N % 8 == 0 when zp != NULL; M >= 0;
@@ -128,23 +145,53 @@ w4a16_status w4a16_check_args(const void* x, const int32_t* wq, const void* scal
                               int64_t M, int64_t N, int64_t K, int32_t group_size,
                               int32_t dtype);
 
-/* The path W4A16_PATH_AUTO resolves to for this problem (host only): the
- * decode kernel for M <= 16 when K <= 4096 and for M <= 8 otherwise, the GEMM
- * above (the crossover measured on MI355X).  Environment overrides:
- * W4A16_M_THRESHOLD=<m> moves the bound, W4A16_FORCE_PATH=gemv|gemm forces
- * one path. */
+/* The path W4A16_PATH_AUTO resolves to for this problem (host only).  The
+ * page "[ROCm][Kernel] Add HybridW4A16LinearKernel: Triton prefill + HIP
+ * skinny decode" (description) sends M <= 5 to its skinny decode kernel and
+ * larger M to its prefill GEMM; that bound was tuned on RDNA.  Here it is
+ * re-measured on MI355X: the decode kernel for M <= 16 when K <= 4096 and for
+ * M <= 8 otherwise, the GEMM above.  Tuning overrides (environment, read
+ * once; see w4a16_reload_tuning): W4A16_M_THRESHOLD=<m> moves the bound,
+ * W4A16_FORCE_PATH=gemv|gemm forces one path. */
 w4a16_path w4a16_select_path(int64_t M, int64_t N, int64_t K, int32_t group_size,
                              int32_t dtype, int32_t has_zp);
 
 /* Workspace bytes w4a16_linear needs for this problem and path (AUTO allowed).
  * 0 means none; otherwise at least 64 KiB.  Layout: the first 64 KiB hold
- * per-tile completion counters, the rest fp32 partial sums of a K split.  The
+ * per-tile completion counters (16384; a split layer with more output tiles
+ * is run as several launches of at most 16384 tiles), the rest fp32 partial
+ * sums of a K split.  The
  * workspace must be zero-filled before its first use; every completed call
  * leaves the counter region zero again (the partial sums are always written
  * before they are read), so one workspace serves later calls of any shape on
  * the same stream.  Calls that overlap in time must not share one. */
 size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size,
                             int32_t dtype, int32_t has_zp, int32_t path);
+
+/* How w4a16_linear_path would run this problem on the current device (host
+ * only; 256 CUs, MI355X's count, when no device is visible).  For logging,
+ * tuning and tests; the numbers describe the launch, not the result.
+ * Errors: W4A16_ERR_INVALID_ARG / W4A16_ERR_UNSUPPORTED as w4a16_check_args
+ * for the sizes, group and dtype (M >= 1 here), W4A16_ERR_UNSUPPORTED for
+ * W4A16_PATH_GEMV with M > W4A16_GEMV_MAX_M, W4A16_ERR_INVALID_ARG for a NULL
+ * out or an unknown path. */
+typedef struct w4a16_plan_info {
+  int32_t path;            /* W4A16_PATH_GEMV or W4A16_PATH_GEMM (AUTO resolved) */
+  int32_t tile_features;   /* output features (rows of wq) per output tile */
+  int32_t tile_tokens;     /* tokens per output tile */
+  int32_t splits;          /* K ranges per output tile (1: K is not split) */
+  int64_t tiles;           /* output tiles */
+  int64_t counter_tiles;   /* most output tiles of one launch that keep a
+                              completion counter in the workspace (0: none) */
+  int32_t launches;        /* kernel launches per call */
+  int32_t waves;           /* waves per workgroup */
+  int32_t two_pass;        /* 1: the K split is summed by a second kernel */
+  int32_t reserved;
+  uint64_t workspace_bytes; /* equals w4a16_workspace_size */
+} w4a16_plan_info;
+
+w4a16_status w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t dtype,
+                        int32_t has_zp, int32_t path, w4a16_plan_info* out);
 
 /* -------------------------------------------------------------- device ---
  * y = x . dequant(wq, scales, zp)^T (+ bias), on the current HIP device,

@@ -21,8 +21,8 @@ W4A16_OK = 0
 W4A16_F16 = 0
 W4A16_BF16 = 1
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
-GEMV_MAX_M = 64
-ABI_VERSION = 2
+GEMV_MAX_M = 16
+ABI_VERSION = 3
 
 STATUS_NAMES = {
     0: "W4A16_OK", 1: "W4A16_ERR_INVALID_ARG", 2: "W4A16_ERR_UNSUPPORTED",
@@ -34,6 +34,7 @@ STATUS_NAMES = {
 _c_int, _c_i32, _c_i64, _c_sz, _vp = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 SIGNATURES = {
     "w4a16_abi_version": (_c_int, []),
+    "w4a16_reload_tuning": (None, []),
     "w4a16_last_error": (ctypes.c_char_p, []),
     "w4a16_pack_weights": (_c_int, [_vp, _c_i64, _c_i64, _vp]),
     "w4a16_unpack_weights": (_c_int, [_vp, _c_i64, _c_i64, _vp]),
@@ -54,6 +55,23 @@ SIGNATURES = {
     "w4a16_moe_linear": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
                                   _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _vp]),
 }
+
+
+class PlanInfo(ctypes.Structure):
+    """w4a16_plan_info (include/w4a16.h)."""
+    _fields_ = [("path", ctypes.c_int32), ("tile_features", ctypes.c_int32),
+                ("tile_tokens", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("tiles", ctypes.c_int64), ("counter_tiles", ctypes.c_int64),
+                ("launches", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("two_pass", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+SIGNATURES["w4a16_plan"] = (_c_int, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                     ctypes.POINTER(PlanInfo)])
 
 
 class W4A16Error(RuntimeError):
@@ -99,6 +117,11 @@ def w4a16_abi_version() -> int:
 
 def w4a16_last_error() -> str:
     return lib.w4a16_last_error().decode()
+
+
+def w4a16_reload_tuning() -> None:
+    """Re-read the tuning environment variables (the library reads them once)."""
+    lib.w4a16_reload_tuning()
 
 
 # ------------------------------------------------------------------ host ---
@@ -158,6 +181,14 @@ def w4a16_select_path(M, N, K, group_size, dtype, has_zp) -> int:
 
 def w4a16_workspace_size(M, N, K, group_size, dtype, has_zp, path=PATH_AUTO) -> int:
     return int(lib.w4a16_workspace_size(M, N, K, group_size, dtype, int(bool(has_zp)), path))
+
+
+def w4a16_plan(M, N, K, group_size, dtype, has_zp, path=PATH_AUTO) -> dict:
+    """How the library would run this problem (host only): path, tile shape,
+    output tiles, K splits, launches, waves, workspace bytes."""
+    info = PlanInfo()
+    _check(lib.w4a16_plan(M, N, K, group_size, dtype, int(bool(has_zp)), path, ctypes.byref(info)))
+    return info.as_dict()
 
 
 def w4a16_check_args(x_ptr, wq_ptr, s_ptr, zp_ptr, bias_ptr, y_ptr, M, N, K, group_size, dtype):

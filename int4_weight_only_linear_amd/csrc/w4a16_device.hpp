@@ -312,6 +312,11 @@ __device__ __forceinline__ GroupConst<DT> group_const(uint16_t s_bits, uint32_t 
   return g;
 }
 
+// s_waitcnt vmcnt(0): every vector memory access of this wave has completed
+// (gfx9 counts stores in vmcnt too).  expcnt and lgkmcnt fields left at their
+// maxima, so only vmcnt is waited for.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Cross-workgroup hand-off of fp32 partial sums (split K) without
 // cache-wide maintenance.  Every XCD has its own L2, so agent-scope
 // release/acquire fences write back and invalidate the whole L2 of the XCD
@@ -319,10 +324,12 @@ __device__ __forceinline__ GroupConst<DT> group_const(uint16_t s_bits, uint32_t 
 // more than the hand-off and evicts the weights the other workgroups are
 // streaming.  Instead the partial sums themselves are written and read with
 // agent-scope relaxed atomic accesses (write-through to, and reads from, the
-// device-coherent level), and the order comes from the waits: a workgroup
-// barrier after the stores (it waits for them to complete) before the
-// completion counter is incremented, and the counter's result, shared
-// through LDS and a barrier, before the loads are issued.
+// device-coherent level), and the order comes from explicit waits: each wave
+// waits for its own partial-sum stores to complete (wait_vm_all: a workgroup
+// barrier alone does not wait for outstanding stores), then a workgroup
+// barrier, then one thread increments the completion counter; the counter's
+// result, shared through LDS and a barrier, orders the last workgroup's
+// loads after every other workgroup's completed stores.
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -29,8 +29,6 @@
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
 
-#include <cstdio>
-#include <cstdlib>
 
 namespace w4a16 {
 
@@ -74,8 +72,6 @@ __device__ __forceinline__ int xcd_unit(int b, int units) {
   const int xcd = b % kXcds, local = b / kXcds;
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
-
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int DT, int GS, bool ASYM, int MB, int CB>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
@@ -419,7 +415,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     uint64_t* mine = reinterpret_cast<uint64_t*>(p.partial) + (size_t)(tile * p.splits + split) * slot;
 #pragma unroll
     for (int i = 0; i < NV / 2; ++i) store_coherent_pair(mine + (size_t)i * kThreads + tid, val(2 * i), val(2 * i + 1));
-    __syncthreads();  // every thread's partial sums are stored
+    // every thread's partial sums have completed (stores count in vmcnt on
+    // gfx950; the barrier itself does not wait for them), then one arrival
+    wait_vm_all();
+    __syncthreads();
     if (tid == 0) last_flag = (arrive(p.counters + tile) == (uint32_t)(p.splits - 1));
     __syncthreads();
     if (!last_flag) return;
@@ -636,9 +635,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool a
     }
   }
   // tuning override "mb,splits[,two_pass[,cb]]" (tile 32*mb x 128*cb, K ranges), e.g. for sweeps
-  if (const char* env = std::getenv("W4A16_GEMM_TILE")) {
-    int mb = 0, splits = 0, tp = 0, cb = 2;
-    if (std::sscanf(env, "%d,%d,%d,%d", &mb, &splits, &tp, &cb) >= 2 && (mb == 4 || mb == 6 || mb == 8) &&
+  const Tuning& tu = tuning();
+  if (tu.gemm_tile_n >= 2) {
+    const int mb = tu.gemm_tile[0], splits = tu.gemm_tile[1];
+    const int tp = tu.gemm_tile_n >= 3 ? tu.gemm_tile[2] : 0;
+    const int cb = tu.gemm_tile_n >= 4 ? tu.gemm_tile[3] : 2;
+    if ((mb == 4 || mb == 6 || mb == 8) &&
         (cb == 2 || (cb == 1 && mb != 6)) && splits >= 1 && splits <= nsteps && (tp == 0 || mb == 4)) {
       const int sps = (nsteps + splits - 1) / splits;
       const int64_t tiles_n = (N + 128 * cb - 1) / (128 * cb);

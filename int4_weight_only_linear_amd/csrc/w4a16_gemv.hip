@@ -1,4 +1,4 @@
-// Skinny split-K W4A16 decode kernels for gfx950 (M <= 64).
+// Skinny split-K W4A16 decode kernel for gfx950 (M <= 16).
 //
 // The pages' decode path ("[ROCm][Kernel] Add HybridW4A16LinearKernel: Triton
 // prefill + HIP skinny decode", description) is a split-K skinny GEMM for
@@ -42,15 +42,13 @@
 //   row tile the partial sums go through the workspace and the last workgroup
 //   to arrive adds them in range order.  Results do not depend on scheduling.
 //
-// gemv_small_kernel serves M <= 16 (one MFMA row tile).  gemv_wide_kernel
-// serves 16 < M <= 64 with up to four row tiles, reading the A operands from
-// global memory (L2-resident) instead of staging x.
+// gemv_small_kernel serves M <= 16 (one MFMA row tile of tokens).  Above
+// that the prefill GEMM is faster at every measured shape.
 #include <type_traits>
 
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
 
-#include <cstdlib>
 
 namespace w4a16 {
 
@@ -62,7 +60,9 @@ struct GemvParams {
   const uint16_t* bias;
   uint16_t* y;
   float* partial;      // [splits][M][N] when splits > 1
-  uint32_t* counters;  // [tiles] when splits > 1; zero between calls
+  uint32_t* counters;  // [launch tiles] when splits > 1; zero between calls
+  int tile_base;       // row tile of blockIdx.x == 0: a split layer with more row
+                       // tiles than counters is launched in chunks of tiles
   int M, N, K, G;
   int sG, gmul;  // scale / zero-point index of (row n, group g): n * sG + g * gmul
   int nchunks;  // K / 32
@@ -166,6 +166,7 @@ __device__ __forceinline__ WeightWalk weight_walk(const uint32_t* wq, int N, int
 template <int DT>
 __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* red, int nwaves,
                                             int nel, int tile, int split, int* last_flag) {
+  uint32_t* const counter = p.counters + (tile - p.tile_base);  // this launch's tiles
   for (int e = threadIdx.x; e < nel; e += blockDim.x) {
     const int mt = e >> 8;
     const int r = (e >> 6) & 3;
@@ -185,9 +186,12 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
   }
   if (p.splits == 1) return;
 
-  __syncthreads();  // every thread's partial sums are stored
+  // every thread's partial sums have completed (stores count in vmcnt on
+  // gfx950; the barrier itself does not wait for them), then one arrival
+  wait_vm_all();
+  __syncthreads();
   if (threadIdx.x == 0)
-    *last_flag = (arrive(p.counters + tile) == (uint32_t)(p.splits - 1));
+    *last_flag = (arrive(counter) == (uint32_t)(p.splits - 1));
   __syncthreads();
   if (!*last_flag) return;
   for (int e = threadIdx.x; e < 16 * p.M; e += blockDim.x) {
@@ -200,7 +204,7 @@ __device__ __forceinline__ void finish_tile(const GemvParams& p, const float* re
       p.y[(size_t)m * p.N + nn] = f32_to_act<DT>(v * p.yscale);
     }
   }
-  if (threadIdx.x == 0) reset_counter(p.counters + tile);  // ready for the next call
+  if (threadIdx.x == 0) reset_counter(counter);  // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
   if constexpr (MOE) {
     if (!select_slot(p)) {
       // not an expert: a zero row (the whole workgroup leaves here)
-      const int n = blockIdx.x * kGemvRowsPerTile + tid;
+      const int n = (blockIdx.x + p.tile_base) * kGemvRowsPerTile + tid;
       if (tid < kGemvRowsPerTile && n < p.N) p.y[n] = 0;
       return;
     }
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
   const int nwaves = p.waves;
   const int col = lane & 15;   // MFMA column: output row within the tile
   const int row4 = lane >> 4;  // 16-lane row of the wave
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.x + p.tile_base;
   const int split = blockIdx.y;
   const int n0 = tile * kGemvRowsPerTile;
 
@@ -648,109 +652,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
 }
 
 // ---------------------------------------------------------------------------
-// 16 < M <= 64: MT row tiles, A operands from global memory
-// ---------------------------------------------------------------------------
-template <int DT, int MT, int GS, bool ASYM, int KPW>
-__global__ __launch_bounds__(1024) void gemv_wide_kernel(const GemvParams p) {
-  constexpr int CPG = GS / 32;
-  constexpr int GPS = 4 / CPG;
-  constexpr int NEL = MT * 256;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int last_flag;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
-  const int col = lane & 15;
-  const int row4 = lane >> 4;
-  const int tile = blockIdx.x;
-  const int split = blockIdx.y;
-  const int n = tile * kGemvRowsPerTile + col;
-  const int nc = min(n, p.N - 1);
-  const WeightWalk ww = weight_walk(p.wq, p.N, p.K, p.nchunks, tile * kGemvRowsPerTile, col, row4);
-  const uint16_t* srow = p.scales + (size_t)nc * p.sG;
-
-  const int ks_begin = split * p.ksteps_per_split;
-  const int ks_end = min(p.ksteps, ks_begin + p.ksteps_per_split);
-  const int my_first = ks_begin + wave * p.kpw;
-  const int my_steps = max(0, min(p.kpw, ks_end - my_first));
-  float* red = reinterpret_cast<float*>(smem);
-
-  u32x4 wv[KPW];
-  uint32_t sv[KPW][GPS];
-  uint32_t zw[KPW][GPS];
-#pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    const int ks = min(my_first + i, ks_end - 1);
-    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ww.at(ks)));
-#pragma unroll
-    for (int h = 0; h < GPS; ++h) {
-      const int grp = min((ks * 4 + h * CPG) / CPG, p.G - 1);
-      sv[i][h] = srow[grp * p.gmul];
-      zw[i][h] = ASYM ? p.zp[(size_t)(nc >> 3) * p.sG + grp * p.gmul] : 0u;
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint32_t mask_v = vgpr_const(0x000F000Fu);
-
-#pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    if (i >= my_steps) break;
-    __builtin_amdgcn_sched_barrier(0);  // this step's work after its own wait
-    const int c0 = (my_first + i) * 4;
-    u32x4 wt = wv[i];
-    if (c0 + 4 > p.nchunks) transpose_rows4(wt);  // incomplete run: stored in order
-    f32x4 tq[MT], tc[MT];
-    uint32_t bc = neg_magic_pair<DT>(8u);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = c0 + t;
-      if (c >= p.nchunks) break;
-      if (ASYM && (t % CPG == 0)) bc = neg_magic_pair<DT>((zw[i][t / CPG] >> (4 * (n & 7))) & 0xFu);
-      const u32x4 bq = (DT == DT_F16) ? qz_word_f16(wt[t], mask_v, bc) : magic_word<DT>(wt[t], mask_v);
-      const u32x4 bcv = {bc, bc, bc, bc};
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = min(mt * 16 + col, p.M - 1);  // rows >= M: any valid row
-        const u32x4 a = *reinterpret_cast<const u32x4*>(p.x + (size_t)m * p.K + c * 32 + row4 * 8);
-        const bool fresh = (t % CPG) == 0;
-        tq[mt] = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : tq[mt]);
-        // bf16: a second MFMA against the constant -(128 + z) removes the offset
-        if constexpr (DT == DT_BF16)
-          tc[mt] = mfma16x16x32<DT>(a, bcv, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : tc[mt]);
-      }
-      if (t % CPG == CPG - 1) {
-        const float s = act_to_f32<DT>((uint16_t)sv[i][t / CPG]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt] += s * tq[mt];
-          if constexpr (DT == DT_BF16) acc[mt] += s * tc[mt];
-        }
-      }
-    }
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave * NEL + (mt * 4 + r) * 64 + lane] = acc[mt][r];
-  __syncthreads();
-  finish_tile<DT>(p, red, nwaves, NEL, tile, split, &last_flag);
-}
-
-// ---------------------------------------------------------------------------
 // planning and launch
 // ---------------------------------------------------------------------------
 
 // one wave's staging region of the M <= 16 kernel: x rows of its run (padded
 // by 16 bytes), the scales of its 16 rows and groups, the zero-point words
-size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int kpw, int group) {
-  const size_t red = (size_t)waves * mtiles * 256 * sizeof(float);
-  if (mtiles > 1) return red;
+size_t gemv_lds_bytes(int waves, int64_t M, int kpw, int group) {
+  const size_t red = (size_t)waves * 256 * sizeof(float);
   return red + (size_t)waves * (size_t)gemv_wave_lds_bytes((int)M, kpw, group);
 }
 
@@ -758,8 +666,6 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   GemvPlan p;
   p.tiles = (int)((N + kGemvRowsPerTile - 1) / kGemvRowsPerTile);
   p.ksteps = (int)((K + kGemvKStep - 1) / kGemvKStep);
-  p.mtiles = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  p.xlds = p.mtiles == 1;
   // k-steps per wave: a power of two, at most kGemvStepsPerWave; with x
   // staged, also small enough that a lane stages at most kGemvXSegsPerThread
   // x segments (M * 16 * kpw segments per wave, 64 lanes): kpw <= 4 * XPT / M.
@@ -772,14 +678,11 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   // slower on K = 9728, where it splits)
   int kpw = kGemvStepsPerWave;
   const bool deep = M == 1 || (M <= 4 && p.ksteps > 4 * kGemvMaxWaves);
-  if (p.xlds)
-    while (kpw > 1 && (M * kpw > 4 * kGemvXSegsPerThread || (kpw > 4 && !deep) || M > 8)) kpw >>= 1;
+  while (kpw > 1 && (M * kpw > 4 * kGemvXSegsPerThread || (kpw > 4 && !deep) || M > 8)) kpw >>= 1;
   // tuning overrides: k-steps per wave (a smaller power of two) and a
   // minimum number of K splits
-  if (const char* env = std::getenv("W4A16_GEMV_KPW")) {
-    const int v = std::atoi(env);
-    if (v >= 1 && v <= kpw && (v & (v - 1)) == 0) kpw = v;
-  }
+  const Tuning& tu = tuning();
+  if (tu.gemv_kpw >= 1 && tu.gemv_kpw <= kpw && (tu.gemv_kpw & (tu.gemv_kpw - 1)) == 0) kpw = tu.gemv_kpw;
   p.kpw = kpw;
   // A K split costs a partial-sum hand-off (2-4 us of coherent memory round
   // trips), more than it saves by filling idle CUs: measured at M = 1 on
@@ -787,24 +690,21 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   // split only (below) when a workgroup's waves or LDS demand it (at most
   // kGemvMaxWaves waves, LDS within the budget).
   int splits = 1;
-  if (const char* env = std::getenv("W4A16_GEMV_SPLITS")) {
-    const int v = std::atoi(env);
-    if (v >= 1 && (v == 1 || p.tiles <= kMaxCounters)) splits = v;  // raised below if it must be
-  }
+  if (tu.gemv_splits >= 1) splits = tu.gemv_splits;  // raised below if it must be
   const size_t budget = p.tiles <= cu_count ? kGemvLdsBudget : kGemvLdsBudgetShared;
   for (;;) {
     if (splits > p.ksteps) splits = p.ksteps;
     const int kps = (p.ksteps + splits - 1) / splits;
     const int waves = (kps + kpw - 1) / kpw;
     if (splits == p.ksteps ||
-        (waves <= kGemvMaxWaves && gemv_lds_bytes(waves, p.mtiles, M, kpw, group) <= budget))
+        (waves <= kGemvMaxWaves && gemv_lds_bytes(waves, M, kpw, group) <= budget))
       break;
     ++splits;
   }
   p.ksteps_per_split = (p.ksteps + splits - 1) / splits;
   p.splits = (p.ksteps + p.ksteps_per_split - 1) / p.ksteps_per_split;
   p.waves = (p.ksteps_per_split + kpw - 1) / kpw;
-  p.lds_bytes = gemv_lds_bytes(p.waves, p.mtiles, M, kpw, group);
+  p.lds_bytes = gemv_lds_bytes(p.waves, M, kpw, group);
   return p;
 }
 
@@ -838,7 +738,7 @@ static hipError_t launch_small(const GemvParams& prm, const GemvPlan& plan, dim3
                     plan.ksteps == 8 * plan.waves && plan.waves <= kGemvMaxWaves &&
                     (prm.sG & 7) == 0 && aligned16(prm.scales) && (!prm.zp || aligned16(prm.zp)) &&
                     (!MOE || ((prm.s_estride & 7) == 0 && (prm.z_estride & 3) == 0)) &&
-                    std::getenv("W4A16_GEMV_NO_WGSZ") == nullptr;
+                    !tuning().gemv_no_wgsz;
   switch (plan.kpw) {
     case 8:
       if (one) {
@@ -864,41 +764,25 @@ static hipError_t launch_small(const GemvParams& prm, const GemvPlan& plan, dim3
   return hipGetLastError();
 }
 
-template <int DT, int MT, int GS, bool ASYM>
-static hipError_t launch_t(const GemvParams& prm, const GemvPlan& plan, hipStream_t s) {
-  dim3 grid(plan.tiles, plan.splits, prm.slots);
+template <int DT, int GS, bool ASYM>
+static hipError_t launch_t(const GemvParams& prm, const GemvPlan& plan, int launch_tiles, hipStream_t s) {
+  dim3 grid(launch_tiles, plan.splits, prm.slots);
   dim3 block(plan.waves * 64);
-  constexpr int KPW = kGemvStepsPerWave;
-  if constexpr (MT == 1) {
-    return prm.moe_ids ? launch_small<DT, GS, ASYM, true>(prm, plan, grid, block, s)
-                       : launch_small<DT, GS, ASYM, false>(prm, plan, grid, block, s);
-  } else {
-    hipLaunchKernelGGL((gemv_wide_kernel<DT, MT, GS, ASYM, KPW>), grid, block, plan.lds_bytes, s, prm);
-    return hipGetLastError();
-  }
+  return prm.moe_ids ? launch_small<DT, GS, ASYM, true>(prm, plan, grid, block, s)
+                     : launch_small<DT, GS, ASYM, false>(prm, plan, grid, block, s);
 }
 
-template <int DT, int MT, int GS>
-static hipError_t launch_z(const GemvParams& prm, const GemvPlan& plan, hipStream_t s) {
-  return prm.zp ? launch_t<DT, MT, GS, true>(prm, plan, s) : launch_t<DT, MT, GS, false>(prm, plan, s);
-}
-
-template <int DT, int MT>
-static hipError_t launch_g(const GemvParams& prm, int group, const GemvPlan& plan, hipStream_t s) {
-  switch (group) {
-    case 32: return launch_z<DT, MT, 32>(prm, plan, s);
-    case 64: return launch_z<DT, MT, 64>(prm, plan, s);
-    case 128: return launch_z<DT, MT, 128>(prm, plan, s);
-    default: return hipErrorInvalidValue;
-  }
+template <int DT, int GS>
+static hipError_t launch_z(const GemvParams& prm, const GemvPlan& plan, int lt, hipStream_t s) {
+  return prm.zp ? launch_t<DT, GS, true>(prm, plan, lt, s) : launch_t<DT, GS, false>(prm, plan, lt, s);
 }
 
 template <int DT>
-static hipError_t launch_m(const GemvParams& prm, int group, const GemvPlan& plan, hipStream_t s) {
-  switch (plan.mtiles) {
-    case 1: return launch_g<DT, 1>(prm, group, plan, s);
-    case 2: return launch_g<DT, 2>(prm, group, plan, s);
-    case 4: return launch_g<DT, 4>(prm, group, plan, s);
+static hipError_t launch_g(const GemvParams& prm, int group, const GemvPlan& plan, int lt, hipStream_t s) {
+  switch (group) {
+    case 32: return launch_z<DT, 32>(prm, plan, lt, s);
+    case 64: return launch_z<DT, 64>(prm, plan, lt, s);
+    case 128: return launch_z<DT, 128>(prm, plan, lt, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -909,7 +793,8 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
       plan.kpw < 1 || plan.kpw > kGemvStepsPerWave)
     return hipErrorInvalidConfiguration;
   // expert-indexed: one M = 1 product per slot, one K range
-  if (moe && (a.M != 1 || plan.splits != 1 || plan.mtiles != 1 || moe->slots < 1 ||
+  if (a.M < 1 || a.M > kGemvMaxM) return hipErrorInvalidConfiguration;
+  if (moe && (a.M != 1 || plan.splits != 1 || moe->slots < 1 ||
               moe->slots > kMaxGridZ))
     return hipErrorInvalidConfiguration;
   GemvParams prm;
@@ -938,6 +823,7 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
   prm.y = static_cast<uint16_t*>(a.y);
   prm.counters = nullptr;
   prm.partial = nullptr;
+  prm.tile_base = 0;
   if (plan.splits > 1) {
     prm.counters = static_cast<uint32_t*>(workspace);
     prm.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
@@ -963,8 +849,19 @@ hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspac
     prm.lg_groups_per_wave = lg;
     prm.wave_lds_bytes = gemv_wave_lds_bytes((int)a.M, plan.kpw, a.group);
   }
-  return a.dtype == DT_F16 ? launch_m<DT_F16>(prm, a.group, plan, stream)
-                           : launch_m<DT_BF16>(prm, a.group, plan, stream);
+  // With a K split every row tile of a launch needs its own completion
+  // counter, and the counter region holds kMaxCounters: a layer with more row
+  // tiles is launched in chunks of row tiles, one after another on the stream
+  // (each chunk's last workgroups leave its counters zero for the next).
+  const int chunk = plan.splits > 1 ? (int)kMaxCounters : plan.tiles;
+  for (int t0 = 0; t0 < plan.tiles; t0 += chunk) {
+    prm.tile_base = t0;
+    const int lt = min(chunk, plan.tiles - t0);
+    const hipError_t e = a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, plan, lt, stream)
+                                           : launch_g<DT_BF16>(prm, a.group, plan, lt, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace w4a16

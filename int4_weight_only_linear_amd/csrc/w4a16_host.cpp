@@ -11,14 +11,70 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
 
 #include "w4a16_internal.h"
+
+namespace w4a16 {
+
+namespace {
+
+Tuning read_tuning() {
+  Tuning t{};
+  t.m_threshold = -1;
+  if (const char* e = std::getenv("W4A16_FORCE_PATH")) {
+    if (std::strcmp(e, "gemv") == 0) t.force_path = W4A16_PATH_GEMV;
+    if (std::strcmp(e, "gemm") == 0) t.force_path = W4A16_PATH_GEMM;
+  }
+  if (const char* e = std::getenv("W4A16_M_THRESHOLD")) {
+    char* end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    if (end != e && v >= 0 && v <= W4A16_GEMV_MAX_M) t.m_threshold = (int)v;
+  }
+  if (const char* e = std::getenv("W4A16_GEMM_TILE")) {
+    const int n = std::sscanf(e, "%d,%d,%d,%d", &t.gemm_tile[0], &t.gemm_tile[1], &t.gemm_tile[2],
+                              &t.gemm_tile[3]);
+    t.gemm_tile_n = n > 0 ? n : 0;
+  }
+  if (const char* e = std::getenv("W4A16_GEMV_KPW")) t.gemv_kpw = std::atoi(e);
+  if (const char* e = std::getenv("W4A16_GEMV_SPLITS")) t.gemv_splits = std::atoi(e);
+  t.gemv_no_wgsz = std::getenv("W4A16_GEMV_NO_WGSZ") != nullptr;
+  if (const char* e = std::getenv("W4A16_LOG")) t.log = *e && std::strcmp(e, "0") != 0;
+  return t;
+}
+
+// The current settings.  A reload publishes a new copy and keeps the old one
+// (a few dozen bytes per reload), so a reader that still holds it stays valid.
+std::atomic<const Tuning*> g_tuning{nullptr};
+std::mutex g_tuning_mutex;
+
+}  // namespace
+
+const Tuning& tuning() {
+  const Tuning* t = g_tuning.load(std::memory_order_acquire);
+  if (t) return *t;
+  std::lock_guard<std::mutex> lock(g_tuning_mutex);
+  t = g_tuning.load(std::memory_order_acquire);
+  if (!t) {
+    t = new Tuning(read_tuning());
+    g_tuning.store(t, std::memory_order_release);
+  }
+  return *t;
+}
+
+void reload_tuning() {
+  std::lock_guard<std::mutex> lock(g_tuning_mutex);
+  g_tuning.store(new Tuning(read_tuning()), std::memory_order_release);
+}
+
+}  // namespace w4a16
 
 namespace {
 
@@ -119,20 +175,16 @@ GroupMap group_map(int32_t g, int64_t K) {
 // above, measured, not the pages'.
 int64_t gemv_threshold(int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t has_zp) {
   (void)N; (void)group; (void)dtype; (void)has_zp;
-  if (const char* env = std::getenv("W4A16_M_THRESHOLD")) {
-    const long v = std::strtol(env, nullptr, 10);
-    if (v >= 0 && v <= W4A16_GEMV_MAX_M) return v;
-  }
+  const int v = w4a16::tuning().m_threshold;
+  if (v >= 0 && v <= W4A16_GEMV_MAX_M) return v;
   return K <= 4096 ? 16 : 8;
 }
 
 w4a16_path resolve_path(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,
                         int32_t has_zp, int32_t path) {
   if (path == W4A16_PATH_GEMV || path == W4A16_PATH_GEMM) return (w4a16_path)path;
-  if (const char* env = std::getenv("W4A16_FORCE_PATH")) {
-    if (std::strcmp(env, "gemv") == 0) return W4A16_PATH_GEMV;
-    if (std::strcmp(env, "gemm") == 0) return W4A16_PATH_GEMM;
-  }
+  const int forced = w4a16::tuning().force_path;
+  if (forced == W4A16_PATH_GEMV || forced == W4A16_PATH_GEMM) return (w4a16_path)forced;
   return M <= gemv_threshold(N, K, group, dtype, has_zp) ? W4A16_PATH_GEMV : W4A16_PATH_GEMM;
 }
 
@@ -148,13 +200,7 @@ size_t workspace_for(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dty
   return w4a16::gemm_workspace_bytes(M, N, K, group, dtype, asym, cu_count);
 }
 
-bool log_enabled() {
-  static const bool on = [] {
-    const char* e = std::getenv("W4A16_LOG");
-    return e && *e && std::strcmp(e, "0") != 0;
-  }();
-  return on;
-}
+bool log_enabled() { return w4a16::tuning().log; }
 
 w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, const int32_t* zp,
                          const void* bias, void* y, int64_t M, int64_t N, int64_t K,
@@ -223,6 +269,8 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
 extern "C" {
 
 int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+void w4a16_reload_tuning(void) { w4a16::reload_tuning(); }
 
 const char* w4a16_last_error(void) { return g_last_error.c_str(); }
 
@@ -365,6 +413,61 @@ size_t w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size,
     g_last_error.clear();
   }
   return workspace_for(M, N, K, kgroup, dtype, has_zp != 0, p, cus);
+}
+
+w4a16_status w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t dtype,
+                        int32_t has_zp, int32_t path, w4a16_plan_info* out) {
+  if (!out) return fail(W4A16_ERR_INVALID_ARG, "plan: out must not be NULL");
+  if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+    return fail(W4A16_ERR_INVALID_ARG, "activation dtype must be fp16 (0) or bf16 (1), got %d", (int)dtype);
+  if (!group_ok(group_size, K))
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "group size must be 32, 64, 128 or K (per-channel, K %% 32 == 0), got %d (K=%lld)",
+                (int)group_size, (long long)K);
+  if (M < 1 || N < 1 || K < group_size || K % group_size || M > INT32_MAX || N > INT32_MAX)
+    return fail(W4A16_ERR_INVALID_ARG, "plan: need M >= 1, N >= 1 and K a positive multiple of the group");
+  if (K > w4a16::kMaxK)
+    return fail(W4A16_ERR_UNSUPPORTED, "K above %lld is not supported", (long long)w4a16::kMaxK);
+  if (has_zp && N % 8)
+    return fail(W4A16_ERR_INVALID_ARG, "packed zero points need N %% 8 == 0, got N=%lld", (long long)N);
+  if (path < W4A16_PATH_AUTO || path > W4A16_PATH_GEMM)
+    return fail(W4A16_ERR_INVALID_ARG, "unknown path %d", (int)path);
+  const GroupMap gm = group_map(group_size, K);
+  const w4a16_path p = resolve_path(M, N, K, gm.kgroup, dtype, has_zp, path);
+  if (p == W4A16_PATH_GEMV && M > W4A16_GEMV_MAX_M)
+    return fail(W4A16_ERR_UNSUPPORTED, "the decode kernel takes M <= %d, got M=%lld",
+                W4A16_GEMV_MAX_M, (long long)M);
+  int cus = kPlanningCUs;
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    const DeviceInfo* d = nullptr;
+    if (device_info(&d) == W4A16_OK) cus = d->cu_count;
+  }
+  w4a16_plan_info r{};
+  r.path = p;
+  if (p == W4A16_PATH_GEMV) {
+    const w4a16::GemvPlan g = w4a16::plan_gemv(M, N, K, gm.kgroup, cus);
+    r.tile_features = w4a16::kGemvRowsPerTile;
+    r.tile_tokens = w4a16::kGemvMaxM;
+    r.splits = g.splits;
+    r.tiles = g.tiles;
+    r.waves = g.waves;
+    r.launches = g.splits > 1 ? (int32_t)((g.tiles + w4a16::kMaxCounters - 1) / w4a16::kMaxCounters) : 1;
+    r.counter_tiles = g.splits > 1 ? std::min<int64_t>(g.tiles, w4a16::kMaxCounters) : 0;
+  } else {
+    const w4a16::GemmPlan g = w4a16::plan_gemm(M, N, K, gm.kgroup, dtype, has_zp != 0, cus);
+    r.tile_features = 128 * g.cb;
+    r.tile_tokens = 32 * g.mb;
+    r.splits = g.splits;
+    r.tiles = g.tiles;
+    r.waves = 4;
+    r.two_pass = g.splits > 1 && g.two_pass;
+    r.launches = r.two_pass ? 2 : 1;
+    r.counter_tiles = g.splits > 1 && !g.two_pass ? g.tiles : 0;
+  }
+  r.workspace_bytes = workspace_for(M, N, K, gm.kgroup, dtype, has_zp != 0, p, cus);
+  *out = r;
+  return ok();
 }
 
 w4a16_status w4a16_linear(const void* x, const int32_t* wq, const void* scales, const int32_t* zp,

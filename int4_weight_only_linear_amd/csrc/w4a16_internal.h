@@ -24,6 +24,23 @@ struct LinearArgs {
   int gmul;   // 1, or 0 for per-channel scales (every group of a row reads column 0)
 };
 
+// ---- tuning overrides ------------------------------------------------------
+// Read from the environment once, at the first call that needs them (so a
+// launch costs no getenv), and again on w4a16_reload_tuning().  None is
+// needed for correctness; they serve sweeps, tests and experiments.
+struct Tuning {
+  int force_path;       // W4A16_FORCE_PATH: 0 none, 1 gemv, 2 gemm
+  int m_threshold;      // W4A16_M_THRESHOLD: -1 for the measured default
+  int gemm_tile[4];     // W4A16_GEMM_TILE "mb,splits[,two_pass[,cb]]"
+  int gemm_tile_n;      //   fields given (0: not set)
+  int gemv_kpw;         // W4A16_GEMV_KPW: 0 for the planner's choice
+  int gemv_splits;      // W4A16_GEMV_SPLITS: 0 for the planner's choice
+  bool gemv_no_wgsz;    // W4A16_GEMV_NO_WGSZ: per-wave scale loads only
+  bool log;             // W4A16_LOG: one line per call on stderr
+};
+const Tuning& tuning();
+void reload_tuning();
+
 // ---- workspace ---------------------------------------------------------------
 // Both kernels that split K keep one completion counter per output tile at the
 // start of the workspace and their fp32 partial sums after this fixed-size
@@ -40,12 +57,13 @@ constexpr int64_t kMaxCounters = (int64_t)(kCounterBytes / sizeof(uint32_t));
 // are reduced through LDS.  With more than one split, each workgroup stores
 // fp32 partial sums and the last one to finish a row tile adds them up in
 // split order (counter in the workspace), so results are deterministic.
-// Splitting only happens when there are fewer row tiles than CUs, so the
-// counters always fit the counter region.
+// A split layer with more row tiles than kMaxCounters is launched in chunks
+// of at most kMaxCounters row tiles (the launches run one after another on
+// the stream), so every launch's counters fit the counter region.
 constexpr int kGemvRowsPerTile = 16;
 constexpr int kGemvKStep = 128;       // k per wave step: 4 chunks of 32
 constexpr int kGemvMaxWaves = 16;     // 1024 threads
-constexpr int kGemvMaxMTiles = 4;     // M <= 64
+constexpr int kGemvMaxM = 16;         // one MFMA row tile of tokens
 constexpr int kGemvStepsPerWave = 8;
 // decode, single token bf16 g128: the workgroup's scales (16 rows x 8 groups
 // per wave, bf16) and packed zero points (2 row blocks x 8 groups per wave)
@@ -69,9 +87,7 @@ struct GemvPlan {
   int splits;            // K ranges per row tile
   int ksteps_per_split;
   int waves;             // waves per workgroup
-  int mtiles;            // 16-row M tiles (1, 2 or 4)
   int kpw;               // k-steps per wave (upper bound)
-  bool xlds;             // x staged in LDS (M <= 16)
   size_t lds_bytes;      // dynamic LDS of one workgroup
 };
 
@@ -87,7 +103,7 @@ __host__ __device__ inline int gemv_wave_lds_bytes(int M, int kpw, int group) {
   b += M * (kr / 16) * 4 + ngr * 16 * 4;
   return (b + 15) / 16 * 16;
 }
-size_t gemv_lds_bytes(int waves, int mtiles, int64_t M, int kpw, int group);
+size_t gemv_lds_bytes(int waves, int64_t M, int kpw, int group);
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N);
 // Expert-indexed decode: slots = M * topk products of one token row with the

@@ -17,3 +17,29 @@ def pytest_configure(config):
 def gpu_available():
     import torch
     return torch.cuda.is_available()
+
+
+@pytest.fixture
+def tuning_env():
+    """Set libw4a16 tuning variables for one test: the library reads them once,
+    so each change is followed by w4a16_reload_tuning(), and at the end the
+    previous values are restored and read again."""
+    import int4_weight_only_linear_amd as L
+    saved = {}
+
+    def set_(name, value):
+        if name not in saved:
+            saved[name] = os.environ.get(name)
+        if value is None:
+            os.environ.pop(name, None)
+        else:
+            os.environ[name] = str(value)
+        L.w4a16_reload_tuning()
+
+    yield set_
+    for name, old in saved.items():
+        if old is None:
+            os.environ.pop(name, None)
+        else:
+            os.environ[name] = old
+    L.w4a16_reload_tuning()

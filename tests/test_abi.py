@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert L.w4a16_abi_version() == L.ABI_VERSION == 2
+    assert L.w4a16_abi_version() == L.ABI_VERSION == 3
     m = re.search(r"#define W4A16_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == L.w4a16_abi_version()
     m = re.search(r"#define W4A16_GEMV_MAX_M (\d+)", open(HEADER).read())
@@ -175,10 +175,10 @@ def test_select_path_by_m():
         assert L.w4a16_select_path(M, 4096, 14336, 128, 1, 1) == L.PATH_GEMM
 
 
-def test_select_path_env_override(monkeypatch):
-    monkeypatch.setenv("W4A16_FORCE_PATH", "gemm")
+def test_select_path_env_override(tuning_env):
+    tuning_env("W4A16_FORCE_PATH", "gemm")
     assert L.w4a16_select_path(1, 4096, 4096, 128, 1, 1) == L.PATH_GEMM
-    monkeypatch.setenv("W4A16_FORCE_PATH", "gemv")
+    tuning_env("W4A16_FORCE_PATH", "gemv")
     assert L.w4a16_select_path(128, 4096, 4096, 128, 1, 1) == L.PATH_GEMV
 
 
@@ -253,3 +253,82 @@ def test_gemm_planner_skips_exactly_the_spilling_tiles():
             spilling.add(tuple(int(v) for v in m.groups()))
     excluded = {(0, 32, 0), (0, 32, 1), (0, 64, 1), (1, 32, 0)}  # (dtype, group, asym)
     assert spilling == {(dt, g, a, mb, 2) for (dt, g, a) in excluded for mb in (6, 8)}
+
+
+# ---- launch plans: the completion counters of one launch fit their region -----
+
+KMAXC = 64 * 1024 // 4  # completion counters in the workspace's counter region
+
+
+@pytest.mark.parametrize("path", [L.PATH_GEMV, L.PATH_GEMM])
+def test_every_plan_keeps_its_counters_in_the_counter_region(path):
+    # every launch's tiles that keep a completion counter must fit the 64 KiB
+    # region; decode layers with more row tiles than that and a K split run
+    # as several launches, each covering at most KMAXC row tiles
+    Ms = (1, 2, 3, 4, 5, 8, 16) if path == L.PATH_GEMV else (17, 64, 128, 1920)
+    Ns = (16, 4096, 262144, 262160, 280000, (1 << 21) - 16)
+    Ks = (128, 4096, 8320, 9728, 28672, 1 << 20, 1 << 24)
+    seen_chunked = False
+    for M in Ms:
+        for N in Ns:
+            for K in Ks:
+                for g in (32, 128):
+                    p = L.w4a16_plan(M, N, K, g, L.W4A16_BF16, True, path)
+                    assert p["path"] == path
+                    assert p["counter_tiles"] <= KMAXC, (M, N, K, g, p)
+                    if p["splits"] > 1 and not p["two_pass"]:
+                        per_launch = -(-p["tiles"] // p["launches"]) if path == L.PATH_GEMV else p["tiles"]
+                        assert per_launch <= KMAXC, (M, N, K, g, p)
+                        assert p["workspace_bytes"] >= 64 * 1024
+                    if path == L.PATH_GEMV and p["splits"] > 1:
+                        assert p["launches"] == -(-p["tiles"] // KMAXC)
+                        seen_chunked |= p["launches"] > 1
+                    assert p["workspace_bytes"] == L.w4a16_workspace_size(M, N, K, g, L.W4A16_BF16, True, path)
+    assert seen_chunked or path == L.PATH_GEMM
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 280000, 28672), (5, 270000, 9728), (5, 262160, 8320)])
+def test_split_decode_beyond_the_counter_region_is_chunked(M, N, K):
+    # shapes whose forced K split has more row tiles than there are counters
+    p = L.w4a16_plan(M, N, K, 128, L.W4A16_BF16, True, L.PATH_GEMV)
+    tiles = -(-N // 16)
+    assert p["tiles"] == tiles > KMAXC and p["splits"] >= 2
+    assert p["launches"] == -(-tiles // KMAXC) >= 2 and p["counter_tiles"] == KMAXC
+    assert p["workspace_bytes"] == 64 * 1024 + p["splits"] * M * N * 4
+
+
+def test_plan_errors():
+    with pytest.raises(L.W4A16Error, match="M <= 16"):
+        L.w4a16_plan(17, 64, 256, 128, 1, False, L.PATH_GEMV)
+    with pytest.raises(L.W4A16Error, match="group size"):
+        L.w4a16_plan(1, 64, 256, 48, 1, False)
+    with pytest.raises(L.W4A16Error, match="unknown path"):
+        L.w4a16_plan(1, 64, 256, 128, 1, False, 9)
+
+
+# ---- the pages' accept set, as stored in tests/golden/accept_set.json --------
+
+def test_accept_set_golden_drives_validation():
+    import json
+    g = json.load(open(os.path.join(GOLDEN, "accept_set.json")))
+    dts = {"float16": L.W4A16_F16, "bfloat16": L.W4A16_BF16}
+    for dt_name in g["act_dtypes"]:
+        for gs in g["group_sizes"]:
+            for wt in g["weight_types"]:
+                zp = 5 * P if wt == "uint4" else None   # uint4b8: no zero points
+                assert _check(dt=dts[dt_name], g=gs, K=4 * gs, zp=zp) == 0, (dt_name, gs, wt)
+                # K must be a multiple of the group (the K divisibility rule)
+                assert _check(dt=dts[dt_name], g=gs, K=4 * gs + 8, zp=zp) != 0
+    # group sizes outside the set (and not per-channel) are refused
+    for gs in (16, 48, 96, 256):
+        if gs not in g["group_sizes"]:
+            assert _check(g=gs, K=4 * 256) == 2
+    # a dtype code outside the two act dtypes is refused
+    assert _check(dt=len(g["act_dtypes"])) == 1
+    # uint4b8 means the stored code carries a bias of 8: symmetric == zero point 8
+    assert O.SYMMETRIC_ZERO == g["symmetric_zero_point"]
+    # the pages route M <= 5 to their skinny decode kernel; the measured MI355X
+    # bound keeps every such M on the decode kernel
+    for M in range(1, g["decode_m_threshold_on_pages"] + 1):
+        for K in (2560, 4096, 14336, 28672):
+            assert L.w4a16_select_path(M, 4096, K, 128, L.W4A16_BF16, True) == L.PATH_GEMV

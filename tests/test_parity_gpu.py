@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from synth import make_case, stream_seed, CONFIGS
-from gpu_util import DeviceCase, assert_close, device_to_bits, note, oracle_rows, sample_rows
+from synth import make_case, stream_seed, stored_words, to_act_bits, CONFIGS
+from gpu_util import DeviceCase, assert_close, bits_to_device, device_to_bits, note, oracle_rows, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -127,7 +127,7 @@ def test_linear_grid(M, N, K, g, dt, sym, bias):
     (1048, 14336, True, True),    # fourteen waves, incomplete last row tile
     (1024, 16384, False, False),  # sixteen waves, the most a workgroup has
 ])
-def test_decode_workgroup_scales(monkeypatch, N, K, sym, bias):
+def test_decode_workgroup_scales(tuning_env, N, K, sym, bias):
     # one token, bf16, groups of 128, K a whole number of 8-step runs and one
     # K range: the instance whose workgroup fetches all its waves' scales and
     # zero points at once.  Same arithmetic in the same order as the per-wave
@@ -135,7 +135,7 @@ def test_decode_workgroup_scales(monkeypatch, N, K, sym, bias):
     c = make_case(1, N, K, 128, O.BF16, sym, bias, seed=("wgsz", N, K, sym, bias))
     d = DeviceCase(c)
     y_shared = d.run(GEMV)
-    monkeypatch.setenv("W4A16_GEMV_NO_WGSZ", "1")
+    tuning_env("W4A16_GEMV_NO_WGSZ", "1")
     y_wave = d.run(GEMV)
     assert np.array_equal(y_shared, y_wave)
     assert_close(y_shared, oracle_rows(c), O.BF16, "workgroup scales")
@@ -303,7 +303,7 @@ def test_workspace_errors():
     assert st == 6 and "workspace" in L.w4a16_last_error()
 
 
-# ---- the workloads at full size, on sampled output rows -----------------------
+# ---- the workloads at full size ------------------------------------------------
 
 def _config_points(name):
     c = CONFIGS[name]
@@ -320,20 +320,28 @@ ALL_POINTS = [p for n in ("llama8b_decode", "qwen3_4b_decode", "llama8b_prefill"
               for p in _config_points(n)]
 
 
+def _every_row(name, K, g):
+    # every output row is compared, except on the sweep's 28672 x 4096 layer
+    # with groups of 32 or 64 (sampled rows: the oracle's whole-layer cost
+    # there would dominate the suite); its groups of 128 run in full
+    return not (name == "sweep" and K == 28672 and g != 128)
+
+
 @pytest.mark.parametrize("name,li,K,N,g,sym,dt,bias", ALL_POINTS)
 def test_config_full_size(name, li, K, N, g, sym, dt, bias):
+    # rows of y are independent, so one oracle product over the largest M
+    # serves every M of the point (its first M rows)
     Ms = CONFIGS[name].Ms
     c = make_case(max(Ms), N, K, g, dt, sym, bias, seed=(name, li, g, sym, dt, bias))
     d = DeviceCase(c)
-    rows = sample_rows(N, seed=li)
+    rows = np.arange(N) if _every_row(name, K, g) else sample_rows(N, seed=li)
+    ref_all = oracle_rows(c, None if len(rows) == N else rows)
     full_x = c.x_bits
     for M in Ms:
-        x = full_x[:M].copy()
-        d.set_x(x)
-        ref = oracle_rows(c, rows)
+        d.set_x(full_x[:M].copy())
         for path in (AUTO,) + paths_for(M):
             y = d.run(path)
-            assert_close(y[:, rows], ref, dt, f"M={M} path={path}")
+            assert_close(y[:, rows], ref_all[:M], dt, f"M={M} path={path}")
 
 
 # ---- dequantised prefill copy: dense product over w4a16_dequant's weights -----
@@ -472,8 +480,8 @@ def test_moe_linear_k_bound(g, kmax):
                                   "4,1,0,1", "4,3,0,1", "4,3,1,1", "8,1,0,1", "8,2,0,1"])
 @pytest.mark.parametrize("M,N,K,g,bias", [(130, 200, 640, 64, True), (128, 264, 1216, 32, False),
                                           (300, 56, 2048, 128, True)])
-def test_gemm_k_split_forms(monkeypatch, dt, tile, M, N, K, g, bias):
-    monkeypatch.setenv("W4A16_GEMM_TILE", tile)
+def test_gemm_k_split_forms(tuning_env, dt, tile, M, N, K, g, bias):
+    tuning_env("W4A16_GEMM_TILE", tile)
     c = make_case(M, N, K, g, dt, False, bias, seed=("ksplit", M, N, K, g, dt, bias))
     d = DeviceCase(c)
     y1 = d.run(GEMM)
@@ -510,9 +518,9 @@ def _graph_replays_match(run_eager, run_captured, reps=3):
     (128, 264, 1216, 32, GEMM, "4,4,1"),     # GEMM, two-pass split
     (300, 520, 1024, 128, GEMM, None),       # GEMM, no split
 ])
-def test_graph_capture_linear(monkeypatch, M, N, K, g, path, tile):
+def test_graph_capture_linear(tuning_env, M, N, K, g, path, tile):
     if tile:
-        monkeypatch.setenv("W4A16_GEMM_TILE", tile)
+        tuning_env("W4A16_GEMM_TILE", tile)
     c = make_case(M, N, K, g, O.BF16, False, True, seed=("graph", M, N, K, g, path))
     d = DeviceCase(c)
     need = L.w4a16_workspace_size(M, N, K, g, O.BF16, True, path)
@@ -540,3 +548,135 @@ def test_graph_capture_dense_and_moe():
     run = lambda out=None: L.w4a16_moe_linear(m["x"], m["wq"], m["s"], m["ids"], m["zp"], m["bias"],
                                               m["w"], group_size=64, out=out)
     _graph_replays_match(lambda: run(), lambda: run(y_moe))
+
+
+# ---- guard bands: nothing is written outside y and the workspace ---------------
+
+CANARY16 = 0x7E5A          # an unlikely output pattern (a bf16 / fp16 NaN-free value)
+CANARY8 = 0xA5
+
+
+@pytest.mark.parametrize("M,N,K,g,path,tile,ypad", [
+    (1, 4096, 4096, 128, GEMV, None, 64),      # decode, one K range, aligned y
+    (4, 264, 1152, 64, GEMV, None, 3),         # decode, ragged tile, y at a 6-byte offset
+    (5, 264, 9728, 128, GEMV, None, 64),       # decode, K split (counters + partials)
+    (3, 40, 20480, 32, GEMV, None, 5),         # decode, K split, incomplete tile
+    (300, 520, 1024, 128, GEMM, None, 64),     # GEMM, no split, 16-byte stores
+    (130, 200, 640, 64, GEMM, "4,3,0", 3),     # GEMM, last-workgroup hand-off, element stores
+    (128, 264, 1216, 32, GEMM, "4,4,1", 64),   # GEMM, two-pass split
+    (129, 13, 256, 64, GEMM, "4,2,1", 7),      # GEMM, two-pass, N not a multiple of 8
+])
+def test_guard_bands_around_y_and_workspace(tuning_env, M, N, K, g, path, tile, ypad):
+    if tile:
+        tuning_env("W4A16_GEMM_TILE", tile)
+    sym = N % 8 != 0
+    c = make_case(M, N, K, g, O.BF16, sym, True, seed=("guard", M, N, K, g, path))
+    d = DeviceCase(c)
+    inputs = [t for t in (d.x, d.wq, d.s, d.zp, d.bias) if t is not None]
+    before = [t.clone() for t in inputs]
+    # y inside a larger buffer whose margins hold a canary
+    ybuf = torch.full((ypad + M * N + 64,), CANARY16, dtype=torch.int16, device="cuda")
+    y = ybuf.view(torch.bfloat16)[ypad:ypad + M * N].view(M, N)
+    need = L.w4a16_workspace_size(M, N, K, g, O.BF16, not sym, path)
+    guard = 4096
+    wbuf = torch.full((need + 2 * guard,), CANARY8, dtype=torch.uint8, device="cuda")
+    wbuf[guard:guard + need].zero_()
+    ws = wbuf[guard:guard + need] if need else None
+    for _ in range(2):
+        L.w4a16_linear_path(d.x, d.wq, d.s, d.zp, d.bias, group_size=g, path=path, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(device_to_bits(y), oracle_rows(c), O.BF16, "guarded y")
+        yb = ybuf.cpu().numpy().view(np.uint16)
+        assert np.all(yb[:ypad] == CANARY16) and np.all(yb[ypad + M * N:] == CANARY16), "write outside y"
+        wb = wbuf.cpu().numpy()
+        assert np.all(wb[:guard] == CANARY8) and np.all(wb[guard + need:] == CANARY8), "write outside workspace"
+        if need:
+            # every completed call leaves the counter region zero
+            assert not wb[guard:guard + 64 * 1024].any(), "counters not reset"
+        for t, t0 in zip(inputs, before):
+            assert torch.equal(t, t0), "an input was modified"
+
+
+# ---- negative and extreme scales on both kernels -------------------------------
+
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("sym,g", [(True, 128), (False, 32), (False, 128)])
+@pytest.mark.parametrize("M", [1, 4])
+def test_negative_and_extreme_scales(dt, sym, g, M):
+    # each 16-row tile draws a base exponent over most of the format's range,
+    # every (row, group) scale a random sign and a further factor of 2^[-3, 3];
+    # outputs are compared tile by tile, relative to the tile's largest output
+    N, K = 320, 1024
+    c = make_case(M, N, K, g, dt, sym, False, seed=("xscale", dt, sym, g, M))
+    rng = np.random.default_rng(stream_seed("xscale", dt, sym, g, M))
+    lo, hi = (-20, 3) if dt == O.F16 else (-90, 90)
+    base = np.repeat(rng.uniform(lo, hi, N // 16), 16)[:, None]
+    e = base + rng.uniform(-3, 3, c.s_bits.shape)
+    sgn = np.where(rng.random(c.s_bits.shape) < 0.5, -1.0, 1.0)
+    c.s_bits = O.f32_to_act_bits((sgn * 2.0 ** e).astype(np.float32), dt)
+    d = DeviceCase(c)
+    # the decode kernel never rounds a weight, so it is held to the exact
+    # oracle; the prefill GEMM multiplies the weights rounded once to the act
+    # dtype (the values w4a16_dequant returns), and with scales that vary by
+    # 2^6 inside a tile that rounding alone can reach the bf16 bound relative
+    # to the tile's largest output, so the GEMM is held to the product over
+    # the same rounded weights
+    zpk = None if sym else O.pack_zeros(c.zp)
+    W = O.act_bits_to_f64(O.dequant_act(O.pack_weights(c.q), c.s_bits, zpk, N, K, g, dt), dt)
+    refs = {GEMV: oracle_rows(c), GEMM: O.act_bits_to_f64(c.x_bits, dt) @ W.T}
+    for path in (GEMV, GEMM):
+        y = d.run(path)
+        for t in range(N // 16):
+            r = slice(16 * t, 16 * t + 16)
+            assert_close(y[:, r], refs[path][:, r], dt, f"path {path} tile {t} (2^{base[16 * t, 0]:.0f})")
+
+
+# ---- a split decode layer with more row tiles than completion counters ---------
+
+@pytest.mark.parametrize("M", [3, 5])
+def test_split_decode_past_the_counter_region(M):
+    # N = 262160 rows = 16385 row tiles, one more than the 16384 counters; K =
+    # 8320 makes three and five tokens split K, so the call runs as two
+    # launches (tiles 0..16383, then 16384).  Tiles on both sides of the chunk
+    # boundary are compared with the oracle, twice (the first call's counters
+    # must be zero again for the second).
+    N, K, g = 262160, 8320, 128
+    wpr, G = K // 8, K // g
+    plan = L.w4a16_plan(M, N, K, g, O.BF16, True, GEMV)
+    assert plan["splits"] >= 2 and plan["launches"] == 2 and plan["tiles"] == 16385, plan
+    dev = torch.device("cuda:0")
+    tiles = sorted({0, 1, 9000, 16382, 16383, 16384})
+    note(f"[gpu] chunked split: drawing {N * K // 2 / 2**30:.2f} GiB of packed weights")
+    wq = torch.empty((N, wpr), dtype=torch.int32, device=dev)
+    tile_words = {}
+    block = 1 << 15
+    for r0 in range(0, N, block):
+        rows = min(block, N - r0)
+        words = stored_words("chunked-w", r0, rows, wpr)
+        wq[r0:r0 + rows].copy_(torch.from_numpy(words.view(np.int32)))
+        for t in tiles:
+            if r0 <= 16 * t < r0 + rows:
+                tile_words[t] = words[16 * t - r0:16 * t - r0 + 16].copy()
+        del words
+    zpk = stored_words("chunked-z", 0, N // 8, G)
+    rng = np.random.default_rng(stream_seed("chunked-s"))
+    s_bits = to_act_bits((np.abs(rng.normal(0.0, 0.02, size=(N, G))) + 1e-3).astype(np.float32), O.BF16)
+    x_bits = to_act_bits(rng.normal(0.0, 1.0, size=(M, K)).astype(np.float32), O.BF16)
+    s, zp = bits_to_device(s_bits, O.BF16, dev), torch.from_numpy(zpk.view(np.int32)).to(dev)
+    x = bits_to_device(x_bits, O.BF16, dev)
+    ws = torch.zeros(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+    first = None
+    for rep in range(2):
+        y = L.w4a16_linear_path(x, wq, s, zp, None, group_size=g, path=GEMV, workspace=ws)
+        torch.cuda.synchronize()
+        yb = device_to_bits(y)
+        assert not ws[:64 * 1024].any().item(), "counters not reset"
+        for t in tiles:
+            r = slice(16 * t, 16 * t + 16)
+            ref = O.linear_ref(x_bits, tile_words[t].view(np.int32), s_bits[r],
+                               zpk[2 * t:2 * t + 2].view(np.int32), None, M, 16, K, g, O.BF16)
+            assert_close(yb[:, r], ref, O.BF16, f"M={M} tile={t} call {rep}")
+        if first is None:
+            first = yb
+        else:
+            assert np.array_equal(first, yb)
