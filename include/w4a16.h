@@ -213,6 +213,27 @@ w4a16_status w4a16_linear_path(const void* x, const int32_t* wq, const void* sca
                                int32_t dtype, void* workspace, size_t workspace_bytes,
                                void* stream, int32_t path);
 
+/* Allocation-free variant of w4a16_linear, for callers that cannot allocate
+ * device memory or take a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, layout,
+ * numerics and results as w4a16_linear with W4A16_PATH_AUTO, minus the
+ * workspace: a K split keeps its completion counters and fp32 partial sums in
+ * a scratch array of W4A16_NOALLOC_SCRATCH_BYTES that the library holds in
+ * device memory, one per GPU, from module load until the process ends.  The
+ * call itself allocates nothing.  Its first call on a device looks up that
+ * device's array and clears its counters with a kernel on `stream`.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (other streams, other
+ * threads) race and give wrong results; serialise them (one stream).
+ * Errors: those of w4a16_linear except W4A16_ERR_WORKSPACE; and
+ * W4A16_ERR_UNSUPPORTED when the problem needs more split-K workspace than
+ * the array holds (w4a16_workspace_size above W4A16_NOALLOC_SCRATCH_BYTES). */
+#define W4A16_NOALLOC_SCRATCH_BYTES (64u << 20)
+w4a16_status w4a16_linear_noalloc(const void* x, const int32_t* wq, const void* scales,
+                                  const int32_t* zp, const void* bias, void* y,
+                                  int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                  int32_t dtype, void* stream);
+
 /* Dequantised weights w[N, K] (activation dtype): (q - z) * s rounded once to
  * nearest-even.  Device pointers; same layout rules as w4a16_linear. */
 w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t* zp,

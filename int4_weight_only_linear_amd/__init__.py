@@ -10,4 +10,5 @@ from ._binding import (  # noqa: F401
     w4a16_linear_path, w4a16_pack_weights, w4a16_pack_zeros, w4a16_select_path,
     w4a16_unpack_device, w4a16_unpack_weights, w4a16_unpack_zeros, w4a16_workspace_size,
     w4a16_linear_dense, w4a16_dense_workspace_size, w4a16_moe_linear, w4a16_reload_tuning, w4a16_plan,
+    w4a16_linear_noalloc, NOALLOC_SCRATCH_BYTES,
 )

@@ -47,6 +47,8 @@ SIGNATURES = {
                               _vp, _c_sz, _vp]),
     "w4a16_linear_path": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32,
                                    _c_i32, _vp, _c_sz, _vp, _c_i32]),
+    "w4a16_linear_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32,
+                                      _c_i32, _vp]),
     "w4a16_dequant": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i32, _c_i32, _vp]),
     "w4a16_unpack_device": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp]),
     "w4a16_linear_dense": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32, _vp, _c_sz,
@@ -311,6 +313,22 @@ def w4a16_linear(x, wq, scales, zp=None, bias=None, *, group_size: int, out=None
     """w4a16_linear_path with the library's own choice of kernel."""
     return w4a16_linear_path(x, wq, scales, zp, bias, group_size=group_size, path=PATH_AUTO,
                              out=out, workspace=workspace)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def w4a16_linear_noalloc(x, wq, scales, zp=None, bias=None, *, group_size: int, out):
+    """w4a16_linear without a workspace: a K split uses the library's own
+    per-GPU scratch (calls that overlap on one GPU race).  `out` is required,
+    so that the call allocates nothing."""
+    torch = _torch()
+    dt, M, N, K, out = _linear_args(x, wq, scales, zp, bias, group_size, out)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        _check(lib.w4a16_linear_noalloc(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), _ptr(zp),
+                                        _ptr(bias), out.data_ptr(), M, N, K, group_size, dt, stream))
+    return out
 
 
 def w4a16_dequant(wq, scales, zp=None, *, group_size: int, out=None):

@@ -73,6 +73,13 @@ __global__ __launch_bounds__(256) void bias_round_kernel(const float* __restrict
   }
 }
 
+// p[0 .. n) = 0 with vector stores (a kernel rather than a memset, so that a
+// caller may capture it in a graph)
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
 int grid_for(int64_t items, int threads) {
   int64_t blocks = (items + threads - 1) / threads;
   const int64_t cap = 256 * 64;  // enough to fill the chip; the loops stride
@@ -114,6 +121,12 @@ hipError_t launch_bias_round(const float* acc, const void* bias, void* y, int64_
     hipLaunchKernelGGL((bias_round_kernel<DT_F16>), grid_for(total, 256), 256, 0, stream, acc, b, out, total, N);
   else
     hipLaunchKernelGGL((bias_round_kernel<DT_BF16>), grid_for(total, 256), 256, 0, stream, acc, b, out, total, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_words(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t n = (int64_t)(bytes / sizeof(uint32_t));
+  hipLaunchKernelGGL(zero_words_kernel, grid_for(n, 256), 256, 0, stream, static_cast<uint32_t*>(p), n);
   return hipGetLastError();
 }
 

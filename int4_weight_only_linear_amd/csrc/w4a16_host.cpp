@@ -111,6 +111,10 @@ struct DeviceInfo {
   bool gfx950 = false;
   int cu_count = 0;
   char arch[64] = {0};
+  // this device's copy of `scratch` (w4a16_linear_noalloc), set up on the
+  // entry point's first call on the device
+  bool scratch_ready = false;
+  void* scratch_ptr = nullptr;
 };
 
 constexpr int kMaxDevices = 64;
@@ -142,6 +146,41 @@ w4a16_status device_info(const DeviceInfo** out) {
   if (!d.gfx950)
     return fail(W4A16_ERR_UNSUPPORTED, "libw4a16 supports gfx950 only; this device is %s", d.arch);
   *out = &d;
+  return W4A16_OK;
+}
+
+// ---- scratch of the allocation-free entry point ----------------------------
+// w4a16_linear_noalloc takes its split-K workspace (completion counters, then
+// fp32 partial sums) from this array instead of from the caller.  Every GPU
+// the library runs on holds its own copy, from module load until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// copy: the address a kernel needs comes from hipGetSymbolAddress, taken once
+// per device with that device current (DeviceInfo::scratch_ptr).
+constexpr size_t kScratchBytes = W4A16_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+
+// This device's scratch address; on the first call on the device the
+// counter region is cleared by a kernel on `stream` (stream-ordered before
+// the launch that follows).
+w4a16_status scratch_for(DeviceInfo& d, int dev, hipStream_t stream, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!d.scratch_ready) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != dev)
+      return fail(W4A16_ERR_DEVICE, "noalloc: device %d is not current", dev);
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(W4A16_ERR_DEVICE, "noalloc: hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    const hipError_t z = w4a16::launch_zero_words(ptr, w4a16::kCounterBytes, stream);
+    if (z != hipSuccess)
+      return fail(W4A16_ERR_LAUNCH, "noalloc: clearing the scratch counters failed: %s", hipGetErrorString(z));
+    d.scratch_ptr = ptr;
+    d.scratch_ready = true;
+  }
+  *out = d.scratch_ptr;
   return W4A16_OK;
 }
 
@@ -484,6 +523,36 @@ w4a16_status w4a16_linear_path(const void* x, const int32_t* wq, const void* sca
                                size_t workspace_bytes, void* stream, int32_t path) {
   return linear_impl(x, wq, scales, zp, bias, y, M, N, K, group_size, dtype, workspace,
                      workspace_bytes, stream, path);
+}
+
+w4a16_status w4a16_linear_noalloc(const void* x, const int32_t* wq, const void* scales,
+                                  const int32_t* zp, const void* bias, void* y, int64_t M,
+                                  int64_t N, int64_t K, int32_t group_size, int32_t dtype,
+                                  void* stream) {
+  w4a16_status st = w4a16_check_args(x, wq, scales, zp, bias, y, M, N, K, group_size, dtype);
+  if (st != W4A16_OK) return st;
+  if (M == 0) return ok();
+  const DeviceInfo* dev = nullptr;
+  st = device_info(&dev);
+  if (st != W4A16_OK) return st;
+  const GroupMap gm = group_map(group_size, K);
+  const w4a16_path p = resolve_path(M, N, K, gm.kgroup, dtype, zp != nullptr, W4A16_PATH_AUTO);
+  const size_t need = workspace_for(M, N, K, gm.kgroup, dtype, zp != nullptr, p, dev->cu_count);
+  if (need > kScratchBytes)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "w4a16_linear_noalloc: this problem needs %zu bytes of split-K workspace, above the "
+                "%zu bytes of scratch it holds; call w4a16_linear with a workspace instead",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    int d = -1;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices)
+      return fail(W4A16_ERR_DEVICE, "noalloc: no current device");
+    st = scratch_for(g_devices[d], d, static_cast<hipStream_t>(stream), &ws);
+    if (st != W4A16_OK) return st;
+  }
+  return linear_impl(x, wq, scales, zp, bias, y, M, N, K, group_size, dtype, ws, need, stream,
+                     W4A16_PATH_AUTO);
 }
 
 w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t* zp, void* w,

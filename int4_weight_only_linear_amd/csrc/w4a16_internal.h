@@ -152,5 +152,7 @@ hipError_t launch_bias_round(const float* acc, const void* bias, void* y, int64_
                              int dtype, hipStream_t stream);
 hipError_t launch_unpack(const int32_t* wq, uint8_t* q, int64_t N, int64_t K,
                          hipStream_t stream);
+// bytes (a multiple of 4) of device memory set to zero by a kernel
+hipError_t launch_zero_words(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace w4a16

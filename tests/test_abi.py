@@ -39,6 +39,8 @@ def test_abi_version():
     assert int(m.group(1)) == L.w4a16_abi_version()
     m = re.search(r"#define W4A16_GEMV_MAX_M (\d+)", open(HEADER).read())
     assert int(m.group(1)) == L.GEMV_MAX_M
+    m = re.search(r"#define W4A16_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == L.NOALLOC_SCRATCH_BYTES
 
 
 # ---- packing: the library's C++ against the oracle --------------------------
