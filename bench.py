@@ -267,8 +267,8 @@ def dense_comparator(players, stream, steps):
         e1.record()
         torch.cuda.synchronize()
         deq_us = e0.elapsed_time(e1) * 1e3
-        ws = torch.empty(L.w4a16_dense_workspace_size(M, N, K, L.W4A16_BF16, False),
-                         dtype=torch.uint8, device=w.device)
+        need = L.w4a16_dense_workspace_size(M, N, K, L.W4A16_BF16, False)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=w.device)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=w.device)
 
         def fn(sp, x=l["x"], w=w, y=y, ws=ws, M=M, N=N, K=K):
@@ -282,7 +282,8 @@ def dense_comparator(players, stream, steps):
                          dequant_once_us=round(deq_us, 1), copy_bytes=N * K * 2))
         del w, ws, y
     return dict(what="w4a16_dequant once (kept resident, 4x the packed bytes), then "
-                     "w4a16_linear_dense (rocBLAS gemm_ex bf16, fp32 accumulation) per call",
+                     "w4a16_linear_dense (the prefill GEMM's dense instances: bf16 MFMA, fp32 "
+                     "accumulation, weight fragments loaded instead of dequantised) per call",
                 per_layer=rows)
 
 

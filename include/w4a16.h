@@ -271,27 +271,29 @@ w4a16_status w4a16_moe_linear(const void* x, const int32_t* wq, const void* scal
  * A caller that keeps w = w4a16_dequant(...) resident (N*K activation-dtype
  * values, four times the packed weights) can run prefill as a dense product:
  *   y[M, N] = x[M, K] . w[N, K]^T (+ bias[N])
- * on the matrix cores (rocBLAS gemm_ex, fp32 accumulation), with the bias
- * added in fp32 before one nearest-even rounding to the activation dtype.
- * Results match w4a16_linear within the output tolerance; they differ from it
- * only in summation order, because the prefill GEMM multiplies the same
- * rounded weights.
- *   x, w, bias, y: device pointers, contiguous row-major, 2-byte aligned;
- *   y must not overlap x, w or bias.  M, N, K below 2^31.
- *   workspace: device memory of at least w4a16_dense_workspace_size bytes,
- *   256-byte aligned, owned by the caller, not overlapping the other buffers;
- *   its content need not be initialised and is scratch after the call.
- * rocBLAS is opened at run time on the first call (the process's loaded copy
- * if any); the first call on a device also creates that device's rocBLAS
- * handle, kept until the process ends.  Calls on one device are serialised
- * on that handle.  Errors: W4A16_ERR_UNSUPPORTED when rocBLAS is unavailable
- * or the GEMM fails, the usual argument, alignment and workspace codes. */
+ * on the matrix cores with fp32 accumulation, the bias added in fp32 before
+ * one nearest-even rounding to the activation dtype.  It runs the prefill
+ * GEMM's own kernel with the weight fragments loaded from w instead of
+ * unpacked from codes, so its results match w4a16_linear's prefill path
+ * (the same rounded weights) up to summation order.
+ *   x, w: device pointers, contiguous row-major, 16-byte aligned; bias, y:
+ *   2-byte aligned; y must not overlap x, w or bias.  K a multiple of 32 (as
+ *   for the dequantised weights of any accepted layer); N*K*2 and M*K*2 below
+ *   4 GiB.
+ *   workspace: device memory of at least w4a16_dense_workspace_size bytes
+ *   (0: none, NULL accepted), 256-byte aligned, zero-filled before its first
+ *   use and then reusable as w4a16_linear's, not overlapping the other
+ *   buffers.
+ * Errors: the usual argument, alignment, size (W4A16_ERR_UNSUPPORTED) and
+ * workspace codes. */
 w4a16_status w4a16_linear_dense(const void* x, const void* w, const void* bias, void* y,
                                 int64_t M, int64_t N, int64_t K, int32_t dtype,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes w4a16_linear_dense needs: 32 MiB of BLAS workspace, plus
- * the fp32 sums M*N*4 (rounded up to 256) when there is a bias.  Host only. */
+/* Workspace bytes w4a16_linear_dense needs: the split-K workspace of its
+ * plan (completion counters and fp32 partial sums, laid out as
+ * w4a16_workspace_size describes), 0 when K is not split.  has_bias does not
+ * change it.  Host only. */
 size_t w4a16_dense_workspace_size(int64_t M, int64_t N, int64_t K, int32_t dtype,
                                   int32_t has_bias);
 

@@ -30,8 +30,7 @@ COMMON = [
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["w4a16_host.cpp", "w4a16_gemv.hip", "w4a16_gemm.hip", "w4a16_elementwise.hip",
-           "w4a16_blas.cpp"]
+SOURCES = ["w4a16_host.cpp", "w4a16_gemv.hip", "w4a16_gemm.hip", "w4a16_elementwise.hip"]
 # the decode kernel takes its first ten arguments preloaded into SGPRs
 EXTRA = {"w4a16_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
 
@@ -90,7 +89,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-ldl", "-o", tmp]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")

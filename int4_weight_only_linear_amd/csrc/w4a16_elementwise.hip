@@ -58,21 +58,6 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict_
   }
 }
 
-// y = acc + bias, rounded once to the activation dtype: the fp32 sums of the
-// dense product over the dequantised weights, with the bias added in fp32
-template <int DT>
-__global__ __launch_bounds__(256) void bias_round_kernel(const float* __restrict__ acc,
-                                                         const uint16_t* __restrict__ bias,
-                                                         uint16_t* __restrict__ y, int64_t total,
-                                                         int64_t N) {
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    float v = acc[idx];
-    if (bias) v += act_to_f32<DT>(bias[idx % N]);
-    y[idx] = f32_to_act<DT>(v);
-  }
-}
-
 // p[0 .. n) = 0 with vector stores (a kernel rather than a memset, so that a
 // caller may capture it in a graph)
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
@@ -109,18 +94,6 @@ hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* 
     else
       hipLaunchKernelGGL((dequant_kernel<DT_BF16, false>), blocks, 256, 0, stream, wqu, s, zpu, out, N, K, group, sG, gmul);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_bias_round(const float* acc, const void* bias, void* y, int64_t M, int64_t N,
-                             int dtype, hipStream_t stream) {
-  const int64_t total = M * N;
-  const uint16_t* b = static_cast<const uint16_t*>(bias);
-  uint16_t* out = static_cast<uint16_t*>(y);
-  if (dtype == DT_F16)
-    hipLaunchKernelGGL((bias_round_kernel<DT_F16>), grid_for(total, 256), 256, 0, stream, acc, b, out, total, N);
-  else
-    hipLaunchKernelGGL((bias_round_kernel<DT_BF16>), grid_for(total, 256), 256, 0, stream, acc, b, out, total, N);
   return hipGetLastError();
 }
 

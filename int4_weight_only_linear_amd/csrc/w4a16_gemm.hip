@@ -26,6 +26,11 @@
 //   same token rows, neighbouring features -- run on the same XCD and share
 //   its L2.  With more than one split, units store fp32 partial tiles and the
 //   last one to finish a tile adds them up in split order (deterministic).
+// * DENSE instances multiply already dequantised act-dtype weights w[N, K]
+//   (the dequantised prefill copy): the same tiles, staging, pipeline and
+//   epilogue, with each lane's A fragments loaded straight from w's rows
+//   (eight 16-byte loads per column block and k-step) instead of unpacked
+//   from codes.
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
 
@@ -73,8 +78,9 @@ __device__ __forceinline__ int xcd_unit(int b, int units) {
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
-template <int DT, int GS, bool ASYM, int MB, int CB>
+template <int DT, int GS, bool ASYM, int MB, int CB, bool DENSE>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
+  static_assert(!DENSE || (GS == 128 && !ASYM), "dense instances carry no quantisation");
   constexpr int BM = 32 * MB;
   constexpr int BN = 128 * CB;           // output features: 32 CB per wave
   constexpr int XBUF = BM * kXRowBytes;  // bytes of one x buffer
@@ -144,10 +150,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   uint32_t woff[CB][2];   // [cb][pc]: byte offset of piece h + 2 pc in run 0
   uint32_t rshift[CB];    // run s starts s << rshift bytes further
   uint32_t tail_w[CB];
+  // DENSE: byte offset of k = 8 h in row n of w; k-step s adds 256 s bytes
+  // and k-sub ks 32 ks
+  uint32_t doff[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int n = min(nw0 + 32 * cb + j, p.N - 1);
     nrow[cb] = n;
+    doff[cb] = (uint32_t)n * (uint32_t)p.K * 2u + 16u * (uint32_t)h;
     const int jj = n & 15;
     const uint32_t t0 = (uint32_t)(n - jj) * (uint32_t)p.wpr;  // tile start, words
     const int tail_words = p.wpr - 16 * p.full_steps;
@@ -164,14 +174,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     }
   }
 
+  constexpr int WP = DENSE ? 8 : 2;  // 16-byte weight pieces per column block and k-step
   struct StepRegs {
-    u32x4 w[CB][2];       // [cb][piece]: word t of piece pc is k-sub 2t + pc
+    u32x4 w[CB][WP];      // [cb][piece]: word t of piece pc is k-sub 2t + pc
+                          // (DENSE: piece ks holds k-sub ks as 8 act values)
     uint16_t s[CB][GPS];  // scales of the step's groups
     uint32_t z[CB][GPS];  // packed zero-point words
   };
   // complete run: pieces h and h + 2 of the run's four 16-byte pieces
   auto load_full = [&](int s, StepRegs& r) {
     const unsigned char* base = reinterpret_cast<const unsigned char*>(p.wq);
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          r.w[cb][ks] = *reinterpret_cast<const u32x4*>(base + (uint32_t)(s * 256 + 32 * ks) + doff[cb]);
+      return;
+    }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const uint32_t run = (uint32_t)s << rshift[cb];
@@ -183,6 +203,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   // incomplete run, stored in slice order: k-sub ks of half h is word 2 ks + h
   auto load_tail = [&](int s, StepRegs& r) {
     const int nks = (p.K - s * kBK) / 16;
+    if constexpr (DENSE) {
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(p.wq);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          r.w[cb][ks] = ks < nks ? *reinterpret_cast<const u32x4*>(base + (uint32_t)(s * 256 + 32 * ks) + doff[cb])
+                                 : u32x4{0u, 0u, 0u, 0u};
+      return;
+    }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -193,6 +223,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
       }
   };
   auto load_meta = [&](int s, StepRegs& r) {
+    if constexpr (DENSE) return;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -217,6 +248,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
       for (int e = 0; e < 16; ++e) acc[rb][cb][e] = 0.f;
 
   auto group_consts = [&](const StepRegs& r, GroupConst<DT> (&gc)[CB][GPS]) {
+    if constexpr (DENSE) return;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -226,6 +258,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
       }
   };
   auto weights = [&](const StepRegs& r, const GroupConst<DT> (&gc)[CB][GPS], int ks, u32x4 (&a)[CB]) {
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) a[cb] = r.w[cb][ks];
+      return;
+    }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const GroupConst<DT>& g = gc[cb][(16 * ks) / GS];
@@ -315,13 +352,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 
   // the next k-step's global loads, spread over k-subs 0..5 of the current
   // one: weights first (k-sub 0), then metadata, then the x pieces
-  constexpr int kMetaLoads = CB * GPS * (ASYM ? 2 : 1);
+  constexpr int kMetaLoads = DENSE ? 0 : CB * GPS * (ASYM ? 2 : 1);
   auto issue_next = [&](int ks, int sn, lds_u8* buf, StepRegs& r) -> int {
     constexpr int DPK = (NDMA + 5) / 6;  // x loads per k-sub
     int n = 0;
     if (ks == 0) {
       load_full(sn, r);
-      n += 2 * CB;
+      n += WP * CB;
     }
     if (ks == 1) {
       load_meta(sn, r);
@@ -517,26 +554,26 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
-template <int DT, int GS, bool ASYM, int MB, int CB>
+template <int DT, int GS, bool ASYM, int MB, int CB, bool DENSE>
 hipError_t launch_t(const GemmParams& prm, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<DT, GS, ASYM, MB, CB>), dim3(prm.units), dim3(kThreads), 0, s, prm);
+  hipLaunchKernelGGL((gemm_kernel<DT, GS, ASYM, MB, CB, DENSE>), dim3(prm.units), dim3(kThreads), 0, s, prm);
   return hipGetLastError();
 }
 
 // tile shapes: 32 mb tokens x 128 cb features; cb = 1 only for mb 4 and 8
-template <int DT, int GS, bool ASYM>
+template <int DT, int GS, bool ASYM, bool DENSE = false>
 hipError_t launch_mb(const GemmParams& prm, int mb, int cb, hipStream_t s) {
   if (cb == 1) {
     switch (mb) {
-      case 4: return launch_t<DT, GS, ASYM, 4, 1>(prm, s);
-      case 8: return launch_t<DT, GS, ASYM, 8, 1>(prm, s);
+      case 4: return launch_t<DT, GS, ASYM, 4, 1, DENSE>(prm, s);
+      case 8: return launch_t<DT, GS, ASYM, 8, 1, DENSE>(prm, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (mb) {
-    case 4: return launch_t<DT, GS, ASYM, 4, 2>(prm, s);
-    case 6: return launch_t<DT, GS, ASYM, 6, 2>(prm, s);
-    case 8: return launch_t<DT, GS, ASYM, 8, 2>(prm, s);
+    case 4: return launch_t<DT, GS, ASYM, 4, 2, DENSE>(prm, s);
+    case 6: return launch_t<DT, GS, ASYM, 6, 2, DENSE>(prm, s);
+    case 8: return launch_t<DT, GS, ASYM, 8, 2, DENSE>(prm, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -572,14 +609,23 @@ hipError_t launch_g(const GemmParams& prm, int group, int mb, int cb, hipStream_
 // keeps its group constants and the next step's metadata beside 192-256
 // accumulators.  Measured at M = 1920 on 6144x4096 they run 1.2-3.6x slower
 // than the 128-token tile, so the planner leaves them out.
+// Dense instances (no group constants) at tile heights 192 and 256 with
+// 256-feature tiles: their eight 16-byte weight pieces per column block and
+// k-step stand where the codes and metadata stood.
+bool dense_tall_tile_spills(int dtype) {
+  (void)dtype;
+  return false;
+}
+
 bool wide_tall_tile_spills(int group, int dtype, bool asym) {
   if (dtype == DT_F16) return group == 32 || (group == 64 && asym);
   return group == 32 && !asym;
 }
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym, int cu_count) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym, int cu_count,
+                   bool dense) {
   GemmPlan best{};
-  const bool tall_wide_ok = !wide_tall_tile_spills(group, dtype, asym);
+  const bool tall_wide_ok = dense ? !dense_tall_tile_spills(dtype) : !wide_tall_tile_spills(group, dtype, asym);
   // where the tall wide tiles are left out, narrow tiles are tried first, so
   // that near-ties go to them: at M = 1920 on 6144x4096 they beat the
   // 128-token wide tile by 1-20 % for those combinations
@@ -661,8 +707,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool a
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym,
-                            int cu_count) {
-  const GemmPlan p = plan_gemm(M, N, K, group, dtype, asym, cu_count);
+                            int cu_count, bool dense) {
+  const GemmPlan p = plan_gemm(M, N, K, group, dtype, asym, cu_count, dense);
   if (p.splits <= 1) return 0;
   if (p.two_pass)
     return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)((N + 7) / 8 * 8) * sizeof(float);
@@ -670,7 +716,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group, int dtyp
 }
 
 hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipStream_t stream) {
-  const GemmPlan plan = plan_gemm(a.M, a.N, a.K, a.group, a.dtype, a.zp != nullptr, cu_count);
+  const GemmPlan plan = plan_gemm(a.M, a.N, a.K, a.group, a.dtype, a.zp != nullptr, cu_count, a.dense);
   GemmParams prm;
   prm.x = static_cast<const uint16_t*>(a.x);
   prm.wq = reinterpret_cast<const uint32_t*>(a.wq);
@@ -702,8 +748,13 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
   prm.two_pass = plan.splits > 1 && plan.two_pass;
   if (prm.two_pass && plan.mb != 4) return hipErrorInvalidConfiguration;
   prm.np = (int)((a.N + 7) / 8 * 8);
-  hipError_t e = a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, plan.mb, plan.cb, stream)
-                                   : launch_g<DT_BF16>(prm, a.group, plan.mb, plan.cb, stream);
+  hipError_t e;
+  if (a.dense)
+    e = a.dtype == DT_F16 ? launch_mb<DT_F16, 128, false, true>(prm, plan.mb, plan.cb, stream)
+                          : launch_mb<DT_BF16, 128, false, true>(prm, plan.mb, plan.cb, stream);
+  else
+    e = a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, plan.mb, plan.cb, stream)
+                          : launch_g<DT_BF16>(prm, a.group, plan.mb, plan.cb, stream);
   if (e != hipSuccess || !prm.two_pass) return e;
   const int64_t quads = (int64_t)prm.M * (prm.np / 4);
   const int blocks = (int)((quads + 255) / 256);

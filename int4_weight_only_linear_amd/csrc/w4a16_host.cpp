@@ -639,12 +639,16 @@ w4a16_status w4a16_moe_linear(const void* x, const int32_t* wq, const void* scal
 }
 
 size_t w4a16_dense_workspace_size(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t has_bias) {
-  (void)K;
-  (void)dtype;
-  if (M <= 0 || N <= 0) return 0;
-  size_t b = w4a16::kDenseBlasWorkspace;
-  if (has_bias) b += ((size_t)M * (size_t)N * sizeof(float) + 255) / 256 * 256;
-  return b;
+  (void)has_bias;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 32 || (dtype != W4A16_F16 && dtype != W4A16_BF16)) return 0;
+  int cus = kPlanningCUs;
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    const DeviceInfo* d = nullptr;
+    if (device_info(&d) == W4A16_OK) cus = d->cu_count;
+    g_last_error.clear();
+  }
+  return w4a16::gemm_workspace_bytes(M, N, K, 128, dtype, false, cus, true);
 }
 
 w4a16_status w4a16_linear_dense(const void* x, const void* w, const void* bias, void* y, int64_t M,
@@ -652,41 +656,42 @@ w4a16_status w4a16_linear_dense(const void* x, const void* w, const void* bias, 
                                 size_t workspace_bytes, void* stream) {
   if (dtype != W4A16_F16 && dtype != W4A16_BF16)
     return fail(W4A16_ERR_INVALID_ARG, "activation dtype must be fp16 (0) or bf16 (1), got %d", (int)dtype);
-  if (M < 0 || N < 1 || K < 1)
-    return fail(W4A16_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1 (M=%lld N=%lld K=%lld)",
+  if (M < 0 || N < 1 || K < 32 || K % 32)
+    return fail(W4A16_ERR_INVALID_ARG, "need M >= 0, N >= 1 and K a positive multiple of 32 (M=%lld N=%lld K=%lld)",
                 (long long)M, (long long)N, (long long)K);
-  if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
-    return fail(W4A16_ERR_UNSUPPORTED, "the dense path takes M, N and K below 2^31");
+  if ((uint64_t)N * (uint64_t)K * 2 > 0xFFFFFFFFull || (uint64_t)M * (uint64_t)K * 2 > 0xFFFFFFFFull ||
+      M > INT32_MAX || N > INT32_MAX)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "the dense path addresses w and x with 32-bit byte offsets: N*K*2 and M*K*2 must be "
+                "below 4 GiB (M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
   if (M == 0) return ok();
   if (!x || !w || !y) return fail(W4A16_ERR_INVALID_ARG, "x, w and y must not be NULL");
-  if (!aligned(x, 2) || !aligned(w, 2) || !aligned(y, 2) || (bias && !aligned(bias, 2)))
-    return fail(W4A16_ERR_ALIGNMENT, "x, w, bias and y must be 2-byte aligned");
+  if (!aligned(x, 16) || !aligned(w, 16))
+    return fail(W4A16_ERR_ALIGNMENT, "x and w must be 16-byte aligned");
+  if (!aligned(y, 2) || (bias && !aligned(bias, 2)))
+    return fail(W4A16_ERR_ALIGNMENT, "bias and y must be 2-byte aligned");
   const size_t ny = act_bytes(M * N);
   if (overlap(y, ny, x, act_bytes(M * K)) || overlap(y, ny, w, act_bytes(N * K)) ||
       overlap(y, ny, bias, bias ? act_bytes(N) : 0))
     return fail(W4A16_ERR_INVALID_ARG, "y must not overlap x, w or bias");
-  const size_t need = w4a16_dense_workspace_size(M, N, K, dtype, bias != nullptr);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
-                workspace_bytes, workspace ? "" : " (NULL)");
-  if (!aligned(workspace, 256)) return fail(W4A16_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
-  if (overlap(workspace, need, y, ny) || overlap(workspace, need, x, act_bytes(M * K)) ||
-      overlap(workspace, need, w, act_bytes(N * K)))
-    return fail(W4A16_ERR_INVALID_ARG, "the workspace must not overlap x, w or y");
   const DeviceInfo* dev = nullptr;
   w4a16_status st = device_info(&dev);
   if (st != W4A16_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float* acc = bias ? reinterpret_cast<float*>(ws + w4a16::kDenseBlasWorkspace) : nullptr;
-  std::string why;
-  if (!w4a16::dense_gemm(x, w, bias ? static_cast<void*>(acc) : y, bias != nullptr, M, N, K, dtype,
-                         ws, w4a16::kDenseBlasWorkspace, s, &why))
-    return fail(W4A16_ERR_UNSUPPORTED, "dense path: %s", why.c_str());
-  if (bias) {
-    hipError_t e = w4a16::launch_bias_round(acc, bias, y, M, N, dtype, s);
-    if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
-  }
+  const size_t need = w4a16::gemm_workspace_bytes(M, N, K, 128, dtype, false, dev->cu_count, true);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(W4A16_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (need > 0 && (overlap(workspace, need, y, ny) || overlap(workspace, need, x, act_bytes(M * K)) ||
+                   overlap(workspace, need, w, act_bytes(N * K))))
+    return fail(W4A16_ERR_INVALID_ARG, "the workspace must not overlap x, w or y");
+  // the prefill GEMM's dense instances: w in place of the packed codes, no
+  // scales or zero points
+  w4a16::LinearArgs a{x, static_cast<const int32_t*>(w), nullptr, nullptr, bias, y, M, N, K, 128, dtype, 0, 0};
+  a.dense = true;
+  const hipError_t e = w4a16::launch_gemm(a, workspace, dev->cu_count, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

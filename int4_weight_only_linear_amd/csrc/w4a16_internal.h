@@ -22,6 +22,7 @@ struct LinearArgs {
   int dtype;
   int sG;     // scale / zero-point row stride, in groups: K / group_size
   int gmul;   // 1, or 0 for per-channel scales (every group of a row reads column 0)
+  bool dense = false;  // prefill GEMM only: wq points at act-dtype weights w[N, K]
 };
 
 // ---- tuning overrides ------------------------------------------------------
@@ -134,22 +135,15 @@ struct GemmPlan {
   // many splits) instead of by the tile's last workgroup
   bool two_pass;
 };
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym, int cu_count);
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym, int cu_count,
+                   bool dense = false);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym,
-                            int cu_count);
+                            int cu_count, bool dense = false);
 hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipStream_t stream);
 
 // ---- elementwise -----------------------------------------------------------
 hipError_t launch_dequant(const int32_t* wq, const void* scales, const int32_t* zp, int sG, int gmul, void* w,
                           int64_t N, int64_t K, int group, int dtype, hipStream_t stream);
-// Dequantised prefill copy: bytes of BLAS workspace the dense path hands to
-// the BLAS (the fp32 sums, when there is a bias, follow them).
-constexpr size_t kDenseBlasWorkspace = 32u << 20;
-bool dense_gemm(const void* x, const void* w, void* d, bool d_f32, int64_t M, int64_t N, int64_t K,
-                int dtype, void* blas_ws, size_t blas_ws_bytes, hipStream_t stream,
-                std::string* why);
-hipError_t launch_bias_round(const float* acc, const void* bias, void* y, int64_t M, int64_t N,
-                             int dtype, hipStream_t stream);
 hipError_t launch_unpack(const int32_t* wq, uint8_t* q, int64_t N, int64_t K,
                          hipStream_t stream);
 // bytes (a multiple of 4) of device memory set to zero by a kernel

@@ -211,17 +211,28 @@ def test_workspace_size():
 
 
 def test_dense_workspace_size_and_argument_checks():
-    mb = 1 << 20
+    # the dense instances of the prefill GEMM plan like the symmetric group-128
+    # GEMM: the same tile and split choices, so the same split workspace
+    for (M, N, K) in ((1920, 4096, 4096), (128, 4096, 4096), (130, 200, 640), (1, 64, 256)):
+        for dt in (L.W4A16_F16, L.W4A16_BF16):
+            want = L.w4a16_workspace_size(M, N, K, 128, dt, False, L.PATH_GEMM)
+            assert L.w4a16_dense_workspace_size(M, N, K, dt, 1) == want
+            assert L.w4a16_dense_workspace_size(M, N, K, dt, 0) == want
+    assert L.w4a16_dense_workspace_size(1920, 4096, 4096, L.W4A16_BF16, 0) == 0   # no split
+    assert L.w4a16_dense_workspace_size(128, 4096, 4096, L.W4A16_BF16, 0) > 64 * 1024
     assert L.w4a16_dense_workspace_size(0, 4096, 4096, L.W4A16_BF16, 1) == 0
-    assert L.w4a16_dense_workspace_size(1920, 4096, 4096, L.W4A16_BF16, 0) == 32 * mb
-    assert L.w4a16_dense_workspace_size(1920, 4096, 4096, L.W4A16_BF16, 1) == 32 * mb + 1920 * 4096 * 4
-    assert L.w4a16_dense_workspace_size(3, 5, 8, L.W4A16_F16, 1) == 32 * mb + 256
     # rejected before any device is touched
-    st = B.lib.w4a16_linear_dense(None, None, None, None, 4, 8, 8, 7, None, 0, None)
+    st = B.lib.w4a16_linear_dense(None, None, None, None, 4, 8, 64, 7, None, 0, None)
     assert st == 1 and "dtype" in L.w4a16_last_error()
-    st = B.lib.w4a16_linear_dense(None, None, None, None, 4, 8, 8, L.W4A16_BF16, None, 0, None)
+    st = B.lib.w4a16_linear_dense(None, None, None, None, 4, 8, 48, L.W4A16_BF16, None, 0, None)
+    assert st == 1 and "multiple of 32" in L.w4a16_last_error()
+    st = B.lib.w4a16_linear_dense(None, None, None, None, 4, 8, 64, L.W4A16_BF16, None, 0, None)
     assert st == 1 and "NULL" in L.w4a16_last_error()
-    assert B.lib.w4a16_linear_dense(None, None, None, None, 0, 8, 8, L.W4A16_BF16, None, 0, None) == 0
+    st = B.lib.w4a16_linear_dense(P + 8, 2 * P, None, 4 * P, 4, 8, 64, L.W4A16_BF16, None, 0, None)
+    assert st == 3 and "16-byte" in L.w4a16_last_error()
+    st = B.lib.w4a16_linear_dense(P, 2 * P, None, 4 * P, 4, 1 << 20, 4096, L.W4A16_BF16, None, 0, None)
+    assert st == 2 and "4 GiB" in L.w4a16_last_error()
+    assert B.lib.w4a16_linear_dense(None, None, None, None, 0, 8, 64, L.W4A16_BF16, None, 0, None) == 0
 
 
 def test_per_channel_group_accept_set():

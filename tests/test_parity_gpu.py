@@ -369,6 +369,20 @@ def test_dense_prefill_copy(dt, M, N, K, g, sym, bias):
     assert_close(d.run(GEMM), ref, dt, "prefill GEMM vs the same weights")
 
 
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("tile", ["8,1,0,2", "6,1,0,2", "4,1,0,1", "4,3,0,2", "4,4,1,1"])
+@pytest.mark.parametrize("M,N,K,g,sym", [(300, 520, 1024, 128, False), (130, 200, 416, 32, True)])
+def test_dense_copy_equals_prefill_gemm_bit_for_bit(tuning_env, dt, tile, M, N, K, g, sym):
+    # with the tile and K split forced to be the same, the dense instance and
+    # the W4A16 GEMM multiply the same rounded weights in the same order
+    tuning_env("W4A16_GEMM_TILE", tile)
+    c = make_case(M, N, K, g, dt, sym, True, seed=("densebits", M, N, K, g, dt, sym))
+    d = DeviceCase(c)
+    w = L.w4a16_dequant(d.wq, d.s, d.zp, group_size=g)
+    y_dense = device_to_bits(L.w4a16_linear_dense(d.x, w, d.bias))
+    assert np.array_equal(y_dense, d.run(GEMM)), f"tile {tile}"
+
+
 # ---- per-channel scales: group_size == K (one scale and zero point per row) ----
 
 @pytest.mark.parametrize("dt", [O.F16, O.BF16])
