@@ -175,14 +175,109 @@ def per_launch_durations(step_lists, reps, stream, passes=5, replays=4):
     return out
 
 
+def host_cores() -> int:
+    """The host cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def graph_launch_ms(fns, stream, passes=5, replays=4, reps=5):
+    """Mean duration of one launch from `fns` (one launch each, e.g. one per
+    weight copy), from HIP events on the launch stream around `replays`
+    replays of a graph of `passes` rounds over them; median over `reps`."""
+    import torch
+    g = capture([[f] for _ in range(passes) for f in fns], stream)
+    g.replay()
+    torch.cuda.synchronize()
+    n = passes * len(fns) * replays
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(replays):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / n)
+    return float(np.median(ts))
+
+
+PAD_STRIDES = (256, 4096)  # bytes added after each 16-row tile (row-stride padding)
+
+
+def decode_ceilings(layers, pool, stream):
+    """What this device sustains on the decode layers' weight bytes, from
+    the ceiling kernels (libw4a16_ceilings), rotating through the same weight
+    copies: a plain streaming read of each layer's packed weights, and the
+    decode kernel's own weight loads alone in its grid (same workgroups,
+    waves and 1 KiB blocks), also on copies whose 16-row tiles are padded
+    (row-stride padding).  Times are per launch."""
+    import torch
+    import int4_weight_only_linear_amd as L
+    from int4_weight_only_linear_amd import ceilings as C
+    sink = torch.zeros(16, dtype=torch.int32, device=pool[0][0][0].device)
+    rows = []
+    for i, l in enumerate(layers):
+        K, N = l["K"], l["N"]
+        tiles = N // 16
+        plan = L.w4a16_plan(1, N, K, GROUP, L.W4A16_BF16, True, L.PATH_GEMV)
+        waves = plan["waves"]
+        kpw = 1 << max(0, (-(-(K // 128) // waves) - 1).bit_length())  # a power of two covering the run
+        wqs = [pool[c][i][0] for c in range(len(pool))]
+        wbytes = wqs[0].numel() * 4
+        t_stream = graph_launch_ms([lambda sp, w=w: C.stream_read(w, sink, sp) for w in wqs], stream)
+        t_loads = graph_launch_ms([lambda sp, w=w: C.decode_loads(w, tiles, K, 8 * K, kpw, waves, sink, sp)
+                                   for w in wqs], stream)
+        row = dict(K=K, N=N, weight_bytes=wbytes, waves=waves, kpw=kpw,
+                   stream_read_us=round(t_stream * 1e3, 3), stream_read_GBs=round(wbytes / t_stream / 1e6, 1),
+                   loads_only_us=round(t_loads * 1e3, 3), loads_only_GBs=round(wbytes / t_loads / 1e6, 1))
+        for pad in PAD_STRIDES:
+            stride = 8 * K + pad
+            padded = []
+            for w in wqs:
+                buf = torch.zeros(tiles * stride, dtype=torch.uint8, device=w.device)
+                buf.view(tiles, stride)[:, :8 * K].copy_(w.view(torch.uint8).view(tiles, 8 * K))
+                padded.append(buf)
+            t_pad = graph_launch_ms([lambda sp, w=w: C.decode_loads(w, tiles, K, stride, kpw, waves, sink, sp)
+                                     for w in padded], stream)
+            row[f"loads_only_pad{pad}_us"] = round(t_pad * 1e3, 3)
+            del padded
+            torch.cuda.empty_cache()
+        rows.append(row)
+    return rows
+
+
+def mfma_ceiling(stream, cu_count, iters=20000):
+    """The sustained bf16 matrix-core rate: independent 32x32x16 MFMA chains
+    on hashed operands, one and two waves per SIMD (libw4a16_ceilings)."""
+    import torch
+    from int4_weight_only_linear_amd import ceilings as C
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    out = {}
+    for wps in (1, 2):
+        blocks = cu_count * wps
+        ms = graph_launch_ms([lambda sp, s=s: C.mfma_loop(blocks, iters, s, sink, sp) for s in range(2)],
+                             stream, passes=2, replays=2, reps=3)
+        out[f"waves_per_simd_{wps}"] = round(blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12, 1)
+    return dict(unit="TFLOP/s", kernel="v_mfma_f32_32x32x16_bf16 chains, hashed operands",
+                **out, best=max(out.values()))
+
+
 def cpu_baseline(layers_host, min_s=10.0):
-    """The oracle (untuned) on this host, 1 thread: whole M=1 decode steps over
-    the layers, repeated until at least `min_s` seconds of oracle work."""
+    """The oracle (untuned) on this host's cores: whole M=1 decode steps over
+    the layers, repeated until at least `min_s` seconds of oracle work.  Its
+    BLAS runs on every core this process may use (numpy's own threading; the
+    unpacking and dequantisation are numpy element-wise, one thread)."""
     import contextlib
     import oracle as O
+    cores = host_cores()
     try:
         from threadpoolctl import threadpool_limits
-        ctx = threadpool_limits(limits=1)
+        ctx = threadpool_limits(limits=cores)
     except ImportError:  # pragma: no cover
         ctx = contextlib.nullcontext()
     packed = [(K, N, c, O.pack_weights(c.q), O.pack_zeros(c.zp)) for (K, N, c) in layers_host]
@@ -196,10 +291,11 @@ def cpu_baseline(layers_host, min_s=10.0):
                 total_bytes += decode_bytes(c.M, N, K, GROUP)
             steps += 1
     layers = ", ".join(f"{K}x{N}" for (K, N, _c) in layers_host)
-    return dict(value=total_bytes / t_total / 1e9, unit="GB/s", cores=1, kind="oracle",
+    return dict(value=total_bytes / t_total / 1e9, unit="GB/s", cores=cores, kind="oracle",
                 seconds=round(t_total, 3),
                 sample=(f"oracle linear_ref (unpack + exact fp32 dequant + fp64 GEMV) over {steps} M=1 "
-                        f"decode step(s), layers {layers} (K x N), single thread; packing not timed"))
+                        f"decode step(s), layers {layers} (K x N), BLAS on {cores} threads; packing not "
+                        f"timed"))
 
 
 def _layer_tensors(case, device):
@@ -445,6 +541,200 @@ def run_report(path_prefix):
     print(json.dumps(dict(report=path_prefix + ".md", points=len(rows), mstar=mstar)), flush=True)
 
 
+# ---- rocprofv3 summaries (profiles/) ------------------------------------------
+
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{kind}_trace -o run -- "
+             "python3 $R/bench.py --profile {kind} --steps {steps}",
+    "pmc": "rocprofv3 --pmc {counters} --output-format csv -d $R/gpurun_out/{kind}_pmc{tag} -o run -- "
+           "python3 $R/bench.py --profile {kind} --steps {steps}",
+    "traffic": "rocprofv3 --pmc {counter} --output-format csv -d $R/gpurun_out/{kind}_{counter} -o run -- "
+               "python3 $R/bench.py --profile {kind} --steps {steps} --calibration-copy-mb 256",
+}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def profile_layers(kind):
+    """(K, N, M, expected Grid_Size_X of the layer's main kernel, work) per
+    layer of a --profile run; work = algorithmic bytes (decode) or flops."""
+    import int4_weight_only_linear_amd as L
+    shapes, M = (DECODE_LAYERS, 1) if kind == "decode" else (PREFILL_LAYERS, 1920)
+    out = []
+    for (K, N) in shapes:
+        p = L.w4a16_plan(M, N, K, GROUP, L.W4A16_BF16, True)
+        threads = 64 * p["waves"]
+        units = p["tiles"] * (p["splits"] if kind == "prefill" else 1)
+        work = decode_bytes(M, N, K, GROUP) if kind == "decode" else 2 * M * N * K
+        out.append(dict(K=K, N=N, M=M, grid=units * threads, plan=p, work=work))
+    return out
+
+
+def _kernel_short(name):
+    """'gemm_kernel<1, 128, true, 8, 2, false>' out of a demangled kernel name."""
+    import re
+    m = re.search(r"(\w+_kernel<[^>]*>)", name)
+    return m.group(1) if m else name.split("(")[0]
+
+
+def _median(v):
+    return float(np.median(np.asarray(v, dtype=np.float64))) if len(v) else float("nan")
+
+
+def summarize_trace(kind, d, steps):
+    """Per layer of a --profile run: launches, mean and median kernel time
+    (End - Start), and GB/s (decode) or TFLOP/s (prefill) against the peak."""
+    rows = [r for r in _csv_rows(os.path.join(d, "run_kernel_trace.csv")) if "w4a16" in r["Kernel_Name"]]
+    layers = profile_layers(kind)
+    unit = "GB/s" if kind == "decode" else "TFLOP/s"
+    peak = HBM_PEAK_GBS if kind == "decode" else MFMA_BF16_PEAK_TFLOPS
+    lines = [f"Command (from /tmp, TMPDIR=/tmp, repository at $R):",
+             "  " + PROFILE_CMDS["trace"].format(kind=kind, steps=steps), "",
+             f"Per layer (End - Start of each dispatch of the layer's kernel; the first launch of each "
+             f"layer, outside the timed loop, included):",
+             f"  layer (K,N)      M     kernel grid   launches  mean_ns    median_ns   {unit}(mean)  frac of {peak:g}"]
+    means = []
+    for l in layers:
+        ts = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows
+              if int(r["Grid_Size_X"]) == l["grid"] and "splitk_reduce" not in r["Kernel_Name"]]
+        names = {_kernel_short(r["Kernel_Name"]) for r in rows if int(r["Grid_Size_X"]) == l["grid"]}
+        mean = float(np.mean(ts)) if ts else float("nan")
+        rate = l["work"] / mean if kind == "decode" else l["work"] / mean / 1e3
+        means.append(mean)
+        lines.append(f"  ({l['K']:5d},{l['N']:5d})  {l['M']:5d}  {l['grid']:10d}   {len(ts):8d}  {mean:9.0f}  "
+                     f"{_median(ts):9.0f}   {rate:10.1f}  {rate / peak:.4f}   {' / '.join(sorted(names))}")
+    if kind == "decode":
+        mb = float(np.mean([l["work"] for l in layers]))
+        mm = float(np.mean(means))
+        lines.append(f"  mean over the layers: {mm:.0f} ns per launch, {mb:.0f} bytes per launch -> "
+                     f"{mb / mm:.1f} GB/s = {mb / mm / HBM_PEAK_GBS:.4f} of {HBM_PEAK_GBS:g}")
+    return "\n".join(lines)
+
+
+PMC_SETS = {
+    "A": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+          "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT"],
+    "B": ["SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
+          "SQ_WAVES", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE"],
+}
+XCDS, SIMDS = 8, 1024
+
+
+def summarize_pmc(kind, dirs, steps):
+    """Per layer, medians over its dispatches: kernel time, the clock
+    (GRBM_GUI_ACTIVE per XCD over the kernel time), MFMA utilisation
+    (SQ_VALU_MFMA_BUSY_CYCLES over GUI-active cycles of all 1024 SIMDs), the
+    bf16 matrix flops the MFMA counters saw, and instructions per MFMA."""
+    layers = profile_layers(kind)
+    per = {}
+    for tag, d in dirs.items():
+        for r in _csv_rows(os.path.join(d, "run_counter_collection.csv")):
+            if "w4a16" not in r["Kernel_Name"]:
+                continue
+            e = per.setdefault((tag, r["Dispatch_Id"]), dict(grid=int(r["Grid_Size"]),
+                                                             ns=int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = ["Commands (from /tmp, TMPDIR=/tmp, repository at $R), one counter set per run:"]
+    for tag in dirs:
+        lines.append("  " + PROFILE_CMDS["pmc"].format(kind=kind, steps=steps, tag=tag,
+                                                         counters=" ".join(PMC_SETS[tag])))
+    lines += ["", "Per layer (median over the layer's dispatches; counters summed over the device):"]
+    for l in layers:
+        a = [e for (tag, _), e in per.items() if tag == "A" and e["grid"] == l["grid"]]
+        b = [e for (tag, _), e in per.items() if tag == "B" and e["grid"] == l["grid"]]
+        lines.append(f"  layer (K,N) = ({l['K']},{l['N']}), M = {l['M']}, plan {l['plan']['tile_tokens']}x"
+                     f"{l['plan']['tile_features']} tiles, {l['plan']['splits']} K range(s), {len(a)} dispatches")
+        if a:
+            ns = _median([e["ns"] for e in a])
+            clk = _median([e["GRBM_GUI_ACTIVE"] / XCDS / e["ns"] for e in a])
+            util = _median([e["SQ_VALU_MFMA_BUSY_CYCLES"] / (e["GRBM_GUI_ACTIVE"] / XCDS * SIMDS) for e in a])
+            tf = _median([e["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / e["ns"] / 1e3 for e in a])
+            valu = _median([e["SQ_INSTS_VALU"] / e["SQ_INSTS_MFMA"] for e in a])
+            lds = _median([e["SQ_INSTS_LDS"] / e["SQ_INSTS_MFMA"] for e in a])
+            conf = _median([e["SQ_LDS_BANK_CONFLICT"] for e in a])
+            busy = _median([e["SQ_VALU_MFMA_BUSY_CYCLES"] / e["SQ_INSTS_MFMA"] for e in a])
+            lines.append(f"    kernel {ns / 1e3:.1f} us, clock {clk:.2f} GHz, MFMA busy {util:.3f} of GUI-active "
+                         f"SIMD cycles ({busy:.0f} busy cycles per MFMA), {tf:.0f} TFLOP/s from "
+                         f"SQ_INSTS_VALU_MFMA_MOPS_BF16*512 ({tf / MFMA_BF16_PEAK_TFLOPS:.3f} of "
+                         f"{MFMA_BF16_PEAK_TFLOPS:g}; algorithmic {l['work'] / ns / 1e3:.0f}), "
+                         f"VALU instructions per MFMA {valu:.2f} (MFMAs included), LDS instructions per MFMA "
+                         f"{lds:.2f}, LDS bank conflicts {conf:.0f}")
+        if b:
+            co = _median([e["SQ_VALU_MFMA_COEXEC_CYCLES"] / (e["GRBM_GUI_ACTIVE"] / XCDS * SIMDS) for e in b])
+            extra = ""
+            if "SQ_WAIT_ANY" in b[0]:
+                wc = [e["SQ_WAVE_CYCLES"] for e in b]
+                extra = (f"; of the waves' cycles: waiting on a dependency or counter "
+                         f"{_median([e['SQ_WAIT_ANY'] / e['SQ_WAVE_CYCLES'] for e in b]):.3f}, waiting to issue "
+                         f"{_median([e['SQ_WAIT_INST_ANY'] / e['SQ_WAVE_CYCLES'] for e in b]):.3f}, issuing "
+                         f"{_median([e['SQ_ACTIVE_INST_ANY'] / e['SQ_WAVE_CYCLES'] for e in b]):.3f}")
+            lines.append(f"    VALU/MFMA co-execution {co:.3f} of GUI-active SIMD cycles; waves "
+                         f"{_median([e['SQ_WAVES'] for e in b]):.0f}{extra}")
+    return "\n".join(lines)
+
+
+def summarize_traffic(kind, fetch_dir, write_dir, steps, copy_mb=256):
+    """HBM bytes per launch of each layer's kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for
+    the calibration copy (reads and writes copy_mb MiB once)."""
+    layers = profile_layers(kind)
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _csv_rows(os.path.join(d, "run_counter_collection.csv"))
+        cal = [float(r["Counter_Value"]) for r in rows
+               if "bitwise_not" in r["Kernel_Name"] or "BitwiseNot" in r["Kernel_Name"]]
+        scale = (copy_mb * 1024) / _median(cal)
+        out[counter] = dict(scale=scale, cal=_median(cal), rows=rows)
+    lines = ["Commands (from /tmp, TMPDIR=/tmp, repository at $R), one counter per run:"]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append("  " + PROFILE_CMDS["traffic"].format(kind=kind, steps=steps, counter=counter))
+    lines += ["", f"Calibration (torch bitwise_not: one elementwise kernel reading and writing {copy_mb} MiB):"]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append(f"  {counter} per dispatch: {out[counter]['cal']:.1f} KiB for {copy_mb * 1024} KiB -> "
+                     f"scale {out[counter]['scale']:.4f}")
+    lines += ["", "Per layer (median KiB per dispatch as counted; bytes after scaling):",
+              "  layer (K,N)      FETCH_KiB   WRITE_KiB   traffic_bytes   algorithmic_bytes   ratio"]
+    tot_t = tot_a = 0.0
+    for l in layers:
+        kib = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            v = [float(r["Counter_Value"]) for r in out[counter]["rows"]
+                 if "w4a16" in r["Kernel_Name"] and int(r["Grid_Size"]) == l["grid"]]
+            kib[counter] = _median(v)
+        t = (kib["FETCH_SIZE"] * out["FETCH_SIZE"]["scale"] + kib["WRITE_SIZE"] * out["WRITE_SIZE"]["scale"]) * 1024
+        alg = decode_bytes(l["M"], l["N"], l["K"], GROUP)
+        tot_t += t
+        tot_a += alg
+        lines.append(f"  ({l['K']:5d},{l['N']:5d})  {kib['FETCH_SIZE']:10.1f}  {kib['WRITE_SIZE']:10.1f}  "
+                     f"{t:14.0f}  {alg:18d}  {t / alg:.4f}")
+    n = len(layers)
+    lines.append(f"  mean traffic per launch: {tot_t / n:.0f} bytes; algorithmic {tot_a / n:.0f}; "
+                 f"ratio {tot_t / tot_a:.4f}")
+    return "\n".join(lines), int(round(tot_t / n))
+
+
+def run_profile(kind, steps, dev):
+    """Eager launches for a profiler: each layer `steps` times in turn."""
+    import torch
+    shapes, M = (DECODE_LAYERS, 1) if kind == "decode" else (PREFILL_LAYERS, 1920)
+    layers = [build_layer(K, N, M, ("bench-" + kind, K, N), dev) for (K, N) in shapes]
+    fns = [Launcher(l, l["wq"], l["zp"], l["s"]) for l in layers]
+    sp = torch.cuda.current_stream().cuda_stream
+    for fn in fns:
+        fn(sp)
+    torch.cuda.synchronize()
+    for fn in fns:
+        for _ in range(steps):
+            fn(sp)
+        torch.cuda.synchronize()
+    print(json.dumps(dict(profile=kind, M=M, layers=[f"{K}x{N}" for (K, N) in shapes], launches_per_layer=steps)),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -459,10 +749,28 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MB (for scaling PMC byte counters)")
+    ap.add_argument("--profile", choices=("decode", "prefill"), default="",
+                    help="instead of the bench line: --steps eager launches of each decode layer (M=1) "
+                         "or prefill layer (M=1920) on one weight copy, for rocprofv3 kernel traces and "
+                         "counters (one dispatch per launch, kernels named per layer by their grid)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="print a profiles/ summary from rocprofv3 csv output (no GPU needed): "
+                         "'trace KIND DIR', 'pmc KIND DIR_A [DIR_B]' or 'traffic KIND FETCH_DIR WRITE_DIR'")
     ap.add_argument("--report", default="",
                     help="instead of the bench line: time every point of the decode, prefill and "
                          "dispatch-sweep workloads on both paths, write <REPORT>.md and .json")
     args = ap.parse_args()
+
+    if args.summarize:
+        what, kind, dirs = args.summarize[0], args.summarize[1], args.summarize[2:]
+        if what == "trace":
+            print(summarize_trace(kind, dirs[0], args.steps))
+        elif what == "pmc":
+            print(summarize_pmc(kind, dict(zip("AB", dirs)), args.steps))
+        elif what == "traffic":
+            text, per_launch = summarize_traffic(kind, dirs[0], dirs[1], args.steps)
+            print(text)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: libw4a16 has no multi-GPU path (row- and "
@@ -480,7 +788,6 @@ def main():
     if args.report:
         run_report(args.report)
         return
-
     if args.calibration_copy_mb:
         # a plain copy of known size: reads and writes exactly n bytes, so the
         # HBM byte counters of this dispatch give their scale on this device
@@ -491,6 +798,10 @@ def main():
             torch.bitwise_not(src, out=dst)  # one elementwise kernel: n bytes in, n out
         torch.cuda.synchronize()
         del src, dst
+
+    if args.profile:
+        run_profile(args.profile, args.steps, dev)
+        return
 
     # ---- decode: four layers at M = 1, weight copies rotated through HBM ----
     layers = [build_layer(K, N, 1, ("bench-decode", K, N), dev) for (K, N) in DECODE_LAYERS]
@@ -523,12 +834,25 @@ def main():
     mean_ms = float(np.mean(durs))
     achieved = mean_bytes / (mean_ms * 1e-3) / 1e9
     traffic = measured_traffic()
+    ceil_rows = decode_ceilings(layers, pool, side)
+    floor_ms = sum(r["stream_read_us"] for r in ceil_rows) * 1e-3
+    loads_ms = sum(r["loads_only_us"] for r in ceil_rows) * 1e-3
+    measured_ceiling = dict(
+        what="ceiling kernels on the same weight copies, per launch (graphs rotating >= 1 GiB)",
+        stream_read_GBs=round(step_bytes / (floor_ms * 1e-3) / 1e9, 1),
+        decode_loads_only_GBs=round(step_bytes / (loads_ms * 1e-3) / 1e9, 1),
+        frac_of_stream_read=round(achieved / (step_bytes / (floor_ms * 1e-3) / 1e9), 4),
+        frac_of_decode_loads_only=round(achieved / (step_bytes / (loads_ms * 1e-3) / 1e9), 4),
+        note="GB/s = the step's algorithmic bytes over the summed per-layer times of reading only "
+             "the packed weights (stream: grid-stride read; loads only: the decode kernel's grid and "
+             "1 KiB blocks, nothing computed); padN: 16-row tiles N bytes apart beyond the packed tile",
+        per_layer=ceil_rows)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     traffic_unit="bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                     kernel="gemv_small_kernel<bf16, group 128, asym>",
                     mean_launch_us=round(mean_ms * 1e3, 3), bytes_per_launch=int(mean_bytes),
-                    per_layer=per_layer)
+                    per_layer=per_layer, measured_ceiling=measured_ceiling)
 
     # ---- prefill: M = 1920 on the three prefill layers ----
     prefill = None
@@ -552,6 +876,8 @@ def main():
                        per_layer=[dict(K=K, N=N, us=round(d * 1e3, 2),
                                        tflops=round(2 * 1920 * N * K / (d * 1e-3) / 1e12, 1))
                                   for (K, N), d in zip(PREFILL_LAYERS, pdurs)])
+        mc = mfma_ceiling(side, torch.cuda.get_device_properties(dev).multi_processor_count)
+        prefill["measured_ceiling"] = dict(mc, frac_of_measured=round(tflops / mc["best"], 4))
         if not args.no_dense:
             prefill["dequantised_copy"] = dense_comparator(players, side, args.prefill_steps)
         del players, plaunch

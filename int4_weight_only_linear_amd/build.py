@@ -31,6 +31,9 @@ COMMON = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["w4a16_host.cpp", "w4a16_gemv.hip", "w4a16_gemm.hip", "w4a16_elementwise.hip"]
+# measurement kernels for the benchmark's ceilings, a library of their own
+CEILING_SOURCES = ["w4a16_ceilings.hip"]
+CEILINGS_LIB = os.path.join(PKG, "libw4a16_ceilings.so")
 # the decode kernel takes its first ten arguments preloaded into SGPRs
 EXTRA = {"w4a16_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
 
@@ -83,19 +86,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile and link libw4a16.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile and link libw4a16.so (and the benchmark's ceiling kernels,
+    libw4a16_ceilings.so); returns the path of libw4a16.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(CEILING_SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES + CEILING_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CEILINGS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILINGS_LIB}")
     return LIB
 
 

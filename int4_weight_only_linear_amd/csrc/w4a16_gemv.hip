@@ -662,7 +662,7 @@ size_t gemv_lds_bytes(int waves, int64_t M, int kpw, int group) {
   return red + (size_t)waves * (size_t)gemv_wave_lds_bytes((int)M, kpw, group);
 }
 
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu_count) {
   GemvPlan p;
   p.tiles = (int)((N + kGemvRowsPerTile - 1) / kGemvRowsPerTile);
   p.ksteps = (int)((K + kGemvKStep - 1) / kGemvKStep);
@@ -671,13 +671,15 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count) {
   // x segments (M * 16 * kpw segments per wave, 64 lanes): kpw <= 4 * XPT / M.
   // The scale and zero-point staging then needs at most 32 * kpw / group and
   // 4 * kpw / group loads per lane, which the kernel's fixed counts cover.
-  // measured on the decode layers: 8 k-steps per wave for one token, 4 for
-  // up to 8 tokens, 1 above (deeper waves are slower there); two to four
-  // tokens keep 8 only where 4 would need more than kGemvMaxWaves waves and
-  // so a K split (M = 2 with 4: 6-13 % faster on K = 2560-4096 layers, 28 %
-  // slower on K = 9728, where it splits)
+  // measured on the decode layers: 8 k-steps per wave for one bf16 token, 4
+  // for up to 8 tokens, 1 above (deeper waves are slower there); one fp16
+  // token and two to four tokens keep 8 only where 4 would need more than
+  // kGemvMaxWaves waves and so a K split (M = 2 with 4: 6-13 % faster on K =
+  // 2560-4096 layers, 28 % slower on K = 9728, where it splits; one fp16
+  // token with 4: 8-9 % faster on K = 2560 and 4096, whose dequantisation
+  // costs more VALU work per weight than bf16's and gains from more waves)
   int kpw = kGemvStepsPerWave;
-  const bool deep = M == 1 || (M <= 4 && p.ksteps > 4 * kGemvMaxWaves);
+  const bool deep = (M == 1 && dtype == DT_BF16) || (M <= 4 && p.ksteps > 4 * kGemvMaxWaves);
   while (kpw > 1 && (M * kpw > 4 * kGemvXSegsPerThread || (kpw > 4 && !deep) || M > 8)) kpw >>= 1;
   // tuning overrides: k-steps per wave (a smaller power of two) and a
   // minimum number of K splits

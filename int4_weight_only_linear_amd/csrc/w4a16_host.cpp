@@ -233,7 +233,7 @@ size_t workspace_for(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dty
                      w4a16_path path, int cu_count) {
   if (M <= 0) return 0;
   if (path == W4A16_PATH_GEMV) {
-    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, group, cu_count);
+    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, group, dtype, cu_count);
     return w4a16::gemv_workspace_bytes(plan, M, N);
   }
   return w4a16::gemm_workspace_bytes(M, N, K, group, dtype, asym, cu_count);
@@ -280,7 +280,7 @@ w4a16_status linear_impl(const void* x, const int32_t* wq, const void* scales, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p == W4A16_PATH_GEMV) {
-    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, group_size, dev->cu_count);
+    const w4a16::GemvPlan plan = w4a16::plan_gemv(M, N, K, group_size, dtype, dev->cu_count);
     if (log_enabled())
       std::fprintf(stderr,
                    "[w4a16] gemv M=%lld N=%lld K=%lld g=%d %s %s tiles=%d splits=%d waves=%d\n",
@@ -485,7 +485,7 @@ w4a16_status w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int
   w4a16_plan_info r{};
   r.path = p;
   if (p == W4A16_PATH_GEMV) {
-    const w4a16::GemvPlan g = w4a16::plan_gemv(M, N, K, gm.kgroup, cus);
+    const w4a16::GemvPlan g = w4a16::plan_gemv(M, N, K, gm.kgroup, dtype, cus);
     r.tile_features = w4a16::kGemvRowsPerTile;
     r.tile_tokens = w4a16::kGemvMaxM;
     r.splits = g.splits;
@@ -627,7 +627,7 @@ w4a16_status w4a16_moe_linear(const void* x, const int32_t* wq, const void* scal
   if (st != W4A16_OK) return st;
   const GroupMap gm = group_map(group_size, K);
   // one K range per slot (the slots fill the device): planned as if for one CU
-  const w4a16::GemvPlan plan = w4a16::plan_gemv(1, N, K, gm.kgroup, 1);
+  const w4a16::GemvPlan plan = w4a16::plan_gemv(1, N, K, gm.kgroup, dtype, 1);
   if (plan.splits != 1)
     return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is too large for one decode workgroup per slot",
                 (long long)K);

@@ -68,7 +68,7 @@ constexpr int kGemvMaxM = 16;         // one MFMA row tile of tokens
 constexpr int kGemvStepsPerWave = 8;
 // decode, single token bf16 g128: the workgroup's scales (16 rows x 8 groups
 // per wave, bf16) and packed zero points (2 row blocks x 8 groups per wave)
-constexpr int kGemvWgSzBytes = kGemvMaxWaves * (16 * 8 * 2 + 2 * 8 * 4);  // k-steps whose loads a wave keeps in flight
+constexpr int kGemvWgSzBytes = kGemvMaxWaves * (16 * 8 * 2 + 2 * 8 * 4);
 // K bound: per-lane byte offsets within a row tile, and products of a row
 // index below 16 with K or a stride, stay in 24-bit / 32-bit arithmetic
 constexpr int64_t kMaxK = int64_t(1) << 24;
@@ -76,10 +76,12 @@ constexpr int kGemvXSegsPerThread = 8;  // 16-byte x loads per thread when x is 
 // Dynamic LDS per decode workgroup (cross-wave reduction + staged x).  The
 // kernel's LDS layout and the host's plan both size it with gemv_lds_bytes,
 // and the plan splits K until it fits the budget.  gfx950 has 160 KiB of LDS
-// per CU: with at most one row tile per CU a workgroup may take 128 KiB (a K
-// split costs a partial-sum hand-off); with more tiles than CUs, 64 KiB, so
-// that several workgroups are resident on a CU at once.
-constexpr size_t kGemvLdsBudget = 128 * 1024;       // the most any plan uses
+// per CU: with at most one row tile per CU a workgroup may take nearly all of
+// it (a K split costs a partial-sum hand-off; 2.5 KiB are left for the
+// kernel's static LDS: the workgroup scale-fetch array of the single-token
+// instance and the split flag); with more tiles than CUs, 64 KiB, so that
+// several workgroups are resident on a CU at once.
+constexpr size_t kGemvLdsBudget = 160 * 1024 - kGemvWgSzBytes - 256;  // the most any plan uses
 constexpr size_t kGemvLdsBudgetShared = 64 * 1024;  // more row tiles than CUs
 
 struct GemvPlan {
@@ -105,7 +107,7 @@ __host__ __device__ inline int gemv_wave_lds_bytes(int M, int kpw, int group) {
   return (b + 15) / 16 * 16;
 }
 size_t gemv_lds_bytes(int waves, int64_t M, int kpw, int group);
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int cu_count);
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu_count);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N);
 // Expert-indexed decode: slots = M * topk products of one token row with the
 // expert topk_ids[slot]'s slice of [E, ...] stacks (see w4a16_moe_linear).

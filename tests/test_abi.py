@@ -345,3 +345,24 @@ def test_accept_set_golden_drives_validation():
     for M in range(1, g["decode_m_threshold_on_pages"] + 1):
         for K in (2560, 4096, 14336, 28672):
             assert L.w4a16_select_path(M, 4096, K, 128, L.W4A16_BF16, True) == L.PATH_GEMV
+
+
+# ---- the benchmark's ceiling kernels: library, header and host checks ---------
+
+def test_ceilings_library_exports_its_header_and_checks_arguments():
+    from int4_weight_only_linear_amd import ceilings as C
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "w4a16_ceilings.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(w4a16c_[a-z_]+)\s*\(", text)))
+    assert declared == sorted(C.SIGNATURES)
+    lib = ctypes.CDLL(C.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    # refused on the host, before any launch (hipErrorInvalidValue = 1)
+    assert C.lib.w4a16c_stream_read(None, 64, P, None) == 1
+    assert C.lib.w4a16c_stream_read(P + 8, 64, P, None) == 1
+    K = 4096
+    assert C.lib.w4a16c_decode_loads(P, 16 * 8 * K, 17, K, 8 * K, 8, 4, P, None) == 1      # tiles past the buffer
+    assert C.lib.w4a16c_decode_loads(P, 16 * 8 * K, 16, K, 8 * K - 16, 8, 4, P, None) == 1  # stride below a tile
+    assert C.lib.w4a16c_decode_loads(P, 16 * 8 * K, 16, K, 8 * K, 4, 4, P, None) == 1      # waves * kpw < K/128
+    assert C.lib.w4a16c_decode_loads(P, 16 * 8 * K, 16, K, 8 * K, 8, 17, P, None) == 1     # more than 16 waves
+    assert C.lib.w4a16c_mfma_loop(0, 10, 1, P, None) == 1

@@ -278,14 +278,26 @@ def test_workspace_reuse_across_shapes():
     # where a later call's counters sit where an earlier call's partial sums were
     # (every shape needs more than 16 waves for one K range, so each is split)
     # (or, at M <= 4 and 8 k-steps a wave, more LDS than one workgroup holds)
-    shapes = [(5, 264, 9728, 128), (4, 2560, 14336, 128), (2, 40, 20480, 64), (3, 1024, 12288, 32)]
+    shapes = [(5, 264, 9728, 128), (4, 2560, 20480, 128), (2, 40, 20480, 64), (3, 1024, 16384, 32)]
     cases = [make_case(M, N, K, g, O.BF16, False, False, seed=("reuse", M, N, K, g))
              for (M, N, K, g) in shapes]
+    for (M, N, K, g) in shapes:
+        assert L.w4a16_plan(M, N, K, g, O.BF16, True, GEMV)["splits"] > 1, (M, N, K, g)
     devs = [DeviceCase(c) for c in cases]
     refs = [oracle_rows(c) for c in cases]
     for _ in range(2):
         for d, ref in zip(devs, refs):
             assert_close(d.run(GEMV), ref, O.BF16, "reuse")
+
+
+@pytest.mark.parametrize("M", [3, 4])
+def test_decode_long_k_one_tile_per_cu_unsplit(M):
+    # three or four tokens on a 14336 x 4096 layer (256 row tiles, one per CU):
+    # with nearly all of the CU's LDS for one workgroup, K stays whole
+    N, K = 4096, 14336
+    assert L.w4a16_plan(M, N, K, 128, O.BF16, True, GEMV)["splits"] == 1
+    c = make_case(M, N, K, 128, O.BF16, False, False, seed=("lds160", M))
+    assert_close(DeviceCase(c).run(GEMV), oracle_rows(c), O.BF16, f"M={M}")
 
 
 def test_workspace_errors():
