@@ -451,11 +451,23 @@ def run_report(path_prefix):
     """Every point of the decode, prefill and dispatch-sweep workloads on both
     paths: per-launch time, GB/s and % of HBM peak, TFLOP/s and % of the
     dense MFMA peak, roofline fraction, and the dispatch crossover M* per
-    (shape, group, quantisation, dtype).  Writes <prefix>.md and <prefix>.json."""
+    (shape, group, quantisation, dtype).  Beside each point, the CPU oracle
+    on this host's cores: unpack + exact dequantisation (once per weight) and
+    its fp64 product at that M, with the GPU's speedup over the two.  Writes
+    <prefix>.md and <prefix>.json."""
+    import contextlib
     import torch
     import int4_weight_only_linear_amd as L
+    import oracle as O
     from synth import make_case
     from synth.configs import CONFIGS
+    cores = host_cores()
+    try:
+        from threadpoolctl import threadpool_limits
+        pool_ctx = threadpool_limits(limits=cores)
+    except ImportError:  # pragma: no cover
+        pool_ctx = contextlib.nullcontext()
+    pool_ctx.__enter__()
     dev = torch.device("cuda:0")
     side = torch.cuda.Stream()
     rows = []
@@ -498,6 +510,31 @@ def run_report(path_prefix):
                                                      TFLOPs=round(tfl, 1),
                                                      mfma_frac=round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
                                                      roofline_frac=round(frac, 4)))
+                            # the oracle on the same case: unpack + exact dequant once,
+                            # then its fp64 product for each M
+                            wq_o = O.pack_weights(c.q)
+                            zp_o = None if sym else O.pack_zeros(c.zp)
+                            t0 = time.perf_counter()
+                            w64 = O.dequant_f32(wq_o, c.s_bits, zp_o, N, K, g, dt).astype(np.float64)
+                            t_deq = time.perf_counter() - t0
+                            b64 = None if c.bias_bits is None else O.act_bits_to_f64(c.bias_bits, dt)
+                            t_gemm = {}
+                            for M in cfg.Ms:
+                                x64 = O.act_bits_to_f64(c.x_bits[:M], dt)
+                                t0 = time.perf_counter()
+                                y64 = x64 @ w64.T
+                                if b64 is not None:
+                                    y64 = y64 + b64[None, :]
+                                t_gemm[M] = time.perf_counter() - t0
+                            del w64
+                            for r in rows:
+                                if (r["config"], r["K"], r["N"], r["group"], r["quant"], r["dtype"], r["bias"]) == \
+                                        (name, K, N, g, "uint4b8" if sym else "uint4+zp", "fp16" if dt == 0 else "bf16",
+                                         bias) and "oracle_ms" not in r:
+                                    r["oracle_dequant_ms"] = round(t_deq * 1e3, 1)
+                                    r["oracle_gemm_ms"] = round(t_gemm[r["M"]] * 1e3, 2)
+                                    r["oracle_ms"] = round((t_deq + t_gemm[r["M"]]) * 1e3, 1)
+                                    r["speedup_vs_oracle"] = round(r["oracle_ms"] / (r["us"] * 1e-3))
                             print(f"[report] {name} K={K} N={N} g={g} {'sym' if sym else 'asym'} "
                                   f"{'fp16' if dt == 0 else 'bf16'} bias={bias}: {len(cfg.Ms)} M values "
                                   f"({time.time() - t_start:.0f}s)", file=sys.stderr, flush=True)
@@ -526,14 +563,19 @@ def run_report(path_prefix):
         f.write("Each point: mean time per launch over a HIP graph of back-to-back launches that rotate\n"
                 "through >= 1 GiB of weight copies (weights stream from HBM).  GB/s = algorithmic bytes\n"
                 "(weights, scales, zp, x, y, bias) / time; TFLOP/s = 2*M*N*K / time; peaks 8 TB/s and\n"
-                "2.5 PFLOP/s.  auto (*) marks the kernel W4A16_PATH_AUTO picks.\n\n")
-        f.write("| config | K | N | M | g | quant | dtype | bias | path | auto | us | GB/s | %HBM | TFLOP/s | %MFMA |\n")
-        f.write("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+                "2.5 PFLOP/s.  auto (*) marks the kernel W4A16_PATH_AUTO picks.  Oracle: the CPU oracle\n"
+                f"on this host ({cores} cores, BLAS on all of them): unpack + exact dequantisation of the\n"
+                "layer (deq, once per weight) + its fp64 product at this M (gemm); x = GPU speedup over\n"
+                "deq + gemm.\n\n")
+        f.write("| config | K | N | M | g | quant | dtype | bias | path | auto | us | GB/s | %HBM | TFLOP/s | "
+                "%MFMA | oracle deq ms | oracle gemm ms | x |\n")
+        f.write("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:
             f.write(f"| {r['config']} | {r['K']} | {r['N']} | {r['M']} | {r['group']} | {r['quant']} | "
                     f"{r['dtype']} | {'y' if r['bias'] else 'n'} | {r['path']} | {'*' if r['auto'] else ''} | "
                     f"{r['us']} | {r['GBs']} | {100 * r['hbm_frac']:.1f} | {r['TFLOPs']} | "
-                    f"{100 * r['mfma_frac']:.1f} |\n")
+                    f"{100 * r['mfma_frac']:.1f} | {r.get('oracle_dequant_ms', '')} | "
+                    f"{r.get('oracle_gemm_ms', '')} | {r.get('speedup_vs_oracle', '')} |\n")
         f.write("\n| K | N | g | quant | dtype | M* (largest M where the decode kernel is faster) |\n")
         f.write("|---|---|---|---|---|---|\n")
         for m in mstar:
@@ -717,6 +759,69 @@ def summarize_traffic(kind, fetch_dir, write_dir, steps, copy_mb=256):
     return "\n".join(lines), int(round(tot_t / n))
 
 
+# ---- performance regression check with a control --------------------------------
+
+QWEN_DECODE_LAYERS = ((2560, 6144), (4096, 2560), (2560, 19456), (9728, 2560))  # (K, N), fp16 sym
+
+
+def perf_points(dev, stream):
+    """Per-launch times (us) of the decode layers at M=1 (Llama bf16 asym, Qwen
+    fp16 sym; graphs rotating >= 1 GiB of weight copies) and the prefill layers
+    at M=1920, plus two controls timed in the same run: a streaming read of
+    1 GiB (GB/s) and the sustained MFMA loop (TFLOP/s)."""
+    import torch
+    import int4_weight_only_linear_amd as L
+    from int4_weight_only_linear_amd import ceilings as C
+    from synth import make_case
+    sink = torch.zeros(16, dtype=torch.int32, device=dev)
+    bufs = [torch.empty(1 << 28, dtype=torch.uint8, device=dev) for _ in range(4)]
+    t = graph_launch_ms([lambda sp, b=b: C.stream_read(b, sink, sp) for b in bufs], stream, passes=2)
+    control = dict(stream_read_GBs=round((1 << 28) / (t * 1e-3) / 1e9, 1),
+                   mfma_TFLOPs=mfma_ceiling(stream, torch.cuda.get_device_properties(dev).multi_processor_count)["best"])
+    del bufs
+    points = {}
+    for fam, shapes, dt, sym in (("llama8b_decode", DECODE_LAYERS, 1, False),
+                                 ("qwen3_4b_decode", QWEN_DECODE_LAYERS, 0, True)):
+        for (K, N) in shapes:
+            c = make_case(1, N, K, GROUP, dt, sym, False, seed=("perf", fam, K, N))
+            wq, zp, s, x, b = _layer_tensors(c, dev)
+            wbytes = wq.numel() * 4 + s.numel() * 2 + (0 if zp is None else zp.numel() * 4)
+            copies = max(2, min(64, math.ceil((1 << 30) / wbytes)))
+            pool = [(wq, zp, s)] + [(wq.clone(), None if zp is None else zp.clone(), s.clone())
+                                    for _ in range(copies - 1)]
+            y = torch.empty((1, N), dtype=x.dtype, device=dev)
+            ms = min(time_point(x, pool, b, y, 1, N, K, GROUP, dt, L.PATH_AUTO, 50, stream) for _ in range(2))
+            points[f"{fam} {K}x{N} M=1"] = round(ms * 1e3, 3)
+            del pool, wq, zp, s
+            torch.cuda.empty_cache()
+    for (K, N) in PREFILL_LAYERS:
+        l = build_layer(K, N, 1920, ("bench-prefill", K, N), dev)
+        fn = Launcher(l, l["wq"], l["zp"], l["s"])
+        fn(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        graph_launch_ms([fn, fn], stream, passes=5, replays=4, reps=2)  # steady clocks
+        ms = graph_launch_ms([fn, fn], stream, passes=3, replays=2, reps=3)
+        points[f"llama8b_prefill {K}x{N} M=1920"] = round(ms * 1e3, 2)
+        del l, fn
+        torch.cuda.empty_cache()
+    return dict(control=control, points_us=points)
+
+
+def perf_compare(base, now, band=1.25):
+    """Each point's time relative to the baseline, divided by how much faster
+    the control runs now than then (stream read for decode points, MFMA loop
+    for prefill points); a point regresses when that ratio exceeds `band`."""
+    out = []
+    for name, t0 in base["points_us"].items():
+        t1 = now["points_us"][name]
+        key, unit = ("mfma_TFLOPs", "mfma") if "prefill" in name else ("stream_read_GBs", "stream")
+        speed = now["control"][key] / base["control"][key]
+        ratio = t1 / t0 * speed
+        out.append(dict(point=name, base_us=t0, now_us=t1, control=unit, control_speedup=round(speed, 3),
+                        normalized_ratio=round(ratio, 3), regressed=ratio > band))
+    return out
+
+
 def run_profile(kind, steps, dev):
     """Eager launches for a profiler: each layer `steps` times in turn."""
     import torch
@@ -756,6 +861,11 @@ def main():
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
                     help="print a profiles/ summary from rocprofv3 csv output (no GPU needed): "
                          "'trace KIND DIR', 'pmc KIND DIR_A [DIR_B]' or 'traffic KIND FETCH_DIR WRITE_DIR'")
+    ap.add_argument("--perf-record", default="", metavar="FILE",
+                    help="measure the performance-regression points and their controls, write FILE (json)")
+    ap.add_argument("--perf-check", default="", metavar="FILE",
+                    help="measure the same points and compare with FILE, normalised by the controls; "
+                         "exit 1 on a regression beyond 25%%")
     ap.add_argument("--report", default="",
                     help="instead of the bench line: time every point of the decode, prefill and "
                          "dispatch-sweep workloads on both paths, write <REPORT>.md and .json")
@@ -768,8 +878,18 @@ def main():
         elif what == "pmc":
             print(summarize_pmc(kind, dict(zip("AB", dirs)), args.steps))
         elif what == "traffic":
+            import hashlib
             text, per_launch = summarize_traffic(kind, dirs[0], dirs[1], args.steps)
+            h = hashlib.sha256()
+            csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "int4_weight_only_linear_amd", "csrc")
+            for f in DECODE_SOURCES:
+                with open(os.path.join(csrc, f), "rb") as fh:
+                    h.update(fh.read())
             print(text)
+            print("\nmachine-readable (read by bench.py; valid only while the hash of the decode kernel "
+                  "sources matches):")
+            print(f"traffic_bytes_per_launch: {per_launch}")
+            print(f"kernel_source_sha256: {h.hexdigest()}")
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -802,6 +922,20 @@ def main():
     if args.profile:
         run_profile(args.profile, args.steps, dev)
         return
+    if args.perf_record or args.perf_check:
+        side = torch.cuda.Stream()
+        now = perf_points(dev, side)
+        now["device"] = torch.cuda.get_device_properties(dev).gcnArchName
+        if args.perf_record:
+            with open(args.perf_record, "w") as f:
+                json.dump(now, f, indent=1)
+            print(json.dumps(now), flush=True)
+            return
+        with open(args.perf_check) as f:
+            base = json.load(f)
+        res = perf_compare(base, now)
+        print(json.dumps(dict(control_now=now["control"], control_base=base["control"], points=res)), flush=True)
+        sys.exit(1 if any(r["regressed"] for r in res) else 0)
 
     # ---- decode: four layers at M = 1, weight copies rotated through HBM ----
     layers = [build_layer(K, N, 1, ("bench-decode", K, N), dev) for (K, N) in DECODE_LAYERS]

@@ -31,3 +31,24 @@ def test_decode_bytes_counts_each_operand_once():
     # the four decode layers' mean: the per-launch figure the roofline uses
     total = sum(bench.decode_bytes(1, n, k, g) for (k, n) in bench.DECODE_LAYERS)
     assert total // len(bench.DECODE_LAYERS) == 28362752
+
+
+def test_perf_compare_normalises_by_the_control():
+    base = dict(control=dict(stream_read_GBs=5000.0, mfma_TFLOPs=1800.0),
+                points_us={"llama8b_decode 4096x4096 M=1": 4.0, "llama8b_prefill 4096x6144 M=1920": 90.0})
+    # 30 % slower on a box whose control is as fast: a regression
+    now = dict(control=dict(stream_read_GBs=5000.0, mfma_TFLOPs=1800.0),
+               points_us={"llama8b_decode 4096x4096 M=1": 5.2, "llama8b_prefill 4096x6144 M=1920": 90.0})
+    res = {r["point"]: r for r in bench.perf_compare(base, now)}
+    assert res["llama8b_decode 4096x4096 M=1"]["regressed"]
+    assert not res["llama8b_prefill 4096x6144 M=1920"]["regressed"]
+    # the same times on a box whose streaming read is 30 % slower: none
+    now["control"]["stream_read_GBs"] = 5000.0 / 1.3
+    res = {r["point"]: r for r in bench.perf_compare(base, now)}
+    assert not res["llama8b_decode 4096x4096 M=1"]["regressed"]
+    assert abs(res["llama8b_decode 4096x4096 M=1"]["normalized_ratio"] - 1.0) < 1e-3
+    # prefill points are normalised by the MFMA control, not the stream read
+    now["points_us"]["llama8b_prefill 4096x6144 M=1920"] = 120.0
+    res = {r["point"]: r for r in bench.perf_compare(base, now)}
+    assert res["llama8b_prefill 4096x6144 M=1920"]["regressed"]
+    assert res["llama8b_prefill 4096x6144 M=1920"]["control"] == "mfma"
