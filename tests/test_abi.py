@@ -166,15 +166,27 @@ def test_zero_point_dtype_message_is_the_pages():
 # ---- path selection and workspace sizing (host logic) -----------------------
 
 def test_select_path_by_m():
-    # K <= 4096: the decode kernel up to M = 16; larger K: up to M = 8
+    sel = lambda M, N, K, g=128: L.w4a16_select_path(M, N, K, g, 1, 1)
+    # K <= 4096: the decode kernel up to M = 16 ...
     for M in (1, 2, 5, 8, 9, 16):
-        assert L.w4a16_select_path(M, 4096, 4096, 128, 1, 1) == L.PATH_GEMV
+        assert sel(M, 4096, 4096) == L.PATH_GEMV
+        assert sel(M, 14336, 4096, 32) == L.PATH_GEMV
     for M in (17, 32, 65, 128, 1920):
-        assert L.w4a16_select_path(M, 4096, 4096, 128, 1, 1) == L.PATH_GEMM
-    for M in (1, 5, 8):
-        assert L.w4a16_select_path(M, 4096, 14336, 128, 1, 1) == L.PATH_GEMV
-    for M in (9, 16, 32, 1920):
-        assert L.w4a16_select_path(M, 4096, 14336, 128, 1, 1) == L.PATH_GEMM
+        assert sel(M, 4096, 4096) == L.PATH_GEMM
+    # ... except groups of 128 on 896 or more row tiles: up to M = 8
+    for M in (1, 8):
+        assert sel(M, 14336, 4096) == L.PATH_GEMV
+    for M in (9, 16):
+        assert sel(M, 14336, 4096) == L.PATH_GEMM
+    # 4096 < K <= 16384: up to M = 12; longer K: up to M = 8
+    for M in (1, 5, 8, 12):
+        assert sel(M, 4096, 14336) == L.PATH_GEMV
+    for M in (13, 16, 32, 1920):
+        assert sel(M, 4096, 14336) == L.PATH_GEMM
+    for M in (1, 8):
+        assert sel(M, 4096, 28672) == L.PATH_GEMV
+    for M in (9, 12, 16):
+        assert sel(M, 4096, 28672) == L.PATH_GEMM
 
 
 def test_select_path_env_override(tuning_env):
