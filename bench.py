@@ -153,7 +153,8 @@ def per_launch_durations(step_lists, reps, stream, passes=5, replays=4):
     stream around `replays` back-to-back replays of a graph holding `passes`
     rounds of that position's launches (one per weight copy), so the graph
     and event overheads are spread over hundreds of launches and the kernels
-    run back to back as they do inside a step.  Median over `reps`."""
+    run back to back as they do inside a step.  (median, p10, p90) over
+    `reps` graph replays, each the mean launch of its replay."""
     import torch
     out = []
     for j in range(len(step_lists[0])):
@@ -171,7 +172,7 @@ def per_launch_durations(step_lists, reps, stream, passes=5, replays=4):
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) / n)
-        out.append(float(np.median(ts)))
+        out.append((float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))))
     return out
 
 
@@ -662,6 +663,7 @@ PMC_SETS = {
           "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT"],
     "B": ["SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
           "SQ_WAVES", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE"],
+    "C": ["TCC_HIT_sum", "TCC_MISS_sum", "MeanOccupancyPerActiveCU", "OccupancyPercent"],  # (the first two and the last are reported)
 }
 XCDS, SIMDS = 8, 1024
 
@@ -688,6 +690,7 @@ def summarize_pmc(kind, dirs, steps):
     for l in layers:
         a = [e for (tag, _), e in per.items() if tag == "A" and e["grid"] == l["grid"]]
         b = [e for (tag, _), e in per.items() if tag == "B" and e["grid"] == l["grid"]]
+        c = [e for (tag, _), e in per.items() if tag == "C" and e["grid"] == l["grid"]]
         lines.append(f"  layer (K,N) = ({l['K']},{l['N']}), M = {l['M']}, plan {l['plan']['tile_tokens']}x"
                      f"{l['plan']['tile_features']} tiles, {l['plan']['splits']} K range(s), {len(a)} dispatches")
         if a:
@@ -716,6 +719,12 @@ def summarize_pmc(kind, dirs, steps):
                          f"{_median([e['SQ_ACTIVE_INST_ANY'] / e['SQ_WAVE_CYCLES'] for e in b]):.3f}")
             lines.append(f"    VALU/MFMA co-execution {co:.3f} of GUI-active SIMD cycles; waves "
                          f"{_median([e['SQ_WAVES'] for e in b]):.0f}{extra}")
+        if c:
+            hit = _median([e["TCC_HIT_sum"] / max(1.0, e["TCC_HIT_sum"] + e["TCC_MISS_sum"]) for e in c])
+            pct = _median([e["OccupancyPercent"] for e in c])
+            lines.append(f"    L2 hit rate {hit:.3f} (TCC_HIT_sum / (HIT + MISS)); occupancy {pct:.1f} % of the "
+                         f"maximum (OccupancyPercent: waves resident over the 32 wave slots of each CU, averaged "
+                         f"over the kernel)")
     return "\n".join(lines)
 
 
@@ -860,7 +869,8 @@ def main():
                          "counters (one dispatch per launch, kernels named per layer by their grid)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
                     help="print a profiles/ summary from rocprofv3 csv output (no GPU needed): "
-                         "'trace KIND DIR', 'pmc KIND DIR_A [DIR_B]' or 'traffic KIND FETCH_DIR WRITE_DIR'")
+                         "'trace KIND DIR', 'pmc KIND DIR_A [DIR_B|- [DIR_C]]' or "
+                         "'traffic KIND FETCH_DIR WRITE_DIR'")
     ap.add_argument("--perf-record", default="", metavar="FILE",
                     help="measure the performance-regression points and their controls, write FILE (json)")
     ap.add_argument("--perf-check", default="", metavar="FILE",
@@ -876,7 +886,7 @@ def main():
         if what == "trace":
             print(summarize_trace(kind, dirs[0], args.steps))
         elif what == "pmc":
-            print(summarize_pmc(kind, dict(zip("AB", dirs)), args.steps))
+            print(summarize_pmc(kind, {t: d for t, d in zip("ABC", dirs) if d != "-"}, args.steps))
         elif what == "traffic":
             import hashlib
             text, per_launch = summarize_traffic(kind, dirs[0], dirs[1], args.steps)
@@ -957,11 +967,13 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
     # per-launch kernel durations of each layer
-    durs = per_launch_durations(launch_lists, max(5, args.steps // copies), side)
+    durs3 = per_launch_durations(launch_lists, max(5, args.steps // copies), side)
+    durs = [d[0] for d in durs3]
     per_layer = []
-    for l, d in zip(layers, durs):
+    for l, (d, d10, d90) in zip(layers, durs3):
         b = decode_bytes(1, l["N"], l["K"], GROUP)
         per_layer.append(dict(K=l["K"], N=l["N"], bytes=b, us=round(d * 1e3, 3),
+                              p10_us=round(d10 * 1e3, 3), p90_us=round(d90 * 1e3, 3),
                               GBs=round(b / (d * 1e-3) / 1e9, 1),
                               frac=round(b / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)))
     mean_bytes = step_bytes / len(layers)
@@ -998,7 +1010,8 @@ def main():
         torch.cuda.synchronize()
         # five passes per graph, so graph launches do not separate the passes
         pms = time_steps(plaunch * 5, args.prefill_steps, max(5, args.prefill_steps // 4), side)
-        pdurs = per_launch_durations(plaunch * 4, max(3, args.prefill_steps // 4), side, passes=1, replays=2)
+        pdurs = [d[0] for d in per_launch_durations(plaunch * 4, max(3, args.prefill_steps // 4), side, passes=1,
+                                                    replays=2)]
         flops = sum(2 * 1920 * N * K for (K, N) in PREFILL_LAYERS)
         tflops = flops / (pms * 1e-3) / 1e12
         prefill = dict(workload="Llama-3.1-8B-shaped prefill, M=1920, layers (K,N) "
