@@ -65,11 +65,11 @@ class PlanInfo(ctypes.Structure):
                 ("tile_tokens", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("counter_tiles", ctypes.c_int64),
                 ("launches", ctypes.c_int32), ("waves", ctypes.c_int32),
-                ("two_pass", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("two_pass", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 SIGNATURES["w4a16_plan"] = (_c_int, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,

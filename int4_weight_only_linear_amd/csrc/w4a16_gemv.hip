@@ -43,7 +43,9 @@
 //   to arrive adds them in range order.  Results do not depend on scheduling.
 //
 // gemv_small_kernel serves M <= 16 (one MFMA row tile of tokens).  Above
-// that the prefill GEMM is faster at every measured shape.
+// that the prefill GEMM is faster at every measured shape.  One token on
+// most shapes runs gemv_one_kernel (further below), which keeps only x in
+// LDS and finishes each group in the 16-lane row that owns it.
 #include <type_traits>
 
 #include "w4a16_device.hpp"
@@ -652,6 +654,216 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
 }
 
 // ---------------------------------------------------------------------------
+// M == 1: one token, one K range, every wave a run of KPW complete k-steps
+// ---------------------------------------------------------------------------
+// The kernel above stages each wave's scales, zero points and bf16 x group
+// sums through LDS and meets twice at workgroup barriers; for one token that
+// bookkeeping costs about as much time as the dequantisation.  This instance
+// keeps only x in LDS:
+// * With one token every row of the MFMA's A operand is x, so all four 16-lane
+//   rows of a result hold the same 16 dot products.  Each 16-lane row R
+//   therefore finishes only the groups it owns -- the R-th quarter of the
+//   wave's run -- and fetches only their scales and zero points: one small
+//   load per tensor and wave, straight into registers (the scale / zero-point
+//   carrier of "[ROCm] Converge the two W4A16 linear kernels onto the
+//   upstream shell", "What this does": no per-group metadata loads), issued
+//   after the weights, since only the end of the run needs them: the waits
+//   for the weights, which complete in issue order, never wait for them.
+// * Both dtypes multiply x by the exact magic value (128 or 1024) + q and
+//   remove (magic + z) per group with the group's sum of x (the general
+//   kernel's bf16 scheme; for fp16 it saves the packed subtraction, 4 of 11
+//   VALU instructions per weight word).  The group sums of x come from the
+//   matrix cores: an MFMA whose A rows are 16 chunks of x and whose B is all
+//   ones gives the 16 chunk sums, its rows ordered so that 16-lane row R
+//   receives the chunks of its own groups.
+// * The 16-lane rows are added with two permlane swaps; the waves through LDS
+//   after one barrier, in wave order.
+// waves per SIMD the register budget is sized for: runs of 8 k-steps, and
+// runs of 4 with 16 groups (groups of 32), hold more registers
+constexpr int one_waves_per_simd(int kpw, int gs) { return kpw == 8 || gs == 32 ? 6 : 8; }
+
+// 16-lane row R of the result takes vR (each v uniform across the wave): two
+// 16-lane swaps pair rows (0, 1) and (2, 3), one 32-lane swap joins the
+// halves.  (A select on the row index would be turned by the compiler into a
+// dynamic index of the source array, kept in scratch memory; a hand-written
+// v_cndmask would read MFMA results without the wait states the compiler
+// inserts for its own instructions.)
+__device__ __forceinline__ float row_select(float v0, float v1, float v2, float v3) {
+  const auto b = [](float f) { return __builtin_bit_cast(uint32_t, f); };
+  const auto lo = __builtin_amdgcn_permlane16_swap(b(v0), b(v1), false, false);  // rows 0, 2: v0; 1, 3: v1
+  const auto hi = __builtin_amdgcn_permlane16_swap(b(v2), b(v3), false, false);  // rows 0, 2: v2; 1, 3: v3
+  const auto r = __builtin_amdgcn_permlane32_swap(lo[0], hi[0], false, false);   // rows 2, 3 from hi
+  return __builtin_bit_cast(float, (uint32_t)r[0]);
+}
+
+// a lane's NW consecutive 32-bit words, read as one load where possible
+template <int NW>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[NW]) {
+  if constexpr (NW == 1) {
+    w[0] = *p;
+  } else if constexpr (NW == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+    static_assert(NW % 4 == 0, "words");
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const u32x4 v = reinterpret_cast<const u32x4*>(p)[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  }
+}
+
+template <int DT, int GS, bool ASYM, int KPW>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_per_simd(KPW, GS)))) void gemv_one_kernel(
+    const uint16_t* a_x, const uint32_t* a_wq, const uint16_t* a_scales, const uint32_t* a_zp, int N, int K,
+    int sG, const uint16_t* bias, uint16_t* y) {
+  constexpr int CPG = GS / 32;            // 32-k chunks per group
+  constexpr int NC = 4 * KPW;             // chunks of a run
+  constexpr int NGW = NC / CPG;           // groups of a run
+  constexpr int OWN = NGW / 4;            // groups each 16-lane row finishes
+  constexpr int KR = KPW * kGemvKStep;    // k of a run
+  constexpr int XPL = KR / 8 / 64;        // 16-byte x segments per lane
+  constexpr int SW = (OWN + 1) / 2;       // words holding the owned scales
+  static_assert(OWN >= 1 && OWN <= 4 && XPL >= 1, "instance");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int col = lane & 15;   // MFMA column: output row within the tile
+  const int row4 = lane >> 4;  // 16-lane row
+  const int n0 = blockIdx.x * kGemvRowsPerTile;
+  const int n = min(n0 + col, N - 1);  // rows past N read row N - 1
+  const int kw0 = wave * KR;           // first k of this wave's run
+  const int g0 = kw0 / GS;             // first group of the run
+  const int gown = g0 + row4 * OWN;    // first group this 16-lane row finishes
+  float* red = reinterpret_cast<float*>(smem);  // [waves][16]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 64 * nwaves + (size_t)wave * 2 * KR);  // [KR]
+
+  // ---- 1. loads: x, then the weights, then scales and zero points ----
+  // (the metadata is needed only after the run, so the waits for the weights
+  // never wait for it)
+  u32x4 xr[XPL];
+  const char* xb = reinterpret_cast<const char*>(a_x + kw0);
+#pragma unroll
+  for (int j = 0; j < XPL; ++j) xr[j] = *reinterpret_cast<const u32x4*>(xb + 16u * (uint32_t)(lane + 64 * j));
+  // the owned groups' zero-point words
+  constexpr int ZW = !ASYM ? 1 : OWN;
+  uint32_t zw[ZW];
+  const uint32_t* zrow = ASYM ? a_zp + (size_t)(n >> 3) * sG : nullptr;
+  if constexpr (!ASYM) zw[0] = 0u;
+
+  __builtin_amdgcn_sched_barrier(0);
+  const WeightWalk ww = weight_walk(a_wq, N, K, K >> 5, n0, col, row4);
+  u32x4 wv[KPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i)
+    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ww.at(wave * KPW + i)));
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t sw[SW];
+  if constexpr (OWN == 1) {
+    sw[0] = a_scales[(size_t)n * sG + gown];
+  } else {
+    load_words<SW>(reinterpret_cast<const uint32_t*>(a_scales + (size_t)n * sG + gown), sw);
+  }
+  if constexpr (ASYM) load_words<ZW>(zrow + gown, zw);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. x to this wave's LDS region; group sums of x ----
+#pragma unroll
+  for (int j = 0; j < XPL; ++j) *reinterpret_cast<u32x4*>(xs + 8 * (lane + 64 * j)) = xr[j];
+  float xsum[OWN];
+  {
+    // MFMA b: A row i is chunk (NC/4) (i / 4) + 4 b + i % 4 of the run and B
+    // is all ones, so the result rows 4R .. 4R+3 of 16-lane row R are the
+    // sums of the chunks of R's own groups
+    constexpr uint32_t ONE2 = DT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0 in both halves
+    const u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
+    const uint16_t* xa0 = xs + ((NC / 4) * (col >> 2) + (col & 3)) * 32 + 8 * row4;
+#pragma unroll
+    for (int b = 0; b < NC / 16; ++b) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(xa0 + 4 * 32 * b);
+      const f32x4 d = mfma16x16x32<DT>(a, ones, f32x4{0.f, 0.f, 0.f, 0.f});
+      if constexpr (CPG == 4) {
+        xsum[b] = (d[0] + d[1]) + (d[2] + d[3]);
+      } else if constexpr (CPG == 2) {
+        xsum[2 * b] = d[0] + d[1];
+        xsum[2 * b + 1] = d[2] + d[3];
+      } else {
+        xsum[4 * b] = d[0];
+        xsum[4 * b + 1] = d[1];
+        xsum[4 * b + 2] = d[2];
+        xsum[4 * b + 3] = d[3];
+      }
+    }
+  }
+
+  // ---- 3. dot products, one k-step at a time as its weights arrive ----
+  // (the loop of the kernel above: x fragments from LDS two chunks ahead, one
+  // MFMA chain per group, x multiplied by magic + q)
+  const uint32_t mask_v = vgpr_const(0x000F000Fu);
+  const uint16_t* xrow = xs + 8 * row4;  // every A row reads x
+  const int zshift = 4 * (n & 7);
+  constexpr int XD = 2;
+  u32x4 xa[XD + 1];
+  auto load_x = [&](int q) { return *reinterpret_cast<const u32x4*>(xrow + q * 32); };
+#pragma unroll
+  for (int q = 0; q < XD; ++q) xa[q] = load_x(q);
+  float chg[NGW];
+  f32x4 ch;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    const int i = q >> 2, t = q & 3;
+    if (t == 0) __builtin_amdgcn_sched_barrier(0);  // each step's work after its own wait
+    if (q + XD < NC) xa[(q + XD) % (XD + 1)] = load_x(q + XD);
+    const u32x4 a = xa[q % (XD + 1)];
+    const int gl = q / CPG;
+    const bool fresh = (q % CPG) == 0;
+    const u32x4 bq = magic_word<DT>(wv[i][t], mask_v);
+    ch = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
+    if (q % CPG == CPG - 1) chg[gl] = ch[0];
+  }
+
+  // ---- 4. each 16-lane row scales its own groups; rows, then waves, added ----
+  float acc = 0.f;
+#pragma unroll
+  for (int t = 0; t < OWN; ++t) {
+    // the group of 16-lane row R is R * OWN + t of the run
+    const float v = row_select(chg[t], chg[OWN + t], chg[2 * OWN + t], chg[3 * OWN + t]);
+    const uint32_t sbits = (sw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+    const float s = act_to_f32<DT>((uint16_t)sbits);
+    {
+      const uint32_t z = ASYM ? (zw[t] >> zshift) & 0xFu : 8u;
+      const float szc = -(Magic<DT>::value + (float)z) * s;
+      acc = __builtin_fmaf(s, v, __builtin_fmaf(szc, xsum[t], acc));
+    }
+  }
+  {
+    const uint32_t a = __builtin_bit_cast(uint32_t, acc);
+    const auto hi = __builtin_amdgcn_permlane32_swap(a, a, false, false);  // [1]: lanes 32..63 in 0..31
+    acc += __builtin_bit_cast(float, (uint32_t)hi[1]);
+    const uint32_t b = __builtin_bit_cast(uint32_t, acc);
+    const auto odd = __builtin_amdgcn_permlane16_swap(b, b, false, false);  // [1]: lanes 16..31 in 0..15
+    acc += __builtin_bit_cast(float, (uint32_t)odd[1]);
+  }
+  if (lane < 16) red[wave * 16 + lane] = acc;
+  __syncthreads();
+  const int nn = n0 + tid;
+  if (tid < kGemvRowsPerTile && nn < N) {
+    float v = 0.f;
+    for (int w = 0; w < nwaves; ++w) v += red[w * 16 + tid];
+    if (bias) v += act_to_f32<DT>(bias[nn]);
+    y[nn] = f32_to_act<DT>(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // planning and launch
 // ---------------------------------------------------------------------------
 
@@ -707,6 +919,19 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu
   p.splits = (p.ksteps + p.ksteps_per_split - 1) / p.ksteps_per_split;
   p.waves = (p.ksteps_per_split + kpw - 1) / kpw;
   p.lds_bytes = gemv_lds_bytes(p.waves, M, kpw, group);
+  // one token: the single-token instance, when K is a whole number of runs of
+  // 8 (else 4) k-steps for at most kGemvMaxWaves waves and a run spans at most
+  // 16 groups (one K range, no tail chunks)
+  if (M == 1 && K % kGemvKStep == 0 && !tu.gemv_no_one && tu.gemv_splits <= 1) {
+    for (int k : {8, 4}) {
+      if (tu.gemv_kpw >= 1 && k != tu.gemv_kpw) continue;
+      if (kGemvKStep * k / group > 16 || p.ksteps % k || p.ksteps / k > kGemvMaxWaves) continue;
+      p.one_kpw = k;
+      p.one_waves = p.ksteps / k;
+      p.one_lds_bytes = gemv_one_lds_bytes(p.one_waves, k);
+      break;
+    }
+  }
   return p;
 }
 
@@ -789,8 +1014,52 @@ static hipError_t launch_g(const GemvParams& prm, int group, const GemvPlan& pla
   }
 }
 
+template <int DT, int GS, bool ASYM>
+static hipError_t launch_one(const LinearArgs& a, const GemvPlan& plan, hipStream_t s) {
+  const dim3 grid(plan.tiles), block(64 * plan.one_waves);
+  const auto x = static_cast<const uint16_t*>(a.x);
+  const auto wq = reinterpret_cast<const uint32_t*>(a.wq);
+  const auto sc = static_cast<const uint16_t*>(a.scales);
+  const auto zp = reinterpret_cast<const uint32_t*>(a.zp);
+  const auto bias = static_cast<const uint16_t*>(a.bias);
+  const auto y = static_cast<uint16_t*>(a.y);
+  const int N = (int)a.N, K = (int)a.K;
+  if (plan.one_kpw == 8) {
+    if constexpr (GS >= 64)
+      hipLaunchKernelGGL((gemv_one_kernel<DT, GS, ASYM, 8>), grid, block, plan.one_lds_bytes, s, x, wq, sc, zp, N, K, a.sG, bias, y);
+    else
+      return hipErrorInvalidConfiguration;
+  } else if (plan.one_kpw == 4) {
+    hipLaunchKernelGGL((gemv_one_kernel<DT, GS, ASYM, 4>), grid, block, plan.one_lds_bytes, s, x, wq, sc, zp, N, K, a.sG, bias, y);
+  } else {
+    return hipErrorInvalidConfiguration;
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_one_g(const LinearArgs& a, const GemvPlan& plan, hipStream_t s) {
+  const bool asym = a.zp != nullptr;
+  switch (a.group) {
+    case 32: return asym ? launch_one<DT, 32, true>(a, plan, s) : launch_one<DT, 32, false>(a, plan, s);
+    case 64: return asym ? launch_one<DT, 64, true>(a, plan, s) : launch_one<DT, 64, false>(a, plan, s);
+    case 128: return asym ? launch_one<DT, 128, true>(a, plan, s) : launch_one<DT, 128, false>(a, plan, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool gemv_one_runs(const LinearArgs& a, const GemvPlan& plan, const MoeArgs* moe) {
+  const auto aligned16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  return plan.one_kpw != 0 && !moe && a.M == 1 && a.gmul == 1 && aligned16(a.scales) &&
+         (!a.zp || aligned16(a.zp)) && plan.one_waves >= 1 && plan.one_waves <= kGemvMaxWaves &&
+         (int64_t)plan.one_waves * plan.one_kpw * kGemvKStep == a.K;
+}
+
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspace,
                        hipStream_t stream, const MoeArgs* moe) {
+  if (gemv_one_runs(a, plan, moe)) {
+    return a.dtype == DT_F16 ? launch_one_g<DT_F16>(a, plan, stream) : launch_one_g<DT_BF16>(a, plan, stream);
+  }
   if (plan.waves < 1 || plan.waves > kGemvMaxWaves || plan.lds_bytes > kGemvLdsBudget ||
       plan.kpw < 1 || plan.kpw > kGemvStepsPerWave)
     return hipErrorInvalidConfiguration;

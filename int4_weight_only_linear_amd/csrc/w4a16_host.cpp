@@ -46,6 +46,7 @@ Tuning read_tuning() {
   if (const char* e = std::getenv("W4A16_GEMV_KPW")) t.gemv_kpw = std::atoi(e);
   if (const char* e = std::getenv("W4A16_GEMV_SPLITS")) t.gemv_splits = std::atoi(e);
   t.gemv_no_wgsz = std::getenv("W4A16_GEMV_NO_WGSZ") != nullptr;
+  t.gemv_no_one = std::getenv("W4A16_GEMV_NO_ONE") != nullptr;
   if (const char* e = std::getenv("W4A16_LOG")) t.log = *e && std::strcmp(e, "0") != 0;
   return t;
 }
@@ -497,11 +498,20 @@ w4a16_status w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int
     const w4a16::GemvPlan g = w4a16::plan_gemv(M, N, K, gm.kgroup, dtype, cus);
     r.tile_features = w4a16::kGemvRowsPerTile;
     r.tile_tokens = w4a16::kGemvMaxM;
-    r.splits = g.splits;
     r.tiles = g.tiles;
-    r.waves = g.waves;
-    r.launches = g.splits > 1 ? (int32_t)((g.tiles + w4a16::kMaxCounters - 1) / w4a16::kMaxCounters) : 1;
-    r.counter_tiles = g.splits > 1 ? std::min<int64_t>(g.tiles, w4a16::kMaxCounters) : 0;
+    if (g.one_kpw && gm.gmul == 1) {
+      // the single-token instance (given 16-byte aligned scales and zero points)
+      r.kernel = 1;
+      r.splits = 1;
+      r.waves = g.one_waves;
+      r.launches = 1;
+      r.counter_tiles = 0;
+    } else {
+      r.splits = g.splits;
+      r.waves = g.waves;
+      r.launches = g.splits > 1 ? (int32_t)((g.tiles + w4a16::kMaxCounters - 1) / w4a16::kMaxCounters) : 1;
+      r.counter_tiles = g.splits > 1 ? std::min<int64_t>(g.tiles, w4a16::kMaxCounters) : 0;
+    }
   } else {
     const w4a16::GemmPlan g = w4a16::plan_gemm(M, N, K, gm.kgroup, dtype, has_zp != 0, cus);
     r.tile_features = 128 * g.cb;

@@ -37,6 +37,7 @@ struct Tuning {
   int gemv_kpw;         // W4A16_GEMV_KPW: 0 for the planner's choice
   int gemv_splits;      // W4A16_GEMV_SPLITS: 0 for the planner's choice
   bool gemv_no_wgsz;    // W4A16_GEMV_NO_WGSZ: per-wave scale loads only
+  bool gemv_no_one;     // W4A16_GEMV_NO_ONE: single tokens on the general decode kernel
   bool log;             // W4A16_LOG: one line per call on stderr
 };
 const Tuning& tuning();
@@ -92,6 +93,14 @@ struct GemvPlan {
   int waves;             // waves per workgroup
   int kpw;               // k-steps per wave (upper bound)
   size_t lds_bytes;      // dynamic LDS of one workgroup
+  // the single-token instance (gemv_one_kernel), when the shape allows it:
+  // k-steps per wave (8 or 4; 0: not this shape), its waves and LDS.  It runs
+  // when, in addition, the scales are group-wise and the scale and zero-point
+  // tensors are 16-byte aligned (otherwise the general kernel runs, with the
+  // fields above).
+  int one_kpw = 0;
+  int one_waves = 0;
+  size_t one_lds_bytes = 0;
 };
 
 // LDS bytes of one wave's staging region (M <= 16 kernel): x [M][kpw*128 + 8]
@@ -107,6 +116,10 @@ __host__ __device__ inline int gemv_wave_lds_bytes(int M, int kpw, int group) {
   return (b + 15) / 16 * 16;
 }
 size_t gemv_lds_bytes(int waves, int64_t M, int kpw, int group);
+// the single-token instance: per wave 16 fp32 sums and its run of x
+inline size_t gemv_one_lds_bytes(int waves, int kpw) {
+  return (size_t)waves * (16 * sizeof(float) + 2 * (size_t)kpw * kGemvKStep);
+}
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu_count);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N);
 // Expert-indexed decode: slots = M * topk products of one token row with the
@@ -121,6 +134,8 @@ constexpr int64_t kMaxGridZ = 65535;
 
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& p, void* workspace,
                        hipStream_t stream, const MoeArgs* moe = nullptr);
+// whether launch_gemv runs the single-token instance for these arguments
+bool gemv_one_runs(const LinearArgs& a, const GemvPlan& p, const MoeArgs* moe = nullptr);
 
 // ---- prefill GEMM ----------------------------------------------------------
 // A workgroup owns 32*mb tokens x 256 output features; `splits` K ranges of

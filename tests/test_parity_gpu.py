@@ -132,6 +132,7 @@ def test_decode_workgroup_scales(tuning_env, N, K, sym, bias):
     # K range: the instance whose workgroup fetches all its waves' scales and
     # zero points at once.  Same arithmetic in the same order as the per-wave
     # instance (bit-identical), and within tolerance of the oracle.
+    tuning_env("W4A16_GEMV_NO_ONE", "1")  # the general kernel's two instances
     c = make_case(1, N, K, 128, O.BF16, sym, bias, seed=("wgsz", N, K, sym, bias))
     d = DeviceCase(c)
     y_shared = d.run(GEMV)
@@ -139,6 +140,58 @@ def test_decode_workgroup_scales(tuning_env, N, K, sym, bias):
     y_wave = d.run(GEMV)
     assert np.array_equal(y_shared, y_wave)
     assert_close(y_shared, oracle_rows(c), O.BF16, "workgroup scales")
+
+
+def _one_token_instance_expected(K, g):
+    # the planner's rule: K a whole number of runs of 8 (else 4) 128-k steps,
+    # at most 16 waves, at most 16 groups per run
+    ks = K // 128
+    return K % 128 == 0 and ((g >= 64 and ks % 8 == 0 and ks // 8 <= 16) or (ks % 4 == 0 and ks // 4 <= 16))
+
+
+@pytest.mark.parametrize("N,K", [(264, 512), (1048, 2048), (520, 2560), (776, 14336)])
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("sym,bias", [(True, False), (False, True)])
+def test_decode_single_token_instance(tuning_env, N, K, g, dt, sym, bias):
+    # one token: the single-token instance (each 16-lane row finishes a quarter
+    # of the groups, metadata in registers, bf16 x group sums on the matrix
+    # cores) against the oracle, and the general kernel on the same case
+    plan = L.w4a16_plan(1, N, K, g, dt, not sym, GEMV)
+    assert plan["kernel"] == int(_one_token_instance_expected(K, g)), (N, K, g, plan)
+    c = make_case(1, N, K, g, dt, sym, bias, seed=("one", N, K, g, dt, sym, bias))
+    d = DeviceCase(c)
+    ref = oracle_rows(c)
+    assert_close(d.run(GEMV), ref, dt, f"kernel {plan['kernel']}")
+    tuning_env("W4A16_GEMV_NO_ONE", "1")
+    assert L.w4a16_plan(1, N, K, g, dt, not sym, GEMV)["kernel"] == 0
+    assert_close(d.run(GEMV), ref, dt, "general kernel")
+
+
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+def test_decode_single_token_instance_four_step_runs(tuning_env, dt):
+    # runs of 4 k-steps where 8 would also fit (8 waves instead of 4)
+    N, K, g = 1048, 4096, 128
+    tuning_env("W4A16_GEMV_KPW", "4")
+    plan = L.w4a16_plan(1, N, K, g, dt, True, GEMV)
+    assert plan["kernel"] == 1 and plan["waves"] == 8, plan
+    c = make_case(1, N, K, g, dt, False, True, seed=("one4", dt))
+    assert_close(DeviceCase(c).run(GEMV), oracle_rows(c), dt, "4-step runs")
+
+
+def test_decode_single_token_unaligned_scales_fall_back():
+    # scales only 2-byte aligned: the general kernel runs instead
+    import torch
+    N, K, g = 520, 2048, 128
+    c = make_case(1, N, K, g, O.BF16, False, True, seed=("one-unaligned",))
+    d = DeviceCase(c)
+    store = torch.empty(N * (K // g) + 1, dtype=d.s.dtype, device=d.s.device)
+    s_off = store[1:].view(N, K // g)
+    s_off.copy_(d.s)
+    assert s_off.data_ptr() % 16 != 0
+    y = L.w4a16_linear_path(d.x, d.wq, s_off, d.zp, d.bias, group_size=g, path=GEMV)
+    torch.cuda.synchronize()
+    assert_close(device_to_bits(y), oracle_rows(c), O.BF16, "unaligned scales")
 
 
 def test_ragged_n_not_multiple_of_eight_symmetric():
