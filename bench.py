@@ -51,8 +51,17 @@ def decode_bytes(M, N, K, g, asym=True, bias=False):
 
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                               "gemv_small_kernel_llama8b_decode_M1_traffic.txt")
+                               "gemv_one_kernel_llama8b_decode_M1_traffic.txt")
 DECODE_SOURCES = ("w4a16_gemv.hip", "w4a16_device.hpp", "w4a16_internal.h")
+
+
+def decode_kernel_name(layer, M=1):
+    """The decode kernel the planner picks for a layer (K, N) at M tokens."""
+    import int4_weight_only_linear_amd as L
+    K, N = layer
+    p = L.w4a16_plan(M, N, K, GROUP, L.W4A16_BF16, True, L.PATH_GEMV)
+    name = "gemv_one_kernel" if p["kernel"] == 1 else "gemv_small_kernel"
+    return f"{name}<bf16, group {GROUP}, asym>"
 
 
 def measured_traffic():
@@ -996,7 +1005,7 @@ def main():
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     traffic_unit="bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
-                    kernel="gemv_small_kernel<bf16, group 128, asym>",
+                    kernel=decode_kernel_name(DECODE_LAYERS[0]),
                     mean_launch_us=round(mean_ms * 1e3, 3), bytes_per_launch=int(mean_bytes),
                     per_layer=per_layer, measured_ceiling=measured_ceiling)
 
