@@ -654,33 +654,37 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
 }
 
 // ---------------------------------------------------------------------------
-// M == 1: one token, one K range, every wave a run of KPW complete k-steps
+// M <= 4: a few tokens, one K range, every wave a run of KPW complete k-steps
 // ---------------------------------------------------------------------------
 // The kernel above stages each wave's scales, zero points and bf16 x group
-// sums through LDS and meets twice at workgroup barriers; for one token that
-// bookkeeping costs about as much time as the dequantisation.  This instance
-// keeps only x in LDS:
-// * With one token every row of the MFMA's A operand is x, so all four 16-lane
-//   rows of a result hold the same 16 dot products.  Each 16-lane row R
-//   therefore finishes only the groups it owns -- the R-th quarter of the
-//   wave's run -- and fetches only their scales and zero points: one small
-//   load per tensor and wave, straight into registers (the scale / zero-point
-//   carrier of "[ROCm] Converge the two W4A16 linear kernels onto the
-//   upstream shell", "What this does": no per-group metadata loads), issued
-//   after the weights, since only the end of the run needs them: the waits
-//   for the weights, which complete in issue order, never wait for them.
+// sums through LDS and meets twice at workgroup barriers; for a few tokens
+// that bookkeeping costs about as much time as the dequantisation.  This
+// instance keeps only x in LDS:
+// * A row i of the MFMA is token i mod MT (MT = 1, 2 or 4 token rows; three
+//   tokens run with MT = 4), so every 16-lane row of a result holds the same
+//   dot products: register r is token r.  Each 16-lane row R therefore
+//   finishes only the groups it owns -- the R-th quarter of the wave's run --
+//   and fetches only their scales and zero points: one small load per tensor
+//   and wave, straight into registers (the scale / zero-point carrier of
+//   "[ROCm] Converge the two W4A16 linear kernels onto the upstream shell",
+//   "What this does": no per-group metadata loads), issued after the weights,
+//   since only the end of the run needs them: the waits for the weights,
+//   which complete in issue order, never wait for them.
 // * Both dtypes multiply x by the exact magic value (128 or 1024) + q and
 //   remove (magic + z) per group with the group's sum of x (the general
 //   kernel's bf16 scheme; for fp16 it saves the packed subtraction, 4 of 11
 //   VALU instructions per weight word).  The group sums of x come from the
-//   matrix cores: an MFMA whose A rows are 16 chunks of x and whose B is all
-//   ones gives the 16 chunk sums, its rows ordered so that 16-lane row R
-//   receives the chunks of its own groups.
-// * The 16-lane rows are added with two permlane swaps; the waves through LDS
-//   after one barrier, in wave order.
-// waves per SIMD the register budget is sized for: runs of 8 k-steps, and
-// runs of 4 with 16 groups (groups of 32), hold more registers
-constexpr int one_waves_per_simd(int kpw, int gs) { return kpw == 8 || gs == 32 ? 6 : 8; }
+//   matrix cores: an MFMA whose A rows are 16 chunks of one token's x and
+//   whose B is all ones gives the 16 chunk sums, its rows ordered so that
+//   16-lane row R receives the chunks of its own groups.
+// * The 16-lane rows are added with two permlane swaps per token; the waves
+//   through LDS after one barrier, in wave order.
+
+// waves per SIMD the register budget is sized for (more tokens and longer
+// runs hold more group sums)
+constexpr int one_waves_per_simd(int kpw, int gs, int mt) {
+  return (128 * kpw / gs) * mt > 16 ? 5 : (kpw == 8 || gs == 32 || mt > 1 ? 6 : 8);
+}
 
 // 16-lane row R of the result takes vR (each v uniform across the wave): two
 // 16-lane swaps pair rows (0, 1) and (2, 3), one 32-lane swap joins the
@@ -694,6 +698,17 @@ __device__ __forceinline__ float row_select(float v0, float v1, float v2, float 
   const auto hi = __builtin_amdgcn_permlane16_swap(b(v2), b(v3), false, false);  // rows 0, 2: v2; 1, 3: v3
   const auto r = __builtin_amdgcn_permlane32_swap(lo[0], hi[0], false, false);   // rows 2, 3 from hi
   return __builtin_bit_cast(float, (uint32_t)r[0]);
+}
+
+// the sum of v over the four 16-lane rows, in lanes 0..15: rows (0 + 2) and
+// (1 + 3), then their sum
+__device__ __forceinline__ float rows_sum(float v) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, v);
+  const auto hi = __builtin_amdgcn_permlane32_swap(a, a, false, false);  // [1]: lanes 32..63 in 0..31
+  v += __builtin_bit_cast(float, (uint32_t)hi[1]);
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto odd = __builtin_amdgcn_permlane16_swap(b, b, false, false);  // [1]: lanes 16..31 in 0..15
+  return v + __builtin_bit_cast(float, (uint32_t)odd[1]);
 }
 
 // a lane's NW consecutive 32-bit words, read as one load where possible
@@ -718,18 +733,18 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[NW])
   }
 }
 
-template <int DT, int GS, bool ASYM, int KPW>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_per_simd(KPW, GS)))) void gemv_one_kernel(
+template <int DT, int GS, bool ASYM, int KPW, int MT>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_per_simd(KPW, GS, MT)))) void gemv_one_kernel(
     const uint16_t* a_x, const uint32_t* a_wq, const uint16_t* a_scales, const uint32_t* a_zp, int N, int K,
-    int sG, const uint16_t* bias, uint16_t* y) {
+    int sG, int M, const uint16_t* bias, uint16_t* y) {
   constexpr int CPG = GS / 32;            // 32-k chunks per group
   constexpr int NC = 4 * KPW;             // chunks of a run
   constexpr int NGW = NC / CPG;           // groups of a run
   constexpr int OWN = NGW / 4;            // groups each 16-lane row finishes
   constexpr int KR = KPW * kGemvKStep;    // k of a run
-  constexpr int XPL = KR / 8 / 64;        // 16-byte x segments per lane
+  constexpr int XPL = KR / 8 / 64;        // 16-byte x segments per lane and token
   constexpr int SW = (OWN + 1) / 2;       // words holding the owned scales
-  static_assert(OWN >= 1 && OWN <= 4 && XPL >= 1, "instance");
+  static_assert(OWN >= 1 && OWN <= 4 && XPL >= 1 && (MT == 1 || MT == 2 || MT == 4), "instance");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -743,22 +758,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   const int kw0 = wave * KR;           // first k of this wave's run
   const int g0 = kw0 / GS;             // first group of the run
   const int gown = g0 + row4 * OWN;    // first group this 16-lane row finishes
-  float* red = reinterpret_cast<float*>(smem);  // [waves][16]
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 64 * nwaves + (size_t)wave * 2 * KR);  // [KR]
+  float* red = reinterpret_cast<float*>(smem);  // [waves][MT][16]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 64 * MT * nwaves + (size_t)wave * MT * 2 * KR);  // [MT][KR]
 
   // ---- 1. loads: x, then the weights, then scales and zero points ----
   // (the metadata is needed only after the run, so the waits for the weights
-  // never wait for it)
-  u32x4 xr[XPL];
-  const char* xb = reinterpret_cast<const char*>(a_x + kw0);
+  // never wait for it; token rows past M read token M - 1)
+  u32x4 xr[MT][XPL];
 #pragma unroll
-  for (int j = 0; j < XPL; ++j) xr[j] = *reinterpret_cast<const u32x4*>(xb + 16u * (uint32_t)(lane + 64 * j));
-  // the owned groups' zero-point words
-  constexpr int ZW = !ASYM ? 1 : OWN;
-  uint32_t zw[ZW];
-  const uint32_t* zrow = ASYM ? a_zp + (size_t)(n >> 3) * sG : nullptr;
-  if constexpr (!ASYM) zw[0] = 0u;
-
+  for (int m = 0; m < MT; ++m) {
+    const char* xb = reinterpret_cast<const char*>(a_x + (size_t)min(m, M - 1) * K + kw0);
+#pragma unroll
+    for (int j = 0; j < XPL; ++j) xr[m][j] = *reinterpret_cast<const u32x4*>(xb + 16u * (uint32_t)(lane + 64 * j));
+  }
   __builtin_amdgcn_sched_barrier(0);
   const WeightWalk ww = weight_walk(a_wq, N, K, K >> 5, n0, col, row4);
   u32x4 wv[KPW];
@@ -772,34 +784,47 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   } else {
     load_words<SW>(reinterpret_cast<const uint32_t*>(a_scales + (size_t)n * sG + gown), sw);
   }
-  if constexpr (ASYM) load_words<ZW>(zrow + gown, zw);
+  // the owned groups' zero-point words
+  constexpr int ZW = ASYM ? OWN : 1;
+  uint32_t zw[ZW];
+  if constexpr (ASYM) {
+    load_words<ZW>(a_zp + (size_t)(n >> 3) * sG + gown, zw);
+  } else {
+    zw[0] = 0u;
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. x to this wave's LDS region; group sums of x ----
 #pragma unroll
-  for (int j = 0; j < XPL; ++j) *reinterpret_cast<u32x4*>(xs + 8 * (lane + 64 * j)) = xr[j];
-  float xsum[OWN];
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int j = 0; j < XPL; ++j) *reinterpret_cast<u32x4*>(xs + m * KR + 8 * (lane + 64 * j)) = xr[m][j];
+  }
+  float xsum[MT][OWN];
   {
-    // MFMA b: A row i is chunk (NC/4) (i / 4) + 4 b + i % 4 of the run and B
-    // is all ones, so the result rows 4R .. 4R+3 of 16-lane row R are the
-    // sums of the chunks of R's own groups
+    // MFMA b of token m: A row i is chunk (NC/4) (i / 4) + 4 b + i % 4 of the
+    // token's run and B is all ones, so the result rows 4R .. 4R+3 of
+    // 16-lane row R are the sums of the chunks of R's own groups
     constexpr uint32_t ONE2 = DT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0 in both halves
     const u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
     const uint16_t* xa0 = xs + ((NC / 4) * (col >> 2) + (col & 3)) * 32 + 8 * row4;
 #pragma unroll
-    for (int b = 0; b < NC / 16; ++b) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(xa0 + 4 * 32 * b);
-      const f32x4 d = mfma16x16x32<DT>(a, ones, f32x4{0.f, 0.f, 0.f, 0.f});
-      if constexpr (CPG == 4) {
-        xsum[b] = (d[0] + d[1]) + (d[2] + d[3]);
-      } else if constexpr (CPG == 2) {
-        xsum[2 * b] = d[0] + d[1];
-        xsum[2 * b + 1] = d[2] + d[3];
-      } else {
-        xsum[4 * b] = d[0];
-        xsum[4 * b + 1] = d[1];
-        xsum[4 * b + 2] = d[2];
-        xsum[4 * b + 3] = d[3];
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int b = 0; b < NC / 16; ++b) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(xa0 + m * KR + 4 * 32 * b);
+        const f32x4 d = mfma16x16x32<DT>(a, ones, f32x4{0.f, 0.f, 0.f, 0.f});
+        if constexpr (CPG == 4) {
+          xsum[m][b] = (d[0] + d[1]) + (d[2] + d[3]);
+        } else if constexpr (CPG == 2) {
+          xsum[m][2 * b] = d[0] + d[1];
+          xsum[m][2 * b + 1] = d[2] + d[3];
+        } else {
+          xsum[m][4 * b] = d[0];
+          xsum[m][4 * b + 1] = d[1];
+          xsum[m][4 * b + 2] = d[2];
+          xsum[m][4 * b + 3] = d[3];
+        }
       }
     }
   }
@@ -808,14 +833,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   // (the loop of the kernel above: x fragments from LDS two chunks ahead, one
   // MFMA chain per group, x multiplied by magic + q)
   const uint32_t mask_v = vgpr_const(0x000F000Fu);
-  const uint16_t* xrow = xs + 8 * row4;  // every A row reads x
+  const uint16_t* xrow = xs + (col & (MT - 1)) * KR + 8 * row4;  // A row i: token i mod MT
   const int zshift = 4 * (n & 7);
   constexpr int XD = 2;
   u32x4 xa[XD + 1];
   auto load_x = [&](int q) { return *reinterpret_cast<const u32x4*>(xrow + q * 32); };
 #pragma unroll
   for (int q = 0; q < XD; ++q) xa[q] = load_x(q);
-  float chg[NGW];
+  float chg[NGW][MT];
   f32x4 ch;
 #pragma unroll
   for (int q = 0; q < NC; ++q) {
@@ -827,39 +852,42 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
     const bool fresh = (q % CPG) == 0;
     const u32x4 bq = magic_word<DT>(wv[i][t], mask_v);
     ch = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
-    if (q % CPG == CPG - 1) chg[gl] = ch[0];
+    if (q % CPG == CPG - 1) {
+#pragma unroll
+      for (int r = 0; r < MT; ++r) chg[gl][r] = ch[r];
+    }
   }
 
   // ---- 4. each 16-lane row scales its own groups; rows, then waves, added ----
-  float acc = 0.f;
+  float acc[MT];
+#pragma unroll
+  for (int r = 0; r < MT; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int t = 0; t < OWN; ++t) {
     // the group of 16-lane row R is R * OWN + t of the run
-    const float v = row_select(chg[t], chg[OWN + t], chg[2 * OWN + t], chg[3 * OWN + t]);
     const uint32_t sbits = (sw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
     const float s = act_to_f32<DT>((uint16_t)sbits);
-    {
-      const uint32_t z = ASYM ? (zw[t] >> zshift) & 0xFu : 8u;
-      const float szc = -(Magic<DT>::value + (float)z) * s;
-      acc = __builtin_fmaf(s, v, __builtin_fmaf(szc, xsum[t], acc));
+    const uint32_t z = ASYM ? (zw[t] >> zshift) & 0xFu : 8u;
+    const float szc = -(Magic<DT>::value + (float)z) * s;  // exact
+#pragma unroll
+    for (int r = 0; r < MT; ++r) {
+      const float v = row_select(chg[t][r], chg[OWN + t][r], chg[2 * OWN + t][r], chg[3 * OWN + t][r]);
+      acc[r] = __builtin_fmaf(s, v, __builtin_fmaf(szc, xsum[r][t], acc[r]));
     }
   }
-  {
-    const uint32_t a = __builtin_bit_cast(uint32_t, acc);
-    const auto hi = __builtin_amdgcn_permlane32_swap(a, a, false, false);  // [1]: lanes 32..63 in 0..31
-    acc += __builtin_bit_cast(float, (uint32_t)hi[1]);
-    const uint32_t b = __builtin_bit_cast(uint32_t, acc);
-    const auto odd = __builtin_amdgcn_permlane16_swap(b, b, false, false);  // [1]: lanes 16..31 in 0..15
-    acc += __builtin_bit_cast(float, (uint32_t)odd[1]);
+#pragma unroll
+  for (int r = 0; r < MT; ++r) {
+    const float v = rows_sum(acc[r]);
+    if (lane < 16) red[(wave * MT + r) * 16 + lane] = v;
   }
-  if (lane < 16) red[wave * 16 + lane] = acc;
   __syncthreads();
-  const int nn = n0 + tid;
-  if (tid < kGemvRowsPerTile && nn < N) {
+  const int m = tid >> 4;
+  const int nn = n0 + (tid & 15);
+  if (m < M && nn < N) {
     float v = 0.f;
-    for (int w = 0; w < nwaves; ++w) v += red[w * 16 + tid];
+    for (int w = 0; w < nwaves; ++w) v += red[(w * MT + m) * 16 + (tid & 15)];
     if (bias) v += act_to_f32<DT>(bias[nn]);
-    y[nn] = f32_to_act<DT>(v);
+    y[(size_t)m * N + nn] = f32_to_act<DT>(v);
   }
 }
 
@@ -919,16 +947,25 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu
   p.splits = (p.ksteps + p.ksteps_per_split - 1) / p.ksteps_per_split;
   p.waves = (p.ksteps_per_split + kpw - 1) / kpw;
   p.lds_bytes = gemv_lds_bytes(p.waves, M, kpw, group);
-  // one token: the single-token instance, when K is a whole number of runs of
-  // 8 (else 4) k-steps for at most kGemvMaxWaves waves and a run spans at most
-  // 16 groups (one K range, no tail chunks)
-  if (M == 1 && K % kGemvKStep == 0 && !tu.gemv_no_one && tu.gemv_splits <= 1) {
-    for (int k : {8, 4}) {
+  // up to four tokens: the few-token instance, when K is a whole number of
+  // runs of 8 (else 4) k-steps for at most kGemvMaxWaves waves, a run spans at
+  // most 16 groups, the group sums per token row and run are at most 32, and
+  // the staged x fits the LDS budget (one K range, no tail chunks)
+  // (runs of 8 first; four token rows measured faster with runs of 4 where
+  // those fit: -1 to -9 % on the decode layers)
+  const int mt = gemv_one_rows(M);
+  if (mt && K % kGemvKStep == 0 && !tu.gemv_no_one && tu.gemv_splits <= 1) {
+    const int order[2] = {mt == 4 ? 4 : 8, mt == 4 ? 8 : 4};
+    for (int k : order) {
       if (tu.gemv_kpw >= 1 && k != tu.gemv_kpw) continue;
-      if (kGemvKStep * k / group > 16 || p.ksteps % k || p.ksteps / k > kGemvMaxWaves) continue;
+      const int ngw = kGemvKStep * k / group;
+      if (ngw > 16 || ngw * mt > 32 || p.ksteps % k || p.ksteps / k > kGemvMaxWaves) continue;
+      const size_t lds = gemv_one_lds_bytes(p.ksteps / k, k, mt);
+      if (lds > budget) continue;
       p.one_kpw = k;
+      p.one_mt = mt;
       p.one_waves = p.ksteps / k;
-      p.one_lds_bytes = gemv_one_lds_bytes(p.one_waves, k);
+      p.one_lds_bytes = lds;
       break;
     }
   }
@@ -1014,27 +1051,34 @@ static hipError_t launch_g(const GemvParams& prm, int group, const GemvPlan& pla
   }
 }
 
+template <int DT, int GS, bool ASYM, int KPW, int MT>
+static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStream_t s) {
+  // instances: at most 16 groups a run, at most 32 group sums per token row
+  constexpr int NGW = kGemvKStep * KPW / GS;
+  if constexpr (NGW > 16 || NGW * MT > 32) {
+    return hipErrorInvalidConfiguration;
+  } else {
+    const dim3 grid(plan.tiles), block(64 * plan.one_waves);
+    hipLaunchKernelGGL((gemv_one_kernel<DT, GS, ASYM, KPW, MT>), grid, block, plan.one_lds_bytes, s,
+                       static_cast<const uint16_t*>(a.x), reinterpret_cast<const uint32_t*>(a.wq),
+                       static_cast<const uint16_t*>(a.scales), reinterpret_cast<const uint32_t*>(a.zp), (int)a.N,
+                       (int)a.K, a.sG, (int)a.M, static_cast<const uint16_t*>(a.bias), static_cast<uint16_t*>(a.y));
+    return hipGetLastError();
+  }
+}
+
 template <int DT, int GS, bool ASYM>
 static hipError_t launch_one(const LinearArgs& a, const GemvPlan& plan, hipStream_t s) {
-  const dim3 grid(plan.tiles), block(64 * plan.one_waves);
-  const auto x = static_cast<const uint16_t*>(a.x);
-  const auto wq = reinterpret_cast<const uint32_t*>(a.wq);
-  const auto sc = static_cast<const uint16_t*>(a.scales);
-  const auto zp = reinterpret_cast<const uint32_t*>(a.zp);
-  const auto bias = static_cast<const uint16_t*>(a.bias);
-  const auto y = static_cast<uint16_t*>(a.y);
-  const int N = (int)a.N, K = (int)a.K;
-  if (plan.one_kpw == 8) {
-    if constexpr (GS >= 64)
-      hipLaunchKernelGGL((gemv_one_kernel<DT, GS, ASYM, 8>), grid, block, plan.one_lds_bytes, s, x, wq, sc, zp, N, K, a.sG, bias, y);
-    else
-      return hipErrorInvalidConfiguration;
-  } else if (plan.one_kpw == 4) {
-    hipLaunchKernelGGL((gemv_one_kernel<DT, GS, ASYM, 4>), grid, block, plan.one_lds_bytes, s, x, wq, sc, zp, N, K, a.sG, bias, y);
-  } else {
-    return hipErrorInvalidConfiguration;
+  const int key = plan.one_kpw * 10 + plan.one_mt;
+  switch (key) {
+    case 81: return launch_one_k<DT, GS, ASYM, 8, 1>(a, plan, s);
+    case 82: return launch_one_k<DT, GS, ASYM, 8, 2>(a, plan, s);
+    case 84: return launch_one_k<DT, GS, ASYM, 8, 4>(a, plan, s);
+    case 41: return launch_one_k<DT, GS, ASYM, 4, 1>(a, plan, s);
+    case 42: return launch_one_k<DT, GS, ASYM, 4, 2>(a, plan, s);
+    case 44: return launch_one_k<DT, GS, ASYM, 4, 4>(a, plan, s);
+    default: return hipErrorInvalidConfiguration;
   }
-  return hipGetLastError();
 }
 
 template <int DT>
@@ -1050,7 +1094,7 @@ static hipError_t launch_one_g(const LinearArgs& a, const GemvPlan& plan, hipStr
 
 bool gemv_one_runs(const LinearArgs& a, const GemvPlan& plan, const MoeArgs* moe) {
   const auto aligned16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-  return plan.one_kpw != 0 && !moe && a.M == 1 && a.gmul == 1 && aligned16(a.scales) &&
+  return plan.one_kpw != 0 && !moe && gemv_one_rows(a.M) == plan.one_mt && a.gmul == 1 && aligned16(a.scales) &&
          (!a.zp || aligned16(a.zp)) && plan.one_waves >= 1 && plan.one_waves <= kGemvMaxWaves &&
          (int64_t)plan.one_waves * plan.one_kpw * kGemvKStep == a.K;
 }

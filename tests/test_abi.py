@@ -322,14 +322,18 @@ def test_split_decode_beyond_the_counter_region_is_chunked(M, N, K):
     assert p["workspace_bytes"] == 64 * 1024 + p["splits"] * M * N * 4
 
 
-def test_plan_reports_the_single_token_instance():
-    # one token with K a whole number of 8- or 4-step runs (at most 16 waves,
-    # at most 16 groups a run) takes the single-token instance; it never splits
+def test_plan_reports_the_few_token_instance():
+    # up to four tokens with K a whole number of 8- or 4-step runs (at most 16
+    # waves, at most 16 groups a run, at most 32 group sums per token row)
+    # take the few-token instance; it never splits K
     for dt in (L.W4A16_F16, L.W4A16_BF16):
-        for (K, g, waves) in ((4096, 128, 4), (4096, 32, 8), (14336, 128, 14), (2560, 64, 5), (512, 32, 1)):
-            p = L.w4a16_plan(1, 4096, K, g, dt, True, L.PATH_GEMV)
-            assert (p["kernel"], p["waves"], p["splits"], p["launches"]) == (1, waves, 1, 1), (K, g, p)
-        for (M, K, g) in ((2, 4096, 128), (1, 14336, 32), (1, 9728, 128), (1, 4160, 64), (1, 28672, 128)):
+        for (M, K, g, waves) in ((1, 4096, 128, 4), (1, 4096, 32, 8), (1, 14336, 128, 14), (1, 2560, 64, 5),
+                                 (1, 512, 32, 1), (2, 4096, 128, 4), (2, 4096, 64, 4), (2, 4096, 32, 8),
+                                 (3, 4096, 128, 8), (4, 4096, 128, 8), (4, 4096, 64, 8), (4, 14336, 128, 14)):
+            p = L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)
+            assert (p["kernel"], p["waves"], p["splits"], p["launches"]) == (1, waves, 1, 1), (M, K, g, p)
+        for (M, K, g) in ((5, 4096, 128), (8, 4096, 128), (1, 14336, 32), (1, 9728, 128), (1, 4160, 64),
+                          (1, 28672, 128), (4, 4096, 32), (3, 14336, 64)):
             assert L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)["kernel"] == 0, (M, K, g)
         # per-channel scales stay on the general kernel
         assert L.w4a16_plan(1, 4096, 4096, 4096, dt, False, L.PATH_GEMV)["kernel"] == 0

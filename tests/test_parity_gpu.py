@@ -142,11 +142,18 @@ def test_decode_workgroup_scales(tuning_env, N, K, sym, bias):
     assert_close(y_shared, oracle_rows(c), O.BF16, "workgroup scales")
 
 
-def _one_token_instance_expected(K, g):
+def _few_token_instance_expected(M, K, g):
     # the planner's rule: K a whole number of runs of 8 (else 4) 128-k steps,
-    # at most 16 waves, at most 16 groups per run
-    ks = K // 128
-    return K % 128 == 0 and ((g >= 64 and ks % 8 == 0 and ks // 8 <= 16) or (ks % 4 == 0 and ks // 4 <= 16))
+    # at most 16 waves, at most 16 groups per run and 32 group sums per token
+    # row (token rows: 1, 2, or 4 for three and four tokens)
+    ks, mt = K // 128, {1: 1, 2: 2, 3: 4, 4: 4}.get(M, 0)
+    if not mt or K % 128:
+        return False
+    for kpw in (8, 4):
+        ngw = 128 * kpw // g
+        if ngw <= 16 and ngw * mt <= 32 and ks % kpw == 0 and ks // kpw <= 16:
+            return True
+    return False
 
 
 @pytest.mark.parametrize("N,K", [(264, 512), (1048, 2048), (520, 2560), (776, 14336)])
@@ -154,17 +161,36 @@ def _one_token_instance_expected(K, g):
 @pytest.mark.parametrize("dt", [O.F16, O.BF16])
 @pytest.mark.parametrize("sym,bias", [(True, False), (False, True)])
 def test_decode_single_token_instance(tuning_env, N, K, g, dt, sym, bias):
-    # one token: the single-token instance (each 16-lane row finishes a quarter
-    # of the groups, metadata in registers, bf16 x group sums on the matrix
-    # cores) against the oracle, and the general kernel on the same case
+    # one token: the few-token instance (each 16-lane row finishes a quarter
+    # of the groups, metadata in registers, x group sums on the matrix cores)
+    # against the oracle, and the general kernel on the same case
     plan = L.w4a16_plan(1, N, K, g, dt, not sym, GEMV)
-    assert plan["kernel"] == int(_one_token_instance_expected(K, g)), (N, K, g, plan)
+    assert plan["kernel"] == int(_few_token_instance_expected(1, K, g)), (N, K, g, plan)
     c = make_case(1, N, K, g, dt, sym, bias, seed=("one", N, K, g, dt, sym, bias))
     d = DeviceCase(c)
     ref = oracle_rows(c)
     assert_close(d.run(GEMV), ref, dt, f"kernel {plan['kernel']}")
     tuning_env("W4A16_GEMV_NO_ONE", "1")
     assert L.w4a16_plan(1, N, K, g, dt, not sym, GEMV)["kernel"] == 0
+    assert_close(d.run(GEMV), ref, dt, "general kernel")
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("N,K", [(264, 512), (1048, 4096), (520, 2560), (776, 14336)])
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+def test_decode_few_token_instance(tuning_env, M, N, K, g, dt):
+    # two to four tokens (three run as four token rows, the fourth never
+    # stored): asymmetric with bias, and symmetric, against the oracle; the
+    # general kernel on the same cases
+    plan = L.w4a16_plan(M, N, K, g, dt, True, GEMV)
+    assert plan["kernel"] == int(_few_token_instance_expected(M, K, g)), (M, N, K, g, plan)
+    for sym, bias in ((False, True), (True, False)):
+        c = make_case(M, N, K, g, dt, sym, bias, seed=("few", M, N, K, g, dt, sym, bias))
+        d = DeviceCase(c)
+        ref = oracle_rows(c)
+        assert_close(d.run(GEMV), ref, dt, f"M={M} kernel {plan['kernel']} sym={sym}")
+    tuning_env("W4A16_GEMV_NO_ONE", "1")
     assert_close(d.run(GEMV), ref, dt, "general kernel")
 
 
@@ -269,19 +295,30 @@ def test_gemm_operands_are_the_dequantised_weights(dt, sym, g):
 
 @pytest.mark.parametrize("path", [GEMV, GEMM])
 @pytest.mark.parametrize("dt", [O.F16, O.BF16])
-def test_all_eights_symmetric_gives_bias(path, dt):
+@pytest.mark.parametrize("few", [True, False])
+def test_all_eights_symmetric_gives_bias(tuning_env, path, dt, few):
     # every weight is (8 - 8) * s = +0.  The GEMM multiplies those zeros, and
-    # the fp16 decode kernel multiplies q - z = 0: both give the bias (or +0)
-    # bit for bit.  The bf16 decode kernel forms sum x*(128+q) - (128+z)*sum x
-    # in fp32, so it leaves a residue of the order of fp32 round-off.
+    # the general decode kernel's fp16 path multiplies q - z = 0: both give the
+    # bias (or +0) bit for bit.  The general kernel's bf16 path and the
+    # few-token instance (both dtypes) form sum x*(magic+q) - (magic+z)*sum x
+    # in fp32, so they leave a residue of the order of fp32 round-off of those
+    # sums, proportional to the magic offset (128 for bf16, 1024 for fp16):
+    # 1e-4 absolute at 128.
+    if path == GEMM and not few:
+        pytest.skip("the decode kernels only")
+    if not few:
+        tuning_env("W4A16_GEMV_NO_ONE", "1")
+    kernel = L.w4a16_plan(4, 64, 512, 64, dt, False, path)["kernel"]
+    assert kernel == int(path == GEMV and few)
     for bias in (False, True):
         c = make_case(4, 64, 512, 64, dt, True, bias, seed=("eights", bias, dt))
         c.q[:] = 8
         y = DeviceCase(c).run(path)
         want = np.broadcast_to(c.bias_bits, y.shape) if bias else np.zeros_like(y)
-        if path == GEMV and dt == O.BF16:
-            err = np.abs(O.bf16_bits_to_f64(y) - O.bf16_bits_to_f64(want)).max()
-            assert err <= 1e-4
+        if path == GEMV and (dt == O.BF16 or kernel == 1):
+            f = O.bf16_bits_to_f64 if dt == O.BF16 else O.f16_bits_to_f64
+            err = np.abs(f(y) - f(want)).max()
+            assert err <= 1e-4 * (128 if dt == O.BF16 else 1024) / 128
         else:
             assert np.array_equal(y, want)     # +0.0 exactly, no negative zeros
 
