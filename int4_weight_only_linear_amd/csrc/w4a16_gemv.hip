@@ -655,6 +655,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
 
 // ---------------------------------------------------------------------------
 // M <= 4: a few tokens, one K range, every wave a run of KPW complete k-steps
+// (the last wave's run may be shorter: a whole number of quarter runs)
 // ---------------------------------------------------------------------------
 // The kernel above stages each wave's scales, zero points and bf16 x group
 // sums through LDS and meets twice at workgroup barriers; for a few tokens
@@ -683,7 +684,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
 // waves per SIMD the register budget is sized for (more tokens and longer
 // runs hold more group sums)
 constexpr int one_waves_per_simd(int kpw, int gs, int mt) {
-  return (128 * kpw / gs) * mt > 16 ? 5 : (kpw == 8 || gs == 32 || mt > 1 ? 6 : 8);
+  return (128 * kpw / gs) * mt > 16 || (kpw == 8 && gs == 64) ? 5 : (kpw == 8 || gs == 32 || mt > 1 ? 6 : 8);
 }
 
 // 16-lane row R of the result takes vR (each v uniform across the wave): two
@@ -733,7 +734,9 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[NW])
   }
 }
 
-template <int DT, int GS, bool ASYM, int KPW, int MT>
+// PART: the last wave's run may be shorter (otherwise every run is whole and
+// the masks and clamps below compile away)
+template <int DT, int GS, bool ASYM, int KPW, int MT, bool PART>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_per_simd(KPW, GS, MT)))) void gemv_one_kernel(
     const uint16_t* a_x, const uint32_t* a_wq, const uint16_t* a_scales, const uint32_t* a_zp, int N, int K,
     int sG, int M, const uint16_t* bias, uint16_t* y) {
@@ -757,7 +760,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   const int n = min(n0 + col, N - 1);  // rows past N read row N - 1
   const int kw0 = wave * KR;           // first k of this wave's run
   const int g0 = kw0 / GS;             // first group of the run
-  const int gown = g0 + row4 * OWN;    // first group this 16-lane row finishes
+  // The last wave's run may stop short of KPW k-steps, after a whole number
+  // of quarter runs (the host checks): 16-lane row R's groups then lie
+  // entirely inside K or entirely past it.  Past K, every load is clamped to
+  // valid memory and the row's groups are dropped at the end.
+  const int ksteps = K >> 7;
+  const bool own_valid = !PART || (wave * KPW + row4 * (KPW / 4)) < ksteps;
+  const int gown = g0 + (own_valid ? row4 * OWN : 0);  // first group this 16-lane row finishes
   float* red = reinterpret_cast<float*>(smem);  // [waves][MT][16]
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 64 * MT * nwaves + (size_t)wave * MT * 2 * KR);  // [MT][KR]
 
@@ -769,14 +778,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   for (int m = 0; m < MT; ++m) {
     const char* xb = reinterpret_cast<const char*>(a_x + (size_t)min(m, M - 1) * K + kw0);
 #pragma unroll
-    for (int j = 0; j < XPL; ++j) xr[m][j] = *reinterpret_cast<const u32x4*>(xb + 16u * (uint32_t)(lane + 64 * j));
+    for (int j = 0; j < XPL; ++j)
+      xr[m][j] = *reinterpret_cast<const u32x4*>(
+          xb + 2u * (uint32_t)(PART ? min(8 * (lane + 64 * j), K - 8 - kw0) : 8 * (lane + 64 * j)));
   }
   __builtin_amdgcn_sched_barrier(0);
   const WeightWalk ww = weight_walk(a_wq, N, K, K >> 5, n0, col, row4);
   u32x4 wv[KPW];
 #pragma unroll
   for (int i = 0; i < KPW; ++i)
-    wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ww.at(wave * KPW + i)));
+    wv[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(ww.at(PART ? min(wave * KPW + i, ksteps - 1) : wave * KPW + i)));
   __builtin_amdgcn_sched_barrier(0);
   uint32_t sw[SW];
   if constexpr (OWN == 1) {
@@ -868,11 +880,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
     const uint32_t sbits = (sw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
     const float s = act_to_f32<DT>((uint16_t)sbits);
     const uint32_t z = ASYM ? (zw[t] >> zshift) & 0xFu : 8u;
-    const float szc = -(Magic<DT>::value + (float)z) * s;  // exact
+    const float szc = own_valid ? -(Magic<DT>::value + (float)z) * s : 0.f;  // exact
+    const float sv = own_valid ? s : 0.f;
 #pragma unroll
     for (int r = 0; r < MT; ++r) {
       const float v = row_select(chg[t][r], chg[OWN + t][r], chg[2 * OWN + t][r], chg[3 * OWN + t][r]);
-      acc[r] = __builtin_fmaf(s, v, __builtin_fmaf(szc, xsum[r][t], acc[r]));
+      acc[r] = __builtin_fmaf(sv, v, __builtin_fmaf(szc, xsum[r][t], acc[r]));
     }
   }
 #pragma unroll
@@ -948,23 +961,30 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu
   p.waves = (p.ksteps_per_split + kpw - 1) / kpw;
   p.lds_bytes = gemv_lds_bytes(p.waves, M, kpw, group);
   // up to four tokens: the few-token instance, when K is a whole number of
-  // runs of 8 (else 4) k-steps for at most kGemvMaxWaves waves, a run spans at
-  // most 16 groups, the group sums per token row and run are at most 32, and
-  // the staged x fits the LDS budget (one K range, no tail chunks)
+  // 128-k steps in runs of 8 (else 4) for at most kGemvMaxWaves waves, the
+  // last run a whole number of quarter runs, a run spans at most 16 groups,
+  // the group sums per token row and run are at most 32, and the staged x
+  // fits the LDS budget (one K range, no tail chunks)
   // (runs of 8 first; four token rows measured faster with runs of 4 where
-  // those fit: -1 to -9 % on the decode layers)
+  // those fit: -1 to -9 % on the decode layers; whole runs before a shorter
+  // last run)
   const int mt = gemv_one_rows(M);
   if (mt && K % kGemvKStep == 0 && !tu.gemv_no_one && tu.gemv_splits <= 1) {
-    const int order[2] = {mt == 4 ? 4 : 8, mt == 4 ? 8 : 4};
-    for (int k : order) {
+    const int a = mt == 4 ? 4 : 8, b = mt == 4 ? 8 : 4;
+    const int order[4][2] = {{a, 0}, {b, 0}, {a, 1}, {b, 1}};  // (k-steps per wave, shorter last run)
+    for (const auto& o : order) {
+      const int k = o[0];
       if (tu.gemv_kpw >= 1 && k != tu.gemv_kpw) continue;
       const int ngw = kGemvKStep * k / group;
-      if (ngw > 16 || ngw * mt > 32 || p.ksteps % k || p.ksteps / k > kGemvMaxWaves) continue;
-      const size_t lds = gemv_one_lds_bytes(p.ksteps / k, k, mt);
+      const int waves = (p.ksteps + k - 1) / k;
+      const int rest = p.ksteps % k;
+      if (ngw > 16 || ngw * mt > 32 || (rest != 0) != (o[1] != 0) || rest % (k / 4) || waves > kGemvMaxWaves)
+        continue;
+      const size_t lds = gemv_one_lds_bytes(waves, k, mt);
       if (lds > budget) continue;
       p.one_kpw = k;
       p.one_mt = mt;
-      p.one_waves = p.ksteps / k;
+      p.one_waves = waves;
       p.one_lds_bytes = lds;
       break;
     }
@@ -1059,7 +1079,9 @@ static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStr
     return hipErrorInvalidConfiguration;
   } else {
     const dim3 grid(plan.tiles), block(64 * plan.one_waves);
-    hipLaunchKernelGGL((gemv_one_kernel<DT, GS, ASYM, KPW, MT>), grid, block, plan.one_lds_bytes, s,
+    const bool part = (int64_t)plan.one_waves * KPW * kGemvKStep != a.K;
+    auto kern = part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true> : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false>;
+    hipLaunchKernelGGL(kern, grid, block, plan.one_lds_bytes, s,
                        static_cast<const uint16_t*>(a.x), reinterpret_cast<const uint32_t*>(a.wq),
                        static_cast<const uint16_t*>(a.scales), reinterpret_cast<const uint32_t*>(a.zp), (int)a.N,
                        (int)a.K, a.sG, (int)a.M, static_cast<const uint16_t*>(a.bias), static_cast<uint16_t*>(a.y));
@@ -1096,7 +1118,8 @@ bool gemv_one_runs(const LinearArgs& a, const GemvPlan& plan, const MoeArgs* moe
   const auto aligned16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   return plan.one_kpw != 0 && !moe && gemv_one_rows(a.M) == plan.one_mt && a.gmul == 1 && aligned16(a.scales) &&
          (!a.zp || aligned16(a.zp)) && plan.one_waves >= 1 && plan.one_waves <= kGemvMaxWaves &&
-         (int64_t)plan.one_waves * plan.one_kpw * kGemvKStep == a.K;
+         (int64_t)(plan.one_waves - 1) * plan.one_kpw * kGemvKStep < a.K &&
+         (int64_t)plan.one_waves * plan.one_kpw * kGemvKStep >= a.K && a.K % kGemvKStep == 0;
 }
 
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspace,

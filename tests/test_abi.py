@@ -329,10 +329,12 @@ def test_plan_reports_the_few_token_instance():
     for dt in (L.W4A16_F16, L.W4A16_BF16):
         for (M, K, g, waves) in ((1, 4096, 128, 4), (1, 4096, 32, 8), (1, 14336, 128, 14), (1, 2560, 64, 5),
                                  (1, 512, 32, 1), (2, 4096, 128, 4), (2, 4096, 64, 4), (2, 4096, 32, 8),
-                                 (3, 4096, 128, 8), (4, 4096, 128, 8), (4, 4096, 64, 8), (4, 14336, 128, 14)):
+                                 (3, 4096, 128, 8), (4, 4096, 128, 8), (4, 4096, 64, 8), (4, 14336, 128, 14),
+                                 # a last run shorter by whole quarter runs
+                                 (1, 9728, 128, 10), (1, 1280, 128, 2), (2, 2176, 128, 5), (4, 3456, 128, 7)):
             p = L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)
             assert (p["kernel"], p["waves"], p["splits"], p["launches"]) == (1, waves, 1, 1), (M, K, g, p)
-        for (M, K, g) in ((5, 4096, 128), (8, 4096, 128), (1, 14336, 32), (1, 9728, 128), (1, 4160, 64),
+        for (M, K, g) in ((5, 4096, 128), (8, 4096, 128), (1, 14336, 32), (1, 4160, 64),
                           (1, 28672, 128), (4, 4096, 32), (3, 14336, 64)):
             assert L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)["kernel"] == 0, (M, K, g)
         # per-channel scales stay on the general kernel
