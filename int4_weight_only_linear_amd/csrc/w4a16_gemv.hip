@@ -654,8 +654,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
 }
 
 // ---------------------------------------------------------------------------
-// M <= 4: a few tokens, one K range, every wave a run of KPW complete k-steps
-// (the last wave's run may be shorter: a whole number of quarter runs)
+// M <= 8: a few tokens, one K range, every wave a run of KPW complete k-steps
+// (the last wave's run may be shorter by whole parts of a run)
 // ---------------------------------------------------------------------------
 // The kernel above stages each wave's scales, zero points and bf16 x group
 // sums through LDS and meets twice at workgroup barriers; for a few tokens
@@ -664,13 +664,15 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
 // * A row i of the MFMA is token i mod MT (MT = 1, 2 or 4 token rows; three
 //   tokens run with MT = 4), so every 16-lane row of a result holds the same
 //   dot products: register r is token r.  Each 16-lane row R therefore
-//   finishes only the groups it owns -- the R-th quarter of the wave's run --
-//   and fetches only their scales and zero points: one small load per tensor
-//   and wave, straight into registers (the scale / zero-point carrier of
-//   "[ROCm] Converge the two W4A16 linear kernels onto the upstream shell",
-//   "What this does": no per-group metadata loads), issued after the weights,
-//   since only the end of the run needs them: the waits for the weights,
-//   which complete in issue order, never wait for them.
+//   finishes only the groups it owns -- the R-th quarter of the wave's run.
+//   With eight token rows (five to eight tokens, only M staged) rows R and
+//   R + 2 hold tokens 4 (R mod 2) + r and finish half the groups each.  A
+//   16-lane row fetches only its groups' scales and zero points: one small
+//   load per tensor and wave, straight into registers (the scale / zero-point
+//   carrier of "[ROCm] Converge the two W4A16 linear kernels onto the
+//   upstream shell", "What this does": no per-group metadata loads), issued
+//   after the weights, since only the end of the run needs them: the waits
+//   for the weights, which complete in issue order, never wait for them.
 // * Both dtypes multiply x by the exact magic value (128 or 1024) + q and
 //   remove (magic + z) per group with the group's sum of x (the general
 //   kernel's bf16 scheme; for fp16 it saves the packed subtraction, 4 of 11
@@ -678,13 +680,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(small_wave
 //   matrix cores: an MFMA whose A rows are 16 chunks of one token's x and
 //   whose B is all ones gives the 16 chunk sums, its rows ordered so that
 //   16-lane row R receives the chunks of its own groups.
-// * The 16-lane rows are added with two permlane swaps per token; the waves
-//   through LDS after one barrier, in wave order.
+// * The 16-lane rows are added with permlane swaps; the waves through LDS
+//   after one barrier, in wave order.
 
 // waves per SIMD the register budget is sized for (more tokens and longer
 // runs hold more group sums)
 constexpr int one_waves_per_simd(int kpw, int gs, int mt) {
-  return (128 * kpw / gs) * mt > 16 || (kpw == 8 && gs == 64) ? 5 : (kpw == 8 || gs == 32 || mt > 1 ? 6 : 8);
+  return mt == 8 ? 4
+                 : ((128 * kpw / gs) * mt > 16 || (kpw == 8 && gs == 64) ? 5 : (kpw == 8 || gs == 32 || mt > 1 ? 6 : 8));
 }
 
 // 16-lane row R of the result takes vR (each v uniform across the wave): two
@@ -710,6 +713,21 @@ __device__ __forceinline__ float rows_sum(float v) {
   const uint32_t b = __builtin_bit_cast(uint32_t, v);
   const auto odd = __builtin_amdgcn_permlane16_swap(b, b, false, false);  // [1]: lanes 16..31 in 0..15
   return v + __builtin_bit_cast(float, (uint32_t)odd[1]);
+}
+
+// 16-lane rows 0 and 1 keep a, rows 2 and 3 take b from rows 0 and 1 (one
+// 32-lane swap)
+__device__ __forceinline__ float half_select(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                  false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]);
+}
+
+// v of 16-lane rows 0 + 2 and 1 + 3, in lanes 0..31
+__device__ __forceinline__ float halves_sum(float v) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, v);
+  const auto hi = __builtin_amdgcn_permlane32_swap(a, a, false, false);  // [1]: lanes 32..63 in 0..31
+  return v + __builtin_bit_cast(float, (uint32_t)hi[1]);
 }
 
 // a lane's NW consecutive 32-bit words, read as one load where possible
@@ -743,11 +761,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   constexpr int CPG = GS / 32;            // 32-k chunks per group
   constexpr int NC = 4 * KPW;             // chunks of a run
   constexpr int NGW = NC / CPG;           // groups of a run
-  constexpr int OWN = NGW / 4;            // groups each 16-lane row finishes
+  constexpr int QR = MT == 8 ? 2 : 4;     // parts of the run's groups: quarters, or halves
+  constexpr int OWN = NGW / QR;           // groups each 16-lane row finishes
+  constexpr int SLOTS = MT == 8 ? 4 : MT; // result registers in use: token slots per 16-lane row
   constexpr int KR = KPW * kGemvKStep;    // k of a run
   constexpr int XPL = KR / 8 / 64;        // 16-byte x segments per lane and token
   constexpr int SW = (OWN + 1) / 2;       // words holding the owned scales
-  static_assert(OWN >= 1 && OWN <= 4 && XPL >= 1 && (MT == 1 || MT == 2 || MT == 4), "instance");
+  static_assert(OWN >= 1 && OWN <= 4 && XPL >= 1 && (MT == 1 || MT == 2 || MT == 4 || MT == 8), "instance");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -756,19 +776,26 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   const int nwaves = blockDim.x >> 6;
   const int col = lane & 15;   // MFMA column: output row within the tile
   const int row4 = lane >> 4;  // 16-lane row
+  // the part of the run's groups this 16-lane row finishes, and the token of
+  // its result register r: with up to four token rows every 16-lane row holds
+  // every token (register r is token r) and finishes a quarter; with eight,
+  // rows R and R + 2 hold tokens 4 (R mod 2) + r and finish a half each
+  const int part = MT == 8 ? row4 >> 1 : row4;
   const int n0 = blockIdx.x * kGemvRowsPerTile;
   const int n = min(n0 + col, N - 1);  // rows past N read row N - 1
   const int kw0 = wave * KR;           // first k of this wave's run
   const int g0 = kw0 / GS;             // first group of the run
   // The last wave's run may stop short of KPW k-steps, after a whole number
-  // of quarter runs (the host checks): 16-lane row R's groups then lie
-  // entirely inside K or entirely past it.  Past K, every load is clamped to
-  // valid memory and the row's groups are dropped at the end.
+  // of parts (the host checks): a 16-lane row's groups then lie entirely
+  // inside K or entirely past it.  Past K, every load is clamped to valid
+  // memory and the row's groups are dropped at the end.
   const int ksteps = K >> 7;
-  const bool own_valid = !PART || (wave * KPW + row4 * (KPW / 4)) < ksteps;
-  const int gown = g0 + (own_valid ? row4 * OWN : 0);  // first group this 16-lane row finishes
+  const bool own_valid = !PART || (wave * KPW + part * (KPW / QR)) < ksteps;
+  const int gown = g0 + (own_valid ? part * OWN : 0);  // first group this 16-lane row finishes
+  // token rows staged in LDS: MT, or the M tokens of an eight-row instance
+  const int rows = MT == 8 ? M : MT;
   float* red = reinterpret_cast<float*>(smem);  // [waves][MT][16]
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 64 * MT * nwaves + (size_t)wave * MT * 2 * KR);  // [MT][KR]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 64 * MT * nwaves + (size_t)wave * rows * 2 * KR);  // [rows][KR]
 
   // ---- 1. loads: x, then the weights, then scales and zero points ----
   // (the metadata is needed only after the run, so the waits for the weights
@@ -776,6 +803,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   u32x4 xr[MT][XPL];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
+    if (MT == 8 && m >= M) break;  // wave-uniform
     const char* xb = reinterpret_cast<const char*>(a_x + (size_t)min(m, M - 1) * K + kw0);
 #pragma unroll
     for (int j = 0; j < XPL; ++j)
@@ -809,50 +837,71 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   // ---- 2. x to this wave's LDS region; group sums of x ----
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
+    if (MT == 8 && m >= M) break;  // wave-uniform
 #pragma unroll
     for (int j = 0; j < XPL; ++j) *reinterpret_cast<u32x4*>(xs + m * KR + 8 * (lane + 64 * j)) = xr[m][j];
   }
-  float xsum[MT][OWN];
+  float xsum[SLOTS][OWN];
   {
-    // MFMA b of token m: A row i is chunk (NC/4) (i / 4) + 4 b + i % 4 of the
-    // token's run and B is all ones, so the result rows 4R .. 4R+3 of
-    // 16-lane row R are the sums of the chunks of R's own groups
     constexpr uint32_t ONE2 = DT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0 in both halves
     const u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
-    const uint16_t* xa0 = xs + ((NC / 4) * (col >> 2) + (col & 3)) * 32 + 8 * row4;
+    if constexpr (MT <= 4) {
+      // MFMA b of token m: A row i is chunk (NC/4) (i / 4) + 4 b + i % 4 of
+      // the token's run and B is all ones, so the result rows 4R .. 4R+3 of
+      // 16-lane row R are the sums of the chunks of R's own groups
+      const uint16_t* xa0 = xs + ((NC / 4) * (col >> 2) + (col & 3)) * 32 + 8 * row4;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+      for (int m = 0; m < MT; ++m) {
 #pragma unroll
-      for (int b = 0; b < NC / 16; ++b) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(xa0 + m * KR + 4 * 32 * b);
-        const f32x4 d = mfma16x16x32<DT>(a, ones, f32x4{0.f, 0.f, 0.f, 0.f});
-        if constexpr (CPG == 4) {
-          xsum[m][b] = (d[0] + d[1]) + (d[2] + d[3]);
-        } else if constexpr (CPG == 2) {
-          xsum[m][2 * b] = d[0] + d[1];
-          xsum[m][2 * b + 1] = d[2] + d[3];
-        } else {
-          xsum[m][4 * b] = d[0];
-          xsum[m][4 * b + 1] = d[1];
-          xsum[m][4 * b + 2] = d[2];
-          xsum[m][4 * b + 3] = d[3];
+        for (int b = 0; b < NC / 16; ++b) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(xa0 + m * KR + 4 * 32 * b);
+          const f32x4 d = mfma16x16x32<DT>(a, ones, f32x4{0.f, 0.f, 0.f, 0.f});
+          if constexpr (CPG == 4) {
+            xsum[m][b] = (d[0] + d[1]) + (d[2] + d[3]);
+          } else if constexpr (CPG == 2) {
+            xsum[m][2 * b] = d[0] + d[1];
+            xsum[m][2 * b + 1] = d[2] + d[3];
+          } else {
+            xsum[m][4 * b] = d[0];
+            xsum[m][4 * b + 1] = d[1];
+            xsum[m][4 * b + 2] = d[2];
+            xsum[m][4 * b + 3] = d[3];
+          }
         }
+      }
+    } else {
+      // owned group t: A row i is token 4 ((i / 4) mod 2) + i % 4 over chunk c
+      // of the group in half i / 8, B all ones, chained over the group's
+      // chunks: register r of 16-lane row R is the group's sum of x for the
+      // row's token slot r
+      const int tk = min(4 * ((col >> 2) & 1) + (col & 3), M - 1);
+      const uint16_t* xa0 = xs + tk * KR + (col >> 3) * (NC / 2) * 32 + 8 * row4;
+#pragma unroll
+      for (int t = 0; t < OWN; ++t) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < CPG; ++c)
+          d = mfma16x16x32<DT>(*reinterpret_cast<const u32x4*>(xa0 + (t * CPG + c) * 32), ones, d);
+#pragma unroll
+        for (int r = 0; r < SLOTS; ++r) xsum[r][t] = d[r];
       }
     }
   }
 
   // ---- 3. dot products, one k-step at a time as its weights arrive ----
   // (the loop of the kernel above: x fragments from LDS two chunks ahead, one
-  // MFMA chain per group, x multiplied by magic + q)
+  // MFMA chain per group, x multiplied by magic + q; A row i reads token
+  // i mod MT)
   const uint32_t mask_v = vgpr_const(0x000F000Fu);
-  const uint16_t* xrow = xs + (col & (MT - 1)) * KR + 8 * row4;  // A row i: token i mod MT
+  const int arow = MT == 8 ? min(col & 7, M - 1) : (col & (MT - 1));
+  const uint16_t* xrow = xs + arow * KR + 8 * row4;
   const int zshift = 4 * (n & 7);
   constexpr int XD = 2;
   u32x4 xa[XD + 1];
   auto load_x = [&](int q) { return *reinterpret_cast<const u32x4*>(xrow + q * 32); };
 #pragma unroll
   for (int q = 0; q < XD; ++q) xa[q] = load_x(q);
-  float chg[NGW][MT];
+  float chg[NGW][SLOTS];
   f32x4 ch;
 #pragma unroll
   for (int q = 0; q < NC; ++q) {
@@ -866,41 +915,54 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
     ch = mfma16x16x32<DT>(a, bq, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : ch);
     if (q % CPG == CPG - 1) {
 #pragma unroll
-      for (int r = 0; r < MT; ++r) chg[gl][r] = ch[r];
+      for (int r = 0; r < SLOTS; ++r) chg[gl][r] = ch[r];
     }
   }
 
   // ---- 4. each 16-lane row scales its own groups; rows, then waves, added ----
-  float acc[MT];
+  float acc[SLOTS];
 #pragma unroll
-  for (int r = 0; r < MT; ++r) acc[r] = 0.f;
+  for (int r = 0; r < SLOTS; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int t = 0; t < OWN; ++t) {
-    // the group of 16-lane row R is R * OWN + t of the run
+    // the group of 16-lane row R is part * OWN + t of the run
     const uint32_t sbits = (sw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
     const float s = act_to_f32<DT>((uint16_t)sbits);
     const uint32_t z = ASYM ? (zw[t] >> zshift) & 0xFu : 8u;
     const float szc = own_valid ? -(Magic<DT>::value + (float)z) * s : 0.f;  // exact
     const float sv = own_valid ? s : 0.f;
 #pragma unroll
-    for (int r = 0; r < MT; ++r) {
-      const float v = row_select(chg[t][r], chg[OWN + t][r], chg[2 * OWN + t][r], chg[3 * OWN + t][r]);
+    for (int r = 0; r < SLOTS; ++r) {
+      float v;
+      if constexpr (MT == 8)
+        v = half_select(chg[t][r], chg[OWN + t][r]);
+      else
+        v = row_select(chg[t][r], chg[OWN + t][r], chg[2 * OWN + t][r], chg[3 * OWN + t][r]);
       acc[r] = __builtin_fmaf(sv, v, __builtin_fmaf(szc, xsum[r][t], acc[r]));
     }
   }
 #pragma unroll
-  for (int r = 0; r < MT; ++r) {
-    const float v = rows_sum(acc[r]);
-    if (lane < 16) red[(wave * MT + r) * 16 + lane] = v;
+  for (int r = 0; r < SLOTS; ++r) {
+    if constexpr (MT == 8) {
+      // rows 0 + 2 (tokens 0..3) and 1 + 3 (tokens 4..7), in lanes 0..31
+      const float v = halves_sum(acc[r]);
+      if (lane < 32) red[(wave * MT + 4 * row4 + r) * 16 + col] = v;
+    } else {
+      const float v = rows_sum(acc[r]);
+      if (lane < 16) red[(wave * MT + r) * 16 + lane] = v;
+    }
   }
   __syncthreads();
-  const int m = tid >> 4;
-  const int nn = n0 + (tid & 15);
-  if (m < M && nn < N) {
-    float v = 0.f;
-    for (int w = 0; w < nwaves; ++w) v += red[(w * MT + m) * 16 + (tid & 15)];
-    if (bias) v += act_to_f32<DT>(bias[nn]);
-    y[(size_t)m * N + nn] = f32_to_act<DT>(v);
+  // 16 M outputs (a workgroup of one wave covers eight tokens in two passes)
+  for (int e = tid; e < 16 * M; e += blockDim.x) {
+    const int m = e >> 4;
+    const int nn = n0 + (e & 15);
+    if (nn < N) {
+      float v = 0.f;
+      for (int w = 0; w < nwaves; ++w) v += red[(w * MT + m) * 16 + (e & 15)];
+      if (bias) v += act_to_f32<DT>(bias[nn]);
+      y[(size_t)m * N + nn] = f32_to_act<DT>(v);
+    }
   }
 }
 
@@ -960,17 +1022,24 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu
   p.splits = (p.ksteps + p.ksteps_per_split - 1) / p.ksteps_per_split;
   p.waves = (p.ksteps_per_split + kpw - 1) / kpw;
   p.lds_bytes = gemv_lds_bytes(p.waves, M, kpw, group);
-  // up to four tokens: the few-token instance, when K is a whole number of
+  // up to eight tokens: the few-token instance, when K is a whole number of
   // 128-k steps in runs of 8 (else 4) for at most kGemvMaxWaves waves, the
-  // last run a whole number of quarter runs, a run spans at most 16 groups,
-  // the group sums per token row and run are at most 32, and the staged x
-  // fits the LDS budget (one K range, no tail chunks)
-  // (runs of 8 first; four token rows measured faster with runs of 4 where
-  // those fit: -1 to -9 % on the decode layers; whole runs before a shorter
-  // last run)
-  const int mt = gemv_one_rows(M);
+  // last run a whole number of parts (quarter runs, half runs for eight
+  // token rows), a 16-lane row finishes at most 4 groups, the group sums per
+  // result register and run are at most 32, and the staged x fits the LDS
+  // budget (one K range, no tail chunks)
+  // (runs of 8 first; four and eight token rows measured faster with runs of
+  // 4 where those fit: -1 to -9 % on the decode layers; whole runs before a
+  // shorter last run)
+  // Eight token rows (five to eight tokens) only where the general kernel
+  // would split K: there they remove the hand-off (14336 x 4096 at M = 5:
+  // 13.5 -> 10.4 us; K = 9728 at M = 5 / 6: -12 / -23 %); where it does not,
+  // staging eight tokens per wave costs more than it saves (K = 2560 and 4096
+  // layers at M = 6 / 8: up to +25 %).
+  const int mt = gemv_one_rows(M) == 8 && p.splits == 1 ? 0 : gemv_one_rows(M);
   if (mt && K % kGemvKStep == 0 && !tu.gemv_no_one && tu.gemv_splits <= 1) {
-    const int a = mt == 4 ? 4 : 8, b = mt == 4 ? 8 : 4;
+    const int a = mt >= 4 ? 4 : 8, b = mt >= 4 ? 8 : 4;
+    const int slots = mt == 8 ? 4 : mt, parts = mt == 8 ? 2 : 4;  // result registers, group parts
     const int order[4][2] = {{a, 0}, {b, 0}, {a, 1}, {b, 1}};  // (k-steps per wave, shorter last run)
     for (const auto& o : order) {
       const int k = o[0];
@@ -978,9 +1047,10 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu
       const int ngw = kGemvKStep * k / group;
       const int waves = (p.ksteps + k - 1) / k;
       const int rest = p.ksteps % k;
-      if (ngw > 16 || ngw * mt > 32 || (rest != 0) != (o[1] != 0) || rest % (k / 4) || waves > kGemvMaxWaves)
+      if (ngw > 16 || ngw / parts > 4 || ngw * slots > 32 || (rest != 0) != (o[1] != 0) || rest % (k / parts) ||
+          waves > kGemvMaxWaves)
         continue;
-      const size_t lds = gemv_one_lds_bytes(waves, k, mt);
+      const size_t lds = gemv_one_lds_bytes(waves, k, mt, M);
       if (lds > budget) continue;
       p.one_kpw = k;
       p.one_mt = mt;
@@ -1073,9 +1143,11 @@ static hipError_t launch_g(const GemvParams& prm, int group, const GemvPlan& pla
 
 template <int DT, int GS, bool ASYM, int KPW, int MT>
 static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStream_t s) {
-  // instances: at most 16 groups a run, at most 32 group sums per token row
+  // instances: at most 16 groups a run, at most 4 finished by a 16-lane row,
+  // at most 32 group sums per result register
   constexpr int NGW = kGemvKStep * KPW / GS;
-  if constexpr (NGW > 16 || NGW * MT > 32) {
+  constexpr int SLOTS = MT == 8 ? 4 : MT, PARTS = MT == 8 ? 2 : 4;
+  if constexpr (NGW > 16 || NGW / PARTS > 4 || NGW * SLOTS > 32) {
     return hipErrorInvalidConfiguration;
   } else {
     const dim3 grid(plan.tiles), block(64 * plan.one_waves);
@@ -1099,6 +1171,8 @@ static hipError_t launch_one(const LinearArgs& a, const GemvPlan& plan, hipStrea
     case 41: return launch_one_k<DT, GS, ASYM, 4, 1>(a, plan, s);
     case 42: return launch_one_k<DT, GS, ASYM, 4, 2>(a, plan, s);
     case 44: return launch_one_k<DT, GS, ASYM, 4, 4>(a, plan, s);
+    case 88: return launch_one_k<DT, GS, ASYM, 8, 8>(a, plan, s);
+    case 48: return launch_one_k<DT, GS, ASYM, 4, 8>(a, plan, s);
     default: return hipErrorInvalidConfiguration;
   }
 }

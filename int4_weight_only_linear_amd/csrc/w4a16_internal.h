@@ -93,7 +93,7 @@ struct GemvPlan {
   int waves;             // waves per workgroup
   int kpw;               // k-steps per wave (upper bound)
   size_t lds_bytes;      // dynamic LDS of one workgroup
-  // the few-token instance (gemv_one_kernel, M <= 4), when the shape allows
+  // the few-token instance (gemv_one_kernel, M <= 8), when the shape allows
   // it: k-steps per wave (8 or 4; 0: not this shape), token rows, its waves
   // and LDS.  It runs when, in addition, the scales are group-wise and the
   // scale and zero-point tensors are 16-byte aligned (otherwise the general
@@ -117,12 +117,14 @@ __host__ __device__ inline int gemv_wave_lds_bytes(int M, int kpw, int group) {
   return (b + 15) / 16 * 16;
 }
 size_t gemv_lds_bytes(int waves, int64_t M, int kpw, int group);
-// the few-token instance: per wave and token row, 16 fp32 sums and the run of x
-inline size_t gemv_one_lds_bytes(int waves, int kpw, int mt) {
-  return (size_t)waves * (size_t)mt * (16 * sizeof(float) + 2 * (size_t)kpw * kGemvKStep);
+// the few-token instance: per wave, 16 fp32 sums per token row and the run of
+// x of each staged token (the MT rows, or the M tokens of an eight-row instance)
+inline size_t gemv_one_lds_bytes(int waves, int kpw, int mt, int64_t M) {
+  const size_t staged = mt == 8 ? (size_t)M : (size_t)mt;
+  return (size_t)waves * (16 * sizeof(float) * (size_t)mt + staged * 2 * (size_t)kpw * kGemvKStep);
 }
 // token rows of the few-token instance for M tokens (0: not served)
-inline int gemv_one_rows(int64_t M) { return M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 0)); }
+inline int gemv_one_rows(int64_t M) { return M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 0))); }
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu_count);
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N);
 // Expert-indexed decode: slots = M * topk products of one token row with the

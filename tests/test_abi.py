@@ -323,19 +323,26 @@ def test_split_decode_beyond_the_counter_region_is_chunked(M, N, K):
 
 
 def test_plan_reports_the_few_token_instance():
-    # up to four tokens with K a whole number of 8- or 4-step runs (at most 16
-    # waves, at most 16 groups a run, at most 32 group sums per token row)
-    # take the few-token instance; it never splits K
+    # up to eight tokens with K a whole number of 128-k steps in runs of 8 or 4
+    # (at most 16 waves, the last run shorter by whole parts), at most 4
+    # groups finished by a 16-lane row, at most 32 group sums per result
+    # register and the staged x within the LDS budget take the few-token
+    # instance; it never splits K
     for dt in (L.W4A16_F16, L.W4A16_BF16):
         for (M, K, g, waves) in ((1, 4096, 128, 4), (1, 4096, 32, 8), (1, 14336, 128, 14), (1, 2560, 64, 5),
                                  (1, 512, 32, 1), (2, 4096, 128, 4), (2, 4096, 64, 4), (2, 4096, 32, 8),
                                  (3, 4096, 128, 8), (4, 4096, 128, 8), (4, 4096, 64, 8), (4, 14336, 128, 14),
-                                 # a last run shorter by whole quarter runs
-                                 (1, 9728, 128, 10), (1, 1280, 128, 2), (2, 2176, 128, 5), (4, 3456, 128, 7)):
+                                 # a last run shorter by whole parts
+                                 (1, 9728, 128, 10), (1, 1280, 128, 2), (2, 2176, 128, 5), (4, 3456, 128, 7),
+                                 # eight token rows (five to eight tokens) where the general
+                                 # kernel would split K
+                                 (5, 14336, 128, 14), (5, 9728, 128, 10), (6, 9728, 128, 10), (7, 9728, 128, 10)):
             p = L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)
             assert (p["kernel"], p["waves"], p["splits"], p["launches"]) == (1, waves, 1, 1), (M, K, g, p)
-        for (M, K, g) in ((5, 4096, 128), (8, 4096, 128), (1, 14336, 32), (1, 4160, 64),
-                          (1, 28672, 128), (4, 4096, 32), (3, 14336, 64)):
+        for (M, K, g) in ((9, 4096, 128), (16, 4096, 128), (1, 14336, 32), (1, 4160, 64), (1, 28672, 128),
+                          (4, 4096, 32), (3, 14336, 64), (6, 14336, 128), (8, 4096, 32), (5, 14336, 64),
+                          # five to eight tokens where the general kernel keeps K whole
+                          (5, 4096, 128), (8, 4096, 128), (8, 512, 128), (7, 2560, 128)):
             assert L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)["kernel"] == 0, (M, K, g)
         # per-channel scales stay on the general kernel
         assert L.w4a16_plan(1, 4096, 4096, 4096, dt, False, L.PATH_GEMV)["kernel"] == 0

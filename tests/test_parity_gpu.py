@@ -142,17 +142,24 @@ def test_decode_workgroup_scales(tuning_env, N, K, sym, bias):
     assert_close(y_shared, oracle_rows(c), O.BF16, "workgroup scales")
 
 
-def _few_token_instance_expected(M, K, g):
-    # the planner's rule: K a whole number of runs of 8 (else 4) 128-k steps,
-    # at most 16 waves, at most 16 groups per run and 32 group sums per token
-    # row (token rows: 1, 2, or 4 for three and four tokens)
-    ks, mt = K // 128, {1: 1, 2: 2, 3: 4, 4: 4}.get(M, 0)
+def _few_token_instance_expected(M, N, K, g):
+    # the planner's rule: K a whole number of 128-k steps in runs of 8 or 4
+    # (four and eight token rows try 4 first; whole runs before a last run
+    # shorter by whole parts), at most 16 waves, at most 4 groups finished by
+    # a 16-lane row, at most 32 group sums per result register, the staged x
+    # within the LDS budget (token rows 1, 2, 4, or 8 for five to eight)
+    ks = K // 128
+    mt = {1: 1, 2: 2, 3: 4, 4: 4}.get(M, 8 if 5 <= M <= 8 else 0)
     if not mt or K % 128:
         return False
-    for kpw in (8, 4):
-        ngw = 128 * kpw // g
-        # the last run may be shorter by whole quarter runs
-        if ngw <= 16 and ngw * mt <= 32 and (ks % kpw) % (kpw // 4) == 0 and -(-ks // kpw) <= 16:
+    slots, parts = (4, 2) if mt == 8 else (mt, 4)
+    a, b = (4, 8) if mt >= 4 else (8, 4)
+    budget = 160 * 1024 - 16 * 320 - 256 if -(-N // 16) <= 256 else 64 * 1024
+    for kpw, short in ((a, False), (b, False), (a, True), (b, True)):
+        ngw, rest, waves = 128 * kpw // g, ks % kpw, -(-ks // kpw)
+        lds = waves * (64 * mt + (M if mt == 8 else mt) * 2 * kpw * 128)
+        if (ngw <= 16 and ngw // parts <= 4 and ngw * slots <= 32 and (rest != 0) == short
+                and rest % (kpw // parts) == 0 and waves <= 16 and lds <= budget):
             return True
     return False
 
@@ -168,7 +175,7 @@ def test_decode_single_token_instance(tuning_env, N, K, g, dt, sym, bias):
     # of the groups, metadata in registers, x group sums on the matrix cores)
     # against the oracle, and the general kernel on the same case
     plan = L.w4a16_plan(1, N, K, g, dt, not sym, GEMV)
-    assert plan["kernel"] == int(_few_token_instance_expected(1, K, g)), (N, K, g, plan)
+    assert plan["kernel"] == int(_few_token_instance_expected(1, N, K, g)), (N, K, g, plan)
     c = make_case(1, N, K, g, dt, sym, bias, seed=("one", N, K, g, dt, sym, bias))
     d = DeviceCase(c)
     ref = oracle_rows(c)
@@ -178,16 +185,23 @@ def test_decode_single_token_instance(tuning_env, N, K, g, dt, sym, bias):
     assert_close(d.run(GEMV), ref, dt, "general kernel")
 
 
-@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("N,K", [(264, 512), (1048, 4096), (520, 2560), (776, 14336), (264, 2176), (136, 9728)])
 @pytest.mark.parametrize("g", [32, 64, 128])
 @pytest.mark.parametrize("dt", [O.F16, O.BF16])
 def test_decode_few_token_instance(tuning_env, M, N, K, g, dt):
-    # two to four tokens (three run as four token rows, the fourth never
-    # stored): asymmetric with bias, and symmetric, against the oracle; the
-    # general kernel on the same cases
+    # two to eight tokens (three run as four token rows, the fourth never
+    # stored; five to eight as eight rows, only M staged; K = 512 is one wave,
+    # whose 64 threads store eight tokens in two passes): asymmetric with
+    # bias, and symmetric, against the oracle; the general kernel on the same
+    # cases
+    # eight token rows only where the general kernel would split K
+    tuning_env("W4A16_GEMV_NO_ONE", "1")
+    general_splits = L.w4a16_plan(M, N, K, g, dt, True, GEMV)["splits"]
+    tuning_env("W4A16_GEMV_NO_ONE", None)
     plan = L.w4a16_plan(M, N, K, g, dt, True, GEMV)
-    assert plan["kernel"] == int(_few_token_instance_expected(M, K, g)), (M, N, K, g, plan)
+    expected = _few_token_instance_expected(M, N, K, g) and (M <= 4 or general_splits > 1)
+    assert plan["kernel"] == int(expected), (M, N, K, g, plan)
     for sym, bias in ((False, True), (True, False)):
         c = make_case(M, N, K, g, dt, sym, bias, seed=("few", M, N, K, g, dt, sym, bias))
         d = DeviceCase(c)
