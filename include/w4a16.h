@@ -265,7 +265,9 @@ w4a16_status w4a16_dequant(const int32_t* wq, const void* scales, const int32_t*
  * scales, bias, y 2.  y must not overlap any input.  Errors as w4a16_linear;
  * W4A16_ERR_UNSUPPORTED when K needs more than one workgroup per slot: with
  * N > 16 that is K above 15360, 13312 or 9216 for groups of 128, 64 or 32
- * (per-channel scales count as the largest of these dividing K). */
+ * (per-channel scales count as the largest of these dividing K), except that
+ * groups of 64 and 128 also run K up to 16384 when K is a multiple of 256
+ * (the single-token decode instance: at most 16 runs of 8 k-steps). */
 w4a16_status w4a16_moe_linear(const void* x, const int32_t* wq, const void* scales,
                               const int32_t* zp, const void* bias, const int32_t* topk_ids,
                               const float* topk_weights, void* y, int64_t M, int64_t topk,

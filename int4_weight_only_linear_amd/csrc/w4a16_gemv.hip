@@ -752,12 +752,21 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[NW])
   }
 }
 
+// expert-indexed mode of the single-token instance: workgroup z is slot z,
+// whose expert ids[z] selects slice e of the weight / scale / zp / bias stacks
+struct OneMoe {
+  const int32_t* ids;
+  const float* weights;  // router weight per slot, or NULL: 1
+  int topk, experts, x_per_slot;
+  size_t w_estride, s_estride, z_estride;  // words / halves / words per expert
+};
+
 // PART: the last wave's run may be shorter (otherwise every run is whole and
-// the masks and clamps below compile away)
-template <int DT, int GS, bool ASYM, int KPW, int MT, bool PART>
+// the masks and clamps below compile away).  MOE: expert-indexed (MT == 1).
+template <int DT, int GS, bool ASYM, int KPW, int MT, bool PART, bool MOE>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_per_simd(KPW, GS, MT)))) void gemv_one_kernel(
     const uint16_t* a_x, const uint32_t* a_wq, const uint16_t* a_scales, const uint32_t* a_zp, int N, int K,
-    int sG, int M, const uint16_t* bias, uint16_t* y) {
+    int sG, int M, const uint16_t* bias, uint16_t* y, const OneMoe moe) {
   constexpr int CPG = GS / 32;            // 32-k chunks per group
   constexpr int NC = 4 * KPW;             // chunks of a run
   constexpr int NGW = NC / CPG;           // groups of a run
@@ -768,9 +777,28 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   constexpr int XPL = KR / 8 / 64;        // 16-byte x segments per lane and token
   constexpr int SW = (OWN + 1) / 2;       // words holding the owned scales
   static_assert(OWN >= 1 && OWN <= 4 && XPL >= 1 && (MT == 1 || MT == 2 || MT == 4 || MT == 8), "instance");
+  static_assert(!MOE || MT == 1, "one token per slot");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x;
+  float yscale = 1.f;
+  if constexpr (MOE) {
+    const int slot = blockIdx.z;
+    const int e = moe.ids[slot];
+    y += (size_t)slot * N;
+    if (e < 0 || e >= moe.experts) {
+      // not an expert: a zero row (the whole workgroup leaves here)
+      const int nz = blockIdx.x * kGemvRowsPerTile + tid;
+      if (tid < kGemvRowsPerTile && nz < N) y[nz] = 0;
+      return;
+    }
+    a_wq += (size_t)e * moe.w_estride;
+    a_scales += (size_t)e * moe.s_estride;
+    if constexpr (ASYM) a_zp += (size_t)e * moe.z_estride;
+    if (bias) bias += (size_t)e * N;
+    a_x += (size_t)(moe.x_per_slot ? slot : slot / moe.topk) * K;
+    if (moe.weights) yscale = moe.weights[slot];
+  }
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = blockDim.x >> 6;
@@ -961,7 +989,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
       float v = 0.f;
       for (int w = 0; w < nwaves; ++w) v += red[(w * MT + m) * 16 + (e & 15)];
       if (bias) v += act_to_f32<DT>(bias[nn]);
-      y[(size_t)m * N + nn] = f32_to_act<DT>(v);
+      y[(size_t)m * N + nn] = f32_to_act<DT>(MOE ? v * yscale : v);
     }
   }
 }
@@ -1142,7 +1170,7 @@ static hipError_t launch_g(const GemvParams& prm, int group, const GemvPlan& pla
 }
 
 template <int DT, int GS, bool ASYM, int KPW, int MT>
-static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStream_t s) {
+static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStream_t s, const MoeArgs* moe) {
   // instances: at most 16 groups a run, at most 4 finished by a 16-lane row,
   // at most 32 group sums per result register
   constexpr int NGW = kGemvKStep * KPW / GS;
@@ -1150,47 +1178,63 @@ static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStr
   if constexpr (NGW > 16 || NGW / PARTS > 4 || NGW * SLOTS > 32) {
     return hipErrorInvalidConfiguration;
   } else {
-    const dim3 grid(plan.tiles), block(64 * plan.one_waves);
     const bool part = (int64_t)plan.one_waves * KPW * kGemvKStep != a.K;
-    auto kern = part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true> : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false>;
+    OneMoe om{};
+    auto kern = part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true, false> : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false, false>;
+    if (moe) {
+      if constexpr (MT == 1) {
+        om = OneMoe{moe->ids, moe->weights, (int)moe->topk, (int)moe->experts, moe->x_per_slot ? 1 : 0,
+                    (size_t)a.N * (size_t)(a.K / 8), (size_t)a.N * (size_t)a.sG, (size_t)(a.N / 8) * (size_t)a.sG};
+        kern = part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true, true> : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false, true>;
+      } else {
+        return hipErrorInvalidConfiguration;
+      }
+    }
+    const dim3 grid(plan.tiles, 1, moe ? (unsigned)moe->slots : 1u), block(64 * plan.one_waves);
     hipLaunchKernelGGL(kern, grid, block, plan.one_lds_bytes, s,
                        static_cast<const uint16_t*>(a.x), reinterpret_cast<const uint32_t*>(a.wq),
                        static_cast<const uint16_t*>(a.scales), reinterpret_cast<const uint32_t*>(a.zp), (int)a.N,
-                       (int)a.K, a.sG, (int)a.M, static_cast<const uint16_t*>(a.bias), static_cast<uint16_t*>(a.y));
+                       (int)a.K, a.sG, (int)a.M, static_cast<const uint16_t*>(a.bias), static_cast<uint16_t*>(a.y),
+                       om);
     return hipGetLastError();
   }
 }
 
 template <int DT, int GS, bool ASYM>
-static hipError_t launch_one(const LinearArgs& a, const GemvPlan& plan, hipStream_t s) {
+static hipError_t launch_one(const LinearArgs& a, const GemvPlan& plan, hipStream_t s, const MoeArgs* moe) {
   const int key = plan.one_kpw * 10 + plan.one_mt;
   switch (key) {
-    case 81: return launch_one_k<DT, GS, ASYM, 8, 1>(a, plan, s);
-    case 82: return launch_one_k<DT, GS, ASYM, 8, 2>(a, plan, s);
-    case 84: return launch_one_k<DT, GS, ASYM, 8, 4>(a, plan, s);
-    case 41: return launch_one_k<DT, GS, ASYM, 4, 1>(a, plan, s);
-    case 42: return launch_one_k<DT, GS, ASYM, 4, 2>(a, plan, s);
-    case 44: return launch_one_k<DT, GS, ASYM, 4, 4>(a, plan, s);
-    case 88: return launch_one_k<DT, GS, ASYM, 8, 8>(a, plan, s);
-    case 48: return launch_one_k<DT, GS, ASYM, 4, 8>(a, plan, s);
+    case 81: return launch_one_k<DT, GS, ASYM, 8, 1>(a, plan, s, moe);
+    case 82: return launch_one_k<DT, GS, ASYM, 8, 2>(a, plan, s, moe);
+    case 84: return launch_one_k<DT, GS, ASYM, 8, 4>(a, plan, s, moe);
+    case 41: return launch_one_k<DT, GS, ASYM, 4, 1>(a, plan, s, moe);
+    case 42: return launch_one_k<DT, GS, ASYM, 4, 2>(a, plan, s, moe);
+    case 44: return launch_one_k<DT, GS, ASYM, 4, 4>(a, plan, s, moe);
+    case 88: return launch_one_k<DT, GS, ASYM, 8, 8>(a, plan, s, moe);
+    case 48: return launch_one_k<DT, GS, ASYM, 4, 8>(a, plan, s, moe);
     default: return hipErrorInvalidConfiguration;
   }
 }
 
 template <int DT>
-static hipError_t launch_one_g(const LinearArgs& a, const GemvPlan& plan, hipStream_t s) {
+static hipError_t launch_one_g(const LinearArgs& a, const GemvPlan& plan, hipStream_t s, const MoeArgs* moe) {
   const bool asym = a.zp != nullptr;
   switch (a.group) {
-    case 32: return asym ? launch_one<DT, 32, true>(a, plan, s) : launch_one<DT, 32, false>(a, plan, s);
-    case 64: return asym ? launch_one<DT, 64, true>(a, plan, s) : launch_one<DT, 64, false>(a, plan, s);
-    case 128: return asym ? launch_one<DT, 128, true>(a, plan, s) : launch_one<DT, 128, false>(a, plan, s);
+    case 32: return asym ? launch_one<DT, 32, true>(a, plan, s, moe) : launch_one<DT, 32, false>(a, plan, s, moe);
+    case 64: return asym ? launch_one<DT, 64, true>(a, plan, s, moe) : launch_one<DT, 64, false>(a, plan, s, moe);
+    case 128: return asym ? launch_one<DT, 128, true>(a, plan, s, moe) : launch_one<DT, 128, false>(a, plan, s, moe);
     default: return hipErrorInvalidValue;
   }
 }
 
 bool gemv_one_runs(const LinearArgs& a, const GemvPlan& plan, const MoeArgs* moe) {
   const auto aligned16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-  return plan.one_kpw != 0 && !moe && gemv_one_rows(a.M) == plan.one_mt && a.gmul == 1 && aligned16(a.scales) &&
+  // expert-indexed: one token per slot, and every expert's scale and zero-point
+  // slices 16-byte aligned like the first
+  if (moe && (a.M != 1 || ((size_t)a.N * (size_t)a.sG) % 8 || ((size_t)(a.N / 8) * (size_t)a.sG) % 4 ||
+              moe->slots < 1 || moe->slots > kMaxGridZ))
+    return false;
+  return plan.one_kpw != 0 && gemv_one_rows(a.M) == plan.one_mt && a.gmul == 1 && aligned16(a.scales) &&
          (!a.zp || aligned16(a.zp)) && plan.one_waves >= 1 && plan.one_waves <= kGemvMaxWaves &&
          (int64_t)(plan.one_waves - 1) * plan.one_kpw * kGemvKStep < a.K &&
          (int64_t)plan.one_waves * plan.one_kpw * kGemvKStep >= a.K && a.K % kGemvKStep == 0;
@@ -1199,7 +1243,7 @@ bool gemv_one_runs(const LinearArgs& a, const GemvPlan& plan, const MoeArgs* moe
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspace,
                        hipStream_t stream, const MoeArgs* moe) {
   if (gemv_one_runs(a, plan, moe)) {
-    return a.dtype == DT_F16 ? launch_one_g<DT_F16>(a, plan, stream) : launch_one_g<DT_BF16>(a, plan, stream);
+    return a.dtype == DT_F16 ? launch_one_g<DT_F16>(a, plan, stream, moe) : launch_one_g<DT_BF16>(a, plan, stream, moe);
   }
   if (plan.waves < 1 || plan.waves > kGemvMaxWaves || plan.lds_bytes > kGemvLdsBudget ||
       plan.kpw < 1 || plan.kpw > kGemvStepsPerWave)

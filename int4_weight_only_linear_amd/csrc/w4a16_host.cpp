@@ -647,11 +647,11 @@ w4a16_status w4a16_moe_linear(const void* x, const int32_t* wq, const void* scal
   const GroupMap gm = group_map(group_size, K);
   // one K range per slot (the slots fill the device): planned as if for one CU
   const w4a16::GemvPlan plan = w4a16::plan_gemv(1, N, K, gm.kgroup, dtype, 1);
-  if (plan.splits != 1)
-    return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is too large for one decode workgroup per slot",
-                (long long)K);
   w4a16::LinearArgs a{x, wq, scales, zp, bias, y, 1, N, K, gm.kgroup, dtype, gm.sG, gm.gmul};
   w4a16::MoeArgs moe{topk_ids, topk_weights, topk, E, slots, x_per_slot != 0};
+  if (plan.splits != 1 && !w4a16::gemv_one_runs(a, plan, &moe))
+    return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is too large for one decode workgroup per slot",
+                (long long)K);
   hipError_t e = w4a16::launch_gemv(a, plan, nullptr, static_cast<hipStream_t>(stream), &moe);
   if (e != hipSuccess) return fail(W4A16_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -359,9 +359,12 @@ def test_power_of_two_scaling_is_exact(path):
     assert np.array_equal(y4, 4 * y1)
 
 
-def test_determinism_with_split_k():
-    # M = 5 takes 4 k-steps a wave: K = 9728 (76 steps) needs more than 16
-    # waves, so K is split across two workgroups
+def test_determinism_with_split_k(tuning_env):
+    # the general decode kernel at M = 5 takes 4 k-steps a wave: K = 9728 (76
+    # steps) needs more than 16 waves, so K is split across two workgroups
+    # (the few-token instance would run it unsplit)
+    tuning_env("W4A16_GEMV_NO_ONE", "1")
+    assert L.w4a16_plan(5, 2560, 9728, 128, O.BF16, True, GEMV)["splits"] == 2
     c = make_case(5, 2560, 9728, 128, O.BF16, False, False, seed=("det",))
     d = DeviceCase(c)
     a = d.run(GEMV)
@@ -385,7 +388,7 @@ def test_workspace_reuse_across_shapes():
     # where a later call's counters sit where an earlier call's partial sums were
     # (every shape needs more than 16 waves for one K range, so each is split)
     # (or, at M <= 4 and 8 k-steps a wave, more LDS than one workgroup holds)
-    shapes = [(5, 264, 9728, 128), (4, 2560, 20480, 128), (2, 40, 20480, 64), (3, 1024, 16384, 32)]
+    shapes = [(5, 264, 20480, 128), (4, 2560, 20480, 128), (2, 40, 20480, 64), (3, 1024, 16384, 32)]
     cases = [make_case(M, N, K, g, O.BF16, False, False, seed=("reuse", M, N, K, g))
              for (M, N, K, g) in shapes]
     for (M, N, K, g) in shapes:
@@ -589,7 +592,9 @@ def test_moe_linear_full_size_sampled():
 @pytest.mark.parametrize("g,kmax", [(128, 15360), (64, 13312), (32, 9216)])
 def test_moe_linear_k_bound(g, kmax):
     # one workgroup per slot: the largest K the header states runs (against
-    # the oracle), the next multiple of 128 is refused before any launch
+    # the oracle), the next multiple of 128 is refused before any launch; for
+    # groups of 64 and 128, K = 16384 (16 runs of 8 k-steps on the
+    # single-token instance) runs too
     E, topk, M, N, dt = 2, 1, 1, 32, O.BF16
     h = _moe_case(E, topk, M, N, kmax, g, dt, False, False, False, False, seed=("moek", g), invalid=False)
     d = _moe_device(h, dt)
@@ -604,6 +609,15 @@ def test_moe_linear_k_bound(g, kmax):
     x2 = torch.zeros((M, K2), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(L.W4A16Error, match="too large for one decode workgroup"):
         L.w4a16_moe_linear(x2, wq2, s2, d["ids"], zp2, None, None, group_size=g)
+    if g >= 64:
+        K3 = 16384
+        h = _moe_case(E, topk, M, N, K3, g, dt, False, False, False, False, seed=("moek3", g), invalid=False)
+        d = _moe_device(h, dt)
+        y = device_to_bits(L.w4a16_moe_linear(d["x"], d["wq"], d["s"], d["ids"], d["zp"], None, None,
+                                              group_size=g))
+        e = int(h["ids"][0, 0])
+        ref = O.linear_ref(h["x"][0:1], h["wq"][e], h["s"][e], h["zp"][e], None, 1, N, K3, g, dt)
+        assert_close(y, ref, dt, f"moe K={K3}")
 
 
 # ---- GEMM K split: last-workgroup hand-off and the two-pass form ----------------
@@ -692,7 +706,8 @@ CANARY8 = 0xA5
 @pytest.mark.parametrize("M,N,K,g,path,tile,ypad", [
     (1, 4096, 4096, 128, GEMV, None, 64),      # decode, one K range, aligned y
     (4, 264, 1152, 64, GEMV, None, 3),         # decode, ragged tile, y at a 6-byte offset
-    (5, 264, 9728, 128, GEMV, None, 64),       # decode, K split (counters + partials)
+    (5, 264, 20480, 128, GEMV, None, 64),      # decode, K split (counters + partials)
+    (5, 264, 9728, 128, GEMV, None, 3),        # decode, eight token rows, shorter last run
     (3, 40, 20480, 32, GEMV, None, 5),         # decode, K split, incomplete tile
     (300, 520, 1024, 128, GEMM, None, 64),     # GEMM, no split, 16-byte stores
     (130, 200, 640, 64, GEMM, "4,3,0", 3),     # GEMM, last-workgroup hand-off, element stores

@@ -50,7 +50,7 @@ def _with_workspace(d):
 PAIRS = [
     # decode with a K split (counters + partials in the scratch), then a
     # smaller split decode
-    ((5, 1024, 9728, 128, O.BF16, False, True), (3, 264, 20480, 32, O.F16, True, False)),
+    ((5, 1024, 20480, 128, O.BF16, False, True), (3, 264, 20480, 32, O.F16, True, False)),
     # prefill GEMM with a K split (128 tokens: few tiles), then a smaller one
     ((128, 4096, 4096, 128, O.BF16, False, False), (130, 200, 640, 64, O.F16, False, True)),
     # a plan with no split (no scratch), then a split decode
