@@ -104,7 +104,7 @@ int w4a16_abi_version(void);
  *   W4A16_GEMM_TILE=mb,splits[,two_pass[,cb]]        prefill tile and K split
  *   W4A16_GEMV_KPW=<k>, W4A16_GEMV_SPLITS=<s>         decode k-steps per wave, K splits
  *   W4A16_GEMV_NO_WGSZ=1                              decode: per-wave scale loads
- *   W4A16_GEMV_NO_ONE=1                               decode: up to four tokens on the general kernel
+ *   W4A16_GEMV_NO_ONE=1                               decode: few tokens on the general kernel
  *   W4A16_LOG=1                                       one line per call on stderr
  * Must not run concurrently with other library calls. */
 void w4a16_reload_tuning(void);
@@ -188,11 +188,12 @@ typedef struct w4a16_plan_info {
   int32_t launches;        /* kernel launches per call */
   int32_t waves;           /* waves per workgroup */
   int32_t two_pass;        /* 1: the K split is summed by a second kernel */
-  int32_t kernel;          /* decode: 1 the few-token instance (M <= 4, K a
-                              whole number of 8- or 4-step runs of 128 for at
-                              most 16 waves, group-wise scales; it runs when
-                              scales and zero points are also 16-byte
-                              aligned), 0 the general decode kernel; GEMM: 0 */
+  int32_t kernel;          /* decode: 1 the few-token instance (M <= 4, and
+                              M <= 8 where the general kernel splits K; K a
+                              whole number of 128-k steps; group-wise scales;
+                              it runs when scales and zero points are also
+                              16-byte aligned), 0 the general decode kernel;
+                              GEMM: 0 */
   uint64_t workspace_bytes; /* equals w4a16_workspace_size */
 } w4a16_plan_info;
 

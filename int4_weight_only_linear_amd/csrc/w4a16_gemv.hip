@@ -752,13 +752,20 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[NW])
   }
 }
 
-// expert-indexed mode of the single-token instance: workgroup z is slot z,
-// whose expert ids[z] selects slice e of the weight / scale / zp / bias stacks
-struct OneMoe {
+// The few-token instance's arguments past the ten preloaded ones.
+// Expert-indexed mode (single token): workgroup z is slot z, whose expert
+// ids[z] selects slice e of the weight / scale / zp / bias stacks.  K split
+// (splits > 1): workgroup y is K range y, of runs_per_split runs; partial
+// sums go to partial[split][M][N] and the last workgroup of a tile to arrive
+// (counters[tile], zero between calls) adds them in range order.
+struct OneArgs {
   const int32_t* ids;
   const float* weights;  // router weight per slot, or NULL: 1
   int topk, experts, x_per_slot;
   size_t w_estride, s_estride, z_estride;  // words / halves / words per expert
+  float* partial;
+  uint32_t* counters;
+  int splits, runs_per_split;
 };
 
 // PART: the last wave's run may be shorter (otherwise every run is whole and
@@ -766,7 +773,7 @@ struct OneMoe {
 template <int DT, int GS, bool ASYM, int KPW, int MT, bool PART, bool MOE>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_per_simd(KPW, GS, MT)))) void gemv_one_kernel(
     const uint16_t* a_x, const uint32_t* a_wq, const uint16_t* a_scales, const uint32_t* a_zp, int N, int K,
-    int sG, int M, const uint16_t* bias, uint16_t* y, const OneMoe moe) {
+    int sG, int M, const uint16_t* bias, uint16_t* y, const OneArgs moe) {
   constexpr int CPG = GS / 32;            // 32-k chunks per group
   constexpr int NC = 4 * KPW;             // chunks of a run
   constexpr int NGW = NC / CPG;           // groups of a run
@@ -811,14 +818,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   const int part = MT == 8 ? row4 >> 1 : row4;
   const int n0 = blockIdx.x * kGemvRowsPerTile;
   const int n = min(n0 + col, N - 1);  // rows past N read row N - 1
-  const int kw0 = wave * KR;           // first k of this wave's run
-  const int g0 = kw0 / GS;             // first group of the run
-  // The last wave's run may stop short of KPW k-steps, after a whole number
-  // of parts (the host checks): a 16-lane row's groups then lie entirely
-  // inside K or entirely past it.  Past K, every load is clamped to valid
-  // memory and the row's groups are dropped at the end.
+  // The last run may stop short of KPW k-steps, after a whole number of parts
+  // (the host checks), and with a K split the last range may hold fewer runs
+  // than waves: a 16-lane row's groups then lie entirely inside K or entirely
+  // past it.  Past K, every load is clamped to valid memory (a wave with no
+  // run reads the last one) and the row's groups are dropped at the end.
   const int ksteps = K >> 7;
-  const bool own_valid = !PART || (wave * KPW + part * (KPW / QR)) < ksteps;
+  const int run = MOE ? wave : (int)blockIdx.y * moe.runs_per_split + wave;  // this wave's run of KPW k-steps
+  const int runc = PART ? min(run, (ksteps - 1) / KPW) : run;
+  const int kw0 = runc * KR;           // first k of this wave's run
+  const int g0 = kw0 / GS;             // first group of the run
+  const bool own_valid = !PART || (run * KPW + part * (KPW / QR)) < ksteps;
   const int gown = g0 + (own_valid ? part * OWN : 0);  // first group this 16-lane row finishes
   // token rows staged in LDS: MT, or the M tokens of an eight-row instance
   const int rows = MT == 8 ? M : MT;
@@ -844,7 +854,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
 #pragma unroll
   for (int i = 0; i < KPW; ++i)
     wv[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(ww.at(PART ? min(wave * KPW + i, ksteps - 1) : wave * KPW + i)));
+        reinterpret_cast<const u32x4*>(ww.at(PART ? min(runc * KPW + i, ksteps - 1) : run * KPW + i)));
   __builtin_amdgcn_sched_barrier(0);
   uint32_t sw[SW];
   if constexpr (OWN == 1) {
@@ -982,16 +992,42 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   }
   __syncthreads();
   // 16 M outputs (a workgroup of one wave covers eight tokens in two passes)
+  const int splits = MOE ? 1 : moe.splits;
   for (int e = tid; e < 16 * M; e += blockDim.x) {
     const int m = e >> 4;
     const int nn = n0 + (e & 15);
     if (nn < N) {
       float v = 0.f;
       for (int w = 0; w < nwaves; ++w) v += red[(w * MT + m) * 16 + (e & 15)];
-      if (bias) v += act_to_f32<DT>(bias[nn]);
-      y[(size_t)m * N + nn] = f32_to_act<DT>(MOE ? v * yscale : v);
+      if (splits == 1) {
+        if (bias) v += act_to_f32<DT>(bias[nn]);
+        y[(size_t)m * N + nn] = f32_to_act<DT>(MOE ? v * yscale : v);
+      } else {
+        store_coherent(moe.partial + ((size_t)blockIdx.y * M + m) * N + nn, v);
+      }
     }
   }
+  if (MOE || splits == 1) return;
+  // K split: every thread's partial sums have completed (stores count in
+  // vmcnt; the barrier does not wait for them), then one arrival; the last
+  // workgroup of the tile adds the K ranges in order
+  __shared__ uint32_t last_range;
+  wait_vm_all();
+  __syncthreads();
+  if (tid == 0) last_range = arrive(moe.counters + blockIdx.x) == (uint32_t)(splits - 1);
+  __syncthreads();
+  if (!last_range) return;
+  for (int e = tid; e < 16 * M; e += blockDim.x) {
+    const int m = e >> 4;
+    const int nn = n0 + (e & 15);
+    if (nn < N) {
+      float v = 0.f;
+      for (int sp = 0; sp < splits; ++sp) v += load_coherent(moe.partial + ((size_t)sp * M + m) * N + nn);
+      if (bias) v += act_to_f32<DT>(bias[nn]);
+      y[(size_t)m * N + nn] = f32_to_act<DT>(v);
+    }
+  }
+  if (tid == 0) reset_counter(moe.counters + blockIdx.x);  // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -1069,30 +1105,50 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu
     const int a = mt >= 4 ? 4 : 8, b = mt >= 4 ? 8 : 4;
     const int slots = mt == 8 ? 4 : mt, parts = mt == 8 ? 2 : 4;  // result registers, group parts
     const int order[4][2] = {{a, 0}, {b, 0}, {a, 1}, {b, 1}};  // (k-steps per wave, shorter last run)
-    for (const auto& o : order) {
-      const int k = o[0];
-      if (tu.gemv_kpw >= 1 && k != tu.gemv_kpw) continue;
-      const int ngw = kGemvKStep * k / group;
-      const int waves = (p.ksteps + k - 1) / k;
-      const int rest = p.ksteps % k;
-      if (ngw > 16 || ngw / parts > 4 || ngw * slots > 32 || (rest != 0) != (o[1] != 0) || rest % (k / parts) ||
-          waves > kGemvMaxWaves)
-        continue;
-      const size_t lds = gemv_one_lds_bytes(waves, k, mt, M);
-      if (lds > budget) continue;
-      p.one_kpw = k;
-      p.one_mt = mt;
-      p.one_waves = waves;
-      p.one_lds_bytes = lds;
-      break;
+    // one K range first; then, where the general kernel splits K too (so no
+    // workspace is needed that it would not need), K ranges of at most
+    // kGemvMaxWaves runs each, the partial sums handed over through the
+    // workspace (tiles within the counter region). Split, one and two token
+    // rows pay where they need no more K ranges than the general kernel
+    // (28672 x 4096: M = 1 / 2 at g128 -21 / -10 %; at g32, 4 ranges against
+    // its 2, +9 / +2 %); four and eight token rows where every workgroup of
+    // the grid runs at once (20480 x 1280 g64 at M = 3 / 4: -14 / -16 %,
+    // 65536 x 1024 at M = 4: -39 %; 28672 x 4096 at M = 3 / 4 in several
+    // rounds: +4 / +2 %).
+    for (int pass = 0; pass < (p.splits > 1 ? 2 : 1) && !p.one_kpw; ++pass) {
+      for (const auto& o : order) {
+        const int k = o[0];
+        if (tu.gemv_kpw >= 1 && k != tu.gemv_kpw) continue;
+        const int ngw = kGemvKStep * k / group;
+        const int runs = (p.ksteps + k - 1) / k;
+        const int rest = p.ksteps % k;
+        const int splits = pass == 0 ? 1 : (runs + kGemvMaxWaves - 1) / kGemvMaxWaves;
+        const int waves = (runs + splits - 1) / splits;
+        if (ngw > 16 || ngw / parts > 4 || ngw * slots > 32 || (rest != 0) != (o[1] != 0) || rest % (k / parts) ||
+            waves > kGemvMaxWaves || (pass == 1 && (splits < 2 || p.tiles > kMaxCounters ||
+                           (mt <= 2 ? splits > p.splits : (int64_t)p.tiles * splits > cu_count))))
+          continue;
+        const size_t lds = gemv_one_lds_bytes(waves, k, mt, M);
+        const size_t one_budget = (int64_t)p.tiles * splits <= cu_count ? kGemvLdsBudget : kGemvLdsBudgetShared;
+        if (lds > one_budget) continue;
+        p.one_kpw = k;
+        p.one_mt = mt;
+        p.one_waves = waves;
+        p.one_splits = splits;
+        p.one_lds_bytes = lds;
+        break;
+      }
     }
   }
   return p;
 }
 
+// enough for whichever kernel runs (the few-token instance falls back to the
+// general kernel for unaligned scales or zero points)
 size_t gemv_workspace_bytes(const GemvPlan& p, int64_t M, int64_t N) {
-  if (p.splits <= 1) return 0;
-  return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
+  const int splits = p.splits > p.one_splits ? p.splits : p.one_splits;
+  if (splits <= 1) return 0;
+  return kCounterBytes + (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
 // x loads per lane an instance stages: the plan gives M <= 2 at 8 k-steps per
@@ -1170,7 +1226,8 @@ static hipError_t launch_g(const GemvParams& prm, int group, const GemvPlan& pla
 }
 
 template <int DT, int GS, bool ASYM, int KPW, int MT>
-static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStream_t s, const MoeArgs* moe) {
+static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStream_t s, const MoeArgs* moe,
+                               void* workspace) {
   // instances: at most 16 groups a run, at most 4 finished by a 16-lane row,
   // at most 32 group sums per result register
   constexpr int NGW = kGemvKStep * KPW / GS;
@@ -1178,19 +1235,33 @@ static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStr
   if constexpr (NGW > 16 || NGW / PARTS > 4 || NGW * SLOTS > 32) {
     return hipErrorInvalidConfiguration;
   } else {
-    const bool part = (int64_t)plan.one_waves * KPW * kGemvKStep != a.K;
-    OneMoe om{};
+    // a run shorter than KPW k-steps, or a K range with fewer runs than waves
+    const int runs = (int)((a.K / kGemvKStep + KPW - 1) / KPW);
+    const bool part = (int64_t)runs * KPW * kGemvKStep != a.K || plan.one_splits * plan.one_waves != runs;
+    OneArgs om{};
+    om.splits = plan.one_splits;
+    om.runs_per_split = plan.one_waves;
+    if (plan.one_splits > 1) {
+      om.counters = static_cast<uint32_t*>(workspace);
+      om.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+    }
     auto kern = part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true, false> : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false, false>;
     if (moe) {
       if constexpr (MT == 1) {
-        om = OneMoe{moe->ids, moe->weights, (int)moe->topk, (int)moe->experts, moe->x_per_slot ? 1 : 0,
-                    (size_t)a.N * (size_t)(a.K / 8), (size_t)a.N * (size_t)a.sG, (size_t)(a.N / 8) * (size_t)a.sG};
+        om.ids = moe->ids;
+        om.weights = moe->weights;
+        om.topk = (int)moe->topk;
+        om.experts = (int)moe->experts;
+        om.x_per_slot = moe->x_per_slot ? 1 : 0;
+        om.w_estride = (size_t)a.N * (size_t)(a.K / 8);
+        om.s_estride = (size_t)a.N * (size_t)a.sG;
+        om.z_estride = (size_t)(a.N / 8) * (size_t)a.sG;
         kern = part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true, true> : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false, true>;
       } else {
         return hipErrorInvalidConfiguration;
       }
     }
-    const dim3 grid(plan.tiles, 1, moe ? (unsigned)moe->slots : 1u), block(64 * plan.one_waves);
+    const dim3 grid(plan.tiles, plan.one_splits, moe ? (unsigned)moe->slots : 1u), block(64 * plan.one_waves);
     hipLaunchKernelGGL(kern, grid, block, plan.one_lds_bytes, s,
                        static_cast<const uint16_t*>(a.x), reinterpret_cast<const uint32_t*>(a.wq),
                        static_cast<const uint16_t*>(a.scales), reinterpret_cast<const uint32_t*>(a.zp), (int)a.N,
@@ -1201,28 +1272,31 @@ static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStr
 }
 
 template <int DT, int GS, bool ASYM>
-static hipError_t launch_one(const LinearArgs& a, const GemvPlan& plan, hipStream_t s, const MoeArgs* moe) {
+static hipError_t launch_one(const LinearArgs& a, const GemvPlan& plan, hipStream_t s, const MoeArgs* moe,
+                             void* ws) {
   const int key = plan.one_kpw * 10 + plan.one_mt;
   switch (key) {
-    case 81: return launch_one_k<DT, GS, ASYM, 8, 1>(a, plan, s, moe);
-    case 82: return launch_one_k<DT, GS, ASYM, 8, 2>(a, plan, s, moe);
-    case 84: return launch_one_k<DT, GS, ASYM, 8, 4>(a, plan, s, moe);
-    case 41: return launch_one_k<DT, GS, ASYM, 4, 1>(a, plan, s, moe);
-    case 42: return launch_one_k<DT, GS, ASYM, 4, 2>(a, plan, s, moe);
-    case 44: return launch_one_k<DT, GS, ASYM, 4, 4>(a, plan, s, moe);
-    case 88: return launch_one_k<DT, GS, ASYM, 8, 8>(a, plan, s, moe);
-    case 48: return launch_one_k<DT, GS, ASYM, 4, 8>(a, plan, s, moe);
+    case 81: return launch_one_k<DT, GS, ASYM, 8, 1>(a, plan, s, moe, ws);
+    case 82: return launch_one_k<DT, GS, ASYM, 8, 2>(a, plan, s, moe, ws);
+    case 84: return launch_one_k<DT, GS, ASYM, 8, 4>(a, plan, s, moe, ws);
+    case 41: return launch_one_k<DT, GS, ASYM, 4, 1>(a, plan, s, moe, ws);
+    case 42: return launch_one_k<DT, GS, ASYM, 4, 2>(a, plan, s, moe, ws);
+    case 44: return launch_one_k<DT, GS, ASYM, 4, 4>(a, plan, s, moe, ws);
+    case 88: return launch_one_k<DT, GS, ASYM, 8, 8>(a, plan, s, moe, ws);
+    case 48: return launch_one_k<DT, GS, ASYM, 4, 8>(a, plan, s, moe, ws);
     default: return hipErrorInvalidConfiguration;
   }
 }
 
 template <int DT>
-static hipError_t launch_one_g(const LinearArgs& a, const GemvPlan& plan, hipStream_t s, const MoeArgs* moe) {
+static hipError_t launch_one_g(const LinearArgs& a, const GemvPlan& plan, hipStream_t s, const MoeArgs* moe,
+                               void* ws) {
   const bool asym = a.zp != nullptr;
   switch (a.group) {
-    case 32: return asym ? launch_one<DT, 32, true>(a, plan, s, moe) : launch_one<DT, 32, false>(a, plan, s, moe);
-    case 64: return asym ? launch_one<DT, 64, true>(a, plan, s, moe) : launch_one<DT, 64, false>(a, plan, s, moe);
-    case 128: return asym ? launch_one<DT, 128, true>(a, plan, s, moe) : launch_one<DT, 128, false>(a, plan, s, moe);
+    case 32: return asym ? launch_one<DT, 32, true>(a, plan, s, moe, ws) : launch_one<DT, 32, false>(a, plan, s, moe, ws);
+    case 64: return asym ? launch_one<DT, 64, true>(a, plan, s, moe, ws) : launch_one<DT, 64, false>(a, plan, s, moe, ws);
+    case 128:
+      return asym ? launch_one<DT, 128, true>(a, plan, s, moe, ws) : launch_one<DT, 128, false>(a, plan, s, moe, ws);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1232,18 +1306,24 @@ bool gemv_one_runs(const LinearArgs& a, const GemvPlan& plan, const MoeArgs* moe
   // expert-indexed: one token per slot, and every expert's scale and zero-point
   // slices 16-byte aligned like the first
   if (moe && (a.M != 1 || ((size_t)a.N * (size_t)a.sG) % 8 || ((size_t)(a.N / 8) * (size_t)a.sG) % 4 ||
-              moe->slots < 1 || moe->slots > kMaxGridZ))
+              moe->slots < 1 || moe->slots > kMaxGridZ || plan.one_splits != 1))
     return false;
+  // the K ranges cover K, the last one not empty; split tiles within the
+  // counter region
+  const int64_t range = (int64_t)plan.one_waves * plan.one_kpw * kGemvKStep;
   return plan.one_kpw != 0 && gemv_one_rows(a.M) == plan.one_mt && a.gmul == 1 && aligned16(a.scales) &&
          (!a.zp || aligned16(a.zp)) && plan.one_waves >= 1 && plan.one_waves <= kGemvMaxWaves &&
-         (int64_t)(plan.one_waves - 1) * plan.one_kpw * kGemvKStep < a.K &&
-         (int64_t)plan.one_waves * plan.one_kpw * kGemvKStep >= a.K && a.K % kGemvKStep == 0;
+         plan.one_splits >= 1 && (plan.one_splits == 1 || plan.tiles <= kMaxCounters) &&
+         (int64_t)(plan.one_splits - 1) * range < a.K && (int64_t)plan.one_splits * range >= a.K &&
+         a.K % kGemvKStep == 0;
 }
 
 hipError_t launch_gemv(const LinearArgs& a, const GemvPlan& plan, void* workspace,
                        hipStream_t stream, const MoeArgs* moe) {
   if (gemv_one_runs(a, plan, moe)) {
-    return a.dtype == DT_F16 ? launch_one_g<DT_F16>(a, plan, stream, moe) : launch_one_g<DT_BF16>(a, plan, stream, moe);
+    if (plan.one_splits > 1 && !workspace) return hipErrorInvalidValue;
+    return a.dtype == DT_F16 ? launch_one_g<DT_F16>(a, plan, stream, moe, workspace)
+                             : launch_one_g<DT_BF16>(a, plan, stream, moe, workspace);
   }
   if (plan.waves < 1 || plan.waves > kGemvMaxWaves || plan.lds_bytes > kGemvLdsBudget ||
       plan.kpw < 1 || plan.kpw > kGemvStepsPerWave)

@@ -502,10 +502,10 @@ w4a16_status w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int
     if (g.one_kpw && gm.gmul == 1) {
       // the single-token instance (given 16-byte aligned scales and zero points)
       r.kernel = 1;
-      r.splits = 1;
+      r.splits = g.one_splits;
       r.waves = g.one_waves;
       r.launches = 1;
-      r.counter_tiles = 0;
+      r.counter_tiles = g.one_splits > 1 ? g.tiles : 0;
     } else {
       r.splits = g.splits;
       r.waves = g.waves;

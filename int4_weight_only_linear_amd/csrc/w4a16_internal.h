@@ -100,7 +100,8 @@ struct GemvPlan {
   // kernel runs, with the fields above).
   int one_kpw = 0;
   int one_mt = 0;
-  int one_waves = 0;
+  int one_waves = 0;     // waves per workgroup: runs per K range
+  int one_splits = 1;    // K ranges (partial sums through the workspace when > 1)
   size_t one_lds_bytes = 0;
 };
 

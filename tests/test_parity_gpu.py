@@ -142,25 +142,44 @@ def test_decode_workgroup_scales(tuning_env, N, K, sym, bias):
     assert_close(y_shared, oracle_rows(c), O.BF16, "workgroup scales")
 
 
-def _few_token_instance_expected(M, N, K, g):
+def _general_splits(tuning_env, M, N, K, g, dt):
+    # K ranges of the general decode kernel for the shape (the few-token
+    # instance off)
+    tuning_env("W4A16_GEMV_NO_ONE", "1")
+    splits = L.w4a16_plan(M, N, K, g, dt, True, GEMV)["splits"]
+    tuning_env("W4A16_GEMV_NO_ONE", None)
+    return splits
+
+
+def _few_token_instance_expected(M, N, K, g, general_splits):
     # the planner's rule: K a whole number of 128-k steps in runs of 8 or 4
     # (four and eight token rows try 4 first; whole runs before a last run
-    # shorter by whole parts), at most 16 waves, at most 4 groups finished by
-    # a 16-lane row, at most 32 group sums per result register, the staged x
-    # within the LDS budget (token rows 1, 2, 4, or 8 for five to eight)
-    ks = K // 128
+    # shorter by whole parts), at most 4 groups finished by a 16-lane row, at
+    # most 32 group sums per result register, the staged x within the LDS
+    # budget (token rows 1, 2, 4, or 8 for five to eight); one K range of at
+    # most 16 runs first, then, where the general kernel splits K too, K
+    # ranges of at most 16 runs (row tiles within the 16384 counters; one and
+    # two token rows in no more K ranges than the general kernel, four and
+    # eight token rows with the grid within the 256 CUs); eight token rows
+    # only where the general kernel splits K
+    ks, tiles = K // 128, -(-N // 16)
     mt = {1: 1, 2: 2, 3: 4, 4: 4}.get(M, 8 if 5 <= M <= 8 else 0)
-    if not mt or K % 128:
+    if not mt or K % 128 or (mt == 8 and general_splits == 1):
         return False
     slots, parts = (4, 2) if mt == 8 else (mt, 4)
     a, b = (4, 8) if mt >= 4 else (8, 4)
-    budget = 160 * 1024 - 16 * 320 - 256 if -(-N // 16) <= 256 else 64 * 1024
-    for kpw, short in ((a, False), (b, False), (a, True), (b, True)):
-        ngw, rest, waves = 128 * kpw // g, ks % kpw, -(-ks // kpw)
-        lds = waves * (64 * mt + (M if mt == 8 else mt) * 2 * kpw * 128)
-        if (ngw <= 16 and ngw // parts <= 4 and ngw * slots <= 32 and (rest != 0) == short
-                and rest % (kpw // parts) == 0 and waves <= 16 and lds <= budget):
-            return True
+    for split_pass in ((False, True) if general_splits > 1 else (False,)):
+        for kpw, short in ((a, False), (b, False), (a, True), (b, True)):
+            ngw, rest, runs = 128 * kpw // g, ks % kpw, -(-ks // kpw)
+            splits = -(-runs // 16) if split_pass else 1
+            waves = -(-runs // splits)
+            budget = 160 * 1024 - 16 * 320 - 256 if tiles * splits <= 256 else 64 * 1024
+            lds = waves * (64 * mt + (M if mt == 8 else mt) * 2 * kpw * 128)
+            if (ngw <= 16 and ngw // parts <= 4 and ngw * slots <= 32 and (rest != 0) == short
+                    and rest % (kpw // parts) == 0 and waves <= 16 and lds <= budget
+                    and (not split_pass or (splits >= 2 and tiles <= 16384 and (
+                        splits <= general_splits if mt <= 2 else tiles * splits <= 256)))):
+                return True
     return False
 
 
@@ -174,8 +193,9 @@ def test_decode_single_token_instance(tuning_env, N, K, g, dt, sym, bias):
     # one token: the few-token instance (each 16-lane row finishes a quarter
     # of the groups, metadata in registers, x group sums on the matrix cores)
     # against the oracle, and the general kernel on the same case
+    gs = _general_splits(tuning_env, 1, N, K, g, dt)
     plan = L.w4a16_plan(1, N, K, g, dt, not sym, GEMV)
-    assert plan["kernel"] == int(_few_token_instance_expected(1, N, K, g)), (N, K, g, plan)
+    assert plan["kernel"] == int(_few_token_instance_expected(1, N, K, g, gs)), (N, K, g, plan)
     c = make_case(1, N, K, g, dt, sym, bias, seed=("one", N, K, g, dt, sym, bias))
     d = DeviceCase(c)
     ref = oracle_rows(c)
@@ -195,13 +215,9 @@ def test_decode_few_token_instance(tuning_env, M, N, K, g, dt):
     # whose 64 threads store eight tokens in two passes): asymmetric with
     # bias, and symmetric, against the oracle; the general kernel on the same
     # cases
-    # eight token rows only where the general kernel would split K
-    tuning_env("W4A16_GEMV_NO_ONE", "1")
-    general_splits = L.w4a16_plan(M, N, K, g, dt, True, GEMV)["splits"]
-    tuning_env("W4A16_GEMV_NO_ONE", None)
+    gs = _general_splits(tuning_env, M, N, K, g, dt)
     plan = L.w4a16_plan(M, N, K, g, dt, True, GEMV)
-    expected = _few_token_instance_expected(M, N, K, g) and (M <= 4 or general_splits > 1)
-    assert plan["kernel"] == int(expected), (M, N, K, g, plan)
+    assert plan["kernel"] == int(_few_token_instance_expected(M, N, K, g, gs)), (M, N, K, g, plan)
     for sym, bias in ((False, True), (True, False)):
         c = make_case(M, N, K, g, dt, sym, bias, seed=("few", M, N, K, g, dt, sym, bias))
         d = DeviceCase(c)
@@ -235,6 +251,28 @@ def test_decode_single_token_unaligned_scales_fall_back():
     y = L.w4a16_linear_path(d.x, d.wq, s_off, d.zp, d.bias, group_size=g, path=GEMV)
     torch.cuda.synchronize()
     assert_close(device_to_bits(y), oracle_rows(c), O.BF16, "unaligned scales")
+
+
+@pytest.mark.parametrize("M,N,K,g,splits", [(1, 264, 28672, 128, 2), (2, 520, 28672, 128, 2),
+                                              (3, 136, 28672, 64, 4), (2, 136, 1 << 16, 64, 4),
+                                              (1, 1048, 1 << 16, 128, 4), (4, 40, 20480, 128, 3)])
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+def test_decode_few_token_instance_k_split(tuning_env, M, N, K, g, splits, dt):
+    # more than 16 runs, where the general kernel splits K too: K ranges of at
+    # most 16 runs, fp32 partial sums through the workspace, the last
+    # workgroup of a row tile adding them in range order; twice (the counters
+    # must be zero again), bit-identical, and against the oracle and the
+    # general kernel
+    plan = L.w4a16_plan(M, N, K, g, dt, True, GEMV)
+    assert (plan["kernel"], plan["splits"]) == (1, splits), plan
+    c = make_case(M, N, K, g, dt, False, True, seed=("fewsplit", M, N, K, g, dt))
+    d = DeviceCase(c)
+    ref = oracle_rows(c)
+    y = d.run(GEMV)
+    assert_close(y, ref, dt, f"{splits} K ranges")
+    assert np.array_equal(d.run(GEMV), y)
+    tuning_env("W4A16_GEMV_NO_ONE", "1")
+    assert_close(d.run(GEMV), ref, dt, "general kernel")
 
 
 def test_ragged_n_not_multiple_of_eight_symmetric():
