@@ -342,11 +342,13 @@ def test_plan_reports_the_few_token_instance():
         # more than 16 runs: K ranges of at most 16 runs, partial sums through
         # the workspace (counters for every row tile), only where the general
         # kernel splits K too (no new workspace need); one and two token rows
-        # in no more K ranges than it, four token rows with at most one
-        # workgroup per CU
+        # in no more K ranges than it, four token rows with at most two
+        # rounds of one workgroup per CU (runs of 8 first)
         for (M, N, K, g, waves, splits) in ((1, 4096, 28672, 128, 14, 2), (2, 4096, 28672, 128, 14, 2),
                                             (1, 4096, 1 << 16, 128, 16, 4), (4, 1024, 1 << 16, 128, 16, 4),
-                                            (3, 1280, 20480, 64, 14, 3), (4, 1280, 20480, 64, 14, 3)):
+                                            (3, 1280, 20480, 64, 14, 3), (4, 1280, 20480, 64, 14, 3),
+                                            (3, 4096, 28672, 128, 14, 2), (4, 4096, 28672, 128, 14, 2),
+                                            (4, 4096, 14336, 64, 14, 2)):
             p = L.w4a16_plan(M, N, K, g, dt, True, L.PATH_GEMV)
             assert (p["kernel"], p["waves"], p["splits"], p["launches"], p["counter_tiles"]) == \
                 (1, waves, splits, 1, N // 16), (M, N, K, g, p)
@@ -355,10 +357,12 @@ def test_plan_reports_the_few_token_instance():
                           (4, 4096, 32), (6, 14336, 128), (8, 4096, 32), (5, 14336, 64),
                           # five to eight tokens where the general kernel keeps K whole
                           (5, 4096, 128), (8, 4096, 128), (8, 512, 128), (7, 2560, 128),
-                          # more K ranges than the general kernel's; four token
-                          # rows in several rounds of workgroups
-                          (1, 28672, 32), (2, 28672, 32), (3, 28672, 64), (4, 20480, 128), (4, 28672, 128)):
+                          # more K ranges than the general kernel's
+                          (1, 28672, 32), (2, 28672, 32)):
             assert L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)["kernel"] == 0, (M, K, g)
+        # four token rows in more than two rounds of workgroups
+        for (M, N, K) in ((3, 8192, 28672), (4, 8192, 28672), (3, 5120, 20480), (4, 5120, 20480)):
+            assert L.w4a16_plan(M, N, K, 128, dt, True, L.PATH_GEMV)["kernel"] == 0, (M, N, K)
         # per-channel scales stay on the general kernel
         assert L.w4a16_plan(1, 4096, 4096, 4096, dt, False, L.PATH_GEMV)["kernel"] == 0
         # the prefill GEMM reports 0
