@@ -782,6 +782,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   constexpr int SLOTS = MT == 8 ? 4 : MT; // result registers in use: token slots per 16-lane row
   constexpr int KR = KPW * kGemvKStep;    // k of a run
   constexpr int XPL = KR / 8 / 64;        // 16-byte x segments per lane and token
+  // staged token rows are KR halves apart plus 64 bytes, so that the token
+  // rows one MFMA operand read touches start in different LDS banks (KR
+  // halves alone is a multiple of the bank span: four token rows read the
+  // same banks, a 4-way conflict on every operand read)
+  constexpr int XR = KR + (MT > 1 ? 32 : 0);
   constexpr int SW = (OWN + 1) / 2;       // words holding the owned scales
   static_assert(OWN >= 1 && OWN <= 4 && XPL >= 1 && (MT == 1 || MT == 2 || MT == 4 || MT == 8), "instance");
   static_assert(!MOE || MT == 1, "one token per slot");
@@ -833,7 +838,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   // token rows staged in LDS: MT, or the M tokens of an eight-row instance
   const int rows = MT == 8 ? M : MT;
   float* red = reinterpret_cast<float*>(smem);  // [waves][MT][16]
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 64 * MT * nwaves + (size_t)wave * rows * 2 * KR);  // [rows][KR]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 64 * MT * nwaves + (size_t)wave * rows * 2 * XR);  // [rows][XR]
 
   // ---- 1. loads: x, then the weights, then scales and zero points ----
   // (the metadata is needed only after the run, so the waits for the weights
@@ -877,7 +882,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   for (int m = 0; m < MT; ++m) {
     if (MT == 8 && m >= M) break;  // wave-uniform
 #pragma unroll
-    for (int j = 0; j < XPL; ++j) *reinterpret_cast<u32x4*>(xs + m * KR + 8 * (lane + 64 * j)) = xr[m][j];
+    for (int j = 0; j < XPL; ++j) *reinterpret_cast<u32x4*>(xs + m * XR + 8 * (lane + 64 * j)) = xr[m][j];
   }
   float xsum[SLOTS][OWN];
   {
@@ -892,7 +897,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
       for (int m = 0; m < MT; ++m) {
 #pragma unroll
         for (int b = 0; b < NC / 16; ++b) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(xa0 + m * KR + 4 * 32 * b);
+          const u32x4 a = *reinterpret_cast<const u32x4*>(xa0 + m * XR + 4 * 32 * b);
           const f32x4 d = mfma16x16x32<DT>(a, ones, f32x4{0.f, 0.f, 0.f, 0.f});
           if constexpr (CPG == 4) {
             xsum[m][b] = (d[0] + d[1]) + (d[2] + d[3]);
@@ -913,7 +918,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
       // chunks: register r of 16-lane row R is the group's sum of x for the
       // row's token slot r
       const int tk = min(4 * ((col >> 2) & 1) + (col & 3), M - 1);
-      const uint16_t* xa0 = xs + tk * KR + (col >> 3) * (NC / 2) * 32 + 8 * row4;
+      const uint16_t* xa0 = xs + tk * XR + (col >> 3) * (NC / 2) * 32 + 8 * row4;
 #pragma unroll
       for (int t = 0; t < OWN; ++t) {
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -932,7 +937,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   // i mod MT)
   const uint32_t mask_v = vgpr_const(0x000F000Fu);
   const int arow = MT == 8 ? min(col & 7, M - 1) : (col & (MT - 1));
-  const uint16_t* xrow = xs + arow * KR + 8 * row4;
+  const uint16_t* xrow = xs + arow * XR + 8 * row4;
   const int zshift = 4 * (n & 7);
   constexpr int XD = 2;
   u32x4 xa[XD + 1];

@@ -122,7 +122,8 @@ size_t gemv_lds_bytes(int waves, int64_t M, int kpw, int group);
 // x of each staged token (the MT rows, or the M tokens of an eight-row instance)
 inline size_t gemv_one_lds_bytes(int waves, int kpw, int mt, int64_t M) {
   const size_t staged = mt == 8 ? (size_t)M : (size_t)mt;
-  return (size_t)waves * (16 * sizeof(float) * (size_t)mt + staged * 2 * (size_t)kpw * kGemvKStep);
+  // (staged token rows 64 bytes apart beyond their x when there are several)
+  return (size_t)waves * (16 * sizeof(float) * (size_t)mt + staged * (2 * (size_t)kpw * kGemvKStep + (mt > 1 ? 64 : 0)));
 }
 // token rows of the few-token instance for M tokens (0: not served)
 inline int gemv_one_rows(int64_t M) { return M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 0))); }

@@ -177,7 +177,7 @@ def _few_token_instance_expected(M, N, K, g, general_splits):
             waves = -(-runs // splits)
             full = tiles * splits <= 256 or (split_pass and mt == 4 and kpw == 8)
             budget = 160 * 1024 - 16 * 320 - 256 if full else 64 * 1024
-            lds = waves * (64 * mt + (M if mt == 8 else mt) * 2 * kpw * 128)
+            lds = waves * (64 * mt + (M if mt == 8 else mt) * (2 * kpw * 128 + (64 if mt > 1 else 0)))
             if (ngw <= 16 and ngw // parts <= 4 and ngw * slots <= 32 and (rest != 0) == short
                     and rest % (kpw // parts) == 0 and waves <= 16 and lds <= budget
                     and (not split_pass or (splits >= 2 and tiles <= 16384 and (
