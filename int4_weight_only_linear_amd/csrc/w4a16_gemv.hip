@@ -769,11 +769,16 @@ struct OneArgs {
 };
 
 // PART: the last wave's run may be shorter (otherwise every run is whole and
-// the masks and clamps below compile away).  MOE: expert-indexed (MT == 1).
-template <int DT, int GS, bool ASYM, int KPW, int MT, bool PART, bool MOE>
+// the masks and clamps below compile away).  MODE: ONE_PLAIN, ONE_MOE
+// (expert-indexed, MT == 1) or ONE_SPLIT (K ranges; a plain launch computes
+// its runs from the wave index alone, with no wait for an argument load
+// before the weight addresses).
+enum { ONE_PLAIN = 0, ONE_MOE = 1, ONE_SPLIT = 2 };
+template <int DT, int GS, bool ASYM, int KPW, int MT, bool PART, int MODE>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_per_simd(KPW, GS, MT)))) void gemv_one_kernel(
     const uint16_t* a_x, const uint32_t* a_wq, const uint16_t* a_scales, const uint32_t* a_zp, int N, int K,
     int sG, int M, const uint16_t* bias, uint16_t* y, const OneArgs moe) {
+  constexpr bool MOE = MODE == ONE_MOE, SPLIT = MODE == ONE_SPLIT;
   constexpr int CPG = GS / 32;            // 32-k chunks per group
   constexpr int NC = 4 * KPW;             // chunks of a run
   constexpr int NGW = NC / CPG;           // groups of a run
@@ -829,7 +834,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   // past it.  Past K, every load is clamped to valid memory (a wave with no
   // run reads the last one) and the row's groups are dropped at the end.
   const int ksteps = K >> 7;
-  const int run = MOE ? wave : (int)blockIdx.y * moe.runs_per_split + wave;  // this wave's run of KPW k-steps
+  const int run = SPLIT ? (int)blockIdx.y * moe.runs_per_split + wave : wave;  // this wave's run of KPW k-steps
   const int runc = PART ? min(run, (ksteps - 1) / KPW) : run;
   const int kw0 = runc * KR;           // first k of this wave's run
   const int g0 = kw0 / GS;             // first group of the run
@@ -997,14 +1002,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   }
   __syncthreads();
   // 16 M outputs (a workgroup of one wave covers eight tokens in two passes)
-  const int splits = MOE ? 1 : moe.splits;
   for (int e = tid; e < 16 * M; e += blockDim.x) {
     const int m = e >> 4;
     const int nn = n0 + (e & 15);
     if (nn < N) {
       float v = 0.f;
       for (int w = 0; w < nwaves; ++w) v += red[(w * MT + m) * 16 + (e & 15)];
-      if (splits == 1) {
+      if constexpr (!SPLIT) {
         if (bias) v += act_to_f32<DT>(bias[nn]);
         y[(size_t)m * N + nn] = f32_to_act<DT>(MOE ? v * yscale : v);
       } else {
@@ -1012,7 +1016,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
       }
     }
   }
-  if (MOE || splits == 1) return;
+  if constexpr (!SPLIT) return;
+  const int splits = moe.splits;
   // K split: every thread's partial sums have completed (stores count in
   // vmcnt; the barrier does not wait for them), then one arrival; the last
   // workgroup of the tile adds the K ranges in order
@@ -1255,7 +1260,11 @@ static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStr
       om.counters = static_cast<uint32_t*>(workspace);
       om.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
     }
-    auto kern = part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true, false> : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false, false>;
+    auto kern = plan.one_splits > 1
+                    ? (part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true, ONE_SPLIT>
+                            : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false, ONE_SPLIT>)
+                    : (part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true, ONE_PLAIN>
+                            : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false, ONE_PLAIN>);
     if (moe) {
       if constexpr (MT == 1) {
         om.ids = moe->ids;
@@ -1266,7 +1275,8 @@ static hipError_t launch_one_k(const LinearArgs& a, const GemvPlan& plan, hipStr
         om.w_estride = (size_t)a.N * (size_t)(a.K / 8);
         om.s_estride = (size_t)a.N * (size_t)a.sG;
         om.z_estride = (size_t)(a.N / 8) * (size_t)a.sG;
-        kern = part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true, true> : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false, true>;
+        kern = part ? gemv_one_kernel<DT, GS, ASYM, KPW, MT, true, ONE_MOE>
+                    : gemv_one_kernel<DT, GS, ASYM, KPW, MT, false, ONE_MOE>;
       } else {
         return hipErrorInvalidConfiguration;
       }
