@@ -842,8 +842,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
   const int gown = g0 + (own_valid ? part * OWN : 0);  // first group this 16-lane row finishes
   // token rows staged in LDS: MT, or the M tokens of an eight-row instance
   const int rows = MT == 8 ? M : MT;
-  float* red = reinterpret_cast<float*>(smem);  // [waves][MT][16]
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 64 * MT * nwaves + (size_t)wave * rows * 2 * XR);  // [rows][XR]
+  // one LDS region per wave: its x ([rows][XR]), then its sums ([MT][16]);
+  // only the final sum over the waves needs the number of waves, which is
+  // read from the dispatch (no wait for it before the run's loads)
+  const int region = rows * 2 * XR + 64 * MT;  // bytes
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + (size_t)wave * region);
+  auto red_of = [&](int w) { return reinterpret_cast<float*>(smem + (size_t)w * region + rows * 2 * XR); };
 
   // ---- 1. loads: x, then the weights, then scales and zero points ----
   // (the metadata is needed only after the run, so the waits for the weights
@@ -994,10 +998,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
     if constexpr (MT == 8) {
       // rows 0 + 2 (tokens 0..3) and 1 + 3 (tokens 4..7), in lanes 0..31
       const float v = halves_sum(acc[r]);
-      if (lane < 32) red[(wave * MT + 4 * row4 + r) * 16 + col] = v;
+      if (lane < 32) red_of(wave)[(4 * row4 + r) * 16 + col] = v;
     } else {
       const float v = rows_sum(acc[r]);
-      if (lane < 16) red[(wave * MT + r) * 16 + lane] = v;
+      if (lane < 16) red_of(wave)[r * 16 + lane] = v;
     }
   }
   __syncthreads();
@@ -1007,7 +1011,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(one_waves_
     const int nn = n0 + (e & 15);
     if (nn < N) {
       float v = 0.f;
-      for (int w = 0; w < nwaves; ++w) v += red[(w * MT + m) * 16 + (e & 15)];
+      for (int w = 0; w < nwaves; ++w) v += red_of(w)[m * 16 + (e & 15)];
       if constexpr (!SPLIT) {
         if (bias) v += act_to_f32<DT>(bias[nn]);
         y[(size_t)m * N + nn] = f32_to_act<DT>(MOE ? v * yscale : v);
