@@ -1109,12 +1109,13 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu
   // (runs of 8 first; four and eight token rows measured faster with runs of
   // 4 where those fit: -1 to -9 % on the decode layers; whole runs before a
   // shorter last run)
-  // Eight token rows (five to eight tokens) only where the general kernel
-  // would split K: there they remove the hand-off (14336 x 4096 at M = 5:
-  // 13.5 -> 10.4 us; K = 9728 at M = 5 / 6: -12 / -23 %); where it does not,
-  // staging eight tokens per wave costs more than it saves (K = 2560 and 4096
-  // layers at M = 6 / 8: up to +25 %).
-  const int mt = gemv_one_rows(M) == 8 && p.splits == 1 ? 0 : gemv_one_rows(M);
+  // Eight token rows (five to eight tokens): where the general kernel would
+  // split K they remove the hand-off (14336 x 4096 at M = 5: 13.5 -> 9.0 us;
+  // K = 9728 at M = 5 / 6: -16 / -23 %); elsewhere, with the staged token
+  // rows in different LDS banks, they are as fast or faster too (Llama decode
+  // step at M = 5: -12 %, 4096 x 28672 17.6 -> 14.2 us; Qwen3-4B at
+  // M = 5 / 6 / 8: -7 / -5 / -7 %).
+  const int mt = gemv_one_rows(M);
   if (mt && K % kGemvKStep == 0 && !tu.gemv_no_one && tu.gemv_splits <= 1) {
     const int a = mt >= 4 ? 4 : 8, b = mt >= 4 ? 8 : 4;
     const int slots = mt == 8 ? 4 : mt, parts = mt == 8 ? 2 : 4;  // result registers, group parts

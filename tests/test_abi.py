@@ -334,9 +334,9 @@ def test_plan_reports_the_few_token_instance():
                                  (3, 4096, 128, 8), (4, 4096, 128, 8), (4, 4096, 64, 8), (4, 14336, 128, 14),
                                  # a last run shorter by whole parts
                                  (1, 9728, 128, 10), (1, 1280, 128, 2), (2, 2176, 128, 5), (4, 3456, 128, 7),
-                                 # eight token rows (five to eight tokens) where the general
-                                 # kernel would split K
-                                 (5, 14336, 128, 14), (5, 9728, 128, 10), (6, 9728, 128, 10), (7, 9728, 128, 10)):
+                                 # eight token rows (five to eight tokens)
+                                 (5, 14336, 128, 14), (5, 9728, 128, 10), (6, 9728, 128, 10), (7, 9728, 128, 10),
+                                 (5, 4096, 128, 8), (8, 4096, 128, 8), (8, 512, 128, 1), (7, 2560, 128, 5)):
             p = L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)
             assert (p["kernel"], p["waves"], p["splits"], p["launches"]) == (1, waves, 1, 1), (M, K, g, p)
         # more than 16 runs: K ranges of at most 16 runs, partial sums through
@@ -355,8 +355,6 @@ def test_plan_reports_the_few_token_instance():
             assert p["workspace_bytes"] >= 64 * 1024 + splits * M * N * 4
         for (M, K, g) in ((9, 4096, 128), (16, 4096, 128), (1, 4160, 64), (1, 14336, 32), (3, 14336, 64),
                           (4, 4096, 32), (6, 14336, 128), (8, 4096, 32), (5, 14336, 64),
-                          # five to eight tokens where the general kernel keeps K whole
-                          (5, 4096, 128), (8, 4096, 128), (8, 512, 128), (7, 2560, 128),
                           # more K ranges than the general kernel's
                           (1, 28672, 32), (2, 28672, 32)):
             assert L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)["kernel"] == 0, (M, K, g)

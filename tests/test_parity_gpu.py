@@ -161,11 +161,10 @@ def _few_token_instance_expected(M, N, K, g, general_splits):
     # ranges of at most 16 runs (row tiles within the 16384 counters; one and
     # two token rows in no more K ranges than the general kernel, four token
     # rows with the grid within twice the 256 CUs, runs of 8 first and with
-    # the whole LDS, eight token rows with the grid within the 256 CUs);
-    # eight token rows only where the general kernel splits K
+    # the whole LDS, eight token rows with the grid within the 256 CUs)
     ks, tiles = K // 128, -(-N // 16)
     mt = {1: 1, 2: 2, 3: 4, 4: 4}.get(M, 8 if 5 <= M <= 8 else 0)
-    if not mt or K % 128 or (mt == 8 and general_splits == 1):
+    if not mt or K % 128:
         return False
     slots, parts = (4, 2) if mt == 8 else (mt, 4)
     a, b = (4, 8) if mt >= 4 else (8, 4)
