@@ -1126,13 +1126,15 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu
     // workspace (tiles within the counter region). Split, one and two token
     // rows pay where they need no more K ranges than the general kernel
     // (28672 x 4096: M = 1 / 2 at g128 -21 / -10 %; at g32, 4 ranges against
-    // its 2, +9 / +2 %); four token rows where the grid is at most two rounds
-    // of one workgroup per CU, trying runs of 8 first with the whole LDS of
-    // the CU (28672 x 4096 at M = 3 / 4: -8 / -10 %; 14336 x 4096 g64 at
-    // M = 4: -15 %; 20480 x 1280 g64: -14 / -16 %; 65536 x 1024 at M = 4:
-    // -39 %; in more rounds the general kernel's smaller workgroups win:
-    // 28672 x 8192 and 20480 x 5120 at M = 3, +6 / +15 %); eight token rows
-    // where every workgroup runs at once.
+    // its 2, +9 / +2 %); four and eight token rows where the grid is at most
+    // two rounds of one workgroup per CU, with the whole LDS of the CU (four
+    // rows try runs of 8 first: 28672 x 4096 at M = 3 / 4: -8 / -10 %;
+    // 14336 x 4096 g64 at M = 4: -15 %; 20480 x 1280 g64: -14 / -16 %;
+    // 65536 x 1024 at M = 4: -39 %; eight rows on 14336 x 4096 at M = 6-8:
+    // -12 %; in more rounds the general kernel's smaller workgroups win:
+    // 28672 x 8192 and 20480 x 5120 at M = 3, +6 / +15 %).  Where workgroups
+    // share CUs, each may use half the LDS (two per CU; eight tokens on
+    // 4096 x 6144 / 28672: -31 / -36 %).
     const int order_split4[4][2] = {{8, 0}, {4, 0}, {8, 1}, {4, 1}};
     for (int pass = 0; pass < (p.splits > 1 ? 2 : 1) && !p.one_kpw; ++pass) {
       for (const auto& o : (pass == 1 && mt == 4 ? order_split4 : order)) {
@@ -1145,11 +1147,11 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group, int dtype, int cu
         const int waves = (runs + splits - 1) / splits;
         if (ngw > 16 || ngw / parts > 4 || ngw * slots > 32 || (rest != 0) != (o[1] != 0) || rest % (k / parts) ||
             waves > kGemvMaxWaves || (pass == 1 && (splits < 2 || p.tiles > kMaxCounters ||
-                           (mt <= 2 ? splits > p.splits : (int64_t)p.tiles * splits > (mt == 4 ? 2 : 1) * cu_count))))
+                           (mt <= 2 ? splits > p.splits : (int64_t)p.tiles * splits > 2 * cu_count))))
           continue;
         const size_t lds = gemv_one_lds_bytes(waves, k, mt, M);
-        const size_t one_budget = (int64_t)p.tiles * splits <= cu_count || (pass == 1 && mt == 4 && k == 8)
-                                      ? kGemvLdsBudget : kGemvLdsBudgetShared;
+        const bool whole_cu = (int64_t)p.tiles * splits <= cu_count || (pass == 1 && (mt == 8 || (mt == 4 && k == 8)));
+        const size_t one_budget = whole_cu ? kGemvLdsBudget : kGemvLdsBudget / 2;
         if (lds > one_budget) continue;
         p.one_kpw = k;
         p.one_mt = mt;

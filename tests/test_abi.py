@@ -342,19 +342,20 @@ def test_plan_reports_the_few_token_instance():
         # more than 16 runs: K ranges of at most 16 runs, partial sums through
         # the workspace (counters for every row tile), only where the general
         # kernel splits K too (no new workspace need); one and two token rows
-        # in no more K ranges than it, four token rows with at most two
-        # rounds of one workgroup per CU (runs of 8 first)
+        # in no more K ranges than it, four and eight token rows with at most
+        # two rounds of one workgroup per CU (four rows try runs of 8 first)
         for (M, N, K, g, waves, splits) in ((1, 4096, 28672, 128, 14, 2), (2, 4096, 28672, 128, 14, 2),
                                             (1, 4096, 1 << 16, 128, 16, 4), (4, 1024, 1 << 16, 128, 16, 4),
                                             (3, 1280, 20480, 64, 14, 3), (4, 1280, 20480, 64, 14, 3),
                                             (3, 4096, 28672, 128, 14, 2), (4, 4096, 28672, 128, 14, 2),
-                                            (4, 4096, 14336, 64, 14, 2)):
+                                            (4, 4096, 14336, 64, 14, 2), (6, 4096, 14336, 128, 14, 2),
+                                            (8, 4096, 14336, 128, 14, 2), (5, 4096, 14336, 64, 14, 2)):
             p = L.w4a16_plan(M, N, K, g, dt, True, L.PATH_GEMV)
             assert (p["kernel"], p["waves"], p["splits"], p["launches"], p["counter_tiles"]) == \
                 (1, waves, splits, 1, N // 16), (M, N, K, g, p)
             assert p["workspace_bytes"] >= 64 * 1024 + splits * M * N * 4
         for (M, K, g) in ((9, 4096, 128), (16, 4096, 128), (1, 4160, 64), (1, 14336, 32), (3, 14336, 64),
-                          (4, 4096, 32), (6, 14336, 128), (8, 4096, 32), (5, 14336, 64),
+                          (4, 4096, 32), (8, 4096, 32),
                           # more K ranges than the general kernel's
                           (1, 28672, 32), (2, 28672, 32)):
             assert L.w4a16_plan(M, 4096, K, g, dt, True, L.PATH_GEMV)["kernel"] == 0, (M, K, g)

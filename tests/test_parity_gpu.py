@@ -159,9 +159,10 @@ def _few_token_instance_expected(M, N, K, g, general_splits):
     # budget (token rows 1, 2, 4, or 8 for five to eight); one K range of at
     # most 16 runs first, then, where the general kernel splits K too, K
     # ranges of at most 16 runs (row tiles within the 16384 counters; one and
-    # two token rows in no more K ranges than the general kernel, four token
-    # rows with the grid within twice the 256 CUs, runs of 8 first and with
-    # the whole LDS, eight token rows with the grid within the 256 CUs)
+    # two token rows in no more K ranges than the general kernel, four and
+    # eight token rows with the grid within twice the 256 CUs and the whole
+    # LDS, four rows trying runs of 8 first); half the LDS budget where
+    # workgroups share CUs
     ks, tiles = K // 128, -(-N // 16)
     mt = {1: 1, 2: 2, 3: 4, 4: 4}.get(M, 8 if 5 <= M <= 8 else 0)
     if not mt or K % 128:
@@ -174,13 +175,13 @@ def _few_token_instance_expected(M, N, K, g, general_splits):
             ngw, rest, runs = 128 * kpw // g, ks % kpw, -(-ks // kpw)
             splits = -(-runs // 16) if split_pass else 1
             waves = -(-runs // splits)
-            full = tiles * splits <= 256 or (split_pass and mt == 4 and kpw == 8)
-            budget = 160 * 1024 - 16 * 320 - 256 if full else 64 * 1024
+            full = tiles * splits <= 256 or (split_pass and (mt == 8 or (mt == 4 and kpw == 8)))
+            budget = (160 * 1024 - 16 * 320 - 256) // (1 if full else 2)
             lds = waves * (64 * mt + (M if mt == 8 else mt) * (2 * kpw * 128 + (64 if mt > 1 else 0)))
             if (ngw <= 16 and ngw // parts <= 4 and ngw * slots <= 32 and (rest != 0) == short
                     and rest % (kpw // parts) == 0 and waves <= 16 and lds <= budget
                     and (not split_pass or (splits >= 2 and tiles <= 16384 and (
-                        splits <= general_splits if mt <= 2 else tiles * splits <= (512 if mt == 4 else 256))))):
+                        splits <= general_splits if mt <= 2 else tiles * splits <= 512)))):
                 return True
     return False
 
@@ -258,7 +259,10 @@ def test_decode_single_token_unaligned_scales_fall_back():
 @pytest.mark.parametrize("M,N,K,g,splits", [(1, 264, 28672, 128, 2), (2, 520, 28672, 128, 2),
                                               (3, 136, 28672, 64, 4), (2, 136, 1 << 16, 64, 4),
                                               (1, 1048, 1 << 16, 128, 4), (4, 40, 20480, 128, 2),
-                                              (3, 520, 28672, 128, 2), (4, 264, 14336, 64, 2)])
+                                              (3, 520, 28672, 128, 2), (4, 264, 14336, 64, 2),
+                                              # eight token rows
+                                              (6, 520, 14336, 128, 2), (8, 136, 20480, 64, 3),
+                                              (7, 264, 28672, 128, 4)])
 @pytest.mark.parametrize("dt", [O.F16, O.BF16])
 def test_decode_few_token_instance_k_split(tuning_env, M, N, K, g, splits, dt):
     # more than 16 runs, where the general kernel splits K too: K ranges of at
