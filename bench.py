@@ -598,6 +598,8 @@ def run_report(path_prefix):
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{kind}_trace -o run -- "
              "python3 $R/bench.py --profile {kind} --steps {steps}",
+    "bench-trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/bench_trace -o run -- "
+                   "python3 $R/bench.py",
     "pmc": "rocprofv3 --pmc {counters} --output-format csv -d $R/gpurun_out/{kind}_pmc{tag} -o run -- "
            "python3 $R/bench.py --profile {kind} --steps {steps}",
     "traffic": "rocprofv3 --pmc {counter} --output-format csv -d $R/gpurun_out/{kind}_{counter} -o run -- "
@@ -637,17 +639,28 @@ def _median(v):
     return float(np.median(np.asarray(v, dtype=np.float64))) if len(v) else float("nan")
 
 
-def summarize_trace(kind, d, steps):
-    """Per layer of a --profile run: launches, mean and median kernel time
-    (End - Start), and GB/s (decode) or TFLOP/s (prefill) against the peak."""
+def summarize_trace(kind, d, steps, of_bench=False):
+    """Per layer of a --profile run (or, of_bench, of the bench line's own
+    run: its decode graphs rotating the weight copies): launches, mean and
+    median kernel time (End - Start), and GB/s (decode) or TFLOP/s
+    (prefill) against the peak."""
     rows = [r for r in _csv_rows(os.path.join(d, "run_kernel_trace.csv")) if "w4a16" in r["Kernel_Name"]]
+    if of_bench:
+        # the decode layers' kernels only: the prefill GEMM runs some of the
+        # same grid sizes, the expert-indexed decode instance (last template
+        # argument 1) its own
+        rows = [r for r in rows if _kernel_short(r["Kernel_Name"]).startswith("gemv_")
+                and not _kernel_short(r["Kernel_Name"]).endswith(", 1>")]
     layers = profile_layers(kind)
     unit = "GB/s" if kind == "decode" else "TFLOP/s"
     peak = HBM_PEAK_GBS if kind == "decode" else MFMA_BF16_PEAK_TFLOPS
+    cmd = PROFILE_CMDS["bench-trace"] if of_bench else PROFILE_CMDS["trace"].format(kind=kind, steps=steps)
+    what = ("every dispatch of the layer's kernel in the bench run: warmup, timed graphs and the per-launch "
+            "timing graphs" if of_bench else
+            "the first launch of each layer, outside the timed loop, included")
     lines = [f"Command (from /tmp, TMPDIR=/tmp, repository at $R):",
-             "  " + PROFILE_CMDS["trace"].format(kind=kind, steps=steps), "",
-             f"Per layer (End - Start of each dispatch of the layer's kernel; the first launch of each "
-             f"layer, outside the timed loop, included):",
+             "  " + cmd, "",
+             f"Per layer (End - Start of each dispatch of the layer's kernel; {what}):",
              f"  layer (K,N)      M     kernel grid   launches  mean_ns    median_ns   {unit}(mean)  frac of {peak:g}"]
     means = []
     for l in layers:
@@ -841,21 +854,31 @@ def perf_compare(base, now, band=1.25):
 
 
 def run_profile(kind, steps, dev):
-    """Eager launches for a profiler: each layer `steps` times in turn."""
+    """Eager launches for a profiler: each layer `steps` times in turn.  Decode
+    launches rotate through the bench's >= 1 GiB of weight copies, so that
+    every launch streams its weights from HBM as in the bench line (on one
+    copy the layer's weights would stay in the 256 MB last-level cache)."""
     import torch
     shapes, M = (DECODE_LAYERS, 1) if kind == "decode" else (PREFILL_LAYERS, 1920)
     layers = [build_layer(K, N, M, ("bench-" + kind, K, N), dev) for (K, N) in shapes]
-    fns = [Launcher(l, l["wq"], l["zp"], l["s"]) for l in layers]
+    copies = 1
+    if kind == "decode":
+        set_bytes = sum(l["wq"].numel() * 4 + l["s"].numel() * 2 + l["zp"].numel() * 4 for l in layers)
+        copies = max(2, math.ceil((1 << 30) / set_bytes))
+    pool = [[(l["wq"], l["zp"], l["s"]) for l in layers]]
+    for _ in range(copies - 1):
+        pool.append([(wq.clone(), zp.clone(), s.clone()) for (wq, zp, s) in pool[0]])
+    fns = [[Launcher(l, *pool[c][i]) for c in range(copies)] for i, l in enumerate(layers)]
     sp = torch.cuda.current_stream().cuda_stream
-    for fn in fns:
-        fn(sp)
+    for per_copy in fns:
+        per_copy[0](sp)
     torch.cuda.synchronize()
-    for fn in fns:
-        for _ in range(steps):
-            fn(sp)
+    for per_copy in fns:
+        for i in range(steps):
+            per_copy[i % copies](sp)
         torch.cuda.synchronize()
-    print(json.dumps(dict(profile=kind, M=M, layers=[f"{K}x{N}" for (K, N) in shapes], launches_per_layer=steps)),
-          flush=True)
+    print(json.dumps(dict(profile=kind, M=M, layers=[f"{K}x{N}" for (K, N) in shapes], launches_per_layer=steps,
+                          weight_copies=copies)), flush=True)
 
 
 def main():
@@ -873,12 +896,14 @@ def main():
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MB (for scaling PMC byte counters)")
     ap.add_argument("--profile", choices=("decode", "prefill"), default="",
-                    help="instead of the bench line: --steps eager launches of each decode layer (M=1) "
-                         "or prefill layer (M=1920) on one weight copy, for rocprofv3 kernel traces and "
-                         "counters (one dispatch per launch, kernels named per layer by their grid)")
+                    help="instead of the bench line: --steps eager launches of each decode layer (M=1, "
+                         "rotating the bench's >= 1 GiB of weight copies) or prefill layer (M=1920, one "
+                         "copy), for rocprofv3 kernel traces and counters (one dispatch per launch, "
+                         "kernels named per layer by their grid)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
                     help="print a profiles/ summary from rocprofv3 csv output (no GPU needed): "
-                         "'trace KIND DIR', 'pmc KIND DIR_A [DIR_B|- [DIR_C]]' or "
+                         "'trace KIND DIR' (a --profile run), 'trace decode DIR bench' (a trace of the "
+                         "bench line's own run), 'pmc KIND DIR_A [DIR_B|- [DIR_C]]' or "
                          "'traffic KIND FETCH_DIR WRITE_DIR'")
     ap.add_argument("--perf-record", default="", metavar="FILE",
                     help="measure the performance-regression points and their controls, write FILE (json)")
@@ -893,7 +918,7 @@ def main():
     if args.summarize:
         what, kind, dirs = args.summarize[0], args.summarize[1], args.summarize[2:]
         if what == "trace":
-            print(summarize_trace(kind, dirs[0], args.steps))
+            print(summarize_trace(kind, dirs[0], args.steps, of_bench=len(dirs) > 1 and dirs[1] == "bench"))
         elif what == "pmc":
             print(summarize_pmc(kind, {t: d for t, d in zip("ABC", dirs) if d != "-"}, args.steps))
         elif what == "traffic":
