@@ -853,6 +853,86 @@ def perf_compare(base, now, band=1.25):
     return out
 
 
+# Megatron-style tensor-parallel shards of the Llama-3.1-8B layers over P GPUs:
+# qkv and gate_up split by output feature (column-parallel: N/P), o and down
+# by input feature (row-parallel: K/P; their partial outputs would be summed
+# across the GPUs).  (name, K, N, split)
+SHARD_LAYERS = (("qkv", 4096, 6144, "N"), ("o", 4096, 4096, "K"), ("gate_up", 4096, 28672, "N"),
+                ("down", 14336, 4096, "K"))
+SHARD_PREFILL = ("qkv", "gate_up", "down")
+
+
+def shard_shape(K, N, split, P):
+    return (K, N // P) if split == "N" else (K // P, N)
+
+
+def run_shards(path_prefix):
+    """One GPU's share of each Llama-3.1-8B layer under P-way tensor
+    parallelism (P = 1, 2, 4, 8), at its real shape: the decode step (M = 1)
+    and the prefill layers (M = 1920), bf16 asym g128, on the path the
+    dispatcher picks, graphs rotating >= 1 GiB of weight copies.  The
+    collectives between the GPUs are not part of it.  Writes <prefix>.md and
+    <prefix>.json."""
+    import torch
+    import int4_weight_only_linear_amd as L
+    from synth import make_case
+    dev = torch.device("cuda:0")
+    side = torch.cuda.Stream()
+    g, dt = GROUP, L.W4A16_BF16
+    rows = []
+    for P in (1, 2, 4, 8):
+        for (name, K0, N0, split) in SHARD_LAYERS:
+            K, N = shard_shape(K0, N0, split, P)
+            Ms = (1, 1920) if name in SHARD_PREFILL else (1,)
+            c = make_case(max(Ms), N, K, g, dt, False, False, seed=("shard", name, P))
+            wq, zp, sc, x_all, b = _layer_tensors(c, dev)
+            wbytes = wq.numel() * 4 + sc.numel() * 2 + zp.numel() * 4
+            copies = max(2, min(64, math.ceil((1 << 30) / wbytes)))
+            pool = [(wq, zp, sc)] + [(wq.clone(), zp.clone(), sc.clone()) for _ in range(copies - 1)]
+            for M in Ms:
+                x = x_all[:M].contiguous()
+                y = torch.empty((M, N), dtype=x.dtype, device=dev)
+                ms = time_point(x, pool, b, y, M, N, K, g, dt, L.PATH_AUTO, 20 if M > 16 else 50, side)
+                plan = L.w4a16_plan(M, N, K, g, dt, True)
+                nbytes = decode_bytes(M, N, K, g)
+                rows.append(dict(P=P, layer=name, split=split, K=K, N=N, M=M, us=round(ms * 1e3, 3),
+                                 GBs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                 TFLOPs=round(2 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                                 kernel=("gemv_one" if plan["kernel"] == 1 else "gemv_small")
+                                 if M <= 16 and int(L.w4a16_select_path(M, N, K, g, dt, True)) == L.PATH_GEMV
+                                 else "gemm", waves=plan["waves"], splits=plan["splits"]))
+                print(f"[shards] P={P} {name} K={K} N={N} M={M}: {ms * 1e3:.2f} us", file=sys.stderr, flush=True)
+            del pool
+            torch.cuda.empty_cache()
+    lines = ["# One GPU's share of the Llama-3.1-8B layers under P-way tensor parallelism", "",
+             f"Command: python bench.py --shards {os.path.basename(path_prefix)}", "",
+             "qkv and gate_up split by output feature (N/P), o and down by input feature (K/P); bf16 activations,",
+             "asymmetric uint4, group 128; the path the dispatcher picks; each point the mean launch over graphs",
+             "rotating >= 1 GiB of weight copies.  The collectives between the GPUs (an all-gather after the",
+             "column-parallel layers where needed, a sum of the row-parallel partial outputs) are not measured.",
+             "Scaling = the P = 1 time / (P x this time): 1 when the share takes 1/P of the time.", "",
+             "| P | M | layer | K | N | kernel | waves | K ranges | us | GB/s | TFLOP/s |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['P']} | {r['M']} | {r['layer']} | {r['K']} | {r['N']} | {r['kernel']} | {r['waves']} | "
+                     f"{r['splits']} | {r['us']} | {r['GBs']} | {r['TFLOPs']} |")
+    lines += ["", "| P | decode step (4 layers, M = 1) us | scaling | prefill (3 layers, M = 1920) us | scaling |",
+              "|---|---|---|---|---|"]
+    tot = {}
+    for P in (1, 2, 4, 8):
+        d = sum(r["us"] for r in rows if r["P"] == P and r["M"] == 1)
+        f = sum(r["us"] for r in rows if r["P"] == P and r["M"] == 1920)
+        tot[P] = (d, f)
+    for P, (d, f) in tot.items():
+        lines.append(f"| {P} | {d:.2f} | {tot[1][0] / (P * d):.3f} | {f:.1f} | {tot[1][1] / (P * f):.3f} |")
+    with open(path_prefix + ".md", "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    with open(path_prefix + ".json", "w") as fh:
+        json.dump(dict(rows=rows, totals={str(P): dict(decode_us=d, prefill_us=f) for P, (d, f) in tot.items()}), fh,
+                  indent=1)
+    print(json.dumps(dict(shards=path_prefix + ".md", totals=tot)), flush=True)
+
+
 def run_profile(kind, steps, dev):
     """Eager launches for a profiler: each layer `steps` times in turn.  Decode
     launches rotate through the bench's >= 1 GiB of weight copies, so that
@@ -910,6 +990,10 @@ def main():
     ap.add_argument("--perf-check", default="", metavar="FILE",
                     help="measure the same points and compare with FILE, normalised by the controls; "
                          "exit 1 on a regression beyond 25%%")
+    ap.add_argument("--shards", default="", metavar="PREFIX",
+                    help="instead of the bench line: time one GPU's share of each Llama-3.1-8B layer under "
+                         "P = 1, 2, 4, 8-way tensor parallelism (decode M=1, prefill M=1920), write "
+                         "<PREFIX>.md and .json")
     ap.add_argument("--report", default="",
                     help="instead of the bench line: time every point of the decode, prefill and "
                          "dispatch-sweep workloads on both paths, write <REPORT>.md and .json")
@@ -951,6 +1035,9 @@ def main():
     import int4_weight_only_linear_amd as L  # noqa: F401  (loads libw4a16; raises if missing)
     if args.report:
         run_report(args.report)
+        return
+    if args.shards:
+        run_shards(args.shards)
         return
     if args.calibration_copy_mb:
         # a plain copy of known size: reads and writes exactly n bytes, so the

@@ -511,6 +511,28 @@ def test_config_full_size(name, li, K, N, g, sym, dt, bias):
             assert_close(y[:, rows], ref_all[:M], dt, f"M={M} path={path}")
 
 
+# ---- one GPU's share under 8-way tensor parallelism ---------------------------
+
+@pytest.mark.parametrize("layer,K,N,Ms", [
+    ("qkv", 4096, 768, (1, 5, 1920)),      # column-parallel: N / 8
+    ("o", 512, 4096, (1, 5)),              # row-parallel: K / 8 (four 128-k steps)
+    ("gate_up", 4096, 3584, (1, 5, 1920)),
+    ("down", 1792, 4096, (1, 5, 1920)),    # fourteen 128-k steps
+])
+def test_tensor_parallel_shard_shapes(layer, K, N, Ms):
+    # the Llama-3.1-8B layers' 8-way shards at their real shapes, on the
+    # path the dispatcher picks and on each kernel that serves the M; every
+    # output row against the oracle
+    c = make_case(max(Ms), N, K, 128, O.BF16, False, True, seed=("tp8", layer))
+    d = DeviceCase(c)
+    ref_all = oracle_rows(c)
+    full_x = c.x_bits
+    for M in Ms:
+        d.set_x(full_x[:M].copy())
+        for path in (AUTO,) + paths_for(M):
+            assert_close(d.run(path), ref_all[:M], O.BF16, f"{layer} M={M} path={path}")
+
+
 # ---- dequantised prefill copy: dense product over w4a16_dequant's weights -----
 
 @pytest.mark.parametrize("dt", [O.F16, O.BF16])
