@@ -368,6 +368,33 @@ def test_plan_reports_the_few_token_instance():
         assert L.w4a16_plan(64, 4096, 4096, 128, dt, True, L.PATH_GEMM)["kernel"] == 0
 
 
+def test_few_token_split_needs_no_workspace_the_general_kernel_would_not(tuning_env):
+    # the few-token instance splits K only where the general kernel splits it
+    # too, so a caller's workspace need (zero or not) is the same with the
+    # instance on or off; its launches stay within 16 waves and the counter
+    # region
+    shapes = [(M, N, K, g) for M in (1, 2, 3, 4, 5, 8) for N in (16, 136, 1024, 4096, 28672)
+              for K in (128, 1152, 4096, 9728, 14336, 20480, 28672, 1 << 16) for g in (32, 64, 128)]
+    for dt in (L.W4A16_F16, L.W4A16_BF16):
+        on = [L.w4a16_plan(M, N, K, g, dt, True, L.PATH_GEMV) for (M, N, K, g) in shapes]
+        tuning_env("W4A16_GEMV_NO_ONE", "1")
+        off = [L.w4a16_plan(M, N, K, g, dt, True, L.PATH_GEMV) for (M, N, K, g) in shapes]
+        tuning_env("W4A16_GEMV_NO_ONE", None)
+        split_seen = False
+        for shape, a, b in zip(shapes, on, off):
+            assert (a["workspace_bytes"] > 0) == (b["workspace_bytes"] > 0), (shape, a, b)
+            if a["kernel"] == 1:
+                assert 1 <= a["waves"] <= 16 and a["launches"] == 1, (shape, a)
+                if a["splits"] > 1:
+                    split_seen = True
+                    assert b["splits"] > 1 and a["counter_tiles"] == a["tiles"] <= KMAXC, (shape, a, b)
+                    M, N = shape[0], shape[1]
+                    assert a["workspace_bytes"] >= 64 * 1024 + a["splits"] * M * N * 4, (shape, a)
+            else:
+                assert a == b, (shape, a, b)
+        assert split_seen
+
+
 def test_plan_errors():
     with pytest.raises(L.W4A16Error, match="M <= 16"):
         L.w4a16_plan(17, 64, 256, 128, 1, False, L.PATH_GEMV)
