@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   // (compiled for the 128-token tile only: in the taller tiles' kernels this
   // block costs the accumulators their registers, and the planner uses the
   // two-pass form at small M only)
-  if constexpr (MB == 4) if (p.splits > 1 && p.two_pass) {
+  if constexpr (MB == 1 || MB == 4) if (p.splits > 1 && p.two_pass) {
     // plain fp32 partial sums, row-major [split][M][np]; splitk_reduce_kernel
     // adds the splits in order.  acc[rb][cb][4a + e] is token m0 + 32 rb + j,
     // feature nw0 + 32 cb + 8a + 4h + e: four consecutive features, 16 bytes.
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   }
   if (p.splits > 1) {
     constexpr int NV = MB * CB * 16;  // accumulator values per thread
-    constexpr int kChunk = 64;
+    constexpr int kChunk = NV < 64 ? NV : 64;
     static_assert(NV % kChunk == 0, "chunking");
     const size_t slot = (size_t)BM * BN / 2;  // pairs per partial tile
     auto val = [&](int q) -> float { return acc[q / (16 * CB)][(q / 16) % CB][q % 16]; };
@@ -560,17 +560,19 @@ hipError_t launch_t(const GemmParams& prm, hipStream_t s) {
   return hipGetLastError();
 }
 
-// tile shapes: 32 mb tokens x 128 cb features; cb = 1 only for mb 4 and 8
+// tile shapes: 32 mb tokens x 128 cb features; cb = 1 only for mb 1, 4 and 8
 template <int DT, int GS, bool ASYM, bool DENSE = false>
 hipError_t launch_mb(const GemmParams& prm, int mb, int cb, hipStream_t s) {
   if (cb == 1) {
     switch (mb) {
+      case 1: return launch_t<DT, GS, ASYM, 1, 1, DENSE>(prm, s);
       case 4: return launch_t<DT, GS, ASYM, 4, 1, DENSE>(prm, s);
       case 8: return launch_t<DT, GS, ASYM, 8, 1, DENSE>(prm, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (mb) {
+    case 1: return launch_t<DT, GS, ASYM, 1, 2, DENSE>(prm, s);
     case 4: return launch_t<DT, GS, ASYM, 4, 2, DENSE>(prm, s);
     case 6: return launch_t<DT, GS, ASYM, 6, 2, DENSE>(prm, s);
     case 8: return launch_t<DT, GS, ASYM, 8, 2, DENSE>(prm, s);
@@ -622,6 +624,50 @@ bool wide_tall_tile_spills(int group, int dtype, bool asym) {
   return group == 32 && !asym;
 }
 
+// Up to 64 tokens: 32-token tiles of 128 features (the weights of a tile
+// are dequantised once for at most 32 tokens, so at small M the matrix cores
+// no longer multiply up to 96 padding rows of a 128-token tile).  A lone
+// unit's k-step waits on memory (the pipeline prefetches one k-step), so K
+// is split until enough units are resident; time model in microseconds,
+// fitted to every K split (1-16, both hand-off forms) at M = 16 and 48 on
+// six Llama-shaped layers (mean error 9 %, its picks within 0-8 % of the
+// best):  0.834 * k-steps per unit * max(1, units / 384) + partial-sum
+// traffic (0.257 us per MB two-pass, 0.480 one-pass) + 7.93.  Measured
+// against the 128-token tiles' plans: M = 9-32 -15 to -31 % on eight layers
+// (Llama and Qwen shapes, fp16 and bf16, groups 32 and 128); M = 48 / 64
+// -1 to -15 % where K <= 16384, +9 / +11 % on 28672 x 4096 (there the
+// 128-token tiles keep M > 32).
+static GemmPlan plan_gemm_thin(int64_t M, int64_t N, int64_t K) {
+  GemmPlan best{};
+  double best_t = 0.0;
+  const int nsteps = (int)((K + kBK - 1) / kBK);
+  const int64_t tiles_n = (N + 127) / 128;
+  const int64_t tiles = ((M + 31) / 32) * tiles_n;
+  for (int splits = 1; splits <= 16 && splits <= nsteps; ++splits) {
+    const int sps = (nsteps + splits - 1) / splits;
+    if ((nsteps + sps - 1) / sps != splits) continue;
+    const int64_t units = tiles * splits;
+    const double resident = units > 384 ? (double)units / 384.0 : 1.0;
+    const double part_mb = splits > 1 ? (double)splits * (double)M * (double)N * 4.0 / 1e6 : 0.0;
+    for (int tp = 0; tp < (splits > 1 ? 2 : 1); ++tp) {
+      if (tp == 0 && splits > 1 && tiles > kMaxCounters) continue;
+      const double t = 0.834 * sps * resident + (tp ? 0.257 : 0.480) * part_mb + 7.93 - 0.02 * tp;
+      if (best.units == 0 || t < best_t) {
+        best_t = t;
+        best.mb = 1;
+        best.cb = 1;
+        best.splits = splits;
+        best.steps_per_split = sps;
+        best.tiles_n = (int)tiles_n;
+        best.tiles = (int)tiles;
+        best.units = (int)units;
+        best.two_pass = tp == 1;
+      }
+    }
+  }
+  return best;
+}
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym, int cu_count,
                    bool dense) {
   GemmPlan best{};
@@ -631,9 +677,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool a
   // 128-token wide tile by 1-20 % for those combinations
   const int cb_order[2] = {tall_wide_ok ? 2 : 1, tall_wide_ok ? 1 : 2};
   double best_cost = 0.0;
+  // (the dense instances too: the same tiles and splits)
+  const bool thin = M <= 32 || (M <= 64 && K <= 16384);
+  if (thin) best = plan_gemm_thin(M, N, K);
   const int nsteps = (int)((K + kBK - 1) / kBK);
   const int cus = cu_count > 0 ? cu_count : 256;
   for (int cb : cb_order) {
+    if (thin) break;
     const int64_t bn = 128 * cb;
     const int64_t tiles_n = (N + bn - 1) / bn;
     for (int mb : {8, 6, 4}) {
@@ -686,8 +736,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool a
     const int mb = tu.gemm_tile[0], splits = tu.gemm_tile[1];
     const int tp = tu.gemm_tile_n >= 3 ? tu.gemm_tile[2] : 0;
     const int cb = tu.gemm_tile_n >= 4 ? tu.gemm_tile[3] : 2;
-    if ((mb == 4 || mb == 6 || mb == 8) &&
-        (cb == 2 || (cb == 1 && mb != 6)) && splits >= 1 && splits <= nsteps && (tp == 0 || mb == 4)) {
+    if ((mb == 1 || mb == 4 || mb == 6 || mb == 8) &&
+        (cb == 2 || (cb == 1 && mb != 6)) && splits >= 1 && splits <= nsteps && (tp == 0 || mb == 1 || mb == 4)) {
       const int sps = (nsteps + splits - 1) / splits;
       const int64_t tiles_n = (N + 128 * cb - 1) / (128 * cb);
       const int64_t tiles = ((M + 32 * mb - 1) / (32 * mb)) * tiles_n;
@@ -746,7 +796,7 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
   prm.steps_per_split = plan.steps_per_split;
   prm.vec_store = (a.N % 8 == 0) && (reinterpret_cast<uintptr_t>(a.y) % 16 == 0);
   prm.two_pass = plan.splits > 1 && plan.two_pass;
-  if (prm.two_pass && plan.mb != 4) return hipErrorInvalidConfiguration;
+  if (prm.two_pass && plan.mb != 1 && plan.mb != 4) return hipErrorInvalidConfiguration;
   prm.np = (int)((a.N + 7) / 8 * 8);
   hipError_t e;
   if (a.dense)

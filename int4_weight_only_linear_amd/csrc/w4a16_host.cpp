@@ -208,24 +208,25 @@ GroupMap group_map(int32_t g, int64_t K) {
 // Decode-kernel threshold.  The pages route M <= 5 to their skinny kernel
 // (tuned on RDNA).  Measured on MI355X (both kernels timed per launch over
 // graphs rotating >= 1 GiB of weights; groups 32/64/128, symmetric and
-// asymmetric, fp16 and bf16): the decode kernel is faster at every M <= 8.
-// Above that it takes one k-step per wave and splits K when K > 16 * 128, and
-// the GEMM overtakes it depending on the layer:
+// asymmetric, fp16 and bf16): the decode kernel is faster at every M <= 8
+// (at K = 28672 within 1-3 % of the GEMM's 32-token tiles at M = 8).  Above
+// that it takes one k-step per wave and splits K when K > 16 * 128, and the
+// GEMM (32-token tiles up to M = 32) overtakes it depending on the layer:
 //   K = 28672:              the GEMM from M = 9 (every sweep combination);
-//   K = 14336 (N = 4096):   decode still 21-28 % faster at M = 10 and 12,
-//                           the GEMM faster at 16;
-//   K = 4096, groups of 128, N >= 14336 (>= 896 row tiles): the GEMM 5-20 %
-//                           faster from M = 10;
-//   K = 4096 otherwise (N = 6144 at every group, N = 14336 and 28672 with
-//                           groups of 32 or 64): decode faster through M = 16
-//                           (within 2 % at two points).
+//   K = 14336 (N = 4096):   within 1 % at M = 9 and 12, the GEMM 35 %
+//                           faster at 16;
+//   K = 4096, N >= 14336 (>= 896 row tiles): the GEMM faster from M = 9 at
+//                           every group (fp16 groups of 32: -11 to -18 % at
+//                           M = 9-16, the one tie at 16 with zero points);
+//   K = 4096, N < 14336:    decode faster through M = 16 (within 3 % at
+//                           M = 12 on 4096 x 6144).
 int64_t gemv_threshold(int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t has_zp) {
-  (void)dtype; (void)has_zp;
+  (void)group; (void)dtype; (void)has_zp;
   const int v = w4a16::tuning().m_threshold;
   if (v >= 0 && v <= W4A16_GEMV_MAX_M) return v;
   if (K > 16384) return 8;
   if (K > 4096) return 12;
-  if (group >= 128 && N >= 14336) return 8;
+  if (N >= 14336) return 8;
   return 16;
 }
 

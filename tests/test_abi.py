@@ -170,14 +170,15 @@ def test_select_path_by_m():
     # K <= 4096: the decode kernel up to M = 16 ...
     for M in (1, 2, 5, 8, 9, 16):
         assert sel(M, 4096, 4096) == L.PATH_GEMV
-        assert sel(M, 14336, 4096, 32) == L.PATH_GEMV
+        assert sel(M, 6144, 4096, 32) == L.PATH_GEMV
     for M in (17, 32, 65, 128, 1920):
         assert sel(M, 4096, 4096) == L.PATH_GEMM
-    # ... except groups of 128 on 896 or more row tiles: up to M = 8
-    for M in (1, 8):
-        assert sel(M, 14336, 4096) == L.PATH_GEMV
-    for M in (9, 16):
-        assert sel(M, 14336, 4096) == L.PATH_GEMM
+    # ... except on 896 or more row tiles (any group): up to M = 8
+    for g in (32, 64, 128):
+        for M in (1, 8):
+            assert sel(M, 14336, 4096, g) == L.PATH_GEMV
+        for M in (9, 16):
+            assert sel(M, 14336, 4096, g) == L.PATH_GEMM
     # 4096 < K <= 16384: up to M = 12; longer K: up to M = 8
     for M in (1, 5, 8, 12):
         assert sel(M, 4096, 14336) == L.PATH_GEMV

@@ -703,6 +703,33 @@ def test_gemm_k_split_forms(tuning_env, dt, tile, M, N, K, g, bias):
     assert np.array_equal(d.run(GEMM), y1), "split-K result changed between runs"
 
 
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+@pytest.mark.parametrize("tile", ["1,1,0,1", "1,3,0,1", "1,5,1,1", "1,2,0", "1,4,1", "1,9,1,1"])
+@pytest.mark.parametrize("M,N,K,g,sym,bias", [(1, 200, 1216, 32, False, True), (17, 264, 2048, 64, True, False),
+                                              (33, 13, 1152, 128, True, True), (64, 520, 4096, 128, False, False)])
+def test_gemm_thin_tiles(tuning_env, dt, tile, M, N, K, g, sym, bias):
+    # 32-token tiles (128 or 256 features): one K range, the last-workgroup
+    # hand-off and the two-pass form; ragged N, K tails, one token and M past
+    # a tile; against the oracle, twice bit-identical
+    tuning_env("W4A16_GEMM_TILE", tile)
+    plan = L.w4a16_plan(M, N, K, g, dt, not sym, GEMM)
+    assert plan["tile_tokens"] == 32, plan
+    c = make_case(M, N, K, g, dt, sym, bias, seed=("thin", M, N, K, g, dt, sym, bias))
+    d = DeviceCase(c)
+    y1 = d.run(GEMM)
+    assert_close(y1, oracle_rows(c), dt, f"GEMM tile {tile}")
+    assert np.array_equal(d.run(GEMM), y1), "split-K result changed between runs"
+
+
+def test_gemm_planner_takes_thin_tiles_up_to_64_tokens():
+    # 32-token tiles up to M = 32, and to M = 64 where K <= 16384
+    for (K, N) in ((4096, 14336), (28672, 4096), (4096, 6144), (14336, 4096)):
+        for M in (1, 9, 16, 32, 48, 64):
+            thin = M <= 32 or K <= 16384
+            assert (L.w4a16_plan(M, N, K, 128, O.BF16, True, GEMM)["tile_tokens"] == 32) == thin, (M, N, K)
+        assert L.w4a16_plan(65, N, K, 128, O.BF16, True, GEMM)["tile_tokens"] >= 128
+
+
 # ---- graph capture: every entry point replays to its eager result --------------
 
 def _graph_replays_match(run_eager, run_captured, reps=3):
