@@ -91,6 +91,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   // the latter)
   __shared__ __attribute__((aligned(1024))) unsigned char xs0[XBUF];
   __shared__ __attribute__((aligned(1024))) unsigned char xs1[XBUF];
+  // 32-token tiles prefetch two k-steps ahead: a third x buffer
+  __shared__ __attribute__((aligned(1024))) unsigned char xs2[MB == 1 ? XBUF : 16];
   __shared__ uint32_t last_flag;
 
   const int tid = threadIdx.x;
@@ -295,6 +297,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
+  // 32-token tiles: the step after next has issued its metadata, then its
+  // WP * CB weight loads and NDMA x loads, each one instruction and the last
+  // vector memory instructions before this barrier; waiting until at most
+  // those are outstanding leaves them in flight and covers everything older
+  // (the next step's loads and x pieces)
+  constexpr int kKeep = WP * CB + NDMA;
+  static_assert(kKeep < 64, "vmcnt");
+  auto step_barrier_keep = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    // vmcnt(kKeep) (bits 3:0 and 15:14), expcnt any, lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt((kKeep & 15) | ((kKeep >> 4) << 14) | (7 << 4));
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // One complete k-step, software pipelined: the x fragments and dequantised
   // weights of k-sub ks + 1 are produced while the MFMAs of ks run, and the
@@ -307,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   // are produced while the last MFMAs of this one run.  On the last step
   // nbuf / nr hold valid but unused data and the prefetch is simply wasted.
   auto compute = [&](const lds_u8* buf, const StepRegs& r, const lds_u8* nbuf,
-                     const StepRegs& nr, auto&& issue) {
+                     const StepRegs& nr, auto&& issue, auto&& barrier) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int c = ks & 1, nx = c ^ 1;
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
         xfrags(buf, ks + 1, b[nx]);
         weights(r, gc, ks + 1, a[nx]);
       } else {
-        step_barrier();
+        barrier();
         group_consts(nr, gc);
         xfrags(nbuf, 0, b[nx]);
         weights(nr, gc, 0, a[nx]);
@@ -372,6 +388,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     return n;
   };
   auto no_issue = [](int) -> int { return 0; };
+  // 32-token tiles: the step after next, all at the first k-sub, in the
+  // order step_barrier_keep's count relies on (metadata, weights, x pieces)
+  auto issue_deep = [&](int ks, int sn, lds_u8* buf, StepRegs& r) -> int {
+    if (ks == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_meta(sn, r);
+      __builtin_amdgcn_sched_barrier(0);
+      load_full(sn, r);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_x(sn, buf, false, 0, NDMA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return 0;
+  };
 
   // ---- main loop over complete runs, two steps per iteration so that each
   // LDS buffer and register set is a compile-time choice; the loop has no
@@ -380,7 +410,48 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   StepRegs ra = {}, rb_ = {};
   int s = s_begin;
   const int nfull = s_full_end - s_begin;
-  if (nfull > 0) {
+  if constexpr (MB == 1) {
+    // 32-token tiles: three x buffers and register sets, the loads of step
+    // s + 2 issued during step s (a thin tile's k-step is shorter than a
+    // memory round trip); steps past the range reload the last one into the
+    // free set (never used)
+    StepRegs rc_ = {};
+    lds_u8* const buf2 = (lds_u8*)xs2;
+    if (nfull > 0) {
+      stage_x(s, buf0, false, 0, NDMA);
+      load_full(s, ra);
+      load_meta(s, ra);
+      issue_deep(0, min(s + 1, s_full_end - 1), buf1, rb_);
+      step_barrier_keep();  // step s landed everywhere; s + 1 may be in flight
+      group_consts(ra, gc);
+      xfrags(buf0, 0, b[0]);
+      weights(ra, gc, 0, a[0]);
+      int left = nfull;
+      for (; left >= 3; left -= 3) {
+        compute(buf0, ra, buf1, rb_, [&](int ks) { return issue_deep(ks, min(s + 2, s_full_end - 1), buf2, rc_); },
+                step_barrier_keep);
+        ++s;
+        compute(buf1, rb_, buf2, rc_, [&](int ks) { return issue_deep(ks, min(s + 2, s_full_end - 1), buf0, ra); },
+                step_barrier_keep);
+        ++s;
+        compute(buf2, rc_, buf0, ra, [&](int ks) { return issue_deep(ks, min(s + 2, s_full_end - 1), buf1, rb_); },
+                step_barrier_keep);
+        ++s;
+      }
+      // the last one or two steps issue nothing and wait for everything at
+      // their barrier (loads whose registers are never read again may be
+      // dropped by the compiler, which would upset a partial count)
+      if (left >= 1) {
+        compute(buf0, ra, buf1, rb_, no_issue, step_barrier);
+        ++s;
+      }
+      if (left >= 2) {
+        compute(buf1, rb_, buf2, rc_, no_issue, step_barrier);
+        ++s;
+      }
+      wait_vm_all();  // no prefetch in flight (into LDS or registers) past the loop
+    }
+  } else if (nfull > 0) {
     stage_x(s, buf0, false, 0, NDMA);
     load_full(s, ra);
     load_meta(s, ra);
@@ -389,16 +460,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     xfrags(buf0, 0, b[0]);
     weights(ra, gc, 0, a[0]);
     for (int it = 0; it < (nfull >> 1); ++it) {
-      compute(buf0, ra, buf1, rb_, [&](int ks) { return issue_next(ks, s + 1, buf1, rb_); });
+      compute(buf0, ra, buf1, rb_, [&](int ks) { return issue_next(ks, s + 1, buf1, rb_); }, step_barrier);
       ++s;
       // after the last pair there is no next step: load a valid one into the
       // free buffer instead of branching (never used)
       const int sn = min(s + 1, s_full_end - 1);
-      compute(buf1, rb_, buf0, ra, [&](int ks) { return issue_next(ks, sn, buf0, ra); });
+      compute(buf1, rb_, buf0, ra, [&](int ks) { return issue_next(ks, sn, buf0, ra); }, step_barrier);
       ++s;
     }
     if (nfull & 1) {
-      compute(buf0, ra, buf1, rb_, no_issue);
+      compute(buf0, ra, buf1, rb_, no_issue, step_barrier);
       ++s;
     }
   }
@@ -626,17 +697,18 @@ bool wide_tall_tile_spills(int group, int dtype, bool asym) {
 
 // Up to 64 tokens: 32-token tiles of 128 features (the weights of a tile
 // are dequantised once for at most 32 tokens, so at small M the matrix cores
-// no longer multiply up to 96 padding rows of a 128-token tile).  A lone
-// unit's k-step waits on memory (the pipeline prefetches one k-step), so K
-// is split until enough units are resident; time model in microseconds,
-// fitted to every K split (1-16, both hand-off forms) at M = 16 and 48 on
-// six Llama-shaped layers (mean error 9 %, its picks within 0-8 % of the
-// best):  0.834 * k-steps per unit * max(1, units / 384) + partial-sum
-// traffic (0.257 us per MB two-pass, 0.480 one-pass) + 7.93.  Measured
-// against the 128-token tiles' plans: M = 9-32 -15 to -31 % on eight layers
+// no longer multiply up to 96 padding rows of a 128-token tile).  A thin
+// tile's k-step is shorter than a memory round trip, so it prefetches two
+// k-steps (the kernel's MB == 1 loop) and K is split until enough units are
+// resident; time model in microseconds, fitted to every K split (1-16, both
+// hand-off forms) at M = 16 and 48 on six Llama-shaped layers (mean error
+// 10 %, its picks within 0-7 % of the best, 2.4 % on average):
+// 0.457 * k-steps per unit * max(1, units / 192) + partial-sum traffic
+// (0.166 us per MB two-pass, 0.382 one-pass) + 7.76 (+ 0.19 two-pass).
+// Against the 128-token tiles' plans: M = 9-32 -15 to -33 % on eight layers
 // (Llama and Qwen shapes, fp16 and bf16, groups 32 and 128); M = 48 / 64
-// -1 to -15 % where K <= 16384, +9 / +11 % on 28672 x 4096 (there the
-// 128-token tiles keep M > 32).
+// lower where K <= 16384; 28672 x 4096 keeps the 128-token tiles above
+// M = 32 (a tie at M = 48).
 static GemmPlan plan_gemm_thin(int64_t M, int64_t N, int64_t K) {
   GemmPlan best{};
   double best_t = 0.0;
@@ -647,11 +719,11 @@ static GemmPlan plan_gemm_thin(int64_t M, int64_t N, int64_t K) {
     const int sps = (nsteps + splits - 1) / splits;
     if ((nsteps + sps - 1) / sps != splits) continue;
     const int64_t units = tiles * splits;
-    const double resident = units > 384 ? (double)units / 384.0 : 1.0;
+    const double resident = units > 192 ? (double)units / 192.0 : 1.0;
     const double part_mb = splits > 1 ? (double)splits * (double)M * (double)N * 4.0 / 1e6 : 0.0;
     for (int tp = 0; tp < (splits > 1 ? 2 : 1); ++tp) {
       if (tp == 0 && splits > 1 && tiles > kMaxCounters) continue;
-      const double t = 0.834 * sps * resident + (tp ? 0.257 : 0.480) * part_mb + 7.93 - 0.02 * tp;
+      const double t = 0.457 * sps * resident + (tp ? 0.166 : 0.382) * part_mb + 7.76 + 0.19 * tp;
       if (best.units == 0 || t < best_t) {
         best_t = t;
         best.mb = 1;

@@ -209,25 +209,26 @@ GroupMap group_map(int32_t g, int64_t K) {
 // (tuned on RDNA).  Measured on MI355X (both kernels timed per launch over
 // graphs rotating >= 1 GiB of weights; groups 32/64/128, symmetric and
 // asymmetric, fp16 and bf16): the decode kernel is faster at every M <= 8
-// (at K = 28672 within 1-3 % of the GEMM's 32-token tiles at M = 8).  Above
-// that it takes one k-step per wave and splits K when K > 16 * 128, and the
-// GEMM (32-token tiles up to M = 32) overtakes it depending on the layer:
-//   K = 28672:              the GEMM from M = 9 (every sweep combination);
-//   K = 14336 (N = 4096):   within 1 % at M = 9 and 12, the GEMM 35 %
-//                           faster at 16;
-//   K = 4096, N >= 14336 (>= 896 row tiles): the GEMM faster from M = 9 at
-//                           every group (fp16 groups of 32: -11 to -18 % at
-//                           M = 9-16, the one tie at 16 with zero points);
-//   K = 4096, N < 14336:    decode faster through M = 16 (within 3 % at
-//                           M = 12 on 4096 x 6144).
+// (at K = 28672 within 1-3 % of the GEMM at M = 8).  Above that it takes one
+// k-step per wave and the GEMM (32-token tiles up to M = 32) overtakes it by
+// layer size:
+//   K = 28672, and K = 14336 / 9728 from 32 M weights (14336 x 4096): the
+//                           GEMM from M = 9 (-11 % there at M = 9-12);
+//   K = 9728 x 2560:        decode through M = 12, the GEMM from 14;
+//   K <= 4096, N >= 14336:  the GEMM from M = 9 at every group;
+//   K <= 4096, 4096 x 6144: decode at M = 9, the GEMM 13-16 % faster at
+//                           M = 10-14, a tie at 16;
+//   K <= 4096, smaller (4096 x 4096, 4096 x 2560, 2560 x 6144): decode
+//                           through M = 16.
 int64_t gemv_threshold(int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t has_zp) {
   (void)group; (void)dtype; (void)has_zp;
   const int v = w4a16::tuning().m_threshold;
   if (v >= 0 && v <= W4A16_GEMV_MAX_M) return v;
+  const int64_t weights = N * K;
   if (K > 16384) return 8;
-  if (K > 4096) return 12;
+  if (K > 4096) return weights >= (int64_t(32) << 20) ? 8 : 12;
   if (N >= 14336) return 8;
-  return 16;
+  return weights >= (int64_t(20) << 20) ? 9 : 16;
 }
 
 w4a16_path resolve_path(int64_t M, int64_t N, int64_t K, int32_t group, int32_t dtype,

@@ -167,27 +167,30 @@ def test_zero_point_dtype_message_is_the_pages():
 
 def test_select_path_by_m():
     sel = lambda M, N, K, g=128: L.w4a16_select_path(M, N, K, g, 1, 1)
-    # K <= 4096: the decode kernel up to M = 16 ...
-    for M in (1, 2, 5, 8, 9, 16):
-        assert sel(M, 4096, 4096) == L.PATH_GEMV
-        assert sel(M, 6144, 4096, 32) == L.PATH_GEMV
-    for M in (17, 32, 65, 128, 1920):
-        assert sel(M, 4096, 4096) == L.PATH_GEMM
-    # ... except on 896 or more row tiles (any group): up to M = 8
+    # the decode kernel up to M = 8 everywhere
+    for (N, K) in ((4096, 4096), (6144, 4096), (14336, 4096), (4096, 14336), (2560, 9728), (4096, 28672)):
+        for M in (1, 5, 8):
+            assert sel(M, N, K) == L.PATH_GEMV, (M, N, K)
+    # K <= 4096: up to M = 16 below 20 M weights, 9 above, 8 on N >= 14336 (any group)
+    for (N, K) in ((4096, 4096), (2560, 4096), (6144, 2560)):
+        for M in (9, 16):
+            assert sel(M, N, K) == L.PATH_GEMV, (M, N, K)
+        assert sel(17, N, K) == L.PATH_GEMM
+    assert sel(9, 6144, 4096) == L.PATH_GEMV and sel(10, 6144, 4096) == L.PATH_GEMM
     for g in (32, 64, 128):
-        for M in (1, 8):
-            assert sel(M, 14336, 4096, g) == L.PATH_GEMV
+        assert sel(8, 14336, 4096, g) == L.PATH_GEMV
         for M in (9, 16):
             assert sel(M, 14336, 4096, g) == L.PATH_GEMM
-    # 4096 < K <= 16384: up to M = 12; longer K: up to M = 8
-    for M in (1, 5, 8, 12):
-        assert sel(M, 4096, 14336) == L.PATH_GEMV
-    for M in (13, 16, 32, 1920):
+    # 4096 < K <= 16384: up to M = 12 below 32 M weights, 8 above; longer K: 8
+    for M in (9, 12):
+        assert sel(M, 2560, 9728) == L.PATH_GEMV
+    for M in (13, 16):
+        assert sel(M, 2560, 9728) == L.PATH_GEMM
+    for M in (9, 12, 16, 1920):
         assert sel(M, 4096, 14336) == L.PATH_GEMM
-    for M in (1, 8):
-        assert sel(M, 4096, 28672) == L.PATH_GEMV
-    for M in (9, 12, 16):
         assert sel(M, 4096, 28672) == L.PATH_GEMM
+    for M in (17, 32, 65, 128, 1920):
+        assert sel(M, 4096, 4096) == L.PATH_GEMM
 
 
 def test_select_path_env_override(tuning_env):
