@@ -701,10 +701,11 @@ bool wide_tall_tile_spills(int group, int dtype, bool asym) {
 // tile's k-step is shorter than a memory round trip, so it prefetches two
 // k-steps (the kernel's MB == 1 loop) and K is split until enough units are
 // resident; time model in microseconds, fitted to every K split (1-16, both
-// hand-off forms) at M = 16 and 48 on six Llama-shaped layers (mean error
-// 10 %, its picks within 0-7 % of the best, 2.4 % on average):
-// 0.457 * k-steps per unit * max(1, units / 192) + partial-sum traffic
-// (0.166 us per MB two-pass, 0.382 one-pass) + 7.76 (+ 0.19 two-pass).
+// hand-off forms) at M = 16 and 48 on ten Llama- and Qwen-shaped layers
+// (K 2560-28672; mean error 6 %, its picks 3.6 % from the best on average,
+// 18 % at worst): 0.528 * k-steps per unit * max(1, units / 224) +
+// 0.528 per extra K range + partial-sum traffic (0.108 us per MB two-pass,
+// 0.314 one-pass) + 4.91 (- 0.06 two-pass).
 // Against the 128-token tiles' plans: M = 9-32 -15 to -33 % on eight layers
 // (Llama and Qwen shapes, fp16 and bf16, groups 32 and 128); M = 48 / 64
 // lower where K <= 16384; 28672 x 4096 keeps the 128-token tiles above
@@ -719,11 +720,12 @@ static GemmPlan plan_gemm_thin(int64_t M, int64_t N, int64_t K) {
     const int sps = (nsteps + splits - 1) / splits;
     if ((nsteps + sps - 1) / sps != splits) continue;
     const int64_t units = tiles * splits;
-    const double resident = units > 192 ? (double)units / 192.0 : 1.0;
+    const double resident = units > 224 ? (double)units / 224.0 : 1.0;
     const double part_mb = splits > 1 ? (double)splits * (double)M * (double)N * 4.0 / 1e6 : 0.0;
     for (int tp = 0; tp < (splits > 1 ? 2 : 1); ++tp) {
       if (tp == 0 && splits > 1 && tiles > kMaxCounters) continue;
-      const double t = 0.457 * sps * resident + (tp ? 0.166 : 0.382) * part_mb + 7.76 + 0.19 * tp;
+      const double t = 0.528 * sps * resident + 0.528 * (splits - 1) + (tp ? 0.108 : 0.314) * part_mb + 4.91 -
+                       0.06 * tp;
       if (best.units == 0 || t < best_t) {
         best_t = t;
         best.mb = 1;
