@@ -758,6 +758,9 @@ def _graph_replays_match(run_eager, run_captured, reps=3):
     (130, 200, 640, 64, GEMM, "4,3,0"),      # GEMM, last-workgroup hand-off
     (128, 264, 1216, 32, GEMM, "4,4,1"),     # GEMM, two-pass split
     (300, 520, 1024, 128, GEMM, None),       # GEMM, no split
+    (2, 1048, 28672, 128, GEMV, None),       # decode, few-token instance with a K split
+    (17, 264, 2048, 64, GEMM, "1,3,0,1"),    # GEMM 32-token tiles, last-workgroup hand-off
+    (33, 520, 4096, 128, GEMM, "1,5,1,1"),   # GEMM 32-token tiles, two-pass split
 ])
 def test_graph_capture_linear(tuning_env, M, N, K, g, path, tile):
     if tile:
@@ -805,6 +808,8 @@ CANARY8 = 0xA5
     (3, 40, 20480, 32, GEMV, None, 5),         # decode, K split, incomplete tile
     (300, 520, 1024, 128, GEMM, None, 64),     # GEMM, no split, 16-byte stores
     (130, 200, 640, 64, GEMM, "4,3,0", 3),     # GEMM, last-workgroup hand-off, element stores
+    (17, 264, 2048, 64, GEMM, "1,3,0,1", 3),   # GEMM 32-token tiles, hand-off, element stores
+    (40, 13, 1152, 128, GEMM, "1,5,1,1", 7),   # GEMM 32-token tiles, two-pass, N not a multiple of 8
     (128, 264, 1216, 32, GEMM, "4,4,1", 64),   # GEMM, two-pass split
     (129, 13, 256, 64, GEMM, "4,2,1", 7),      # GEMM, two-pass, N not a multiple of 8
 ])
