@@ -55,6 +55,8 @@ PAIRS = [
     ((128, 4096, 4096, 128, O.BF16, False, False), (130, 200, 640, 64, O.F16, False, True)),
     # a plan with no split (no scratch), then a split decode
     ((1, 4096, 4096, 128, O.BF16, False, False), (5, 40, 9728, 64, O.BF16, False, True)),
+    # the GEMM's 32-token tiles with a K split, then a smaller one
+    ((40, 4096, 14336, 128, O.BF16, False, True), (17, 264, 2048, 64, O.F16, True, False)),
 ]
 
 
