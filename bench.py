@@ -497,6 +497,14 @@ def run_report(path_prefix):
                             copies = max(2, min(64, math.ceil((1 << 30) / wbytes)))
                             pool = [(wq, zp, s)] + [(wq.clone(), None if zp is None else zp.clone(), s.clone())
                                                     for _ in range(copies - 1)]
+                            # decode layers: a plain streaming read of the same packed weight
+                            # copies, the rate a kernel that only reads them reaches
+                            t_read = None
+                            if name.endswith("_decode"):
+                                from int4_weight_only_linear_amd import ceilings as C
+                                sink = torch.zeros(16, dtype=torch.int32, device=dev)
+                                t_read = graph_launch_ms([lambda sp, w=w: C.stream_read(w, sink, sp)
+                                                          for (w, _, _) in pool], side)
                             for M in cfg.Ms:
                                 x = x_all[:M].contiguous()
                                 y = torch.empty((M, N), dtype=x.dtype, device=dev)
@@ -520,6 +528,9 @@ def run_report(path_prefix):
                                                      TFLOPs=round(tfl, 1),
                                                      mfma_frac=round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
                                                      roofline_frac=round(frac, 4)))
+                                    if t_read is not None:
+                                        rows[-1]["read_us"] = round(t_read * 1e3, 3)
+                                        rows[-1]["of_read"] = round(t_read / ms, 3)
                             # the oracle on the same case: unpack + exact dequant once,
                             # then its fp64 product for each M
                             wq_o = O.pack_weights(c.q)
@@ -576,15 +587,17 @@ def run_report(path_prefix):
                 "2.5 PFLOP/s.  auto (*) marks the kernel W4A16_PATH_AUTO picks.  Oracle: the CPU oracle\n"
                 f"on this host ({cores} cores, BLAS on all of them): unpack + exact dequantisation of the\n"
                 "layer (deq, once per weight) + its fp64 product at this M (gemm); x = GPU speedup over\n"
-                "deq + gemm.\n\n")
+                "deq + gemm.  read us: a plain streaming read of the same packed weight copies (decode\n"
+                "layers; the rate a kernel that only reads them reaches); of read = read us / us.\n\n")
         f.write("| config | K | N | M | g | quant | dtype | bias | path | auto | us | GB/s | %HBM | TFLOP/s | "
-                "%MFMA | oracle deq ms | oracle gemm ms | x |\n")
-        f.write("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+                "%MFMA | read us | of read | oracle deq ms | oracle gemm ms | x |\n")
+        f.write("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:
             f.write(f"| {r['config']} | {r['K']} | {r['N']} | {r['M']} | {r['group']} | {r['quant']} | "
                     f"{r['dtype']} | {'y' if r['bias'] else 'n'} | {r['path']} | {'*' if r['auto'] else ''} | "
                     f"{r['us']} | {r['GBs']} | {100 * r['hbm_frac']:.1f} | {r['TFLOPs']} | "
-                    f"{100 * r['mfma_frac']:.1f} | {r.get('oracle_dequant_ms', '')} | "
+                    f"{100 * r['mfma_frac']:.1f} | {r.get('read_us', '')} | {r.get('of_read', '')} | "
+                    f"{r.get('oracle_dequant_ms', '')} | "
                     f"{r.get('oracle_gemm_ms', '')} | {r.get('speedup_vs_oracle', '')} |\n")
         f.write("\n| K | N | g | quant | dtype | M* (largest M where the decode kernel is faster) |\n")
         f.write("|---|---|---|---|---|---|\n")
