@@ -196,6 +196,13 @@ typedef struct w4a16_plan_info {
                               16-byte aligned), 0 the general decode kernel;
                               GEMM: 0 */
   uint64_t workspace_bytes; /* equals w4a16_workspace_size */
+  /* GEMM tail launch (0 when there is none): the tiles past the last full
+     round of workgroups (K unsplit) run as a second launch of tiles half as
+     tall, tail_tile_tokens x tail_tile_features, tail_tiles of them (two per
+     tile; halves wholly past M included, they exit at once) */
+  int32_t tail_tile_tokens;
+  int32_t tail_tile_features;
+  int64_t tail_tiles;
 } w4a16_plan_info;
 
 w4a16_status w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t dtype,

@@ -66,7 +66,8 @@ class PlanInfo(ctypes.Structure):
                 ("tiles", ctypes.c_int64), ("counter_tiles", ctypes.c_int64),
                 ("launches", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("two_pass", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("tail_tile_tokens", ctypes.c_int32),
+                ("tail_tile_features", ctypes.c_int32), ("tail_tiles", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -31,6 +31,8 @@
 //   epilogue, with each lane's A fragments loaded straight from w's rows
 //   (eight 16-byte loads per column block and k-step) instead of unpacked
 //   from codes.
+#include <algorithm>
+
 #include "w4a16_device.hpp"
 #include "w4a16_internal.h"
 
@@ -61,8 +63,11 @@ struct GemmParams {
   int wpr;             // words per weight row, K / 8
   int nsteps;          // ceil(K / 128)
   int full_steps;      // K / 128: steps over complete (transposed) runs
-  int tiles_n;         // ceil(N / (128 * CB))
-  int units;           // tiles * splits = grid size
+  int tiles_n;         // tiles per row of the plan's tile grid
+  int units;           // grid size: this launch's tiles * splits
+  // a tail launch covers tiles tile0.. of the plan's grid, each with two
+  // tiles half as tall (this launch's instance; sub_m = 1), else tile0 = 0
+  int tile0, sub_m;
   int splits;
   int steps_per_split;
   int vec_store;       // y rows are 16-byte aligned and N % 8 == 0
@@ -104,9 +109,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   const int unit = xcd_unit(blockIdx.x, p.units);
   const int tile = unit / p.splits;
   const int split = unit - tile * p.splits;
-  const int mt = tile / p.tiles_n;
-  const int nt = tile - mt * p.tiles_n;
+  // this launch's tile `tile` is half r of the plan's tile w (the same tile
+  // when tile0 = 0 and sub_m = 0); a half wholly past M has nothing to do
+  const int w = p.tile0 + (tile >> p.sub_m);
+  const int wm = w / p.tiles_n;
+  const int mt = (wm << p.sub_m) + (tile & p.sub_m);
+  const int nt = w - wm * p.tiles_n;
   const int m0 = mt * BM;
+  if (m0 >= p.M) return;
   const int nw0 = nt * BN + wave * 32 * CB;  // first output feature of this wave
   const int s_begin = split * p.steps_per_split;
   const int s_end = min(p.nsteps, s_begin + p.steps_per_split);
@@ -710,6 +720,9 @@ bool wide_tall_tile_spills(int group, int dtype, bool asym) {
 // (Llama and Qwen shapes, fp16 and bf16, groups 32 and 128); M = 48 / 64
 // lower where K <= 16384; 28672 x 4096 keeps the 128-token tiles above
 // M = 32 (a tie at M = 48).
+// the second kernel of a tail launch: its start after the first one drains
+constexpr double kTailLaunchCycles = 4000.0;
+
 static GemmPlan plan_gemm_thin(int64_t M, int64_t N, int64_t K) {
   GemmPlan best{};
   double best_t = 0.0;
@@ -791,6 +804,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool a
           if (tp == 0 && splits > 1 && tiles > kMaxCounters) continue;
           if (best.units == 0 || c < best_cost * 0.98) {
             best_cost = c;
+            best = GemmPlan{};
             best.mb = mb;
             best.cb = cb;
             best.splits = splits;
@@ -799,6 +813,37 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool a
             best.tiles = (int)tiles;
             best.units = (int)units;
             best.two_pass = tp == 1;
+          }
+        }
+        // Tail launch: where the unsplit 256-token tiles end in a partial
+        // round, the tiles past the last full round run as a second launch of
+        // 128-token tiles, in one round; halves wholly past M cost nothing
+        // (4096 x 28672 at M = 1920: 896 tiles of 256 x 256 are 3.5 rounds, the
+        // last half of the CUs idle; as 3 rounds plus 144 tiles of 128 x 256
+        // it measured -5.6 %).  A tail k-step takes at least 0.8 of the plan
+        // tile's (its loads' round trip, not its MFMAs, sets the pace: measured
+        // 0.77-0.82 for 128 x 256 tails, 0.89 for 128 x 128 tails of 256 x 256
+        // tiles, which the planner therefore never picks).
+        if (mb == 8 && splits == 1 && units > cus && units % cus != 0) {
+          const int64_t full = units / cus * cus;
+          int64_t busy = 0;  // halves with output to compute
+          for (int64_t w = full; w < tiles; ++w) busy += (w / tiles_n) * bm + bm / 2 < M ? 2 : 1;
+          const double tstep = std::max(380.0 * cb * 4 + 1000.0, 0.8 * (380.0 * cb * mb + 1000.0));
+          const double tc = (double)(full / cus) * loop + (double)((busy + cus - 1) / cus) * nsteps * tstep +
+                            kTailLaunchCycles;
+          if (tc < best_cost * 0.98) {
+            best_cost = tc;
+            best = GemmPlan{};
+            best.mb = mb;
+            best.cb = cb;
+            best.splits = 1;
+            best.steps_per_split = sps;
+            best.tiles_n = (int)tiles_n;
+            best.tiles = (int)tiles;
+            best.units = (int)full;
+            best.tail_mb = 4;
+            best.tail_tile0 = (int)full;
+            best.tail_units = (int)(2 * (tiles - full));
           }
         }
       }
@@ -816,6 +861,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool a
       const int64_t tiles_n = (N + 128 * cb - 1) / (128 * cb);
       const int64_t tiles = ((M + 32 * mb - 1) / (32 * mb)) * tiles_n;
       if (splits == 1 || tp == 1 || tiles <= kMaxCounters) {
+        best = GemmPlan{};
         best.two_pass = splits > 1 && tp == 1;
         best.mb = mb;
         best.cb = cb;
@@ -866,6 +912,8 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
   prm.full_steps = (int)(a.K / kBK);
   prm.tiles_n = plan.tiles_n;
   prm.units = plan.units;
+  prm.tile0 = 0;
+  prm.sub_m = 0;
   prm.splits = plan.splits;
   prm.steps_per_split = plan.steps_per_split;
   prm.vec_store = (a.N % 8 == 0) && (reinterpret_cast<uintptr_t>(a.y) % 16 == 0);
@@ -879,6 +927,19 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
   else
     e = a.dtype == DT_F16 ? launch_g<DT_F16>(prm, a.group, plan.mb, plan.cb, stream)
                           : launch_g<DT_BF16>(prm, a.group, plan.mb, plan.cb, stream);
+  if (e == hipSuccess && plan.tail_units > 0) {
+    GemmParams t = prm;
+    t.units = plan.tail_units;
+    t.tile0 = plan.tail_tile0;
+    t.sub_m = 1;
+    if (2 * plan.tail_mb != plan.mb || plan.splits != 1) return hipErrorInvalidConfiguration;
+    if (a.dense)
+      e = a.dtype == DT_F16 ? launch_mb<DT_F16, 128, false, true>(t, plan.tail_mb, plan.cb, stream)
+                            : launch_mb<DT_BF16, 128, false, true>(t, plan.tail_mb, plan.cb, stream);
+    else
+      e = a.dtype == DT_F16 ? launch_g<DT_F16>(t, a.group, plan.tail_mb, plan.cb, stream)
+                            : launch_g<DT_BF16>(t, a.group, plan.tail_mb, plan.cb, stream);
+  }
   if (e != hipSuccess || !prm.two_pass) return e;
   const int64_t quads = (int64_t)prm.M * (prm.np / 4);
   const int blocks = (int)((quads + 255) / 256);

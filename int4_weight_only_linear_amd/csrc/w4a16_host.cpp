@@ -522,8 +522,13 @@ w4a16_status w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int
     r.tiles = g.tiles;
     r.waves = 4;
     r.two_pass = g.splits > 1 && g.two_pass;
-    r.launches = r.two_pass ? 2 : 1;
+    r.launches = (r.two_pass ? 2 : 1) + (g.tail_units > 0 ? 1 : 0);
     r.counter_tiles = g.splits > 1 && !g.two_pass ? g.tiles : 0;
+    if (g.tail_units > 0) {
+      r.tail_tile_tokens = 32 * g.tail_mb;
+      r.tail_tile_features = 128 * g.cb;
+      r.tail_tiles = g.tail_units;
+    }
   }
   r.workspace_bytes = workspace_for(M, N, K, gm.kgroup, dtype, has_zp != 0, p, cus);
   *out = r;

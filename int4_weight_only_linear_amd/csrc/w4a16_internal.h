@@ -158,6 +158,11 @@ struct GemmPlan {
   // K split summed by a second kernel from plain fp32 partials (small M,
   // many splits) instead of by the tile's last workgroup
   bool two_pass;
+  // tail launch (K unsplit): the tiles from tail_tile0 on, past the last
+  // full round of workgroups, run as a second launch of tiles half as tall
+  // (32 tail_mb tokens, two per tile) in one round; tail_units = 0: none.
+  // units is then tail_tile0, the first launch's grid.
+  int tail_mb, tail_tile0, tail_units;
 };
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int group, int dtype, bool asym, int cu_count,
                    bool dense = false);

@@ -284,6 +284,41 @@ def test_gemm_planner_skips_exactly_the_spilling_tiles():
     assert spilling == {(dt, g, a, mb, 2) for (dt, g, a) in excluded for mb in (6, 8)}
 
 
+def test_gemm_tail_launch_plans():
+    # Where K is not split and the 256-token tiles end in a partial round of
+    # workgroups, the planner may run the tiles past the last full round as a
+    # second launch of 128-token tiles (two per tile): the ones with output to
+    # compute fit in one round, and no workspace is needed.
+    cus = 256  # the planning CU count without a device, and MI355X's
+    seen = set()
+    for (K, N) in ((4096, 6144), (4096, 28672), (14336, 4096), (2560, 19456), (1024, 16512), (2048, 8264),
+                   (1024, 28672), (1024, 8264)):
+        for M in (128, 200, 520, 777, 1000, 1300, 1920, 2100, 4096):
+            for dt, g, asym in ((O.BF16, 128, True), (O.F16, 32, True), (O.BF16, 64, False)):
+                p = L.w4a16_plan(M, N, K, g, dt, asym, L.PATH_GEMM)
+                if not p["tail_tiles"]:
+                    assert p["tail_tile_tokens"] == 0 and p["tail_tile_features"] == 0, p
+                    continue
+                tt, tf = p["tail_tile_tokens"], p["tail_tile_features"]
+                sm, sn = 2, 1
+                assert (p["tile_tokens"], tt, tf) == (256, 128, p["tile_features"]), p
+                assert p["splits"] == 1 and not p["two_pass"] and p["launches"] == 2 and p["workspace_bytes"] == 0, p
+                full = p["tiles"] // cus * cus
+                assert p["tiles"] % cus and full >= cus, p
+                assert p["tail_tiles"] == (p["tiles"] - full) * sm * sn, p
+                tn = -(-N // p["tile_features"])
+                busy = sum(1 for w in range(full, p["tiles"]) for a in range(sm) for b in range(sn)
+                           if ((w // tn) * sm + a) * tt < M and ((w % tn) * sn + b) * tf < N)
+                assert 0 < busy <= cus, (M, N, K, p)
+                seen.add(tf)
+    assert seen == {128, 256}, seen
+    # the Llama-3.1-8B up-projection shape at M = 1920: 896 tiles of 256 x 256,
+    # the last 128 as 128 x 256 tiles (the half past M exits at once)
+    p = L.w4a16_plan(1920, 28672, 4096, 128, O.BF16, True, L.PATH_GEMM)
+    assert (p["tile_tokens"], p["tile_features"], p["tiles"]) == (256, 256, 896), p
+    assert (p["tail_tile_tokens"], p["tail_tile_features"], p["tail_tiles"]) == (128, 256, 256), p
+
+
 # ---- launch plans: the completion counters of one launch fit their region -----
 
 KMAXC = 64 * 1024 // 4  # completion counters in the workspace's counter region

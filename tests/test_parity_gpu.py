@@ -730,6 +730,42 @@ def test_gemm_planner_takes_thin_tiles_up_to_64_tokens():
         assert L.w4a16_plan(65, N, K, 128, O.BF16, True, GEMM)["tile_tokens"] >= 128
 
 
+# ---- GEMM tail launch: the tiles past the last full round as smaller tiles ------
+
+_TAIL_CASES = [
+    # M, N, K, g, dt, sym, bias: 256-token tiles, the tail in 128-token tiles
+    (1300, 28672, 1024, 128, O.BF16, False, True),   # 256 features, the last tiles' upper halves past M
+    (1300, 28672, 1024, 128, O.F16, True, False),    # the same in fp16, symmetric
+    (1000, 16512, 1024, 32, O.F16, False, True),     # 128 features, both halves of every tail tile
+    (1000, 8264, 2048, 32, O.F16, False, False),     # 128 features, N not a multiple of the tile
+    (2100, 8264, 1024, 32, O.F16, True, True),       # ragged M and N
+]
+
+
+@pytest.mark.parametrize("M,N,K,g,dt,sym,bias", _TAIL_CASES)
+def test_gemm_tail_launch(tuning_env, M, N, K, g, dt, sym, bias):
+    # every output against the oracle, and bit-identical to the same tiles
+    # run without the tail launch (each output's sums in the same order)
+    plan = L.w4a16_plan(M, N, K, g, dt, not sym, GEMM)
+    assert plan["tail_tiles"] > 0 and plan["launches"] == 2 and plan["workspace_bytes"] == 0, plan
+    c = make_case(M, N, K, g, dt, sym, bias, seed=("tail", M, N, K, g, dt, sym, bias))
+    d = DeviceCase(c)
+    y = d.run(GEMM)
+    assert_close(y, oracle_rows(c), dt, "GEMM with a tail launch")
+    tuning_env("W4A16_GEMM_TILE", f"{plan['tile_tokens'] // 32},1,0,{plan['tile_features'] // 128}")
+    assert L.w4a16_plan(M, N, K, g, dt, not sym, GEMM)["tail_tiles"] == 0
+    assert np.array_equal(d.run(GEMM), y), "tail launch differs from the same tiles without it"
+
+
+def test_dense_copy_with_tail_launch():
+    M, N, K, g = 1300, 28672, 1024, 128
+    assert L.w4a16_plan(M, N, K, g, O.BF16, True, GEMM)["tail_tiles"] > 0
+    c = make_case(M, N, K, g, O.BF16, False, True, seed=("densetail", M, N, K))
+    d = DeviceCase(c)
+    w = L.w4a16_dequant(d.wq, d.s, d.zp, group_size=g)
+    assert np.array_equal(device_to_bits(L.w4a16_linear_dense(d.x, w, d.bias)), d.run(GEMM))
+
+
 # ---- graph capture: every entry point replays to its eager result --------------
 
 def _graph_replays_match(run_eager, run_captured, reps=3):
@@ -761,6 +797,7 @@ def _graph_replays_match(run_eager, run_captured, reps=3):
     (2, 1048, 28672, 128, GEMV, None),       # decode, few-token instance with a K split
     (17, 264, 2048, 64, GEMM, "1,3,0,1"),    # GEMM 32-token tiles, last-workgroup hand-off
     (33, 520, 4096, 128, GEMM, "1,5,1,1"),   # GEMM 32-token tiles, two-pass split
+    (1300, 28672, 1024, 128, GEMM, None),    # GEMM with a tail launch (two kernels)
 ])
 def test_graph_capture_linear(tuning_env, M, N, K, g, path, tile):
     if tile:
@@ -812,6 +849,7 @@ CANARY8 = 0xA5
     (40, 13, 1152, 128, GEMM, "1,5,1,1", 7),   # GEMM 32-token tiles, two-pass, N not a multiple of 8
     (128, 264, 1216, 32, GEMM, "4,4,1", 64),   # GEMM, two-pass split
     (129, 13, 256, 64, GEMM, "4,2,1", 7),      # GEMM, two-pass, N not a multiple of 8
+    (1300, 28672, 1024, 128, GEMM, None, 3),   # GEMM with a tail launch, element stores
 ])
 def test_guard_bands_around_y_and_workspace(tuning_env, M, N, K, g, path, tile, ypad):
     if tile:
