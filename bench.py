@@ -628,7 +628,9 @@ def _csv_rows(path):
 
 def profile_layers(kind):
     """(K, N, M, expected Grid_Size_X of the layer's main kernel, work) per
-    layer of a --profile run; work = algorithmic bytes (decode) or flops."""
+    layer of a --profile run; work = algorithmic bytes (decode) or flops.
+    Prefill layers also carry their GEMM tile (mb, cb) and, for a plan with
+    a tail launch, the tail kernel's grid and tile."""
     import int4_weight_only_linear_amd as L
     shapes, M = (DECODE_LAYERS, 1) if kind == "decode" else (PREFILL_LAYERS, 1920)
     out = []
@@ -637,8 +639,42 @@ def profile_layers(kind):
         threads = 64 * p["waves"]
         units = p["tiles"] * (p["splits"] if kind == "prefill" else 1)
         work = decode_bytes(M, N, K, GROUP) if kind == "decode" else 2 * M * N * K
-        out.append(dict(K=K, N=N, M=M, grid=units * threads, plan=p, work=work))
+        l = dict(K=K, N=N, M=M, grid=units * threads, plan=p, work=work, tile=None, tail_grid=0, tail_tile=None)
+        if kind == "prefill":
+            l["tile"] = (p["tile_tokens"] // 32, p["tile_features"] // 128)
+            if p["tail_tiles"]:
+                # the first launch covers the tiles before the tail's (two tail tiles per tile)
+                l["grid"] = (p["tiles"] - p["tail_tiles"] // 2) * threads
+                l["tail_grid"] = p["tail_tiles"] * threads
+                l["tail_tile"] = (p["tail_tile_tokens"] // 32, p["tail_tile_features"] // 128)
+        out.append(l)
     return out
+
+
+def _gemm_tile(name):
+    """(mb, cb) of a demangled gemm_kernel name, else None."""
+    import re
+    m = re.search(r"gemm_kernel<\d+, \d+, \w+, (\d+), (\d+), \w+>", name)
+    return (int(m.group(1)), int(m.group(2))) if m else None
+
+
+def _layer_calls(l, disp):
+    """The calls of layer l among dispatch records (dicts with grid, tile,
+    start, end): one record per dispatch of its kernel, or, for a plan with a
+    tail launch, its first launch together with the next tail launch."""
+    def match(d, grid, tile):
+        return d["grid"] == grid and (tile is None or d["tile"] == tile)
+    main = sorted((d for d in disp if match(d, l["grid"], l["tile"])), key=lambda d: d["start"])
+    if not l["tail_grid"]:
+        return [[d] for d in main]
+    tails = sorted((d for d in disp if match(d, l["tail_grid"], l["tail_tile"])), key=lambda d: d["start"])
+    calls = []
+    for d in main:
+        t = next((t for t in tails if t["start"] >= d["end"]), None)
+        if t is not None:
+            tails.remove(t)
+            calls.append([d, t])
+    return calls
 
 
 def _kernel_short(name):
@@ -673,18 +709,29 @@ def summarize_trace(kind, d, steps, of_bench=False):
             "the first launch of each layer, outside the timed loop, included")
     lines = [f"Command (from /tmp, TMPDIR=/tmp, repository at $R):",
              "  " + cmd, "",
-             f"Per layer (End - Start of each dispatch of the layer's kernel; {what}):",
+             f"Per layer (End - Start of each dispatch of the layer's kernel; a call with a tail launch: its two "
+             f"kernels' End - Start added; {what}):",
              f"  layer (K,N)      M     kernel grid   launches  mean_ns    median_ns   {unit}(mean)  frac of {peak:g}"]
+    disp = [dict(grid=int(r["Grid_Size_X"]), tile=_gemm_tile(_kernel_short(r["Kernel_Name"])),
+                 start=int(r["Start_Timestamp"]), end=int(r["End_Timestamp"]), name=_kernel_short(r["Kernel_Name"]))
+            for r in rows if "splitk_reduce" not in r["Kernel_Name"]]
     means = []
     for l in layers:
-        ts = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows
-              if int(r["Grid_Size_X"]) == l["grid"] and "splitk_reduce" not in r["Kernel_Name"]]
-        names = {_kernel_short(r["Kernel_Name"]) for r in rows if int(r["Grid_Size_X"]) == l["grid"]}
+        calls = _layer_calls(l, disp)
+        # a call with a tail launch: its two kernels' durations added
+        ts = [sum(d["end"] - d["start"] for d in c) for c in calls]
+        names = {d["name"] for c in calls for d in c}
         mean = float(np.mean(ts)) if ts else float("nan")
         rate = l["work"] / mean if kind == "decode" else l["work"] / mean / 1e3
         means.append(mean)
         lines.append(f"  ({l['K']:5d},{l['N']:5d})  {l['M']:5d}  {l['grid']:10d}   {len(ts):8d}  {mean:9.0f}  "
                      f"{_median(ts):9.0f}   {rate:10.1f}  {rate / peak:.4f}   {' / '.join(sorted(names))}")
+        if l["tail_grid"] and calls:
+            first = [c[0]["end"] - c[0]["start"] for c in calls]
+            tail = [c[1]["end"] - c[1]["start"] for c in calls]
+            lines.append(f"      of which the first launch (grid {l['grid']}) mean {np.mean(first):.0f} ns, the tail "
+                         f"launch (grid {l['tail_grid']}) mean {np.mean(tail):.0f} ns; the layer's first call "
+                         f"{first[0]} + {tail[0]} ns")
     if kind == "decode":
         mb = float(np.mean([l["work"] for l in layers]))
         mm = float(np.mean(means))
@@ -714,20 +761,35 @@ def summarize_pmc(kind, dirs, steps):
         for r in _csv_rows(os.path.join(d, "run_counter_collection.csv")):
             if "w4a16" not in r["Kernel_Name"]:
                 continue
-            e = per.setdefault((tag, r["Dispatch_Id"]), dict(grid=int(r["Grid_Size"]),
-                                                             ns=int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            e = per.setdefault((tag, r["Dispatch_Id"]), dict(
+                grid=int(r["Grid_Size"]), tile=_gemm_tile(_kernel_short(r["Kernel_Name"])),
+                start=int(r["Start_Timestamp"]), end=int(r["End_Timestamp"]),
+                ns=int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
             e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+
+    def calls_of(tag, l):
+        # a call with a tail launch: both kernels' times and counters added
+        out = []
+        for c in _layer_calls(l, [e for (t, _), e in per.items() if t == tag]):
+            m = dict(c[0])
+            for e in c[1:]:
+                for k, v in e.items():
+                    if k not in ("grid", "tile", "start", "end"):
+                        m[k] = m.get(k, 0.0) + v
+            out.append(m)
+        return out
     lines = ["Commands (from /tmp, TMPDIR=/tmp, repository at $R), one counter set per run:"]
     for tag in dirs:
         lines.append("  " + PROFILE_CMDS["pmc"].format(kind=kind, steps=steps, tag=tag,
                                                          counters=" ".join(PMC_SETS[tag])))
     lines += ["", "Per layer (median over the layer's dispatches; counters summed over the device):"]
     for l in layers:
-        a = [e for (tag, _), e in per.items() if tag == "A" and e["grid"] == l["grid"]]
-        b = [e for (tag, _), e in per.items() if tag == "B" and e["grid"] == l["grid"]]
-        c = [e for (tag, _), e in per.items() if tag == "C" and e["grid"] == l["grid"]]
+        a, b, c = calls_of("A", l), calls_of("B", l), calls_of("C", l)
+        tail = (f", the last {l['plan']['tail_tiles'] // 2} as {l['plan']['tail_tiles']} "
+                f"{l['plan']['tail_tile_tokens']}x{l['plan']['tail_tile_features']} tiles in a tail launch "
+                f"(counters and times of the two kernels added)" if l["tail_grid"] else "")
         lines.append(f"  layer (K,N) = ({l['K']},{l['N']}), M = {l['M']}, plan {l['plan']['tile_tokens']}x"
-                     f"{l['plan']['tile_features']} tiles, {l['plan']['splits']} K range(s), {len(a)} dispatches")
+                     f"{l['plan']['tile_features']} tiles{tail}, {l['plan']['splits']} K range(s), {len(a)} calls")
         if a:
             ns = _median([e["ns"] for e in a])
             clk = _median([e["GRBM_GUI_ACTIVE"] / XCDS / e["ns"] for e in a])
