@@ -150,9 +150,10 @@ w4a16_status w4a16_check_args(const void* x, const int32_t* wq, const void* scal
  * page "[ROCm][Kernel] Add HybridW4A16LinearKernel: Triton prefill + HIP
  * skinny decode" (description) sends M <= 5 to its skinny decode kernel and
  * larger M to its prefill GEMM; that bound was tuned on RDNA.  Here it is
- * re-measured on MI355X: the decode kernel for M <= 8 always; when
- * 4096 < K <= 16384 for M <= 12 below 32 Mi weights (N * K); when K <= 4096
- * for M <= 16 below 20 Mi weights and M <= 9 above, except with N >= 14336
+ * re-measured on MI355X: the decode kernel for M <= 8, except M <= 6 when
+ * K > 16384 with 160 Mi weights (N * K) or more and groups of 64 or more; when
+ * 4096 < K <= 16384 for M <= 12 below 32 Mi weights; when K <= 4096 for
+ * M <= 16 below 20 Mi weights and M <= 9 above, except with N >= 14336
  * (M <= 8); the GEMM above.  Tuning overrides (environment, read
  * once; see w4a16_reload_tuning): W4A16_M_THRESHOLD=<m> moves the bound,
  * W4A16_FORCE_PATH=gemv|gemm forces one path. */

@@ -221,11 +221,13 @@ GroupMap group_map(int32_t g, int64_t K) {
 //   K <= 4096, smaller (4096 x 4096, 4096 x 2560, 2560 x 6144): decode
 //                           through M = 16.
 int64_t gemv_threshold(int64_t N, int64_t K, int32_t group, int32_t dtype, int32_t has_zp) {
-  (void)group; (void)dtype; (void)has_zp;
+  (void)dtype; (void)has_zp;
   const int v = w4a16::tuning().m_threshold;
   if (v >= 0 && v <= W4A16_GEMV_MAX_M) return v;
   const int64_t weights = N * K;
-  if (K > 16384) return 8;
+  // K > 16384: from 160 Mi weights on, with groups of 64 or more, the GEMM's
+  // 32-token tiles win from M = 7 (28672 x 8192: -7 to -26 % at M = 7 / 8)
+  if (K > 16384) return weights >= (int64_t(160) << 20) && group >= 64 ? 6 : 8;
   if (K > 4096) return weights >= (int64_t(32) << 20) ? 8 : 12;
   if (N >= 14336) return 8;
   return weights >= (int64_t(20) << 20) ? 9 : 16;

@@ -189,6 +189,11 @@ def test_select_path_by_m():
     for M in (9, 12, 16, 1920):
         assert sel(M, 4096, 14336) == L.PATH_GEMM
         assert sel(M, 4096, 28672) == L.PATH_GEMM
+    # K > 16384 from 160 Mi weights with groups of 64 or more: up to M = 6
+    for g in (64, 128):
+        assert sel(6, 8192, 28672, g) == L.PATH_GEMV and sel(7, 8192, 28672, g) == L.PATH_GEMM
+    assert sel(8, 8192, 28672, 32) == L.PATH_GEMV and sel(9, 8192, 28672, 32) == L.PATH_GEMM
+    assert sel(8, 5120, 20480) == L.PATH_GEMV  # 100 Mi weights
     for M in (17, 32, 65, 128, 1920):
         assert sel(M, 4096, 4096) == L.PATH_GEMM
 
