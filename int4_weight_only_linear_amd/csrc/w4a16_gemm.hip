@@ -66,7 +66,8 @@ struct GemmParams {
   int tiles_n;         // tiles per row of the plan's tile grid
   int units;           // grid size: this launch's tiles * splits
   // a tail launch covers tiles tile0.. of the plan's grid, each with two
-  // tiles half as tall (this launch's instance; sub_m = 1), else tile0 = 0
+  // tiles half as tall (this launch's instance; sub_m = 1); otherwise
+  // tile0 = 0 and sub_m = 0 (sub_m is a shift and a mask: 0 or 1 only)
   int tile0, sub_m;
   int splits;
   int steps_per_split;
@@ -919,6 +920,7 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
   prm.vec_store = (a.N % 8 == 0) && (reinterpret_cast<uintptr_t>(a.y) % 16 == 0);
   prm.two_pass = plan.splits > 1 && plan.two_pass;
   if (prm.two_pass && plan.mb != 1 && plan.mb != 4) return hipErrorInvalidConfiguration;
+  if (plan.tail_units > 0 && (2 * plan.tail_mb != plan.mb || plan.splits != 1)) return hipErrorInvalidConfiguration;
   prm.np = (int)((a.N + 7) / 8 * 8);
   hipError_t e;
   if (a.dense)
@@ -932,7 +934,6 @@ hipError_t launch_gemm(const LinearArgs& a, void* workspace, int cu_count, hipSt
     t.units = plan.tail_units;
     t.tile0 = plan.tail_tile0;
     t.sub_m = 1;
-    if (2 * plan.tail_mb != plan.mb || plan.splits != 1) return hipErrorInvalidConfiguration;
     if (a.dense)
       e = a.dtype == DT_F16 ? launch_mb<DT_F16, 128, false, true>(t, plan.tail_mb, plan.cb, stream)
                             : launch_mb<DT_BF16, 128, false, true>(t, plan.tail_mb, plan.cb, stream);
