@@ -393,6 +393,73 @@ def dense_comparator(players, stream, steps):
                 per_layer=rows)
 
 
+def vendor_dense(x, w, steps, stream, copies_bytes=1 << 30):
+    """torch's bf16 matmul (the vendor BLAS on this image) of x [M, K] with a
+    dequantised copy w [N, K] (transposed once to [K, N]), per call, graphs
+    rotating >= copies_bytes of copies: the dense comparator of the prefill
+    GEMM.  Returns microseconds per call."""
+    import torch
+    wt = w.t().contiguous()
+    pool = [wt] + [wt.clone() for _ in range(max(1, math.ceil(copies_bytes / (wt.numel() * 2))) - 1)]
+    y = torch.empty((x.shape[0], w.shape[0]), dtype=x.dtype, device=x.device)
+    with torch.cuda.stream(stream):
+        for ww in pool[:2]:  # its first calls set up the library (not allowed under graph capture)
+            torch.matmul(x, ww, out=y)
+    torch.cuda.synchronize()
+    ms = graph_launch_ms([lambda sp, ww=ww: torch.matmul(x, ww, out=y) for ww in pool], stream,
+                         passes=3, replays=2, reps=max(3, steps // 10))
+    del pool, wt, y
+    torch.cuda.empty_cache()
+    return ms * 1e3
+
+
+def run_vendor(path_prefix):
+    """The W4A16 prefill GEMM against torch's bf16 matmul (the vendor BLAS)
+    on the dequantised copy of the same weights, on the Llama prefill layers
+    at M = 128, 256 and 1920; both timed per call over graphs rotating
+    >= 1 GiB of weight copies.  Writes <prefix>.md and .json."""
+    import torch
+    import int4_weight_only_linear_amd as L
+    dev = torch.device("cuda:0")
+    side = torch.cuda.Stream()
+    rows = []
+    for (K, N) in PREFILL_LAYERS:
+        l = build_layer(K, N, 1920, ("vendor", K, N), dev)
+        wbytes = l["wq"].numel() * 4 + l["s"].numel() * 2 + l["zp"].numel() * 4
+        pool = [(l["wq"], l["zp"], l["s"])] + [(l["wq"].clone(), l["zp"].clone(), l["s"].clone())
+                                               for _ in range(max(2, math.ceil((1 << 30) / wbytes)) - 1)]
+        w = L.w4a16_dequant(l["wq"], l["s"], l["zp"], group_size=GROUP)
+        for M in (128, 256, 1920):
+            x = l["x"][:M].contiguous()
+            y = torch.empty((M, N), dtype=x.dtype, device=dev)
+            t_w4 = time_point(x, pool, None, y, M, N, K, GROUP, L.W4A16_BF16, L.PATH_GEMM, 20, side) * 1e3
+            t_v = vendor_dense(x, w, 30, side)
+            tf = lambda t: 2 * M * N * K / (t * 1e-6) / 1e12
+            p = L.w4a16_plan(M, N, K, GROUP, L.W4A16_BF16, True, L.PATH_GEMM)
+            rows.append(dict(K=K, N=N, M=M, w4a16_us=round(t_w4, 1), w4a16_tflops=round(tf(t_w4), 1),
+                             vendor_us=round(t_v, 1), vendor_tflops=round(tf(t_v), 1),
+                             speedup=round(t_v / t_w4, 2),
+                             plan=f"{p['tile_tokens']}x{p['tile_features']}, {p['splits']} K range(s)"
+                                  + (", two-pass" if p["two_pass"] else "") + (", tail launch" if p["tail_tiles"] else "")))
+            print(f"[vendor] {K}x{N} M={M}: {rows[-1]}", file=sys.stderr, flush=True)
+        del pool, w, l
+        torch.cuda.empty_cache()
+    with open(path_prefix + ".json", "w") as f:
+        json.dump(dict(rows=rows, torch=torch.__version__), f)
+    with open(path_prefix + ".md", "w") as f:
+        f.write("# W4A16 prefill GEMM against the vendor BLAS on a dequantised copy (Llama-3.1-8B-shaped layers, bf16)\n\n")
+        f.write(f"Command: python bench.py --vendor {os.path.basename(path_prefix)}\n\n")
+        f.write("Both per call, from HIP events around graphs rotating >= 1 GiB of weight copies: the W4A16 GEMM on the\n"
+                "packed weights (asym uint4, g128), and torch.matmul (torch " + torch.__version__ + ", bf16, the image's\n"
+                "vendor BLAS) on the same weights dequantised once to bf16 and transposed to [K, N] (4x the packed bytes).\n\n")
+        f.write("| K | N | M | W4A16 plan | W4A16 us | TFLOP/s | vendor dense us | TFLOP/s | W4A16 speedup |\n")
+        f.write("|---|---|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| {r['K']} | {r['N']} | {r['M']} | {r['plan']} | {r['w4a16_us']} | {r['w4a16_tflops']} | "
+                    f"{r['vendor_us']} | {r['vendor_tflops']} | {r['speedup']} |\n")
+    print(json.dumps(dict(vendor=path_prefix + ".md", points=len(rows))), flush=True)
+
+
 MOE_LAYERS = (("gate_up", 1536, 2048, False), ("down", 2048, 768, True))  # (name, N, K, x per slot)
 MOE_EXPERTS, MOE_TOPK = 128, 8
 
@@ -1069,6 +1136,10 @@ def main():
                     help="instead of the bench line: time one GPU's share of each Llama-3.1-8B layer under "
                          "P = 1, 2, 4, 8-way tensor parallelism (decode M=1, prefill M=1920), write "
                          "<PREFIX>.md and .json")
+    ap.add_argument("--vendor", default="", metavar="PREFIX",
+                    help="instead of the bench line: the prefill GEMM against torch's bf16 matmul (vendor BLAS) "
+                         "on a dequantised copy, Llama prefill layers at M = 128, 256, 1920; write <PREFIX>.md "
+                         "and .json")
     ap.add_argument("--report", default="",
                     help="instead of the bench line: time every point of the decode, prefill and "
                          "dispatch-sweep workloads on both paths, write <REPORT>.md and .json")
@@ -1113,6 +1184,9 @@ def main():
         return
     if args.shards:
         run_shards(args.shards)
+        return
+    if args.vendor:
+        run_vendor(args.vendor)
         return
     if args.calibration_copy_mb:
         # a plain copy of known size: reads and writes exactly n bytes, so the
@@ -1223,6 +1297,16 @@ def main():
         prefill["measured_ceiling"] = dict(mc, frac_of_measured=round(tflops / mc["best"], 4))
         if not args.no_dense:
             prefill["dequantised_copy"] = dense_comparator(players, side, args.prefill_steps)
+            vrows = []
+            for l in players:
+                w = L.w4a16_dequant(l["wq"], l["s"], l["zp"], group_size=GROUP)
+                t = vendor_dense(l["x"], w, args.prefill_steps, side)
+                vrows.append(dict(K=l["K"], N=l["N"], us=round(t, 2),
+                                  tflops=round(2 * l["M"] * l["N"] * l["K"] / (t * 1e-6) / 1e12, 1)))
+                del w
+            prefill["vendor_dense"] = dict(what="torch.matmul (bf16, the vendor BLAS) on the dequantised copy, "
+                                                "transposed to [K, N], graphs rotating >= 1 GiB of copies",
+                                           per_layer=vrows)
         del players, plaunch
 
     moe = None
