@@ -52,3 +52,23 @@ def test_perf_compare_normalises_by_the_control():
     res = {r["point"]: r for r in bench.perf_compare(base, now)}
     assert res["llama8b_prefill 4096x6144 M=1920"]["regressed"]
     assert res["llama8b_prefill 4096x6144 M=1920"]["control"] == "mfma"
+
+
+def test_prefill_profiles_pair_each_first_launch_with_its_tail():
+    # The 4096 x 28672 prefill layer at M = 1920 runs as a first launch plus
+    # a tail launch whose grid equals the 14336 x 4096 layer's: the summaries
+    # must tell them apart by their tiles and add the two kernels of a call.
+    layers = bench.profile_layers("prefill")
+    big = next(l for l in layers if (l["K"], l["N"]) == (4096, 28672))
+    other = next(l for l in layers if (l["K"], l["N"]) == (14336, 4096))
+    assert big["tail_grid"] and big["tail_tile"] == (4, 2) and big["tile"] == (8, 2)
+    assert big["tail_grid"] == other["grid"] and other["tile"] == (8, 2) and not other["tail_grid"]
+    d = lambda grid, tile, t0, t1: dict(grid=grid, tile=tile, start=t0, end=t1)
+    disp = [d(big["grid"], (8, 2), 0, 300), d(big["tail_grid"], (4, 2), 300, 370),
+            d(other["grid"], (8, 2), 400, 600),
+            d(big["grid"], (8, 2), 700, 1010), d(big["tail_grid"], (4, 2), 1010, 1085)]
+    calls = bench._layer_calls(big, disp)
+    assert [sum(x["end"] - x["start"] for x in c) for c in calls] == [370, 385]
+    assert [len(c) for c in bench._layer_calls(other, disp)] == [1]
+    assert bench._gemm_tile("gemm_kernel<1, 128, true, 4, 2, false>") == (4, 2)
+    assert bench._gemm_tile("gemv_one_kernel<1, 128, true, 8, 1, false, 0>") is None
