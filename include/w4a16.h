@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 3
+#define W4A16_ABI_VERSION 4
 
 typedef enum w4a16_status {
   W4A16_OK = 0,

@@ -22,7 +22,7 @@ W4A16_F16 = 0
 W4A16_BF16 = 1
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 GEMV_MAX_M = 16
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STATUS_NAMES = {
     0: "W4A16_OK", 1: "W4A16_ERR_INVALID_ARG", 2: "W4A16_ERR_UNSUPPORTED",

@@ -355,9 +355,8 @@ def test_gemm_operands_are_the_dequantised_weights(dt, sym, g):
     assert np.array_equal(nz(y), nz(W.T))
 
 
-@pytest.mark.parametrize("path", [GEMV, GEMM])
+@pytest.mark.parametrize("path,few", [(GEMV, True), (GEMV, False), (GEMM, True)])  # few: decode kernels only
 @pytest.mark.parametrize("dt", [O.F16, O.BF16])
-@pytest.mark.parametrize("few", [True, False])
 def test_all_eights_symmetric_gives_bias(tuning_env, path, dt, few):
     # every weight is (8 - 8) * s = +0.  The GEMM multiplies those zeros, and
     # the general decode kernel's fp16 path multiplies q - z = 0: both give the
@@ -366,8 +365,6 @@ def test_all_eights_symmetric_gives_bias(tuning_env, path, dt, few):
     # in fp32, so they leave a residue of the order of fp32 round-off of those
     # sums, proportional to the magic offset (128 for bf16, 1024 for fp16):
     # 1e-4 absolute at 128.
-    if path == GEMM and not few:
-        pytest.skip("the decode kernels only")
     if not few:
         tuning_env("W4A16_GEMV_NO_ONE", "1")
     kernel = L.w4a16_plan(4, 64, 512, 64, dt, False, path)["kernel"]
