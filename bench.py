@@ -647,7 +647,7 @@ def run_report(path_prefix):
         json.dump(dict(rows=rows, mstar=mstar), f)
     with open(path_prefix + ".md", "w") as f:
         f.write("# W4A16 linear on MI355X: every decode, prefill and crossover-sweep point on both kernels\n\n")
-        f.write(f"Command: python bench.py --report {path_prefix}\n\n")
+        f.write(f"Command: python bench.py --report {os.path.basename(path_prefix)}\n\n")
         f.write("Each point: mean time per launch over a HIP graph of back-to-back launches that rotate\n"
                 "through >= 1 GiB of weight copies (weights stream from HBM).  GB/s = algorithmic bytes\n"
                 "(weights, scales, zp, x, y, bias) / time; TFLOP/s = 2*M*N*K / time; peaks 8 TB/s and\n"
@@ -675,14 +675,15 @@ def run_report(path_prefix):
 
 # ---- rocprofv3 summaries (profiles/) ------------------------------------------
 
+# $R: the repository; $OUT: any directory for the profiler's CSV output
 PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{kind}_trace -o run -- "
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/{kind}_trace -o run -- "
              "python3 $R/bench.py --profile {kind} --steps {steps}",
-    "bench-trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/bench_trace -o run -- "
+    "bench-trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/bench_trace -o run -- "
                    "python3 $R/bench.py",
-    "pmc": "rocprofv3 --pmc {counters} --output-format csv -d $R/gpurun_out/{kind}_pmc{tag} -o run -- "
+    "pmc": "rocprofv3 --pmc {counters} --output-format csv -d $OUT/{kind}_pmc{tag} -o run -- "
            "python3 $R/bench.py --profile {kind} --steps {steps}",
-    "traffic": "rocprofv3 --pmc {counter} --output-format csv -d $R/gpurun_out/{kind}_{counter} -o run -- "
+    "traffic": "rocprofv3 --pmc {counter} --output-format csv -d $OUT/{kind}_{counter} -o run -- "
                "python3 $R/bench.py --profile {kind} --steps {steps} --calibration-copy-mb 256",
 }
 
@@ -774,7 +775,7 @@ def summarize_trace(kind, d, steps, of_bench=False):
     what = ("every dispatch of the layer's kernel in the bench run: warmup, timed graphs and the per-launch "
             "timing graphs" if of_bench else
             "the first launch of each layer, outside the timed loop, included")
-    lines = [f"Command (from /tmp, TMPDIR=/tmp, repository at $R):",
+    lines = [f"Command (from /tmp, TMPDIR=/tmp, repository at $R, CSV output under $OUT):",
              "  " + cmd, "",
              f"Per layer (End - Start of each dispatch of the layer's kernel; a call with a tail launch: its two "
              f"kernels' End - Start added; {what}):",
@@ -845,7 +846,7 @@ def summarize_pmc(kind, dirs, steps):
                         m[k] = m.get(k, 0.0) + v
             out.append(m)
         return out
-    lines = ["Commands (from /tmp, TMPDIR=/tmp, repository at $R), one counter set per run:"]
+    lines = ["Commands (from /tmp, TMPDIR=/tmp, repository at $R, CSV output under $OUT), one counter set per run:"]
     for tag in dirs:
         lines.append("  " + PROFILE_CMDS["pmc"].format(kind=kind, steps=steps, tag=tag,
                                                          counters=" ".join(PMC_SETS[tag])))
@@ -904,7 +905,7 @@ def summarize_traffic(kind, fetch_dir, write_dir, steps, copy_mb=256):
                if "bitwise_not" in r["Kernel_Name"] or "BitwiseNot" in r["Kernel_Name"]]
         scale = (copy_mb * 1024) / _median(cal)
         out[counter] = dict(scale=scale, cal=_median(cal), rows=rows)
-    lines = ["Commands (from /tmp, TMPDIR=/tmp, repository at $R), one counter per run:"]
+    lines = ["Commands (from /tmp, TMPDIR=/tmp, repository at $R, CSV output under $OUT), one counter per run:"]
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         lines.append("  " + PROFILE_CMDS["traffic"].format(kind=kind, steps=steps, counter=counter))
     lines += ["", f"Calibration (torch bitwise_not: one elementwise kernel reading and writing {copy_mb} MiB):"]
