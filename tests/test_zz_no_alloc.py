@@ -57,6 +57,8 @@ PAIRS = [
     ((1, 4096, 4096, 128, O.BF16, False, False), (5, 40, 9728, 64, O.BF16, False, True)),
     # the GEMM's 32-token tiles with a K split, then a smaller one
     ((40, 4096, 14336, 128, O.BF16, False, True), (17, 264, 2048, 64, O.F16, True, False)),
+    # a GEMM plan with a tail launch (two kernels, no scratch), then a split decode
+    ((1300, 28672, 1024, 128, O.BF16, False, True), (5, 40, 9728, 64, O.BF16, False, True)),
 ]
 
 
