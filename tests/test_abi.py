@@ -495,3 +495,47 @@ def test_ceilings_library_exports_its_header_and_checks_arguments():
     assert C.lib.w4a16c_decode_loads(P, 16 * 8 * K, 16, K, 8 * K, 4, 4, P, None) == 1      # waves * kpw < K/128
     assert C.lib.w4a16c_decode_loads(P, 16 * 8 * K, 16, K, 8 * K, 8, 17, P, None) == 1     # more than 16 waves
     assert C.lib.w4a16c_mfma_loop(0, 10, 1, P, None) == 1
+
+
+def test_gemm_plans_hold_their_invariants_on_random_shapes():
+    # Any GEMM plan: its tiles cover M x N exactly once; K ranges of whole
+    # 128-k steps with none empty; a tail launch only for unsplit 256-token
+    # tiles past whole rounds, in one round of 128-token tiles; the workspace
+    # is the counter region plus the plan's fp32 partials, nothing without a
+    # split; and the counters of a one-pass split fit their region.
+    hyp = pytest.importorskip("hypothesis")
+    st = pytest.importorskip("hypothesis.strategies")
+    kinds = set()
+
+    @hyp.settings(max_examples=400, deadline=None, derandomize=True)
+    @hyp.given(M=st.integers(9, 8192), N=st.integers(1, 40000).map(lambda n: 8 * n),
+               ksteps=st.integers(1, 160), g=st.sampled_from([32, 64, 128]), dt=st.sampled_from([O.F16, O.BF16]),
+               zp=st.booleans())
+    def check(M, N, ksteps, g, dt, zp):
+        K = 128 * ksteps
+        p = L.w4a16_plan(M, N, K, g, dt, zp, L.PATH_GEMM)
+        bm, bn = p["tile_tokens"], p["tile_features"]
+        assert bm in (32, 128, 192, 256) and bn in (128, 256), p
+        assert p["tiles"] == -(-M // bm) * -(-N // bn), p
+        s = p["splits"]
+        assert 1 <= s <= ksteps, p
+        sps = -(-ksteps // s)
+        assert -(-ksteps // sps) == s, p  # every K range holds steps
+        if p["tail_tiles"]:
+            full = p["tiles"] // 256 * 256
+            assert bm == 256 and s == 1 and not p["two_pass"] and p["launches"] == 2, p
+            assert (p["tail_tile_tokens"], p["tail_tile_features"]) == (128, bn), p
+            assert full >= 256 and p["tiles"] > full and p["tail_tiles"] == 2 * (p["tiles"] - full), p
+        ws = p["workspace_bytes"]
+        if s == 1:
+            assert ws == 0 and p["launches"] == (2 if p["tail_tiles"] else 1), p
+        elif p["two_pass"]:
+            assert ws == KMAXC * 4 + s * M * (-(-N // 8) * 8) * 4 and p["launches"] == 2, p
+        else:
+            assert p["tiles"] <= KMAXC and p["counter_tiles"] == p["tiles"], p
+            assert ws == KMAXC * 4 + p["tiles"] * s * bm * bn * 4, p
+        assert ws == L.w4a16_workspace_size(M, N, K, g, dt, zp, L.PATH_GEMM)
+        kinds.add("tail" if p["tail_tiles"] else "unsplit" if s == 1 else "two-pass" if p["two_pass"] else "one-pass")
+
+    check()
+    assert kinds == {"tail", "unsplit", "two-pass", "one-pass"}, kinds
