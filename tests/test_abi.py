@@ -539,3 +539,49 @@ def test_gemm_plans_hold_their_invariants_on_random_shapes():
 
     check()
     assert kinds == {"tail", "unsplit", "two-pass", "one-pass"}, kinds
+
+
+def test_decode_plans_hold_their_invariants_on_random_shapes():
+    # Any decode plan (M <= 16): one workgroup per 16-row tile per K range; at
+    # most 16 waves; the few-token instance only for M <= 8 with K a whole
+    # number of 128-k steps, its K ranges covering K with none empty; split
+    # tiles keep their counters in the region (several launches beyond it);
+    # a workspace exactly when some K is split, sized for the larger split.
+    hyp = pytest.importorskip("hypothesis")
+    st = pytest.importorskip("hypothesis.strategies")
+    kinds = set()
+
+    @hyp.settings(max_examples=400, deadline=None, derandomize=True)
+    @hyp.given(M=st.integers(1, 16), N=st.integers(1, 20000).map(lambda n: 8 * n),
+               kg=st.integers(1, 400), g=st.sampled_from([32, 64, 128]), dt=st.sampled_from([O.F16, O.BF16]),
+               zp=st.booleans())
+    def check(M, N, kg, g, dt, zp):
+        K = g * kg
+        p = L.w4a16_plan(M, N, K, g, dt, zp, L.PATH_GEMV)
+        assert p["path"] == L.PATH_GEMV and p["tiles"] == -(-N // 16), p
+        assert 1 <= p["waves"] <= 16 and p["splits"] >= 1, p
+        ksteps = -(-K // 128)
+        s, w = p["splits"], p["waves"]
+        if p["kernel"] == 1:
+            assert M <= 8 and K % 128 == 0 and p["launches"] == 1, p
+            # K ranges of w runs of 4 or 8 k-steps cover K, the last range not empty
+            assert any((s - 1) * w * kpw < ksteps <= s * w * kpw for kpw in (4, 8)), p
+            assert s == 1 or p["tiles"] <= KMAXC, p
+        else:
+            # K ranges of ceil(ksteps / s) steps, each in w runs of 1-8 steps
+            kps = -(-ksteps // s)
+            assert s <= ksteps and -(-ksteps // kps) == s, p
+            assert any(-(-kps // kpw) == w for kpw in (1, 2, 4, 8)), p
+            if s > 1:
+                assert p["launches"] == -(-p["tiles"] // KMAXC), p
+        assert p["counter_tiles"] <= KMAXC, p
+        ws = p["workspace_bytes"]
+        if ws == 0:
+            assert s == 1 and p["counter_tiles"] == 0, p
+        if s > 1:
+            assert ws >= KMAXC * 4 + s * M * N * 4, p
+        assert ws == L.w4a16_workspace_size(M, N, K, g, dt, zp, L.PATH_GEMV)
+        kinds.add((p["kernel"], p["splits"] > 1))
+
+    check()
+    assert kinds == {(0, False), (0, True), (1, False), (1, True)}, kinds
