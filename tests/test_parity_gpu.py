@@ -727,6 +727,31 @@ def test_gemm_planner_takes_thin_tiles_up_to_64_tokens():
         assert L.w4a16_plan(65, N, K, 128, O.BF16, True, GEMM)["tile_tokens"] >= 128
 
 
+# ---- random shapes through the automatic path ----------------------------------
+
+def _random_shape(i):
+    # seeded per index: decode and GEMM sizes, ragged N (multiples of 8 with
+    # zero points, any N without), K a multiple of the group (often of 128),
+    # every group, dtype, quantisation and bias
+    r = np.random.default_rng(stream_seed(("random-shape", i)))
+    g = int(r.choice([32, 64, 128]))
+    sym = bool(r.integers(2))
+    M = int(r.integers(1, 17)) if r.random() < 0.5 else int(r.integers(17, 400))
+    N = int(r.integers(1, 260)) * 8 - (int(r.integers(0, 8)) if sym else 0)
+    K = g * int(r.integers(1, 4096 // g + 1))
+    if r.random() < 0.5:
+        K = max(128, K // 128 * 128)
+    return M, max(N, 1), K, g, int(r.choice([O.F16, O.BF16])), sym, bool(r.integers(2))
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_shapes_match_the_oracle(i):
+    M, N, K, g, dt, sym, bias = _random_shape(i)
+    c = make_case(M, N, K, g, dt, sym, bias, seed=("random", i))
+    y = DeviceCase(c).run(L.PATH_AUTO)
+    assert_close(y, oracle_rows(c), dt, f"shape {(M, N, K, g, dt, sym, bias)}")
+
+
 # ---- GEMM tail launch: the tiles past the last full round as smaller tiles ------
 
 _TAIL_CASES = [
