@@ -752,6 +752,26 @@ def test_random_shapes_match_the_oracle(i):
     assert_close(y, oracle_rows(c), dt, f"shape {(M, N, K, g, dt, sym, bias)}")
 
 
+def _random_large_shape(i):
+    # seeded per index: prefill sizes whose plans take the tall and wide tiles,
+    # K splits and tail launches
+    r = np.random.default_rng(stream_seed(("random-large-shape", i)))
+    g = int(r.choice([32, 64, 128]))
+    M = int(r.integers(400, 2049))
+    N = int(r.integers(256, 2049)) * 8
+    K = g * int(r.integers(128 // g, 8192 // g + 1))
+    return M, N, K, g, int(r.choice([O.F16, O.BF16])), bool(r.integers(2)), bool(r.integers(2))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_large_shapes_match_the_oracle_on_sampled_rows(i):
+    M, N, K, g, dt, sym, bias = _random_large_shape(i)
+    c = make_case(M, N, K, g, dt, sym, bias, seed=("random-large", i))
+    y = DeviceCase(c).run(L.PATH_AUTO)
+    rows = sample_rows(N, seed=i, blocks=6)
+    assert_close(y[:, rows], oracle_rows(c, rows), dt, f"shape {(M, N, K, g, dt, sym, bias)}")
+
+
 # ---- GEMM tail launch: the tiles past the last full round as smaller tiles ------
 
 _TAIL_CASES = [
